@@ -1,0 +1,29 @@
+"""Plain, slow CPU oracle for MXFP4 block quantization and the MXFP4-weight x BF16-activation MoE layer.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import anything from this package.  The product path (``mixed_precision_moe_amd``)
+never imports it, and this package never imports the product path: the two share no code.
+
+Floating point is evaluated in float64 unless a page fixes the precision.  Each function cites the
+passage it follows.  Page tags used throughout:
+
+* [P1] prhub summary of vLLM PR #46915 (weight/scale interleave fix in the SM90 MXFP4 fused-MoE test).
+* [P2] prhub report of vLLM PR #51038, "[Bugfix][Quantization] Fix MXFP4 conversion for FlashInfer
+  CUTLASS" (the checkpoint-to-kernel weight conversion, the [w1; w3] -> [w3; w1] swap, bias -> bf16).
+* [P3] prhub summary of vLLM PR #43557 (the E8M0 scale fix in the MXFP4 MoE CUTLASS kernel: the 0.75
+  round-up rule, the tiled scale layout and the Python reference helpers).
+* [NS] the workload specification this library is built to (OCP-MX MXFP4: 32-element blocks, E2M1
+  round-to-nearest-even saturating at +-6, two nibbles per byte; top-k routing, SwiGLU defined as
+  silu(w1 half) * (w3 half), grouped GEMMs and a weighted combine; tolerance
+  |y - y_ref| <= 2e-2 * rms(y_ref) + 1e-3).
+
+Readings of points the pages leave open are stated where they are used and collected in the design doc.
+
+Parity status:  every function here is pinned by a ``-m "not gpu"`` test against something other than
+itself (hand values, closed forms, brute force, textbook cases or an independent library routine),
+except the two layout conventions the pages never state -- the nibble order inside a byte and the
+sign kept on codes that round to zero.  Those two are "parity unpinned" with respect to the pages:
+they are fixed by this library's ABI and tested only for internal consistency.
+"""
+
+from . import quant, convert, route, moe  # noqa: F401

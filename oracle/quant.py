@@ -1,0 +1,157 @@
+"""Oracle: OCP-MX MXFP4 block quantization, dequantization and the tiled scale layout.
+
+Test infrastructure only (see the package docstring).  Pure NumPy; exact arithmetic:
+bf16 inputs are widened exactly, the scaled magnitude |x| * 2**(127 - e) is an exact float64 product,
+and every rounding decision is a comparison against exact midpoints.
+"""
+
+import numpy as np
+
+BLOCK = 32
+"""Elements per scale block along K.  [P3 Key source snippets, test_mxfp4_moe.py: the untile helper
+divides K by the MXFP4 block size of 32]  [NS: 32-element blocks]"""
+
+E2M1_MAGNITUDES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+"""Magnitude of each 3-bit E2M1 code (OCP-MX FP4: 1 sign, 2 exponent, 1 mantissa bit, bias 1).
+The largest magnitude 6.0 is the one [P3 Motivation] compares max/scale against."""
+
+
+def bf16_to_f64(bits):
+    """Exact value of bf16 bit patterns (uint16) as float64: the pattern is the top half of a binary32."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def e8m0_from_amax(amax):
+    """E8M0 scale byte for blocks whose largest magnitude is ``amax`` (binary32 values).
+
+    [P3 Implementation breakdown, item 1; Key source snippets: compute_reference_e8m0_scale in
+    test_mxfp4_moe.py and the UE8M0_SF branch of cvt_warp_fp16_to_fp4 in nvfp4_utils.cuh, which state
+    the same rule twice]:
+      * a block maximum that is not positive gives 0;
+      * otherwise take the binary32 bit pattern of the maximum, add 2**21 so that a significand of
+        1.75 or more carries into the next binade, keep only sign and exponent (mask 0xFF800000) and
+        read the biased exponent B from bits 23..30;
+      * the scale exponent is B - 2, floored at 0 and capped at 254.
+    """
+    a = np.asarray(amax, dtype=np.float32)
+    bits = a.view(np.uint32).astype(np.uint64)
+    rounded = (bits + np.uint64(1 << 21)) & np.uint64(0xFF800000)
+    biased = ((rounded >> np.uint64(23)) & np.uint64(0xFF)).astype(np.int64)
+    e = np.minimum(np.maximum(biased - 2, 0), 254)
+    return np.where(a > 0, e, 0).astype(np.uint8)
+
+
+def e2m1_magnitude_code(v):
+    """E2M1 magnitude code of v >= 0 (float64), round to nearest, ties to the even code, saturating.
+
+    [NS: E2M1 elements, round-to-nearest-even, saturating at +-6]  The representable magnitudes are
+    E2M1_MAGNITUDES; the midpoints between neighbours are 0.25, 0.75, 1.25, 1.75, 2.5, 3.5 and 5.
+    On a midpoint the neighbour with the even code wins (0.25 -> 0, 0.75 -> 1.0, 1.25 -> 1.0,
+    1.75 -> 2.0, 2.5 -> 2.0, 3.5 -> 4.0, 5 -> 4.0), and anything above 5 becomes 6.0 (code 7).
+    """
+    v = np.asarray(v, dtype=np.float64)
+    c = (v > 0.25).astype(np.uint8)
+    c += v >= 0.75
+    c += v > 1.25
+    c += v >= 1.75
+    c += v > 2.5
+    c += v >= 3.5
+    c += v > 5.0
+    return c
+
+
+def quantize_ref(x_bits):
+    """MXFP4 quantization of a bf16 matrix.
+
+    x_bits: uint16 [M, K] bf16 bit patterns, K a multiple of 32.
+    Returns (q, scales): q uint8 [M, K/2] packed E2M1 codes, scales uint8 [M, K/32] E8M0 bytes.
+
+    Steps for every 32-element block along K:
+      1. amax = max |x| over the block (the pages reduce the block with a max over the lanes' values;
+         reading: the maximum of magnitudes, as the not-positive branch of the reference implies)
+         [P3 Key source snippets].
+      2. e = e8m0_from_amax(amax).
+      3. v = |x| * 2**(127 - e), exact in float64; magnitude code by e2m1_magnitude_code [NS].
+      4. sign bit 0x8 set when the input's sign bit is set, also when the magnitude code is 0
+         (reading: the sign is kept; the pages are silent).
+      5. two codes per byte, element 2j in the low nibble and 2j+1 in the high nibble
+         (reading: the pages only say "packed 4-bit" [P1 Implementation breakdown] and keep K/2 as the
+         last dimension [P2 Key source snippets, the conversion test's w13 of shape [1, 4, 4]]).
+    """
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    M, K = x_bits.shape
+    if K % BLOCK:
+        raise ValueError("K must be a multiple of 32")
+    blocks = x_bits.reshape(M, K // BLOCK, BLOCK)
+    mag = bf16_to_f64(blocks & np.uint16(0x7FFF))
+    amax = mag.max(axis=-1)  # a bf16 value, so its binary32 form is exact
+    e = e8m0_from_amax(amax.astype(np.float32))
+    v = mag * np.ldexp(1.0, 127 - e.astype(np.int64))[..., None]
+    code = e2m1_magnitude_code(v)
+    code |= ((blocks >> np.uint16(15)).astype(np.uint8) << np.uint8(3))
+    code = code.reshape(M, K)
+    q = (code[:, 0::2] | (code[:, 1::2] << np.uint8(4))).astype(np.uint8)
+    return q, e
+
+
+def unpack_codes(q):
+    """Inverse of the nibble packing of quantize_ref: uint8 [..., K/2] -> uint8 codes [..., K]."""
+    q = np.asarray(q, dtype=np.uint8)
+    out = np.empty(q.shape[:-1] + (q.shape[-1] * 2,), dtype=np.uint8)
+    out[..., 0::2] = q & np.uint8(0xF)
+    out[..., 1::2] = q >> np.uint8(4)
+    return out
+
+
+def dequant_ref(q, scales):
+    """x_hat = (-1)**s * E2M1_MAGNITUDES[code & 7] * 2**(e - 127), float64.
+
+    [P3 Key source snippets: the kernel rebuilds the scale from the E8M0 byte as 2**(e - 127); the
+    pages' test checks the reconstruction error]  Reading: 2**(e - 127) for every e including 0
+    (the kernel snippet's bit-shift rebuild would give +0.0 for e = 0; the two differ only for blocks
+    whose maximum is below about 2**-124).
+    q: uint8 [..., K/2], scales: uint8 [..., K/32].
+    """
+    codes = unpack_codes(q)
+    mag = E2M1_MAGNITUDES[codes & 7]
+    sign = np.where(codes & 8, -1.0, 1.0)
+    s = np.ldexp(1.0, np.asarray(scales, dtype=np.int64) - 127)
+    s = np.repeat(s, BLOCK, axis=-1)
+    return sign * mag * s
+
+
+def tiled_scale_shape(M, K):
+    """[mTiles, kTiles, 32, 4, 4] for an [M, K] matrix: 128 rows by 4 scale columns per 512-byte tile.
+    [P3 Key source snippets, untile_cutlass_scale]"""
+    sk = K // BLOCK
+    return ((M + 127) // 128, (sk + 3) // 4, 32, 4, 4)
+
+
+def tile_scales(flat):
+    """Flat E8M0 scales [M, SK] -> tiled uint8 [mTiles, kTiles, 32, 4, 4].
+
+    The byte at tiled[mT, kT, oM, iM, iK] is flat[mT*128 + iM*32 + oM, kT*4 + iK]; padding rows
+    (>= M) and padding columns (>= SK) hold 0 (reading: the pages only read the first
+    padded_M*padded_SK bytes back).  This is the layout whose inverse the pages give as a permute of
+    axes (0, 3, 2, 1, 4) followed by a reshape to (padded_M, padded_SK).  [P3 Key source snippets,
+    untile_cutlass_scale]
+    """
+    flat = np.asarray(flat, dtype=np.uint8)
+    M, SK = flat.shape
+    mt, kt = (M + 127) // 128, (SK + 3) // 4
+    out = np.zeros((mt, kt, 32, 4, 4), dtype=np.uint8)
+    r, c = np.indices((M, SK))
+    out[r // 128, c // 4, r % 32, (r % 128) // 32, c % 4] = flat
+    return out
+
+
+def untile_scales(tiled, rows, K):
+    """Tiled scale bytes -> flat [rows, K/32], following the pages' inverse: view the first
+    padded_M*padded_SK bytes as [mTiles, kTiles, 32, 4, 4], permute axes (0, 3, 2, 1, 4), reshape to
+    (padded_M, padded_SK) and crop.  [P3 Key source snippets, untile_cutlass_scale]"""
+    sk = K // BLOCK
+    mt, kt = (rows + 127) // 128, (sk + 3) // 4
+    b = np.asarray(tiled, dtype=np.uint8).reshape(-1)[: mt * 128 * kt * 4]
+    t = b.reshape(mt, kt, 32, 4, 4).transpose(0, 3, 2, 1, 4)
+    return np.ascontiguousarray(t).reshape(mt * 128, kt * 4)[:rows, :sk]
