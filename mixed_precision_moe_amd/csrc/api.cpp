@@ -1,0 +1,298 @@
+// C ABI of the library: argument validation (before any device work), workspace carving and the
+// stream-ordered launch sequence.  Declarations and the contract of every entry point are in
+// include/mxfp4moe.h.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+
+#include "common.h"
+
+#define MX_API extern "C" __attribute__((visibility("default")))
+
+// launchers (defined next to their kernels)
+int launch_quantize(const void* x, int64_t M, int64_t K, int64_t ldx, void* q, void* sflat, void* stiled,
+                    hipStream_t stream);
+int launch_repack_gfx950(const MoeGeom& g, const BlobOffsets& o, bool bias, const void* w13_q, const void* w13_s,
+                         const void* w2_q, const void* w2_s, const void* b13, const void* b2, int bias_is_fp32,
+                         void* out, hipStream_t stream);
+int launch_unpack_gfx950(const MoeGeom& g, const BlobOffsets& o, bool bias, const void* packed, void* w13_q,
+                         void* w13_s, void* w2_q, void* w2_s, void* b13, void* b2, hipStream_t stream);
+int launch_repack_standard(const MoeGeom& g, bool bias, const void* w13_q, const void* w13_s, const void* w2_q,
+                           const void* w2_s, const void* b13, const void* b2, int bias_is_fp32, bool swap, bool tiled,
+                           const size_t off[6], void* out, hipStream_t stream);
+int launch_xprep(const void* x, int64_t T, int64_t ldx, const MoeGeom& g, void* xq, void* xs, float* yacc,
+                 int32_t* counts, hipStream_t stream);
+int launch_zero_i32(int32_t* p, int n, hipStream_t stream);
+int launch_route(const float* logits, int64_t T, int E, int k, int renormalize, int32_t* ids, float* w,
+                 int32_t* counts, hipStream_t stream);
+int launch_place(const int32_t* ids, const int32_t* counts, int64_t T, int k, int E, int BM, int32_t* offsets,
+                 int32_t* poffsets, int32_t* sorted_pairs, int32_t* prow_pair, void* tiles, int32_t* ntiles,
+                 hipStream_t stream);
+int launch_gemms(int MT, const MoeGeom& g, const uint8_t* blob, const BlobOffsets& o, bool bias, const uint8_t* xq,
+                 const uint8_t* xs, const int32_t* prow_pair, const float* topw, const void* tiles, const int32_t* ntiles,
+                 int64_t max_tiles, uint8_t* actq, uint8_t* acts, float* yacc, int k, hipStream_t stream);
+int launch_finish(const float* yacc, void* y, int64_t n, hipStream_t stream);
+
+namespace {
+
+constexpr int kMaxE = 1024;
+constexpr int kMaxTopK = 32;
+
+inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+inline hipStream_t S(void* s) { return (hipStream_t)s; }
+
+int check_dims(const mxfp4_moe_dims* d) {
+  if (!d) return MXFP4_ERR_NULL;
+  if (d->E < 1 || d->H < 32 || d->I < 32 || d->H % 32 || d->I % 32) return MXFP4_ERR_SHAPE;
+  if (d->has_bias != 0 && d->has_bias != 1) return MXFP4_ERR_SHAPE;
+  if ((int64_t)d->E * 2 * d->I > (1LL << 31) || (int64_t)d->E * d->H > (1LL << 31)) return MXFP4_ERR_SHAPE;
+  return MXFP4_OK;
+}
+
+bool valid_layout(uint32_t layout) {
+  return layout == MXFP4_LAYOUT_GFX950 || layout == MXFP4_LAYOUT_STD_W31 || layout == MXFP4_LAYOUT_SCALE_TILED ||
+         layout == (MXFP4_LAYOUT_STD_W31 | MXFP4_LAYOUT_SCALE_TILED);
+}
+
+void standard_sizes(const mxfp4_moe_dims* d, uint32_t layout, size_t sz[6]) {
+  const int64_t E = d->E, H = d->H, I = d->I;
+  const bool tiled = layout & MXFP4_LAYOUT_SCALE_TILED;
+  sz[0] = (size_t)(E * 2 * I * (H / 2));
+  sz[2] = (size_t)(E * H * (I / 2));
+  if (tiled) {
+    sz[1] = (size_t)(E * cdiv(2 * I, 128) * cdiv(H / 32, 4) * 512);
+    sz[3] = (size_t)(E * cdiv(H, 128) * cdiv(I / 32, 4) * 512);
+  } else {
+    sz[1] = (size_t)(E * 2 * I * (H / 32));
+    sz[3] = (size_t)(E * H * (I / 32));
+  }
+  sz[4] = d->has_bias ? (size_t)(E * 2 * I * 2) : 0;
+  sz[5] = d->has_bias ? (size_t)(E * H * 2) : 0;
+}
+
+size_t standard_offsets(const mxfp4_moe_dims* d, uint32_t layout, size_t off[6]) {
+  size_t sz[6];
+  standard_sizes(d, layout, sz);
+  size_t p = 0;
+  for (int i = 0; i < 6; i++) {
+    off[i] = p;
+    p = (size_t)align256((int64_t)(p + sz[i]));
+  }
+  return p;
+}
+
+int choose_mt(int64_t P, int64_t E) {
+  const int64_t avg = P / (E > 0 ? E : 1);
+  if (avg < 48) return 1;
+  if (avg < 160) return 2;
+  return 4;
+}
+
+struct RouteWs {
+  uint64_t counts, poffsets, prow_pair, tiles, ntiles, total;
+  int64_t max_tiles;
+};
+
+RouteWs route_ws(int64_t T, int64_t E, int64_t k) {
+  RouteWs w;
+  const int64_t P = T * k;
+  const int64_t nrows = ((P + 31 * E + 31) / 32) * 32 + 128;
+  w.max_tiles = cdiv(P, 32) + E;
+  uint64_t p = 0;
+  auto take = [&](uint64_t bytes) { uint64_t o = p; p = align256((int64_t)(p + bytes)); return o; };
+  w.counts = take(4 * E);
+  w.poffsets = take(4 * (E + 1));
+  w.prow_pair = take(4 * nrows);
+  w.tiles = take(16 * w.max_tiles);
+  w.ntiles = take(16);
+  w.total = p;
+  return w;
+}
+
+int check_route_args(int64_t T, int32_t E, int32_t top_k) {
+  if (T < 0 || E < 1 || E > kMaxE || top_k < 1 || top_k > E || top_k > kMaxTopK) return MXFP4_ERR_SHAPE;
+  if (T * top_k + 32LL * E + 256 > (1LL << 31) - 1) return MXFP4_ERR_SHAPE;
+  return MXFP4_OK;
+}
+
+}  // namespace
+
+MX_API const char* mxfp4_status_str(int status) {
+  switch (status) {
+    case MXFP4_OK: return "ok";
+    case MXFP4_ERR_NULL: return "a required pointer is NULL";
+    case MXFP4_ERR_SHAPE: return "a size or dimension is out of range";
+    case MXFP4_ERR_ALIGN: return "a pointer or stride is misaligned";
+    case MXFP4_ERR_WORKSPACE: return "workspace or output buffer too small";
+    case MXFP4_ERR_LAYOUT: return "unknown layout, or packed weights that do not match the dimensions";
+    case MXFP4_ERR_DEVICE: return "a HIP call or kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+MX_API uint32_t mxfp4_version(void) { return (1u << 16) | 0u; }
+
+MX_API size_t mxfp4_tiled_scale_bytes(int64_t M, int64_t K) {
+  if (M < 0 || K < 32 || K % 32) return 0;
+  return (size_t)(cdiv(M, 128) * cdiv(K / 32, 4) * 512);
+}
+
+MX_API int mxfp4_quantize(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, void* q_u8, void* scale_flat_u8,
+                          void* scale_tiled_u8, void* stream) {
+  if (M < 0 || K < 32 || K % 32 || ldx < K || ldx % 8) return MXFP4_ERR_SHAPE;
+  if (M > (1LL << 40) / (ldx > 0 ? ldx : 1)) return MXFP4_ERR_SHAPE;
+  if (M == 0) return MXFP4_OK;
+  if (!x_bf16 || !q_u8) return MXFP4_ERR_NULL;
+  if (!aligned(x_bf16, 16) || !aligned(q_u8, 4) || (scale_tiled_u8 && !aligned(scale_tiled_u8, 4)))
+    return MXFP4_ERR_ALIGN;
+  return launch_quantize(x_bf16, M, K, ldx, q_u8, scale_flat_u8, scale_tiled_u8, S(stream));
+}
+
+MX_API size_t mxfp4_repack_bytes(const mxfp4_moe_dims* d, uint32_t layout) {
+  if (check_dims(d) != MXFP4_OK || !valid_layout(layout)) return 0;
+  if (layout == MXFP4_LAYOUT_GFX950) return (size_t)blob_offsets(moe_geom(d->E, d->H, d->I), d->has_bias).total;
+  size_t off[6];
+  return standard_offsets(d, layout, off);
+}
+
+MX_API int mxfp4_repack_offsets(const mxfp4_moe_dims* d, uint32_t layout, size_t offsets_out[6]) {
+  int st = check_dims(d);
+  if (st) return st;
+  if (!offsets_out) return MXFP4_ERR_NULL;
+  if (!valid_layout(layout) || layout == MXFP4_LAYOUT_GFX950) return MXFP4_ERR_LAYOUT;
+  standard_offsets(d, layout, offsets_out);
+  return MXFP4_OK;
+}
+
+MX_API int mxfp4_repack_weights(const mxfp4_moe_dims* d, const void* w13_q, const void* w13_s, const void* w2_q,
+                                const void* w2_s, const void* b13, const void* b2, int32_t bias_is_fp32,
+                                uint32_t layout, void* out, size_t out_bytes, void* stream) {
+  int st = check_dims(d);
+  if (st) return st;
+  if (!valid_layout(layout)) return MXFP4_ERR_LAYOUT;
+  if (!w13_q || !w13_s || !w2_q || !w2_s || !out) return MXFP4_ERR_NULL;
+  if (d->has_bias && (!b13 || !b2)) return MXFP4_ERR_NULL;
+  if (!aligned(w13_q, 16) || !aligned(w2_q, 16) || !aligned(out, 256)) return MXFP4_ERR_ALIGN;
+  if (d->has_bias && (!aligned(b13, bias_is_fp32 ? 4 : 2) || !aligned(b2, bias_is_fp32 ? 4 : 2)))
+    return MXFP4_ERR_ALIGN;
+  const size_t need = mxfp4_repack_bytes(d, layout);
+  if (out_bytes < need) return MXFP4_ERR_WORKSPACE;
+  const MoeGeom g = moe_geom(d->E, d->H, d->I);
+  if (layout == MXFP4_LAYOUT_GFX950)
+    return launch_repack_gfx950(g, blob_offsets(g, d->has_bias), d->has_bias, w13_q, w13_s, w2_q, w2_s, b13, b2,
+                                bias_is_fp32, out, S(stream));
+  size_t off[6];
+  standard_offsets(d, layout, off);
+  return launch_repack_standard(g, d->has_bias, w13_q, w13_s, w2_q, w2_s, b13, b2, bias_is_fp32,
+                                (layout & MXFP4_LAYOUT_STD_W31) != 0, (layout & MXFP4_LAYOUT_SCALE_TILED) != 0, off, out,
+                                S(stream));
+}
+
+static int read_header(const void* packed, BlobHeader* h, hipStream_t stream) {
+  if (hipMemcpyAsync(h, packed, sizeof(BlobHeader), hipMemcpyDeviceToHost, stream) != hipSuccess)
+    return MXFP4_ERR_DEVICE;
+  if (hipStreamSynchronize(stream) != hipSuccess) return MXFP4_ERR_DEVICE;
+  return MXFP4_OK;
+}
+
+static int header_matches(const mxfp4_moe_dims* d, const BlobHeader& h) {
+  if (std::memcmp(h.magic, MX_BLOB_MAGIC, 8) != 0 || h.version != MX_BLOB_VERSION) return 0;
+  if (h.E != d->E || h.H != d->H || h.I != d->I || h.has_bias != d->has_bias) return 0;
+  const BlobOffsets o = blob_offsets(moe_geom(d->E, d->H, d->I), d->has_bias);
+  return h.off_w13q == o.w13q && h.off_w13s == o.w13s && h.off_w2q == o.w2q && h.off_w2s == o.w2s &&
+         h.off_b13 == o.b13 && h.off_b2 == o.b2 && h.total == o.total;
+}
+
+MX_API int mxfp4_check_packed(const mxfp4_moe_dims* d, const void* packed, void* stream) {
+  int st = check_dims(d);
+  if (st) return st;
+  if (!packed) return MXFP4_ERR_NULL;
+  if (!aligned(packed, 256)) return MXFP4_ERR_ALIGN;
+  BlobHeader h;
+  st = read_header(packed, &h, S(stream));
+  if (st) return st;
+  return header_matches(d, h) ? MXFP4_OK : MXFP4_ERR_LAYOUT;
+}
+
+MX_API int mxfp4_unpack_weights(const mxfp4_moe_dims* d, const void* packed, void* w13_q, void* w13_s, void* w2_q,
+                                void* w2_s, void* b13_bf16, void* b2_bf16, void* stream) {
+  int st = check_dims(d);
+  if (st) return st;
+  if (!packed || !w13_q || !w13_s || !w2_q || !w2_s) return MXFP4_ERR_NULL;
+  if (!aligned(packed, 256) || !aligned(w13_q, 16) || !aligned(w2_q, 16)) return MXFP4_ERR_ALIGN;
+  if ((b13_bf16 && !aligned(b13_bf16, 2)) || (b2_bf16 && !aligned(b2_bf16, 2))) return MXFP4_ERR_ALIGN;
+  BlobHeader h;
+  st = read_header(packed, &h, S(stream));
+  if (st) return st;
+  if (!header_matches(d, h)) return MXFP4_ERR_LAYOUT;
+  const MoeGeom g = moe_geom(d->E, d->H, d->I);
+  return launch_unpack_gfx950(g, blob_offsets(g, d->has_bias), d->has_bias, packed, w13_q, w13_s, w2_q, w2_s, b13_bf16,
+                              b2_bf16, S(stream));
+}
+
+MX_API size_t moe_mxfp4_route_workspace_bytes(int64_t T, int32_t E, int32_t top_k) {
+  if (check_route_args(T, E, top_k) != MXFP4_OK) return 0;
+  return (size_t)route_ws(T, E, top_k).total;
+}
+
+MX_API int moe_mxfp4_route(const float* router_logits, int64_t T, int32_t E, int32_t top_k, int32_t renormalize,
+                           int32_t* topk_ids, float* topk_w, int32_t* expert_offsets, int32_t* sorted_pairs,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_route_args(T, E, top_k);
+  if (st) return st;
+  if (!expert_offsets || !workspace) return MXFP4_ERR_NULL;
+  if (T > 0 && (!router_logits || !topk_ids || !topk_w || !sorted_pairs)) return MXFP4_ERR_NULL;
+  if (!aligned(router_logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) || !aligned(expert_offsets, 4) ||
+      !aligned(sorted_pairs, 4) || !aligned(workspace, 256))
+    return MXFP4_ERR_ALIGN;
+  const RouteWs w = route_ws(T, E, top_k);
+  if (workspace_bytes < w.total) return MXFP4_ERR_WORKSPACE;
+  uint8_t* ws = (uint8_t*)workspace;
+  int32_t* counts = (int32_t*)(ws + w.counts);
+  if ((st = launch_zero_i32(counts, E, S(stream)))) return st;
+  if ((st = launch_route(router_logits, T, E, top_k, renormalize, topk_ids, topk_w, counts, S(stream)))) return st;
+  return launch_place(topk_ids, counts, T, top_k, E, 32, expert_offsets, (int32_t*)(ws + w.poffsets), sorted_pairs,
+                      (int32_t*)(ws + w.prow_pair), ws + w.tiles, (int32_t*)(ws + w.ntiles), S(stream));
+}
+
+MX_API size_t moe_mxfp4_workspace_bytes(const mxfp4_moe_dims* d, int64_t T, int32_t top_k) {
+  if (check_dims(d) != MXFP4_OK || check_route_args(T, d->E, top_k) != MXFP4_OK) return 0;
+  return (size_t)fwd_ws(moe_geom(d->E, d->H, d->I), T, top_k).total;
+}
+
+MX_API int moe_mxfp4_forward(const mxfp4_moe_dims* d, const void* packed_gfx950, const void* x_bf16, int64_t T,
+                             int64_t ldx, const float* router_logits, int32_t top_k, int32_t renormalize, void* y_bf16,
+                             int32_t* topk_ids, float* topk_w, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_dims(d);
+  if (st) return st;
+  if ((st = check_route_args(T, d->E, top_k))) return st;
+  if (ldx < d->H || ldx % 8) return MXFP4_ERR_SHAPE;
+  if (T == 0) return MXFP4_OK;
+  if (!packed_gfx950 || !x_bf16 || !router_logits || !y_bf16 || !workspace) return MXFP4_ERR_NULL;
+  if (!aligned(packed_gfx950, 256) || !aligned(x_bf16, 16) || !aligned(router_logits, 4) || !aligned(y_bf16, 16) ||
+      !aligned(workspace, 256) || (topk_ids && !aligned(topk_ids, 4)) || (topk_w && !aligned(topk_w, 4)))
+    return MXFP4_ERR_ALIGN;
+  const MoeGeom g = moe_geom(d->E, d->H, d->I);
+  const FwdWs w = fwd_ws(g, T, top_k);
+  if (workspace_bytes < w.total) return MXFP4_ERR_WORKSPACE;
+  const BlobOffsets o = blob_offsets(g, d->has_bias);
+  uint8_t* ws = (uint8_t*)workspace;
+  const int64_t P = T * top_k;
+  int32_t* ids = topk_ids ? topk_ids : (int32_t*)(ws + w.ids);
+  float* wts = topk_w ? topk_w : (float*)(ws + w.w);
+  int32_t* counts = (int32_t*)(ws + w.counts);
+  float* yacc = (float*)(ws + w.yacc);
+  const int MT = choose_mt(P, g.E);
+  hipStream_t s = S(stream);
+  if ((st = launch_xprep(x_bf16, T, ldx, g, ws + w.xq, ws + w.xs, yacc, counts, s))) return st;
+  if ((st = launch_route(router_logits, T, (int)g.E, top_k, renormalize, ids, wts, counts, s))) return st;
+  if ((st = launch_place(ids, counts, T, top_k, (int)g.E, 32 * MT, (int32_t*)(ws + w.offsets),
+                         (int32_t*)(ws + w.poffsets), (int32_t*)(ws + w.sorted_pairs), (int32_t*)(ws + w.prow_pair),
+                         ws + w.tiles, (int32_t*)(ws + w.ntiles), s)))
+    return st;
+  if ((st = launch_gemms(MT, g, (const uint8_t*)packed_gfx950, o, d->has_bias, ws + w.xq, ws + w.xs,
+                         (const int32_t*)(ws + w.prow_pair), wts, ws + w.tiles, (const int32_t*)(ws + w.ntiles),
+                         w.max_tiles, ws + w.actq, ws + w.acts, yacc, top_k, s)))
+    return st;
+  return launch_finish(yacc, y_bf16, T * g.H, s);
+}

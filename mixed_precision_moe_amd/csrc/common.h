@@ -1,0 +1,152 @@
+// Shared definitions of the gfx950 MXFP4 / MoE library: vector types, the E8M0 rule, and the
+// device-memory layouts that the kernels agree on.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mxfp4moe.h"
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x32_t __attribute__((ext_vector_type(32)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+
+#define MX_DEV __device__ __forceinline__
+
+// ---------------------------------------------------------------------------------------------
+// E8M0 scale of a block from the binary32 bits of its largest magnitude (the 0.75 round-up rule):
+// add 2^21 so significands >= 1.75 carry into the next binade, take the biased exponent B,
+// e = B - 2 clamped to [0, 254]; a zero maximum gives 0.
+// [P3 Implementation breakdown item 1; Key source snippets, the UE8M0_SF branch]
+MX_DEV uint32_t e8m0_from_amax_bits(uint32_t amax_bits) {
+  uint32_t b = ((amax_bits + (1u << 21)) >> 23) & 0xFFu;
+  uint32_t e = b > 2u ? b - 2u : 0u;
+  e = e < 254u ? e : 254u;
+  return amax_bits == 0u ? 0u : e;
+}
+
+// The scale operand of the gfx950 scaled conversions: only its exponent field is used, as an E8M0
+// exponent (field 0 means 2^-127), so the byte shifted into place is the scale.
+MX_DEV float e8m0_as_scale_operand(uint32_t e) { return __uint_as_float(e << 23); }
+
+MX_DEV float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// binary32 -> bf16 bits, round to nearest even (finite inputs).
+MX_DEV uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Execution layout of the MoE weights (the blob written by mxfp4_repack_weights(GFX950)).
+//
+// The GEMMs run on v_mfma_scale_f32_32x32x64_f8f6f4.  For an operand tile of 32 rows x 64 K, lane l
+// holds row (l % 32) and the 32 consecutive K of block (l / 32); fp4 is 16 bytes per lane (element
+// i in nibble i, low nibble first), fp6 is 24 bytes per lane (element i in bits 6i..6i+5); the lane's
+// E8M0 scale is one byte of a 32-bit register selected by the instruction's op_sel.
+//
+//   w13 q : [E][I/32 it][nkt1][2 (gate, up)][64 lanes][16 B]   lane: row it*32 + l%32 of w1 (gate)
+//           or w3 (up), K block 2*kt + l/32 along H.  Blocks past H/32 are zero.
+//   w13 s : [E][I/32][ngrp1][2][64 lanes][4 B]   byte j = scale of K block 2*(4*grp + j) + l/32.
+//   w2 q  : [E][H/32 nt][nkt2][64 lanes][16 B]   lane: row nt*32 + l%32 of w2, K block 2*kt + l/32
+//           along I, elements of the block in the order W2_PERM (the order in which the first GEMM's
+//           epilogue leaves the activation).
+//   w2 s  : [E][H/32][ngrp2][64][4 B]
+//   b13   : bf16 [E][2I] (gate half first), b2 : bf16 [E][H]
+// nkt = ceil(K / 64) tiles of 64 along K, ngrp = ceil(nkt / 4) groups of four tiles (one scale
+// register per lane per group).
+struct BlobHeader {
+  char magic[8];
+  uint32_t version;
+  int32_t E, H, I, has_bias;
+  uint32_t reserved0;
+  uint64_t off_w13q, off_w13s, off_w2q, off_w2s, off_b13, off_b2, total;
+};
+static_assert(sizeof(BlobHeader) <= 256, "header fits in 256 bytes");
+
+#define MX_BLOB_MAGIC "MX4GFX95"
+#define MX_BLOB_VERSION 1u
+
+struct MoeGeom {
+  int64_t E, H, I;
+  int64_t nkt1, ngrp1;  // along H (first GEMM's K)
+  int64_t nkt2, ngrp2;  // along I (second GEMM's K)
+  int64_t nit, nht;     // I/32, H/32
+};
+
+static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+static inline int64_t align256(int64_t a) { return (a + 255) & ~(int64_t)255; }
+
+static inline MoeGeom moe_geom(int64_t E, int64_t H, int64_t I) {
+  MoeGeom g;
+  g.E = E; g.H = H; g.I = I;
+  g.nkt1 = cdiv(H, 64); g.ngrp1 = cdiv(g.nkt1, 4);
+  g.nkt2 = cdiv(I, 64); g.ngrp2 = cdiv(g.nkt2, 4);
+  g.nit = I / 32; g.nht = H / 32;
+  return g;
+}
+
+struct BlobOffsets {
+  uint64_t w13q, w13s, w2q, w2s, b13, b2, total;
+};
+
+static inline BlobOffsets blob_offsets(const MoeGeom& g, bool bias) {
+  BlobOffsets o;
+  uint64_t p = 256;
+  o.w13q = p; p = align256(p + (uint64_t)g.E * g.nit * g.nkt1 * 2 * 1024);
+  o.w13s = p; p = align256(p + (uint64_t)g.E * g.nit * g.ngrp1 * 2 * 256);
+  o.w2q = p;  p = align256(p + (uint64_t)g.E * g.nht * g.nkt2 * 1024);
+  o.w2s = p;  p = align256(p + (uint64_t)g.E * g.nht * g.ngrp2 * 256);
+  o.b13 = p;  p = align256(p + (bias ? (uint64_t)g.E * 2 * g.I * 2 : 0));
+  o.b2 = p;   p = align256(p + (bias ? (uint64_t)g.E * g.H * 2 : 0));
+  o.total = p;
+  return o;
+}
+
+// Position p of a 32-element K block of the second GEMM's operands holds element W2_PERM(p) of
+// the block: the first GEMM's transposed output leaves lane half h with block elements
+// 8*jj + 4*h + i (accumulator index 4*jj + i), which it stores at positions 16*h + 4*jj + i.
+__host__ __device__ inline int w2_perm(int p) { return 8 * ((p & 15) >> 2) + 4 * (p >> 4) + (p & 3); }
+
+// ---------------------------------------------------------------------------------------------
+// Forward-pass workspace.  Rows of the expert-sorted order are padded per expert to a multiple of
+// 32 ("padded rows"); a padded row with no pair has pair index -1.
+//   xq  : [T][2*nkt1 blocks][48 B]  per token and 32-element block of x: 24 B hi E2M3 codes, 24 B lo
+//   xs  : [T][ngrp1][2 (hi, lo)][2 (block parity)][4 (tile in group)]  E8M0 bytes
+//   actq: [row group of 32][nkt2][64 lanes][48 B]  the second GEMM's A operand, lane (row l%32,
+//         K block l/32): 24 B hi, 24 B lo
+//   acts: [row group][ngrp2][64 lanes][2 (hi, lo)][4 (tile in group)]
+//   tiles: int4 (expert, first padded row, valid rows, 0) per M tile of the GEMMs
+struct FwdWs {
+  uint64_t counts, offsets, poffsets, sorted_pairs, ids, w, prow_pair, tiles, ntiles, xq, xs, actq, acts, yacc, total;
+  int64_t nrows_alloc, max_tiles;
+};
+
+static inline FwdWs fwd_ws(const MoeGeom& g, int64_t T, int64_t k) {
+  FwdWs w;
+  const int64_t P = T * k;
+  w.nrows_alloc = ((P + 31 * g.E + 31) / 32) * 32 + 128;
+  w.max_tiles = cdiv(P, 32) + g.E;
+  uint64_t p = 0;
+  auto take = [&](uint64_t bytes) { uint64_t o = p; p = align256(p + bytes); return o; };
+  w.counts = take(4 * g.E);
+  w.offsets = take(4 * (g.E + 1));
+  w.poffsets = take(4 * (g.E + 1));
+  w.sorted_pairs = take(4 * P);
+  w.ids = take(4 * P);
+  w.w = take(4 * P);
+  w.prow_pair = take(4 * w.nrows_alloc);
+  w.tiles = take(16 * w.max_tiles);
+  w.ntiles = take(16);
+  w.xq = take((uint64_t)T * 2 * g.nkt1 * 48);
+  w.xs = take((uint64_t)T * g.ngrp1 * 16);
+  w.actq = take((uint64_t)(w.nrows_alloc / 32) * g.nkt2 * 64 * 48);
+  w.acts = take((uint64_t)(w.nrows_alloc / 32) * g.ngrp2 * 64 * 8);
+  w.yacc = take((uint64_t)T * g.H * 4);
+  w.total = p;
+  return w;
+}

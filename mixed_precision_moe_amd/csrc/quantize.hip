@@ -1,0 +1,99 @@
+// MXFP4 block quantization of a bf16 matrix on gfx950.
+//
+// [P3 Implementation breakdown item 1; Key source snippets: the E8M0 reference helper, the UE8M0_SF
+//  branch of the FP16/BF16 -> FP4 converter and the tiled-scale untile helper; NS element rule]
+//
+// Work split: a wave covers 512 consecutive columns (16 blocks) of four rows; lane l owns eight
+// bf16 (one 16-byte load) of each row, four lanes per 32-element block.  The block maximum is a
+// max of bf16 magnitude bits (monotone for non-negative values), reduced over the four lanes.
+// Elements are encoded by v_cvt_scalef32_pk_fp4_bf16, which divides by the E8M0 scale and rounds
+// to nearest even with saturation and a kept sign -- the element rule exactly (checked against the
+// oracle on every bf16 pattern under every exponent).  The grid also covers the padding of the tiled
+// layout (rows up to a multiple of 128, columns up to a multiple of 128), whose lanes read nothing and
+// write zero scale bytes there.
+#include "common.h"
+
+namespace {
+
+constexpr int kRowsPerWave = 4;
+constexpr int kWaves = 4;
+constexpr int kRowsPerBlock = kRowsPerWave * kWaves;  // 16
+
+__global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                                       int64_t ldx, uint8_t* __restrict__ q,
+                                                       uint8_t* __restrict__ sflat, uint8_t* __restrict__ stiled,
+                                                       int64_t Mpad, int64_t Kpad, int64_t kTiles) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t col = (int64_t)blockIdx.x * 512 + lane * 8;
+  const bool col_live = col < Kpad;   // uniform over each 16-lane (128-column) group
+  const bool col_in = col < K;        // uniform over each 4-lane block (K % 32 == 0)
+  const int64_t nby = Mpad / kRowsPerBlock;
+  for (int64_t by = blockIdx.y; by < nby; by += gridDim.y) {
+  const int64_t row0 = by * kRowsPerBlock + wave * kRowsPerWave;
+
+  u32x4_t v[kRowsPerWave];
+#pragma unroll
+  for (int r = 0; r < kRowsPerWave; r++) {
+    const int64_t row = row0 + r;
+    if (col_in && row < M)
+      v[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(x + row * ldx + col));
+    else
+      v[r] = u32x4_t{0u, 0u, 0u, 0u};
+  }
+
+#pragma unroll
+  for (int r = 0; r < kRowsPerWave; r++) {
+    const int64_t row = row0 + r;
+    // largest magnitude among this lane's eight values
+    uint32_t w[4] = {v[r][0], v[r][1], v[r][2], v[r][3]};
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      uint32_t lo = w[i] & 0x7FFFu, hi = (w[i] >> 16) & 0x7FFFu;
+      m = max(m, max(lo, hi));
+    }
+    m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+    const uint32_t e = e8m0_from_amax_bits(m << 16);
+    const float s = e8m0_as_scale_operand(e);
+
+    uint32_t packed = 0;
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(packed, __builtin_bit_cast(bf16x2_t, w[0]), s, 0);
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(packed, __builtin_bit_cast(bf16x2_t, w[1]), s, 1);
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(packed, __builtin_bit_cast(bf16x2_t, w[2]), s, 2);
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(packed, __builtin_bit_cast(bf16x2_t, w[3]), s, 3);
+
+    const bool live = col_in && row < M;
+    if (live) {
+      *reinterpret_cast<uint32_t*>(q + row * (K / 2) + col / 2) = packed;
+      if (sflat && (lane & 3) == 0) sflat[row * (K / 32) + col / 32] = (uint8_t)e;
+    }
+    // tiled scales: the four blocks of a 128-column tile live in lanes 16j, 16j+4, 16j+8, 16j+12
+    uint32_t e1 = (uint32_t)__shfl_down((int)e, 4);
+    uint32_t e2 = (uint32_t)__shfl_down((int)e, 8);
+    uint32_t e3 = (uint32_t)__shfl_down((int)e, 12);
+    if (stiled && col_live && (lane & 15) == 0) {
+      const int64_t mT = row >> 7, iM = (row >> 5) & 3, oM = row & 31;
+      const int64_t kT = col >> 7;
+      const uint32_t word = e | (e1 << 8) | (e2 << 16) | (e3 << 24);
+      *reinterpret_cast<uint32_t*>(stiled + ((mT * kTiles + kT) * 32 + oM) * 16 + iM * 4) = word;
+    }
+  }
+  }
+}
+
+}  // namespace
+
+int launch_quantize(const void* x, int64_t M, int64_t K, int64_t ldx, void* q, void* sflat, void* stiled,
+                    hipStream_t stream) {
+  const int64_t mTiles = (M + 127) / 128;
+  const int64_t kTiles = (K / 32 + 3) / 4;
+  const int64_t Mpad = mTiles * 128;
+  const int64_t Kpad = kTiles * 128;
+  const int64_t nby = Mpad / kRowsPerBlock;
+  dim3 grid((unsigned)((Kpad + 511) / 512), (unsigned)(nby < 65535 ? nby : 65535));
+  hipLaunchKernelGGL(quantize_kernel, grid, dim3(256), 0, stream, (const uint16_t*)x, M, K, ldx, (uint8_t*)q,
+                     (uint8_t*)sflat, (uint8_t*)stiled, Mpad, Kpad, kTiles);
+  return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
+}

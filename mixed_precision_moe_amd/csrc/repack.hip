@@ -1,0 +1,301 @@
+// Load-time weight conversion: the standard MXFP4 checkpoint tensors -> this library's execution
+// layout (and back), plus the pages' own layouts as checked conversions.
+//
+// [P2 Implementation breakdown items 1-3; Key source snippets: the unified conversion entry returns
+//  (w13, w2, w13 scale, w2 scale, b13, b2), swaps the fused gate/up halves [w1; w3] -> [w3; w1] for
+//  the CUTLASS backends, exchanges the bias halves and casts both biases to bf16]
+// [P3 Key source snippets: the tiled scale layout [mTiles, kTiles, 32, 4, 4]]
+//
+// The execution layout keeps the gate/up order of the checkpoint and instead pairs gate tile i with
+// up tile i, so one wave sees both halves of SwiGLU for the same columns; the swap and the tiled
+// scales exist only as checked conversions.  All kernels are grid-stride loops over output units.
+#include "common.h"
+
+namespace {
+
+#define GRID_STRIDE(i, n) for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < (n); i += (int64_t)gridDim.x * blockDim.x)
+
+__global__ void write_header_kernel(uint8_t* out, BlobHeader h) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) *reinterpret_cast<BlobHeader*>(out) = h;
+  // zero the rest of the 256-byte header
+  for (int i = sizeof(BlobHeader) + threadIdx.x; i < 256; i += blockDim.x) out[i] = 0;
+}
+
+// w13 q: one 16-byte chunk per (e, it, kt, gu, lane)
+__global__ void pack_w13q_kernel(const uint8_t* __restrict__ src, u32x4_t* __restrict__ dst, MoeGeom g, int64_t n) {
+  GRID_STRIDE(i, n) {
+    int64_t t = i;
+    const int lane = (int)(t & 63); t >>= 6;
+    const int gu = (int)(t & 1); t >>= 1;
+    const int64_t kt = t % g.nkt1; t /= g.nkt1;
+    const int64_t it = t % g.nit; const int64_t e = t / g.nit;
+    const int64_t row = gu * g.I + it * 32 + (lane & 31);
+    const int64_t blk = 2 * kt + (lane >> 5);
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (blk < g.H / 32)
+      v = *reinterpret_cast<const u32x4_t*>(src + (e * 2 * g.I + row) * (g.H / 2) + blk * 16);
+    dst[i] = v;
+  }
+}
+
+__global__ void unpack_w13q_kernel(const u32x4_t* __restrict__ src, uint8_t* __restrict__ dst, MoeGeom g, int64_t n) {
+  GRID_STRIDE(i, n) {
+    int64_t t = i;
+    const int lane = (int)(t & 63); t >>= 6;
+    const int gu = (int)(t & 1); t >>= 1;
+    const int64_t kt = t % g.nkt1; t /= g.nkt1;
+    const int64_t it = t % g.nit; const int64_t e = t / g.nit;
+    const int64_t row = gu * g.I + it * 32 + (lane & 31);
+    const int64_t blk = 2 * kt + (lane >> 5);
+    if (blk < g.H / 32)
+      *reinterpret_cast<u32x4_t*>(dst + (e * 2 * g.I + row) * (g.H / 2) + blk * 16) = src[i];
+  }
+}
+
+// w13 s: one dword per (e, it, grp, gu, lane); byte j = scale of K block 2*(4*grp + j) + lane/32
+__global__ void pack_w13s_kernel(const uint8_t* __restrict__ src, uint32_t* __restrict__ dst, MoeGeom g, int64_t n) {
+  GRID_STRIDE(i, n) {
+    int64_t t = i;
+    const int lane = (int)(t & 63); t >>= 6;
+    const int gu = (int)(t & 1); t >>= 1;
+    const int64_t grp = t % g.ngrp1; t /= g.ngrp1;
+    const int64_t it = t % g.nit; const int64_t e = t / g.nit;
+    const int64_t row = gu * g.I + it * 32 + (lane & 31);
+    uint32_t word = 0;
+    for (int j = 0; j < 4; j++) {
+      const int64_t blk = 2 * (4 * grp + j) + (lane >> 5);
+      if (blk < g.H / 32) word |= (uint32_t)src[(e * 2 * g.I + row) * (g.H / 32) + blk] << (8 * j);
+    }
+    dst[i] = word;
+  }
+}
+
+__global__ void unpack_w13s_kernel(const uint32_t* __restrict__ src, uint8_t* __restrict__ dst, MoeGeom g, int64_t n) {
+  GRID_STRIDE(i, n) {
+    int64_t t = i;
+    const int lane = (int)(t & 63); t >>= 6;
+    const int gu = (int)(t & 1); t >>= 1;
+    const int64_t grp = t % g.ngrp1; t /= g.ngrp1;
+    const int64_t it = t % g.nit; const int64_t e = t / g.nit;
+    const int64_t row = gu * g.I + it * 32 + (lane & 31);
+    const uint32_t word = src[i];
+    for (int j = 0; j < 4; j++) {
+      const int64_t blk = 2 * (4 * grp + j) + (lane >> 5);
+      if (blk < g.H / 32) dst[(e * 2 * g.I + row) * (g.H / 32) + blk] = (uint8_t)(word >> (8 * j));
+    }
+  }
+}
+
+// Block element order of the second GEMM (w2_perm): output 16-bit words [w0, w2, w4, w6, w1, w3, w5, w7]
+// of the source block (each 16-bit word holds four consecutive elements).
+MX_DEV u32x4_t perm_w2_block(u32x4_t s) {
+  const uint32_t w0 = s[0] & 0xFFFF, w1 = s[0] >> 16, w2 = s[1] & 0xFFFF, w3 = s[1] >> 16;
+  const uint32_t w4 = s[2] & 0xFFFF, w5 = s[2] >> 16, w6 = s[3] & 0xFFFF, w7 = s[3] >> 16;
+  return u32x4_t{w0 | (w2 << 16), w4 | (w6 << 16), w1 | (w3 << 16), w5 | (w7 << 16)};
+}
+MX_DEV u32x4_t unperm_w2_block(u32x4_t d) {
+  const uint32_t w0 = d[0] & 0xFFFF, w2 = d[0] >> 16, w4 = d[1] & 0xFFFF, w6 = d[1] >> 16;
+  const uint32_t w1 = d[2] & 0xFFFF, w3 = d[2] >> 16, w5 = d[3] & 0xFFFF, w7 = d[3] >> 16;
+  return u32x4_t{w0 | (w1 << 16), w2 | (w3 << 16), w4 | (w5 << 16), w6 | (w7 << 16)};
+}
+
+// w2 q: one 16-byte chunk per (e, nt, kt, lane)
+__global__ void pack_w2q_kernel(const uint8_t* __restrict__ src, u32x4_t* __restrict__ dst, MoeGeom g, int64_t n) {
+  GRID_STRIDE(i, n) {
+    int64_t t = i;
+    const int lane = (int)(t & 63); t >>= 6;
+    const int64_t kt = t % g.nkt2; t /= g.nkt2;
+    const int64_t nt = t % g.nht; const int64_t e = t / g.nht;
+    const int64_t row = nt * 32 + (lane & 31);
+    const int64_t blk = 2 * kt + (lane >> 5);
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (blk < g.I / 32)
+      v = perm_w2_block(*reinterpret_cast<const u32x4_t*>(src + (e * g.H + row) * (g.I / 2) + blk * 16));
+    dst[i] = v;
+  }
+}
+
+__global__ void unpack_w2q_kernel(const u32x4_t* __restrict__ src, uint8_t* __restrict__ dst, MoeGeom g, int64_t n) {
+  GRID_STRIDE(i, n) {
+    int64_t t = i;
+    const int lane = (int)(t & 63); t >>= 6;
+    const int64_t kt = t % g.nkt2; t /= g.nkt2;
+    const int64_t nt = t % g.nht; const int64_t e = t / g.nht;
+    const int64_t row = nt * 32 + (lane & 31);
+    const int64_t blk = 2 * kt + (lane >> 5);
+    if (blk < g.I / 32)
+      *reinterpret_cast<u32x4_t*>(dst + (e * g.H + row) * (g.I / 2) + blk * 16) = unperm_w2_block(src[i]);
+  }
+}
+
+__global__ void pack_w2s_kernel(const uint8_t* __restrict__ src, uint32_t* __restrict__ dst, MoeGeom g, int64_t n) {
+  GRID_STRIDE(i, n) {
+    int64_t t = i;
+    const int lane = (int)(t & 63); t >>= 6;
+    const int64_t grp = t % g.ngrp2; t /= g.ngrp2;
+    const int64_t nt = t % g.nht; const int64_t e = t / g.nht;
+    const int64_t row = nt * 32 + (lane & 31);
+    uint32_t word = 0;
+    for (int j = 0; j < 4; j++) {
+      const int64_t blk = 2 * (4 * grp + j) + (lane >> 5);
+      if (blk < g.I / 32) word |= (uint32_t)src[(e * g.H + row) * (g.I / 32) + blk] << (8 * j);
+    }
+    dst[i] = word;
+  }
+}
+
+__global__ void unpack_w2s_kernel(const uint32_t* __restrict__ src, uint8_t* __restrict__ dst, MoeGeom g, int64_t n) {
+  GRID_STRIDE(i, n) {
+    int64_t t = i;
+    const int lane = (int)(t & 63); t >>= 6;
+    const int64_t grp = t % g.ngrp2; t /= g.ngrp2;
+    const int64_t nt = t % g.nht; const int64_t e = t / g.nht;
+    const int64_t row = nt * 32 + (lane & 31);
+    const uint32_t word = src[i];
+    for (int j = 0; j < 4; j++) {
+      const int64_t blk = 2 * (4 * grp + j) + (lane >> 5);
+      if (blk < g.I / 32) dst[(e * g.H + row) * (g.I / 32) + blk] = (uint8_t)(word >> (8 * j));
+    }
+  }
+}
+
+// Bias -> bf16 (round to nearest even from fp32, or a copy of bf16).  `swap_cols`: exchange the two
+// halves of each row of `cols` columns (the fused gate/up bias) as the checked [w3; w1] conversion does.
+__global__ void bias_kernel(const void* __restrict__ src, uint16_t* __restrict__ dst, int is_fp32, int64_t rows,
+                            int64_t cols, int swap_cols, int64_t n) {
+  GRID_STRIDE(i, n) {
+    const int64_t r = i / cols, c = i % cols;
+    int64_t cs = c;
+    if (swap_cols) cs = (c + cols / 2) % cols;
+    const int64_t si = r * cols + cs;
+    uint32_t b;
+    if (is_fp32) b = f32_to_bf16_bits(reinterpret_cast<const float*>(src)[si]);
+    else b = reinterpret_cast<const uint16_t*>(src)[si];
+    dst[i] = (uint16_t)b;
+  }
+}
+
+// Row copy of a [E, R, W] byte tensor with optional exchange of the row halves (16-byte units; W % 16 == 0).
+__global__ void rows_copy16_kernel(const u32x4_t* __restrict__ src, u32x4_t* __restrict__ dst, int64_t R,
+                                   int64_t W16, int swap_rows, int64_t n) {
+  GRID_STRIDE(i, n) {
+    const int64_t c = i % W16;
+    const int64_t rr = (i / W16) % R;
+    const int64_t e = i / (W16 * R);
+    int64_t rs = rr;
+    if (swap_rows) rs = (rr + R / 2) % R;
+    dst[i] = src[(e * R + rs) * W16 + c];
+  }
+}
+
+// Row copy of a [E, R, W] byte tensor, byte units.
+__global__ void rows_copy8_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int64_t R, int64_t W,
+                                  int swap_rows, int64_t n) {
+  GRID_STRIDE(i, n) {
+    const int64_t c = i % W;
+    const int64_t rr = (i / W) % R;
+    const int64_t e = i / (W * R);
+    int64_t rs = rr;
+    if (swap_rows) rs = (rr + R / 2) % R;
+    dst[i] = src[(e * R + rs) * W + c];
+  }
+}
+
+// Per-expert tiled scales [E][mT][kT][32][4][4] from flat [E][R][SK]; byte (mT,kT,oM,iM,iK) holds the
+// scale of row mT*128 + iM*32 + oM, column kT*4 + iK, or 0 past the matrix.
+__global__ void tile_scales_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int64_t R, int64_t SK,
+                                   int swap_rows, int64_t n) {
+  const int64_t mT = (R + 127) / 128, kT = (SK + 3) / 4;
+  const int64_t per = mT * kT * 512;
+  GRID_STRIDE(i, n) {
+    const int64_t e = i / per;
+    int64_t t = i % per;
+    const int64_t iK = t & 3, iM = (t >> 2) & 3, oM = (t >> 4) & 31;
+    t >>= 9;
+    const int64_t kt = t % kT, mt = t / kT;
+    const int64_t row = mt * 128 + iM * 32 + oM, col = kt * 4 + iK;
+    uint8_t v = 0;
+    if (row < R && col < SK) {
+      int64_t rs = row;
+      if (swap_rows) rs = (row + R / 2) % R;
+      v = src[(e * R + rs) * SK + col];
+    }
+    dst[i] = v;
+  }
+}
+
+inline unsigned grid_for(int64_t n, int threads = 256) {
+  int64_t b = (n + threads - 1) / threads;
+  if (b > 65536) b = 65536;
+  if (b < 1) b = 1;
+  return (unsigned)b;
+}
+
+}  // namespace
+
+#define LAUNCH1D(kern, n, ...)                                                                   \
+  do {                                                                                           \
+    if ((n) > 0) hipLaunchKernelGGL(kern, dim3(grid_for(n)), dim3(256), 0, stream, __VA_ARGS__, (int64_t)(n)); \
+  } while (0)
+
+int launch_repack_gfx950(const MoeGeom& g, const BlobOffsets& o, bool bias, const void* w13_q, const void* w13_s,
+                         const void* w2_q, const void* w2_s, const void* b13, const void* b2, int bias_is_fp32,
+                         void* out, hipStream_t stream) {
+  uint8_t* base = (uint8_t*)out;
+  BlobHeader h = {};
+  for (int i = 0; i < 8; i++) h.magic[i] = MX_BLOB_MAGIC[i];
+  h.version = MX_BLOB_VERSION;
+  h.E = (int32_t)g.E; h.H = (int32_t)g.H; h.I = (int32_t)g.I; h.has_bias = bias ? 1 : 0;
+  h.off_w13q = o.w13q; h.off_w13s = o.w13s; h.off_w2q = o.w2q; h.off_w2s = o.w2s;
+  h.off_b13 = o.b13; h.off_b2 = o.b2; h.total = o.total;
+  hipLaunchKernelGGL(write_header_kernel, dim3(1), dim3(64), 0, stream, base, h);
+  LAUNCH1D(pack_w13q_kernel, g.E * g.nit * g.nkt1 * 2 * 64, (const uint8_t*)w13_q, (u32x4_t*)(base + o.w13q), g);
+  LAUNCH1D(pack_w13s_kernel, g.E * g.nit * g.ngrp1 * 2 * 64, (const uint8_t*)w13_s, (uint32_t*)(base + o.w13s), g);
+  LAUNCH1D(pack_w2q_kernel, g.E * g.nht * g.nkt2 * 64, (const uint8_t*)w2_q, (u32x4_t*)(base + o.w2q), g);
+  LAUNCH1D(pack_w2s_kernel, g.E * g.nht * g.ngrp2 * 64, (const uint8_t*)w2_s, (uint32_t*)(base + o.w2s), g);
+  if (bias) {
+    LAUNCH1D(bias_kernel, g.E * 2 * g.I, b13, (uint16_t*)(base + o.b13), bias_is_fp32, g.E, 2 * g.I, 0);
+    LAUNCH1D(bias_kernel, g.E * g.H, b2, (uint16_t*)(base + o.b2), bias_is_fp32, g.E, g.H, 0);
+  }
+  return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
+}
+
+int launch_unpack_gfx950(const MoeGeom& g, const BlobOffsets& o, bool bias, const void* packed, void* w13_q,
+                         void* w13_s, void* w2_q, void* w2_s, void* b13, void* b2, hipStream_t stream) {
+  const uint8_t* base = (const uint8_t*)packed;
+  LAUNCH1D(unpack_w13q_kernel, g.E * g.nit * g.nkt1 * 2 * 64, (const u32x4_t*)(base + o.w13q), (uint8_t*)w13_q, g);
+  LAUNCH1D(unpack_w13s_kernel, g.E * g.nit * g.ngrp1 * 2 * 64, (const uint32_t*)(base + o.w13s), (uint8_t*)w13_s, g);
+  LAUNCH1D(unpack_w2q_kernel, g.E * g.nht * g.nkt2 * 64, (const u32x4_t*)(base + o.w2q), (uint8_t*)w2_q, g);
+  LAUNCH1D(unpack_w2s_kernel, g.E * g.nht * g.ngrp2 * 64, (const uint32_t*)(base + o.w2s), (uint8_t*)w2_s, g);
+  if (bias) {
+    if (b13) LAUNCH1D(bias_kernel, g.E * 2 * g.I, base + o.b13, (uint16_t*)b13, 0, g.E, 2 * g.I, 0);
+    if (b2) LAUNCH1D(bias_kernel, g.E * g.H, base + o.b2, (uint16_t*)b2, 0, g.E, g.H, 0);
+  }
+  return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
+}
+
+// Checked conversions: the six standard tensors at `off`, w13 halves exchanged when `swap`, scales tiled
+// per expert when `tiled`.
+int launch_repack_standard(const MoeGeom& g, bool bias, const void* w13_q, const void* w13_s, const void* w2_q,
+                           const void* w2_s, const void* b13, const void* b2, int bias_is_fp32, bool swap, bool tiled,
+                           const size_t off[6], void* out, hipStream_t stream) {
+  uint8_t* base = (uint8_t*)out;
+  const int sw = swap ? 1 : 0;
+  LAUNCH1D(rows_copy16_kernel, g.E * 2 * g.I * (g.H / 32), (const u32x4_t*)w13_q, (u32x4_t*)(base + off[0]), 2 * g.I,
+           g.H / 32, sw);
+  LAUNCH1D(rows_copy16_kernel, g.E * g.H * (g.I / 32), (const u32x4_t*)w2_q, (u32x4_t*)(base + off[2]), g.H, g.I / 32, 0);
+  if (tiled) {
+    const int64_t n13 = g.E * cdiv(2 * g.I, 128) * cdiv(g.H / 32, 4) * 512;
+    const int64_t n2 = g.E * cdiv(g.H, 128) * cdiv(g.I / 32, 4) * 512;
+    LAUNCH1D(tile_scales_kernel, n13, (const uint8_t*)w13_s, base + off[1], 2 * g.I, g.H / 32, sw);
+    LAUNCH1D(tile_scales_kernel, n2, (const uint8_t*)w2_s, base + off[3], g.H, g.I / 32, 0);
+  } else {
+    LAUNCH1D(rows_copy8_kernel, g.E * 2 * g.I * (g.H / 32), (const uint8_t*)w13_s, base + off[1], 2 * g.I, g.H / 32, sw);
+    LAUNCH1D(rows_copy8_kernel, g.E * g.H * (g.I / 32), (const uint8_t*)w2_s, base + off[3], g.H, g.I / 32, 0);
+  }
+  if (bias) {
+    LAUNCH1D(bias_kernel, g.E * 2 * g.I, b13, (uint16_t*)(base + off[4]), bias_is_fp32, g.E, 2 * g.I, sw);
+    LAUNCH1D(bias_kernel, g.E * g.H, b2, (uint16_t*)(base + off[5]), bias_is_fp32, g.E, g.H, 0);
+  }
+  return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
+}
