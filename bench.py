@@ -1,0 +1,280 @@
+#!/usr/bin/env python3
+"""Benchmark of the MXFP4 MoE layer and the MXFP4 quantizer on one MI355X.
+
+A step is one MoE layer forward on the prefill-shaped workload (8192 bf16 tokens, 128 experts, top-8,
+hidden 2048, intermediate 768, MXFP4 weights): activation split, routing, pair sort, first grouped
+GEMM + SwiGLU, second grouped GEMM + weighted combine, bf16 output.  `value` is algorithmic TFLOP/s
+of that layer (2 * T * k * 3 * H * I flops per step).  The same run times the quantizer on the
+8192 x 7168 bf16 matrix (GB/s of algorithmic traffic) and the decode-shaped layer, and times the CPU
+oracle on a bounded sample as a reported baseline.  Inputs are synthetic and seeded; weights are
+quantized from random bf16 masters.  Prints one JSON line.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import mixed_precision_moe_amd as mx  # noqa: E402
+from mixed_precision_moe_amd import synth  # noqa: E402
+from mixed_precision_moe_amd._lib import MoeDims, check, lib  # noqa: E402
+from tests.gpu_common import bf16_dev, gpu_standard_weights  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+PEAK_FP4_TFLOPS = 10100.0  # MI355X dense MXFP4 / MXFP6 MFMA
+STAGES = ["act_split", "route", "pair_sort", "gemm1_swiglu", "gemm2_combine", "bf16_out"]
+STAGE_KERNELS = ["xprep_kernel", "route_kernel", "place_kernel", "gemm1_kernel", "gemm2_kernel", "finish_kernel"]
+
+
+def moe_flops(cfg):
+    return 2.0 * cfg.T * cfg.k * 3 * cfg.H * cfg.I
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class MoeBench:
+    def __init__(self, cfg, rotations):
+        self.cfg = cfg
+        w = gpu_standard_weights(cfg)
+        self.packed = [mx.repack_weights(*w)]
+        for _ in range(1, rotations):  # extra weight copies so consecutive steps cannot hit in the 256 MB cache
+            self.packed.append(self.packed[0].clone())
+        del w
+        x_bits, logits = synth.moe_activations(cfg)
+        self.x = [bf16_dev(x_bits) for _ in range(rotations)]
+        self.logits = [torch.from_numpy(logits).cuda() for _ in range(rotations)]
+        self.y = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device="cuda")
+        self.d = MoeDims(cfg.E, cfg.H, cfg.I, 1 if cfg.bias else 0)
+        import ctypes
+        self.ctypes = ctypes
+        nws = lib().moe_mxfp4_workspace_bytes(ctypes.byref(self.d), cfg.T, cfg.k)
+        self.ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+        self.stream = torch.cuda.current_stream()
+        self.i = 0
+
+    def step(self, events=None):
+        c = self.ctypes
+        r = self.i % len(self.x)
+        self.i += 1
+        args = [c.byref(self.d), c.c_void_p(self.packed[r % len(self.packed)].data_ptr()), c.c_void_p(self.x[r].data_ptr()),
+                self.cfg.T, self.cfg.H, c.c_void_p(self.logits[r].data_ptr()), self.cfg.k,
+                1 if self.cfg.renormalize else 0, c.c_void_p(self.y.data_ptr()), None, None,
+                c.c_void_p(self.ws.data_ptr()), self.ws.numel(), c.c_void_p(self.stream.cuda_stream)]
+        if events is None:
+            check("moe_mxfp4_forward", lib().moe_mxfp4_forward(*args))
+        else:
+            arr = (c.c_void_p * len(events))(*events)
+            check("moe_mxfp4_forward_profiled", lib().moe_mxfp4_forward_profiled(*args, arr, len(events)))
+
+
+class HipEvents:
+    """Raw HIP events (recorded by the library itself on its stream)."""
+
+    def __init__(self, n):
+        import ctypes
+        self.c = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.ev = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(h)) == 0
+            self.ev.append(h)
+
+    def elapsed_ms(self, a, b):
+        f = self.c.c_float()
+        assert self.hip.hipEventElapsedTime(self.c.byref(f), self.ev[a], self.ev[b]) == 0
+        return f.value
+
+    def __del__(self):
+        for h in getattr(self, "ev", []):
+            self.hip.hipEventDestroy(h)
+
+
+def time_moe(b, steps, warmup):
+    for _ in range(warmup):
+        b.step()
+    ns = len(STAGES) + 1
+    evs = HipEvents(steps * ns)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        b.step(evs.ev[s * ns:(s + 1) * ns])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    per_stage = np.zeros(len(STAGES))
+    for s in range(steps):
+        for j in range(len(STAGES)):
+            per_stage[j] += evs.elapsed_ms(s * ns + j, s * ns + j + 1)
+    per_stage /= steps
+    return (t1 - t0) * 1e3 / steps, per_stage
+
+
+def bench_quantize(steps, warmup, rotations=4):
+    M, K = synth.QUANT_CONFIG["M"], synth.QUANT_CONFIG["K"]
+    bits = synth.quant_matrix(M, K, cid=synth.QUANT_CONFIG["cid"])
+    xs = [bf16_dev(bits) for _ in range(rotations)]
+    qs = [torch.empty((M, K // 2), dtype=torch.uint8, device="cuda") for _ in range(rotations)]
+    sfs = [torch.empty((M, K // 32), dtype=torch.uint8, device="cuda") for _ in range(rotations)]
+    sts = [torch.empty(mx.tiled_scale_shape(M, K), dtype=torch.uint8, device="cuda") for _ in range(rotations)]
+    L = lib()
+    import ctypes
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def one(i):
+        r = i % rotations
+        check("mxfp4_quantize", L.mxfp4_quantize(ctypes.c_void_p(xs[r].data_ptr()), M, K, K,
+                                                 ctypes.c_void_p(qs[r].data_ptr()), ctypes.c_void_p(sfs[r].data_ptr()),
+                                                 ctypes.c_void_p(sts[r].data_ptr()), st))
+    for i in range(warmup):
+        one(i)
+    n = max(steps, 20)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(n):
+        one(i)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    ms = np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(n)])
+    nbytes = M * K * 2 + M * K // 2 + 2 * (M * K // 32)  # bf16 in, nibbles, flat + tiled scales (no padding here)
+    return {"workload": f"quantize bf16 {M}x{K} -> E2M1 nibbles + E8M0 flat and tiled scales", "ms": float(ms),
+            "bytes": nbytes, "GB_s": nbytes / (ms * 1e-3) / 1e9, "launches": n}
+
+
+def cpu_baselines(cfg, x_bits, logits):
+    """The oracle, untuned, on bounded samples of the two workloads."""
+    from oracle import moe as M
+    from oracle import quant as Q
+    from tests.gpu_common import LazyExperts
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = None
+    cores = len(os.sched_getaffinity(0))
+    # MoE: a few sampled tokens of the prefill workload; the oracle dequantizes every expert they use in
+    # fp64, which dominates its time
+    ntok = 4
+    rows = np.sort(np.random.default_rng(1).choice(cfg.T, size=ntok, replace=False))
+    w13, w2 = LazyExperts(cfg, "w13"), LazyExperts(cfg, "w2")
+    from oracle.route import route_ref
+    ids, _ = route_ref(logits, cfg.k)
+    from concurrent.futures import ThreadPoolExecutor
+    from tests.gpu_common import workers
+    with ThreadPoolExecutor(workers()) as ex:  # quantizing the masters is input preparation, not timed
+        list(ex.map(lambda e: (w13.get(e), w2.get(e)), np.unique(ids[rows])))
+    t0 = time.perf_counter()
+    M.moe_ref(x_bits, logits, cfg.k, w13.q, w13.s, w2.q, w2.s, None, None, tokens=rows)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * ntok * cfg.k * 3 * cfg.H * cfg.I
+    moe = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "blas_threads": blas_threads,
+           "kind": "oracle", "seconds": dt,
+           "sample": f"{ntok} of {cfg.T} prefill tokens ({len(np.unique(ids[rows]))} experts dequantized in fp64); "
+                     "weights pre-quantized outside the timed region"}
+    # quantizer: 512 rows of the 8192 x 7168 matrix
+    Mq, K = synth.QUANT_CONFIG["M"], synth.QUANT_CONFIG["K"]
+    sub = synth.quant_matrix(Mq, K, cid=synth.QUANT_CONFIG["cid"])[:512]
+    t0 = time.perf_counter()
+    q, s = Q.quantize_ref(sub)
+    Q.tile_scales(s)
+    dt = time.perf_counter() - t0
+    nbytes = 512 * K * 2 + 512 * K // 2 + 2 * 512 * K // 32
+    quant = {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle", "seconds": dt,
+             "sample": f"512 of {Mq} rows of the quantize matrix"}
+    return moe, quant
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-quantize", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this library has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "needs a GPU"
+    torch.cuda.set_device(0)
+
+    cfg = synth.MOE_CONFIGS["prefill"]
+    log(f"[bench] building prefill workload T={cfg.T} E={cfg.E} k={cfg.k} H={cfg.H} I={cfg.I}")
+    b = MoeBench(cfg, rotations=2)
+    log("[bench] timing prefill MoE")
+    ms, stages = time_moe(b, args.steps, args.warmup)
+    flops = moe_flops(cfg)
+    value = flops / (ms * 1e-3) / 1e12
+    P = cfg.T * cfg.k
+    g1_flops = 2.0 * P * cfg.H * 2 * cfg.I
+    g2_flops = 2.0 * P * cfg.I * cfg.H
+    g1_ms, g2_ms = stages[3], stages[4]
+    roofline = {"bound": "mfma", "kernel": "gemm1_kernel (first grouped GEMM + SwiGLU)",
+                "achieved": g1_flops / (g1_ms * 1e-3) / 1e12, "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
+                "frac": g1_flops / (g1_ms * 1e-3) / 1e12 / PEAK_FP4_TFLOPS, "traffic": None,
+                "flops_per_launch": g1_flops, "avg_launch_ms": g1_ms}
+    out = {
+        "metric": "MXFP4 MoE layer TFLOP/s + quantize GB/s, % of MI355X roofline, 1 GPU",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp4 weights x fp6 (hi+lo) activations, fp32 accumulate", "data": "synthetic",
+        "config": {"workload": "prefill-shaped MXFP4 MoE layer, bf16 tokens", "T": cfg.T, "E": cfg.E, "top_k": cfg.k,
+                   "H": cfg.H, "I": cfg.I, "bias": cfg.bias, "parallelism": "single GPU"},
+        "roofline": roofline,
+        "stages_ms": {n: float(v) for n, v in zip(STAGES, stages)},
+        "layer_frac_of_fp4_peak": value / PEAK_FP4_TFLOPS,
+        "gemm2": {"achieved_TFLOP_s": g2_flops / (g2_ms * 1e-3) / 1e12, "avg_launch_ms": g2_ms},
+    }
+    x_bits_host, logits_host = synth.moe_activations(cfg)
+    del b
+    torch.cuda.empty_cache()
+
+    if not args.no_quantize:
+        log("[bench] timing quantize")
+        qr = bench_quantize(args.steps, args.warmup)
+        qr["roofline"] = {"bound": "hbm", "kernel": "quantize_kernel", "achieved": qr["GB_s"], "peak": PEAK_HBM_GBS,
+                          "unit": "GB/s", "frac": qr["GB_s"] / PEAK_HBM_GBS, "traffic": None}
+        out["quantize"] = qr
+        torch.cuda.empty_cache()
+
+    if not args.no_decode:
+        dcfg = synth.MOE_CONFIGS["decode"]
+        log("[bench] timing decode MoE")
+        db = MoeBench(dcfg, rotations=2)
+        dms, dstages = time_moe(db, max(args.steps, 50), args.warmup)
+        _, logits_d = synth.moe_activations(dcfg)
+        from oracle.route import route_ref  # only to count touched experts for the byte count
+        touched = len(np.unique(route_ref(logits_d, dcfg.k)[0]))
+        per_expert = (2 * dcfg.I * dcfg.H // 2 + 2 * dcfg.I * dcfg.H // 32 + dcfg.H * dcfg.I // 2 +
+                      dcfg.H * dcfg.I // 32 + 2 * (2 * dcfg.I + dcfg.H))
+        nbytes = touched * per_expert + dcfg.T * dcfg.H * 4 + dcfg.T * dcfg.E * 4
+        out["decode"] = {"workload": "decode-shaped MXFP4 MoE layer (T=64, E=128, top-8, H=2048, I=768, biases)",
+                         "ms": dms, "stages_ms": {n: float(v) for n, v in zip(STAGES, dstages)},
+                         "touched_experts": touched, "algorithmic_bytes": nbytes,
+                         "GB_s": nbytes / (dms * 1e-3) / 1e9, "frac_of_hbm": nbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                         "TFLOP_s": moe_flops(dcfg) / (dms * 1e-3) / 1e12}
+        del db
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample")
+        moe_cpu, q_cpu = cpu_baselines(cfg, x_bits_host, logits_host)
+        out["cpu_baseline"] = moe_cpu
+        if "quantize" in out:
+            out["quantize"]["cpu_baseline"] = q_cpu
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -163,6 +163,16 @@ int moe_mxfp4_forward(const mxfp4_moe_dims* d, const void* packed_gfx950, const 
                       const float* router_logits, int32_t top_k, int32_t renormalize, void* y_bf16, int32_t* topk_ids,
                       float* topk_w, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Same as moe_mxfp4_forward, and records events[i] (hipEvent_t passed as void*, created by the caller)
+ * on `stream` at stage boundaries: events[0] before the first launch, then after each stage in the
+ * order activation split, routing, pair sort/tile schedule, first GEMM (+SwiGLU), second GEMM
+ * (+combine), bf16 output -- 7 events in all.  Only the first n_events are recorded.  For per-stage
+ * timing (measurement); the computation is identical. */
+int moe_mxfp4_forward_profiled(const mxfp4_moe_dims* d, const void* packed_gfx950, const void* x_bf16, int64_t T,
+                               int64_t ldx, const float* router_logits, int32_t top_k, int32_t renormalize,
+                               void* y_bf16, int32_t* topk_ids, float* topk_w, void* workspace, size_t workspace_bytes,
+                               void* stream, void* const* events, int32_t n_events);
+
 #ifdef __cplusplus
 }
 #endif

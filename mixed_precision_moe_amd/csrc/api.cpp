@@ -28,9 +28,12 @@ int launch_route(const float* logits, int64_t T, int E, int k, int renormalize, 
 int launch_place(const int32_t* ids, const int32_t* counts, int64_t T, int k, int E, int BM, int32_t* offsets,
                  int32_t* poffsets, int32_t* sorted_pairs, int32_t* prow_pair, void* tiles, int32_t* ntiles,
                  hipStream_t stream);
-int launch_gemms(int MT, const MoeGeom& g, const uint8_t* blob, const BlobOffsets& o, bool bias, const uint8_t* xq,
-                 const uint8_t* xs, const int32_t* prow_pair, const float* topw, const void* tiles, const int32_t* ntiles,
-                 int64_t max_tiles, uint8_t* actq, uint8_t* acts, float* yacc, int k, hipStream_t stream);
+int launch_gemm1(int MT, const MoeGeom& g, const uint8_t* blob, const BlobOffsets& o, bool bias, const uint8_t* xq,
+                 const uint8_t* xs, const int32_t* prow_pair, const void* tiles, const int32_t* ntiles, int64_t max_tiles,
+                 uint8_t* actq, uint8_t* acts, int k, hipStream_t stream);
+int launch_gemm2(int MT, const MoeGeom& g, const uint8_t* blob, const BlobOffsets& o, bool bias, const uint8_t* actq,
+                 const uint8_t* acts, const int32_t* prow_pair, const float* topw, const void* tiles,
+                 const int32_t* ntiles, int64_t max_tiles, float* yacc, int k, hipStream_t stream);
 int launch_finish(const float* yacc, void* y, int64_t n, hipStream_t stream);
 
 namespace {
@@ -260,13 +263,15 @@ MX_API size_t moe_mxfp4_workspace_bytes(const mxfp4_moe_dims* d, int64_t T, int3
   return (size_t)fwd_ws(moe_geom(d->E, d->H, d->I), T, top_k).total;
 }
 
-MX_API int moe_mxfp4_forward(const mxfp4_moe_dims* d, const void* packed_gfx950, const void* x_bf16, int64_t T,
-                             int64_t ldx, const float* router_logits, int32_t top_k, int32_t renormalize, void* y_bf16,
-                             int32_t* topk_ids, float* topk_w, void* workspace, size_t workspace_bytes, void* stream) {
+static int forward_impl(const mxfp4_moe_dims* d, const void* packed_gfx950, const void* x_bf16, int64_t T,
+                        int64_t ldx, const float* router_logits, int32_t top_k, int32_t renormalize, void* y_bf16,
+                        int32_t* topk_ids, float* topk_w, void* workspace, size_t workspace_bytes, hipStream_t s,
+                        void* const* events, int32_t n_events) {
   int st = check_dims(d);
   if (st) return st;
   if ((st = check_route_args(T, d->E, top_k))) return st;
   if (ldx < d->H || ldx % 8) return MXFP4_ERR_SHAPE;
+  if (n_events < 0 || (n_events > 0 && !events)) return MXFP4_ERR_NULL;
   if (T == 0) return MXFP4_OK;
   if (!packed_gfx950 || !x_bf16 || !router_logits || !y_bf16 || !workspace) return MXFP4_ERR_NULL;
   if (!aligned(packed_gfx950, 256) || !aligned(x_bf16, 16) || !aligned(router_logits, 4) || !aligned(y_bf16, 16) ||
@@ -283,16 +288,47 @@ MX_API int moe_mxfp4_forward(const mxfp4_moe_dims* d, const void* packed_gfx950,
   int32_t* counts = (int32_t*)(ws + w.counts);
   float* yacc = (float*)(ws + w.yacc);
   const int MT = choose_mt(P, g.E);
-  hipStream_t s = S(stream);
-  if ((st = launch_xprep(x_bf16, T, ldx, g, ws + w.xq, ws + w.xs, yacc, counts, s))) return st;
-  if ((st = launch_route(router_logits, T, (int)g.E, top_k, renormalize, ids, wts, counts, s))) return st;
+  int ev = 0;
+  auto mark = [&]() -> int {
+    if (ev < n_events && hipEventRecord((hipEvent_t)events[ev], s) != hipSuccess) return MXFP4_ERR_DEVICE;
+    ev++;
+    return MXFP4_OK;
+  };
+  if ((st = mark())) return st;
+  if ((st = launch_xprep(x_bf16, T, ldx, g, ws + w.xq, ws + w.xs, yacc, counts, s)) || (st = mark())) return st;
+  if ((st = launch_route(router_logits, T, (int)g.E, top_k, renormalize, ids, wts, counts, s)) || (st = mark()))
+    return st;
   if ((st = launch_place(ids, counts, T, top_k, (int)g.E, 32 * MT, (int32_t*)(ws + w.offsets),
                          (int32_t*)(ws + w.poffsets), (int32_t*)(ws + w.sorted_pairs), (int32_t*)(ws + w.prow_pair),
-                         ws + w.tiles, (int32_t*)(ws + w.ntiles), s)))
+                         ws + w.tiles, (int32_t*)(ws + w.ntiles), s)) ||
+      (st = mark()))
     return st;
-  if ((st = launch_gemms(MT, g, (const uint8_t*)packed_gfx950, o, d->has_bias, ws + w.xq, ws + w.xs,
+  if ((st = launch_gemm1(MT, g, (const uint8_t*)packed_gfx950, o, d->has_bias, ws + w.xq, ws + w.xs,
+                         (const int32_t*)(ws + w.prow_pair), ws + w.tiles, (const int32_t*)(ws + w.ntiles), w.max_tiles,
+                         ws + w.actq, ws + w.acts, top_k, s)) ||
+      (st = mark()))
+    return st;
+  if ((st = launch_gemm2(MT, g, (const uint8_t*)packed_gfx950, o, d->has_bias, ws + w.actq, ws + w.acts,
                          (const int32_t*)(ws + w.prow_pair), wts, ws + w.tiles, (const int32_t*)(ws + w.ntiles),
-                         w.max_tiles, ws + w.actq, ws + w.acts, yacc, top_k, s)))
+                         w.max_tiles, yacc, top_k, s)) ||
+      (st = mark()))
     return st;
-  return launch_finish(yacc, y_bf16, T * g.H, s);
+  if ((st = launch_finish(yacc, y_bf16, T * g.H, s)) || (st = mark())) return st;
+  return MXFP4_OK;
+}
+
+MX_API int moe_mxfp4_forward(const mxfp4_moe_dims* d, const void* packed_gfx950, const void* x_bf16, int64_t T,
+                             int64_t ldx, const float* router_logits, int32_t top_k, int32_t renormalize, void* y_bf16,
+                             int32_t* topk_ids, float* topk_w, void* workspace, size_t workspace_bytes, void* stream) {
+  return forward_impl(d, packed_gfx950, x_bf16, T, ldx, router_logits, top_k, renormalize, y_bf16, topk_ids, topk_w,
+                      workspace, workspace_bytes, S(stream), nullptr, 0);
+}
+
+MX_API int moe_mxfp4_forward_profiled(const mxfp4_moe_dims* d, const void* packed_gfx950, const void* x_bf16,
+                                      int64_t T, int64_t ldx, const float* router_logits, int32_t top_k,
+                                      int32_t renormalize, void* y_bf16, int32_t* topk_ids, float* topk_w,
+                                      void* workspace, size_t workspace_bytes, void* stream, void* const* events,
+                                      int32_t n_events) {
+  return forward_impl(d, packed_gfx950, x_bf16, T, ldx, router_logits, top_k, renormalize, y_bf16, topk_ids, topk_w,
+                      workspace, workspace_bytes, S(stream), events, n_events);
 }

@@ -278,27 +278,40 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const uint8_t* __restrict__ 
 
 }  // namespace
 
-int launch_gemms(int MT, const MoeGeom& g, const uint8_t* blob, const BlobOffsets& o, bool bias, const uint8_t* xq,
-                 const uint8_t* xs, const int32_t* prow_pair, const float* topw, const void* tiles, const int32_t* ntiles,
-                 int64_t max_tiles, uint8_t* actq, uint8_t* acts, float* yacc, int k, hipStream_t stream) {
+static unsigned tiles_grid_y(int64_t max_tiles) { return (unsigned)(max_tiles < 65535 ? max_tiles : 65535); }
+
+int launch_gemm1(int MT, const MoeGeom& g, const uint8_t* blob, const BlobOffsets& o, bool bias, const uint8_t* xq,
+                 const uint8_t* xs, const int32_t* prow_pair, const void* tiles, const int32_t* ntiles, int64_t max_tiles,
+                 uint8_t* actq, uint8_t* acts, int k, hipStream_t stream) {
   const uint16_t* b13 = bias ? (const uint16_t*)(blob + o.b13) : nullptr;
-  const uint16_t* b2 = bias ? (const uint16_t*)(blob + o.b2) : nullptr;
-  const unsigned gy = (unsigned)(max_tiles < 65535 ? max_tiles : 65535);
-  dim3 grid1((unsigned)cdiv(g.nit, 4), gy);
-  dim3 grid2((unsigned)cdiv(g.nht, 4), gy);
-#define G1(MTV)                                                                                                    \
-  hipLaunchKernelGGL(gemm1_kernel<MTV>, grid1, dim3(256), 0, stream, blob + o.w13q, (const uint32_t*)(blob + o.w13s), b13, \
-                     xq, xs, prow_pair, (const int4*)tiles, ntiles, actq, acts, g, k)
-#define G2(MTV)                                                                                                    \
-  hipLaunchKernelGGL(gemm2_kernel<MTV>, grid2, dim3(256), 0, stream, blob + o.w2q, (const uint32_t*)(blob + o.w2s), b2,    \
-                     actq, acts, prow_pair, topw, (const int4*)tiles, ntiles, yacc, g, k)
+  dim3 grid((unsigned)cdiv(g.nit, 4), tiles_grid_y(max_tiles));
+#define G1(MTV)                                                                                                   \
+  hipLaunchKernelGGL(gemm1_kernel<MTV>, grid, dim3(256), 0, stream, blob + o.w13q, (const uint32_t*)(blob + o.w13s), \
+                     b13, xq, xs, prow_pair, (const int4*)tiles, ntiles, actq, acts, g, k)
   switch (MT) {
-    case 1: G1(1); G2(1); break;
-    case 2: G1(2); G2(2); break;
-    case 4: G1(4); G2(4); break;
+    case 1: G1(1); break;
+    case 2: G1(2); break;
+    case 4: G1(4); break;
     default: return MXFP4_ERR_SHAPE;
   }
 #undef G1
+  return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
+}
+
+int launch_gemm2(int MT, const MoeGeom& g, const uint8_t* blob, const BlobOffsets& o, bool bias, const uint8_t* actq,
+                 const uint8_t* acts, const int32_t* prow_pair, const float* topw, const void* tiles,
+                 const int32_t* ntiles, int64_t max_tiles, float* yacc, int k, hipStream_t stream) {
+  const uint16_t* b2 = bias ? (const uint16_t*)(blob + o.b2) : nullptr;
+  dim3 grid((unsigned)cdiv(g.nht, 4), tiles_grid_y(max_tiles));
+#define G2(MTV)                                                                                                   \
+  hipLaunchKernelGGL(gemm2_kernel<MTV>, grid, dim3(256), 0, stream, blob + o.w2q, (const uint32_t*)(blob + o.w2s), b2, \
+                     actq, acts, prow_pair, topw, (const int4*)tiles, ntiles, yacc, g, k)
+  switch (MT) {
+    case 1: G2(1); break;
+    case 2: G2(2); break;
+    case 4: G2(4); break;
+    default: return MXFP4_ERR_SHAPE;
+  }
 #undef G2
   return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
 }
