@@ -193,6 +193,41 @@ def cpu_baselines(cfg, x_bits, logits):
     return moe, quant
 
 
+def run_quantize(args):
+    log("[bench] timing quantize")
+    qr = bench_quantize(args.steps, args.warmup)
+    qr["roofline"] = {"bound": "hbm", "kernel": "quantize_kernel", "achieved": qr["GB_s"], "peak": PEAK_HBM_GBS,
+                      "unit": "GB/s", "frac": qr["GB_s"] / PEAK_HBM_GBS, "traffic": None}
+    return qr
+
+
+def run_decode(args):
+    dcfg = synth.MOE_CONFIGS["decode"]
+    log("[bench] timing decode MoE")
+    db = MoeBench(dcfg, rotations=2)
+    dms, dstages = time_moe(db, max(args.steps, 50), args.warmup)
+    _, logits_d = synth.moe_activations(dcfg)
+    from oracle.route import route_ref  # only to count the experts the batch touches, for the byte count
+    touched = len(np.unique(route_ref(logits_d, dcfg.k)[0]))
+    per_expert = (2 * dcfg.I * dcfg.H // 2 + 2 * dcfg.I * dcfg.H // 32 + dcfg.H * dcfg.I // 2 +
+                  dcfg.H * dcfg.I // 32 + 2 * (2 * dcfg.I + dcfg.H))
+    nbytes = touched * per_expert + dcfg.T * dcfg.H * 4 + dcfg.T * dcfg.E * 4
+    return {"workload": "decode-shaped MXFP4 MoE layer (T=64, E=128, top-8, H=2048, I=768, biases)",
+            "ms": dms, "stages_ms": {n: float(v) for n, v in zip(STAGES, dstages)},
+            "touched_experts": touched, "algorithmic_bytes": nbytes,
+            "GB_s": nbytes / (dms * 1e-3) / 1e9, "frac_of_hbm": nbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "TFLOP_s": moe_flops(dcfg) / (dms * 1e-3) / 1e12}
+
+
+def only_secondary(args):
+    out = {"metric": "MXFP4 MoE layer TFLOP/s + quantize GB/s, % of MI355X roofline, 1 GPU", "only": args.only}
+    if args.only == "decode":
+        out["decode"] = run_decode(args)
+    else:
+        out["quantize"] = run_quantize(args)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -201,7 +236,15 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-quantize", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode", "quantize"], default=None,
+                    help="time one workload only (for profiler runs); the JSON line then holds that workload")
     args = ap.parse_args()
+    if args.only == "prefill":
+        args.no_decode = args.no_quantize = args.no_cpu_baseline = True
+    elif args.only == "decode":
+        args.no_quantize = args.no_cpu_baseline = True
+    elif args.only == "quantize":
+        args.no_decode = args.no_cpu_baseline = True
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this library has no multi-GPU path); got --gpus {args.gpus}",
               file=sys.stderr)
@@ -210,6 +253,8 @@ def main():
     torch.cuda.set_device(0)
 
     cfg = synth.MOE_CONFIGS["prefill"]
+    if args.only in ("decode", "quantize"):
+        return only_secondary(args)
     log(f"[bench] building prefill workload T={cfg.T} E={cfg.E} k={cfg.k} H={cfg.H} I={cfg.I}")
     b = MoeBench(cfg, rotations=2)
     log("[bench] timing prefill MoE")
@@ -228,7 +273,7 @@ def main():
         "metric": "MXFP4 MoE layer TFLOP/s + quantize GB/s, % of MI355X roofline, 1 GPU",
         "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp4 weights x fp6 (hi+lo) activations, fp32 accumulate", "data": "synthetic",
+        "dtype": "fp4 weights x three-term fp6 activations, fp32 accumulate", "data": "synthetic",
         "config": {"workload": "prefill-shaped MXFP4 MoE layer, bf16 tokens", "T": cfg.T, "E": cfg.E, "top_k": cfg.k,
                    "H": cfg.H, "I": cfg.I, "bias": cfg.bias, "parallelism": "single GPU"},
         "roofline": roofline,
@@ -241,30 +286,11 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.no_quantize:
-        log("[bench] timing quantize")
-        qr = bench_quantize(args.steps, args.warmup)
-        qr["roofline"] = {"bound": "hbm", "kernel": "quantize_kernel", "achieved": qr["GB_s"], "peak": PEAK_HBM_GBS,
-                          "unit": "GB/s", "frac": qr["GB_s"] / PEAK_HBM_GBS, "traffic": None}
-        out["quantize"] = qr
+        out["quantize"] = run_quantize(args)
         torch.cuda.empty_cache()
 
     if not args.no_decode:
-        dcfg = synth.MOE_CONFIGS["decode"]
-        log("[bench] timing decode MoE")
-        db = MoeBench(dcfg, rotations=2)
-        dms, dstages = time_moe(db, max(args.steps, 50), args.warmup)
-        _, logits_d = synth.moe_activations(dcfg)
-        from oracle.route import route_ref  # only to count touched experts for the byte count
-        touched = len(np.unique(route_ref(logits_d, dcfg.k)[0]))
-        per_expert = (2 * dcfg.I * dcfg.H // 2 + 2 * dcfg.I * dcfg.H // 32 + dcfg.H * dcfg.I // 2 +
-                      dcfg.H * dcfg.I // 32 + 2 * (2 * dcfg.I + dcfg.H))
-        nbytes = touched * per_expert + dcfg.T * dcfg.H * 4 + dcfg.T * dcfg.E * 4
-        out["decode"] = {"workload": "decode-shaped MXFP4 MoE layer (T=64, E=128, top-8, H=2048, I=768, biases)",
-                         "ms": dms, "stages_ms": {n: float(v) for n, v in zip(STAGES, dstages)},
-                         "touched_experts": touched, "algorithmic_bytes": nbytes,
-                         "GB_s": nbytes / (dms * 1e-3) / 1e9, "frac_of_hbm": nbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                         "TFLOP_s": moe_flops(dcfg) / (dms * 1e-3) / 1e12}
-        del db
+        out["decode"] = run_decode(args)
         torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:

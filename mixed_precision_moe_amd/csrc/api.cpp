@@ -20,8 +20,8 @@ int launch_unpack_gfx950(const MoeGeom& g, const BlobOffsets& o, bool bias, cons
 int launch_repack_standard(const MoeGeom& g, bool bias, const void* w13_q, const void* w13_s, const void* w2_q,
                            const void* w2_s, const void* b13, const void* b2, int bias_is_fp32, bool swap, bool tiled,
                            const size_t off[6], void* out, hipStream_t stream);
-int launch_xprep(const void* x, int64_t T, int64_t ldx, const MoeGeom& g, void* xq, void* xs, float* yacc,
-                 int32_t* counts, hipStream_t stream);
+int launch_xprep(const void* x, int64_t T, int64_t ldx, const MoeGeom& g, void* xq, void* xs, int32_t* counts,
+                 hipStream_t stream);
 int launch_zero_i32(int32_t* p, int n, hipStream_t stream);
 int launch_route(const float* logits, int64_t T, int E, int k, int renormalize, int32_t* ids, float* w,
                  int32_t* counts, hipStream_t stream);
@@ -33,8 +33,8 @@ int launch_gemm1(int MT, const MoeGeom& g, const uint8_t* blob, const BlobOffset
                  uint8_t* actq, uint8_t* acts, int k, hipStream_t stream);
 int launch_gemm2(int MT, const MoeGeom& g, const uint8_t* blob, const BlobOffsets& o, bool bias, const uint8_t* actq,
                  const uint8_t* acts, const int32_t* prow_pair, const float* topw, const void* tiles,
-                 const int32_t* ntiles, int64_t max_tiles, float* yacc, int k, hipStream_t stream);
-int launch_finish(const float* yacc, void* y, int64_t n, hipStream_t stream);
+                 const int32_t* ntiles, int64_t max_tiles, float* obuf, int64_t T, int k, hipStream_t stream);
+int launch_combine(const float* obuf, void* y, int64_t T, int64_t H, int k, hipStream_t stream);
 
 namespace {
 
@@ -286,7 +286,7 @@ static int forward_impl(const mxfp4_moe_dims* d, const void* packed_gfx950, cons
   int32_t* ids = topk_ids ? topk_ids : (int32_t*)(ws + w.ids);
   float* wts = topk_w ? topk_w : (float*)(ws + w.w);
   int32_t* counts = (int32_t*)(ws + w.counts);
-  float* yacc = (float*)(ws + w.yacc);
+  float* obuf = (float*)(ws + w.obuf);
   const int MT = choose_mt(P, g.E);
   int ev = 0;
   auto mark = [&]() -> int {
@@ -295,7 +295,7 @@ static int forward_impl(const mxfp4_moe_dims* d, const void* packed_gfx950, cons
     return MXFP4_OK;
   };
   if ((st = mark())) return st;
-  if ((st = launch_xprep(x_bf16, T, ldx, g, ws + w.xq, ws + w.xs, yacc, counts, s)) || (st = mark())) return st;
+  if ((st = launch_xprep(x_bf16, T, ldx, g, ws + w.xq, ws + w.xs, counts, s)) || (st = mark())) return st;
   if ((st = launch_route(router_logits, T, (int)g.E, top_k, renormalize, ids, wts, counts, s)) || (st = mark()))
     return st;
   if ((st = launch_place(ids, counts, T, top_k, (int)g.E, 32 * MT, (int32_t*)(ws + w.offsets),
@@ -310,10 +310,10 @@ static int forward_impl(const mxfp4_moe_dims* d, const void* packed_gfx950, cons
     return st;
   if ((st = launch_gemm2(MT, g, (const uint8_t*)packed_gfx950, o, d->has_bias, ws + w.actq, ws + w.acts,
                          (const int32_t*)(ws + w.prow_pair), wts, ws + w.tiles, (const int32_t*)(ws + w.ntiles),
-                         w.max_tiles, yacc, top_k, s)) ||
+                         w.max_tiles, obuf, T, top_k, s)) ||
       (st = mark()))
     return st;
-  if ((st = launch_finish(yacc, y_bf16, T * g.H, s)) || (st = mark())) return st;
+  if ((st = launch_combine(obuf, y_bf16, T, g.H, top_k, s)) || (st = mark())) return st;
   return MXFP4_OK;
 }
 

@@ -113,16 +113,24 @@ static inline BlobOffsets blob_offsets(const MoeGeom& g, bool bias) {
 __host__ __device__ inline int w2_perm(int p) { return 8 * ((p & 15) >> 2) + 4 * (p >> 4) + (p & 3); }
 
 // ---------------------------------------------------------------------------------------------
+// Activations enter the block-scaled MFMA as kTerms E2M3 terms x = t0 + t1 + t2, each with its own
+// E8M0 scale per 32 elements: 24 bytes per term per lane; a lane's operand slot holds the three terms
+// back to back (72 bytes) padded to kSlot = 80 bytes (five 16-byte loads).
+constexpr int kTerms = 3;
+constexpr int kSlot = 80;
+
+// ---------------------------------------------------------------------------------------------
 // Forward-pass workspace.  Rows of the expert-sorted order are padded per expert to a multiple of
 // 32 ("padded rows"); a padded row with no pair has pair index -1.
-//   xq  : [T][2*nkt1 blocks][48 B]  per token and 32-element block of x: 24 B hi E2M3 codes, 24 B lo
-//   xs  : [T][ngrp1][2 (hi, lo)][2 (block parity)][4 (tile in group)]  E8M0 bytes
-//   actq: [row group of 32][nkt2][64 lanes][48 B]  the second GEMM's A operand, lane (row l%32,
-//         K block l/32): 24 B hi, 24 B lo
-//   acts: [row group][ngrp2][64 lanes][2 (hi, lo)][4 (tile in group)]
+//   xq  : [T][2*nkt1 blocks][kSlot]  per token and 32-element block of x: the kTerms E2M3 terms
+//   xs  : [T][ngrp1][kTerms][2 (block parity)][4 (tile in group)]  E8M0 bytes
+//   actq: [row group of 32][nkt2][64 lanes][kSlot]  the second GEMM's A operand, lane (row l%32,
+//         K block l/32)
+//   acts: [row group][ngrp2][64 lanes][kTerms][4 (tile in group)]
 //   tiles: int4 (expert, first padded row, valid rows, 0) per M tile of the GEMMs
+//   obuf: fp32 [T*k][H], row t*k + j = topk_w[t][j] * (expert output + b2) of the token's j-th expert
 struct FwdWs {
-  uint64_t counts, offsets, poffsets, sorted_pairs, ids, w, prow_pair, tiles, ntiles, xq, xs, actq, acts, yacc, total;
+  uint64_t counts, offsets, poffsets, sorted_pairs, ids, w, prow_pair, tiles, ntiles, xq, xs, actq, acts, obuf, total;
   int64_t nrows_alloc, max_tiles;
 };
 
@@ -142,11 +150,11 @@ static inline FwdWs fwd_ws(const MoeGeom& g, int64_t T, int64_t k) {
   w.prow_pair = take(4 * w.nrows_alloc);
   w.tiles = take(16 * w.max_tiles);
   w.ntiles = take(16);
-  w.xq = take((uint64_t)T * 2 * g.nkt1 * 48);
-  w.xs = take((uint64_t)T * g.ngrp1 * 16);
-  w.actq = take((uint64_t)(w.nrows_alloc / 32) * g.nkt2 * 64 * 48);
-  w.acts = take((uint64_t)(w.nrows_alloc / 32) * g.ngrp2 * 64 * 8);
-  w.yacc = take((uint64_t)T * g.H * 4);
+  w.xq = take((uint64_t)T * 2 * g.nkt1 * kSlot);
+  w.xs = take((uint64_t)T * g.ngrp1 * kTerms * 8);
+  w.actq = take((uint64_t)(w.nrows_alloc / 32) * g.nkt2 * 64 * kSlot);
+  w.acts = take((uint64_t)(w.nrows_alloc / 32) * g.ngrp2 * 64 * kTerms * 4);
+  w.obuf = take((uint64_t)P * g.H * 4);
   w.total = p;
   return w;
 }

@@ -11,12 +11,13 @@ namespace {
 
 typedef decltype(__builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(bf16x32_t{}, 1.0f)) fp6x32_t;
 
-// Split 32 bf16 values into hi + lo, each 32 E2M3 codes with an E8M0 scale from the 0.75 round-up
-// rule (block maximum / scale < 7 <= 7.5, the E2M3 maximum, so neither term saturates).  The
-// remainder x - hi is exact in bf16: hi is a multiple of x's ulp within one grid step of x.
-struct Fp6Pair {
-  fp6x32_t hi, lo;
-  uint32_t ehi, elo;
+// Split 32 bf16 values into kTerms E2M3 terms x = t0 + t1 + t2: each term is the current remainder
+// quantized with its own E8M0 scale from the 0.75 round-up rule (block maximum / scale < 7 <= 7.5, the
+// E2M3 maximum, so no term saturates), and the next remainder is exact in bf16 (a term is a multiple
+// of the remainder's ulp within one grid step of it).
+struct Fp6Split {
+  fp6x32_t t[kTerms];
+  uint32_t e[kTerms];
 };
 
 MX_DEV uint32_t amax_bits32(const uint32_t* w) {  // 16 words = 32 bf16 -> largest magnitude bits
@@ -26,43 +27,41 @@ MX_DEV uint32_t amax_bits32(const uint32_t* w) {  // 16 words = 32 bf16 -> large
   return m;
 }
 
-MX_DEV Fp6Pair split_fp6(const uint32_t* w /* 16 words */) {
-  Fp6Pair p;
-  bf16x32_t v;
+MX_DEV Fp6Split split_fp6(const uint32_t* w /* 16 words */) {
+  Fp6Split p;
+  uint32_t cur[16];
 #pragma unroll
-  for (int i = 0; i < 16; i++) {
-    bf16x2_t two = __builtin_bit_cast(bf16x2_t, w[i]);
-    v[2 * i] = two[0];
-    v[2 * i + 1] = two[1];
-  }
-  p.ehi = e8m0_from_amax_bits(amax_bits32(w) << 16);
-  const float shi = e8m0_as_scale_operand(p.ehi);
-  p.hi = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(v, shi);
-  auto deq = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(p.hi, shi);
-  uint32_t r[16];
+  for (int i = 0; i < 16; i++) cur[i] = w[i];
 #pragma unroll
-  for (int i = 0; i < 16; i++) {
-    const float a = bf16_bits_to_f32(w[i] & 0xFFFFu) - deq[2 * i];
-    const float b = bf16_bits_to_f32(w[i] >> 16) - deq[2 * i + 1];
-    r[i] = f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
-  }
-  bf16x32_t rv;
+  for (int term = 0; term < kTerms; term++) {
+    bf16x32_t v;
 #pragma unroll
-  for (int i = 0; i < 16; i++) {
-    bf16x2_t two = __builtin_bit_cast(bf16x2_t, r[i]);
-    rv[2 * i] = two[0];
-    rv[2 * i + 1] = two[1];
+    for (int i = 0; i < 16; i++) {
+      bf16x2_t two = __builtin_bit_cast(bf16x2_t, cur[i]);
+      v[2 * i] = two[0];
+      v[2 * i + 1] = two[1];
+    }
+    p.e[term] = e8m0_from_amax_bits(amax_bits32(cur) << 16);
+    const float sc = e8m0_as_scale_operand(p.e[term]);
+    p.t[term] = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(v, sc);
+    if (term + 1 < kTerms) {
+      const auto deq = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(p.t[term], sc);
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        const float a = bf16_bits_to_f32(cur[i] & 0xFFFFu) - deq[2 * i];
+        const float b = bf16_bits_to_f32(cur[i] >> 16) - deq[2 * i + 1];
+        cur[i] = f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+      }
+    }
   }
-  p.elo = e8m0_from_amax_bits(amax_bits32(r) << 16);
-  p.lo = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(rv, e8m0_as_scale_operand(p.elo));
   return p;
 }
 
-// x [T, ldx] bf16 -> xq/xs (hi/lo E2M3 per 32-element block, K padded to a multiple of 64 with zero
-// blocks); also clears the fp32 combine accumulator and the per-expert pair counters.
+// x [T, ldx] bf16 -> xq/xs (three E2M3 terms per 32-element block, K padded to a multiple of 64 with
+// zero blocks); also clears the per-expert pair counters.
 __global__ __launch_bounds__(256) void xprep_kernel(const uint16_t* __restrict__ x, int64_t ldx, int64_t H, int64_t nblk,
                                                     int64_t ngrp, uint8_t* __restrict__ xq, uint8_t* __restrict__ xs,
-                                                    float* __restrict__ yacc, int32_t* __restrict__ counts, int E,
+                                                    int32_t* __restrict__ counts, int E,
                                                     int64_t n) {
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i < E; i += blockDim.x) counts[i] = 0;
@@ -81,20 +80,17 @@ __global__ __launch_bounds__(256) void xprep_kernel(const uint16_t* __restrict__
 #pragma unroll
       for (int j = 0; j < 16; j++) w[j] = 0;
     }
-    Fp6Pair p = split_fp6(w);
-    u32x4_t* dst = reinterpret_cast<u32x4_t*>(xq + (t * nblk + b) * 48);
-    dst[0] = u32x4_t{p.hi[0], p.hi[1], p.hi[2], p.hi[3]};
-    dst[1] = u32x4_t{p.hi[4], p.hi[5], p.lo[0], p.lo[1]};
-    dst[2] = u32x4_t{p.lo[2], p.lo[3], p.lo[4], p.lo[5]};
+    const Fp6Split p = split_fp6(w);
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(xq + (t * nblk + b) * kSlot);
+    dst[0] = u32x4_t{p.t[0][0], p.t[0][1], p.t[0][2], p.t[0][3]};
+    dst[1] = u32x4_t{p.t[0][4], p.t[0][5], p.t[1][0], p.t[1][1]};
+    dst[2] = u32x4_t{p.t[1][2], p.t[1][3], p.t[1][4], p.t[1][5]};
+    dst[3] = u32x4_t{p.t[2][0], p.t[2][1], p.t[2][2], p.t[2][3]};
+    dst[4] = u32x4_t{p.t[2][4], p.t[2][5], 0u, 0u};
     const int64_t grp = b >> 3, j = (b & 7) >> 1, par = b & 1;
-    uint8_t* s = xs + (t * ngrp + grp) * 16 + par * 4 + j;
-    s[0] = (uint8_t)p.ehi;
-    s[8] = (uint8_t)p.elo;
-    if (in) {
-      f32x4_t* y = reinterpret_cast<f32x4_t*>(yacc + t * H + b * 32);
+    uint8_t* s = xs + (t * ngrp + grp) * (kTerms * 8) + par * 4 + j;
 #pragma unroll
-      for (int q = 0; q < 8; q++) y[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int term = 0; term < kTerms; term++) s[term * 8] = (uint8_t)p.e[term];
   }
 }
 
@@ -248,20 +244,6 @@ __global__ __launch_bounds__(256) void place_kernel(const int32_t* __restrict__ 
   }
 }
 
-// y = bf16(yacc), eight values per thread.
-__global__ __launch_bounds__(256) void finish_kernel(const float* __restrict__ yacc, uint16_t* __restrict__ y, int64_t n8) {
-  GRID_STRIDE(i, n8) {
-    const f32x4_t a = reinterpret_cast<const f32x4_t*>(yacc)[2 * i];
-    const f32x4_t b = reinterpret_cast<const f32x4_t*>(yacc)[2 * i + 1];
-    u32x4_t o;
-    o[0] = f32_to_bf16_bits(a[0]) | (f32_to_bf16_bits(a[1]) << 16);
-    o[1] = f32_to_bf16_bits(a[2]) | (f32_to_bf16_bits(a[3]) << 16);
-    o[2] = f32_to_bf16_bits(b[0]) | (f32_to_bf16_bits(b[1]) << 16);
-    o[3] = f32_to_bf16_bits(b[2]) | (f32_to_bf16_bits(b[3]) << 16);
-    reinterpret_cast<u32x4_t*>(y)[i] = o;
-  }
-}
-
 inline unsigned grid_for(int64_t n, int threads = 256) {
   int64_t b = (n + threads - 1) / threads;
   if (b > 65536) b = 65536;
@@ -271,12 +253,12 @@ inline unsigned grid_for(int64_t n, int threads = 256) {
 
 }  // namespace
 
-int launch_xprep(const void* x, int64_t T, int64_t ldx, const MoeGeom& g, void* xq, void* xs, float* yacc,
-                 int32_t* counts, hipStream_t stream) {
+int launch_xprep(const void* x, int64_t T, int64_t ldx, const MoeGeom& g, void* xq, void* xs, int32_t* counts,
+                 hipStream_t stream) {
   const int64_t nblk = 2 * g.nkt1;
   const int64_t n = T * nblk;
   hipLaunchKernelGGL(xprep_kernel, dim3(grid_for(n)), dim3(256), 0, stream, (const uint16_t*)x, ldx, g.H, nblk,
-                     g.ngrp1, (uint8_t*)xq, (uint8_t*)xs, yacc, counts, (int)g.E, n);
+                     g.ngrp1, (uint8_t*)xq, (uint8_t*)xs, counts, (int)g.E, n);
   return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
 }
 
@@ -305,9 +287,3 @@ int launch_place(const int32_t* ids, const int32_t* counts, int64_t T, int k, in
   return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
 }
 
-int launch_finish(const float* yacc, void* y, int64_t n, hipStream_t stream) {
-  const int64_t n8 = n / 8;
-  if (n8 > 0)
-    hipLaunchKernelGGL(finish_kernel, dim3(grid_for(n8)), dim3(256), 0, stream, yacc, (uint16_t*)y, n8);
-  return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
-}
