@@ -20,20 +20,14 @@ int launch_unpack_gfx950(const MoeGeom& g, const BlobOffsets& o, bool bias, cons
 int launch_repack_standard(const MoeGeom& g, bool bias, const void* w13_q, const void* w13_s, const void* w2_q,
                            const void* w2_s, const void* b13, const void* b2, int bias_is_fp32, bool swap, bool tiled,
                            const size_t off[6], void* out, hipStream_t stream);
-int launch_xprep(const void* x, int64_t T, int64_t ldx, const MoeGeom& g, void* xq, void* xs, int32_t* counts,
-                 hipStream_t stream);
-int launch_zero_i32(int32_t* p, int n, hipStream_t stream);
+int launch_xprep(const void* x, int64_t T, int64_t ldx, const MoeGeom& g, void* xq, void* xs, hipStream_t stream);
 int launch_route(const float* logits, int64_t T, int E, int k, int renormalize, int32_t* ids, float* w,
-                 int32_t* counts, hipStream_t stream);
-int launch_place(const int32_t* ids, const int32_t* counts, int64_t T, int k, int E, int BM, int32_t* offsets,
-                 int32_t* poffsets, int32_t* sorted_pairs, int32_t* prow_pair, void* tiles, int32_t* ntiles,
-                 hipStream_t stream);
-int launch_gemm1(int MT, const MoeGeom& g, const uint8_t* blob, const BlobOffsets& o, bool bias, const uint8_t* xq,
-                 const uint8_t* xs, const int32_t* prow_pair, const void* tiles, const int32_t* ntiles, int64_t max_tiles,
-                 uint8_t* actq, uint8_t* acts, int k, hipStream_t stream);
-int launch_gemm2(int MT, const MoeGeom& g, const uint8_t* blob, const BlobOffsets& o, bool bias, const uint8_t* actq,
-                 const uint8_t* acts, const int32_t* prow_pair, const float* topw, const void* tiles,
-                 const int32_t* ntiles, int64_t max_tiles, float* obuf, int64_t T, int k, hipStream_t stream);
+                 int32_t* blkcnt, hipStream_t stream);
+int launch_place(const int32_t* ids, const float* w, int32_t* blkcnt, int64_t T, int k, int E, int BM, int32_t* offsets,
+                 int32_t* poffsets, int32_t* sorted_pairs, int32_t* prow_pair, int32_t* prow_tok, float* prow_w,
+                 void* tiles, int32_t* ntiles, hipStream_t stream);
+int launch_gemm1(int NRG, const GemmArgs& a, int64_t max_tiles, hipStream_t stream);
+int launch_gemm2(int NRG, const GemmArgs& a, int64_t max_tiles, hipStream_t stream);
 int launch_combine(const float* obuf, void* y, int64_t T, int64_t H, int k, hipStream_t stream);
 
 namespace {
@@ -84,7 +78,8 @@ size_t standard_offsets(const mxfp4_moe_dims* d, uint32_t layout, size_t off[6])
   return p;
 }
 
-int choose_mt(int64_t P, int64_t E) {
+// Row groups of 32 per GEMM M tile from the mean rows per expert.
+int choose_nrg(int64_t P, int64_t E) {
   const int64_t avg = P / (E > 0 ? E : 1);
   if (avg < 48) return 1;
   if (avg < 160) return 2;
@@ -92,7 +87,7 @@ int choose_mt(int64_t P, int64_t E) {
 }
 
 struct RouteWs {
-  uint64_t counts, poffsets, prow_pair, tiles, ntiles, total;
+  uint64_t blkcnt, poffsets, prow_pair, prow_tok, prow_w, tiles, ntiles, total;
   int64_t max_tiles;
 };
 
@@ -103,9 +98,11 @@ RouteWs route_ws(int64_t T, int64_t E, int64_t k) {
   w.max_tiles = cdiv(P, 32) + E;
   uint64_t p = 0;
   auto take = [&](uint64_t bytes) { uint64_t o = p; p = align256((int64_t)(p + bytes)); return o; };
-  w.counts = take(4 * E);
+  w.blkcnt = take(4 * cdiv(T, kRouteTokens) * E + 4);
   w.poffsets = take(4 * (E + 1));
   w.prow_pair = take(4 * nrows);
+  w.prow_tok = take(4 * nrows);
+  w.prow_w = take(4 * nrows);
   w.tiles = take(16 * w.max_tiles);
   w.ntiles = take(16);
   w.total = p;
@@ -251,11 +248,11 @@ MX_API int moe_mxfp4_route(const float* router_logits, int64_t T, int32_t E, int
   const RouteWs w = route_ws(T, E, top_k);
   if (workspace_bytes < w.total) return MXFP4_ERR_WORKSPACE;
   uint8_t* ws = (uint8_t*)workspace;
-  int32_t* counts = (int32_t*)(ws + w.counts);
-  if ((st = launch_zero_i32(counts, E, S(stream)))) return st;
-  if ((st = launch_route(router_logits, T, E, top_k, renormalize, topk_ids, topk_w, counts, S(stream)))) return st;
-  return launch_place(topk_ids, counts, T, top_k, E, 32, expert_offsets, (int32_t*)(ws + w.poffsets), sorted_pairs,
-                      (int32_t*)(ws + w.prow_pair), ws + w.tiles, (int32_t*)(ws + w.ntiles), S(stream));
+  int32_t* blkcnt = (int32_t*)(ws + w.blkcnt);
+  if ((st = launch_route(router_logits, T, E, top_k, renormalize, topk_ids, topk_w, blkcnt, S(stream)))) return st;
+  return launch_place(topk_ids, topk_w, blkcnt, T, top_k, E, 32, expert_offsets, (int32_t*)(ws + w.poffsets),
+                      sorted_pairs, (int32_t*)(ws + w.prow_pair), (int32_t*)(ws + w.prow_tok), (float*)(ws + w.prow_w),
+                      ws + w.tiles, (int32_t*)(ws + w.ntiles), S(stream));
 }
 
 MX_API size_t moe_mxfp4_workspace_bytes(const mxfp4_moe_dims* d, int64_t T, int32_t top_k) {
@@ -285,9 +282,8 @@ static int forward_impl(const mxfp4_moe_dims* d, const void* packed_gfx950, cons
   const int64_t P = T * top_k;
   int32_t* ids = topk_ids ? topk_ids : (int32_t*)(ws + w.ids);
   float* wts = topk_w ? topk_w : (float*)(ws + w.w);
-  int32_t* counts = (int32_t*)(ws + w.counts);
   float* obuf = (float*)(ws + w.obuf);
-  const int MT = choose_mt(P, g.E);
+  const int NRG = choose_nrg(P, g.E);
   int ev = 0;
   auto mark = [&]() -> int {
     if (ev < n_events && hipEventRecord((hipEvent_t)events[ev], s) != hipSuccess) return MXFP4_ERR_DEVICE;
@@ -295,24 +291,30 @@ static int forward_impl(const mxfp4_moe_dims* d, const void* packed_gfx950, cons
     return MXFP4_OK;
   };
   if ((st = mark())) return st;
-  if ((st = launch_xprep(x_bf16, T, ldx, g, ws + w.xq, ws + w.xs, counts, s)) || (st = mark())) return st;
-  if ((st = launch_route(router_logits, T, (int)g.E, top_k, renormalize, ids, wts, counts, s)) || (st = mark()))
-    return st;
-  if ((st = launch_place(ids, counts, T, top_k, (int)g.E, 32 * MT, (int32_t*)(ws + w.offsets),
-                         (int32_t*)(ws + w.poffsets), (int32_t*)(ws + w.sorted_pairs), (int32_t*)(ws + w.prow_pair),
-                         ws + w.tiles, (int32_t*)(ws + w.ntiles), s)) ||
+  if ((st = launch_xprep(x_bf16, T, ldx, g, ws + w.xq, ws + w.xs, s)) || (st = mark())) return st;
+  if ((st = launch_route(router_logits, T, (int)g.E, top_k, renormalize, ids, wts, (int32_t*)(ws + w.blkcnt), s)) ||
       (st = mark()))
     return st;
-  if ((st = launch_gemm1(MT, g, (const uint8_t*)packed_gfx950, o, d->has_bias, ws + w.xq, ws + w.xs,
-                         (const int32_t*)(ws + w.prow_pair), ws + w.tiles, (const int32_t*)(ws + w.ntiles), w.max_tiles,
-                         ws + w.actq, ws + w.acts, top_k, s)) ||
+  if ((st = launch_place(ids, wts, (int32_t*)(ws + w.blkcnt), T, top_k, (int)g.E, 32 * NRG, (int32_t*)(ws + w.offsets),
+                         (int32_t*)(ws + w.poffsets), nullptr, (int32_t*)(ws + w.prow_pair),
+                         (int32_t*)(ws + w.prow_tok), (float*)(ws + w.prow_w), ws + w.tiles,
+                         (int32_t*)(ws + w.ntiles), s)) ||
       (st = mark()))
     return st;
-  if ((st = launch_gemm2(MT, g, (const uint8_t*)packed_gfx950, o, d->has_bias, ws + w.actq, ws + w.acts,
-                         (const int32_t*)(ws + w.prow_pair), wts, ws + w.tiles, (const int32_t*)(ws + w.ntiles),
-                         w.max_tiles, obuf, T, top_k, s)) ||
-      (st = mark()))
-    return st;
+  const uint8_t* blob = (const uint8_t*)packed_gfx950;
+  GemmArgs a1 = {blob + o.w13q, blob + o.w13s, d->has_bias ? (const uint16_t*)(blob + o.b13) : nullptr,
+                 ws + w.xq, ws + w.xs, (const int32_t*)(ws + w.prow_tok), (const int32_t*)(ws + w.prow_pair),
+                 (const float*)(ws + w.prow_w), (const int4*)(ws + w.tiles), (const int32_t*)(ws + w.ntiles),
+                 ws + w.actq, ws + w.acts, nullptr, g};
+  if ((st = launch_gemm1(NRG, a1, w.max_tiles, s)) || (st = mark())) return st;
+  GemmArgs a2 = a1;
+  a2.wq = blob + o.w2q;
+  a2.ws = blob + o.w2s;
+  a2.bias = d->has_bias ? (const uint16_t*)(blob + o.b2) : nullptr;
+  a2.xq = ws + w.actq;
+  a2.xs = ws + w.acts;
+  a2.obuf = obuf;
+  if ((st = launch_gemm2(NRG, a2, w.max_tiles, s)) || (st = mark())) return st;
   if ((st = launch_combine(obuf, y_bf16, T, g.H, top_k, s)) || (st = mark())) return st;
   return MXFP4_OK;
 }

@@ -49,16 +49,20 @@ MX_DEV uint32_t f32_to_bf16_bits(float f) {
 // i in nibble i, low nibble first), fp6 is 24 bytes per lane (element i in bits 6i..6i+5); the lane's
 // E8M0 scale is one byte of a 32-bit register selected by the instruction's op_sel.
 //
-//   w13 q : [E][I/32 it][nkt1][2 (gate, up)][64 lanes][16 B]   lane: row it*32 + l%32 of w1 (gate)
-//           or w3 (up), K block 2*kt + l/32 along H.  Blocks past H/32 are zero.
-//   w13 s : [E][I/32][ngrp1][2][64 lanes][4 B]   byte j = scale of K block 2*(4*grp + j) + l/32.
-//   w2 q  : [E][H/32 nt][nkt2][64 lanes][16 B]   lane: row nt*32 + l%32 of w2, K block 2*kt + l/32
-//           along I, elements of the block in the order W2_PERM (the order in which the first GEMM's
-//           epilogue leaves the activation).
-//   w2 s  : [E][H/32][ngrp2][64][4 B]
+// Weight tiles (32 output rows each) are grouped in column blocks of kCB = 16 tiles.  Per expert, per
+// column block and per 64-wide K step the blob holds the 16 tiles' operands back to back (16 KB, one
+// 1 KB piece per tile in lane order) and then, in the scale array, one 16-byte record per lane with
+// the scale byte of each of the 16 tiles:
+//   w13 q : [E][ncb1][nkt1][16 tiles][64 lanes][16 B]   tile j of block c: activation tile
+//           it = 8c + j/2, gate (w1 rows it*32..) for even j, up (w3 rows) for odd j; lane l: row
+//           l%32 of the tile, K block 2*kt + l/32 along H.  Tiles past I/32 and blocks past H/32 are 0.
+//   w13 s : [E][ncb1][nkt1][64 lanes][16 tiles]  bytes
+//   w2 q  : [E][ncb2][nkt2][16][64][16 B]   tile j of block c: output columns (16c + j)*32.. of H;
+//           lane l: row l%32 of the tile, K block 2*kt + l/32 along I, elements of the block in the
+//           order W2_PERM (the order in which the first GEMM's epilogue leaves the activation).
+//   w2 s  : [E][ncb2][nkt2][64][16]
 //   b13   : bf16 [E][2I] (gate half first), b2 : bf16 [E][H]
-// nkt = ceil(K / 64) tiles of 64 along K, ngrp = ceil(nkt / 4) groups of four tiles (one scale
-// register per lane per group).
+// nkt = ceil(K / 64) steps along K; ncb1 = ceil(2 * (I/32) / 16), ncb2 = ceil((H/32) / 16).
 struct BlobHeader {
   char magic[8];
   uint32_t version;
@@ -69,13 +73,15 @@ struct BlobHeader {
 static_assert(sizeof(BlobHeader) <= 256, "header fits in 256 bytes");
 
 #define MX_BLOB_MAGIC "MX4GFX95"
-#define MX_BLOB_VERSION 1u
+#define MX_BLOB_VERSION 2u
+
+constexpr int kCB = 16;  // weight tiles per column block
 
 struct MoeGeom {
   int64_t E, H, I;
-  int64_t nkt1, ngrp1;  // along H (first GEMM's K)
-  int64_t nkt2, ngrp2;  // along I (second GEMM's K)
-  int64_t nit, nht;     // I/32, H/32
+  int64_t nkt1, nkt2;  // 64-wide K steps along H (first GEMM) and along I (second GEMM)
+  int64_t nit, nht;    // I/32, H/32
+  int64_t ncb1, ncb2;  // column blocks of the two GEMMs
 };
 
 static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -84,9 +90,11 @@ static inline int64_t align256(int64_t a) { return (a + 255) & ~(int64_t)255; }
 static inline MoeGeom moe_geom(int64_t E, int64_t H, int64_t I) {
   MoeGeom g;
   g.E = E; g.H = H; g.I = I;
-  g.nkt1 = cdiv(H, 64); g.ngrp1 = cdiv(g.nkt1, 4);
-  g.nkt2 = cdiv(I, 64); g.ngrp2 = cdiv(g.nkt2, 4);
+  g.nkt1 = cdiv(H, 64);
+  g.nkt2 = cdiv(I, 64);
   g.nit = I / 32; g.nht = H / 32;
+  g.ncb1 = cdiv(2 * g.nit, kCB);
+  g.ncb2 = cdiv(g.nht, kCB);
   return g;
 }
 
@@ -97,10 +105,10 @@ struct BlobOffsets {
 static inline BlobOffsets blob_offsets(const MoeGeom& g, bool bias) {
   BlobOffsets o;
   uint64_t p = 256;
-  o.w13q = p; p = align256(p + (uint64_t)g.E * g.nit * g.nkt1 * 2 * 1024);
-  o.w13s = p; p = align256(p + (uint64_t)g.E * g.nit * g.ngrp1 * 2 * 256);
-  o.w2q = p;  p = align256(p + (uint64_t)g.E * g.nht * g.nkt2 * 1024);
-  o.w2s = p;  p = align256(p + (uint64_t)g.E * g.nht * g.ngrp2 * 256);
+  o.w13q = p; p = align256(p + (uint64_t)g.E * g.ncb1 * g.nkt1 * kCB * 1024);
+  o.w13s = p; p = align256(p + (uint64_t)g.E * g.ncb1 * g.nkt1 * 1024);
+  o.w2q = p;  p = align256(p + (uint64_t)g.E * g.ncb2 * g.nkt2 * kCB * 1024);
+  o.w2s = p;  p = align256(p + (uint64_t)g.E * g.ncb2 * g.nkt2 * 1024);
   o.b13 = p;  p = align256(p + (bias ? (uint64_t)g.E * 2 * g.I * 2 : 0));
   o.b2 = p;   p = align256(p + (bias ? (uint64_t)g.E * g.H * 2 : 0));
   o.total = p;
@@ -113,24 +121,30 @@ static inline BlobOffsets blob_offsets(const MoeGeom& g, bool bias) {
 __host__ __device__ inline int w2_perm(int p) { return 8 * ((p & 15) >> 2) + 4 * (p >> 4) + (p & 3); }
 
 // ---------------------------------------------------------------------------------------------
-// Activations enter the block-scaled MFMA as kTerms E2M3 terms x = t0 + t1 + t2, each with its own
-// E8M0 scale per 32 elements: 24 bytes per term per lane; a lane's operand slot holds the three terms
-// back to back (72 bytes) padded to kSlot = 80 bytes (five 16-byte loads).
-constexpr int kTerms = 3;
-constexpr int kSlot = 80;
+// Activations enter the block-scaled MFMA as kTerms E2M3 terms x = t0 + t1, each with its own E8M0
+// scale per 32 elements: 24 bytes per term per lane, the two terms back to back in a kSlot = 48 byte
+// slot; the two scale bytes of a slot sit in one dword (term 0 in the low byte, two zero bytes).
+constexpr int kTerms = 2;
+constexpr int kSlot = 48;
 
 // ---------------------------------------------------------------------------------------------
 // Forward-pass workspace.  Rows of the expert-sorted order are padded per expert to a multiple of
-// 32 ("padded rows"); a padded row with no pair has pair index -1.
-//   xq  : [T][2*nkt1 blocks][kSlot]  per token and 32-element block of x: the kTerms E2M3 terms
-//   xs  : [T][ngrp1][kTerms][2 (block parity)][4 (tile in group)]  E8M0 bytes
+// 32 ("padded rows"); a padded row with no pair has pair index -1, token 0 and weight 0.
+//   blkcnt : [nblk_route][E]  pairs per (block of kRouteTokens tokens, expert); after the scan, the
+//            exclusive prefix over blocks
+//   xq  : [T][2*nkt1 blocks][kSlot]  per token and 32-element block of x: the two E2M3 terms
+//   xs  : [T][2*nkt1 blocks][4]      E8M0 bytes of the two terms, two zero bytes (one dword per slot:
+//         LDS DMA moves whole dwords per lane)
 //   actq: [row group of 32][nkt2][64 lanes][kSlot]  the second GEMM's A operand, lane (row l%32,
 //         K block l/32)
-//   acts: [row group][ngrp2][64 lanes][kTerms][4 (tile in group)]
+//   acts: [row group][nkt2][64 lanes][4]
 //   tiles: int4 (expert, first padded row, valid rows, 0) per M tile of the GEMMs
 //   obuf: fp32 [T*k][H], row t*k + j = topk_w[t][j] * (expert output + b2) of the token's j-th expert
+constexpr int kRouteTokens = 64;
+
 struct FwdWs {
-  uint64_t counts, offsets, poffsets, sorted_pairs, ids, w, prow_pair, tiles, ntiles, xq, xs, actq, acts, obuf, total;
+  uint64_t blkcnt, offsets, poffsets, sorted_pairs, ids, w, prow_pair, prow_tok, prow_w, tiles, ntiles, xq, xs, actq,
+      acts, obuf, total;
   int64_t nrows_alloc, max_tiles;
 };
 
@@ -141,20 +155,40 @@ static inline FwdWs fwd_ws(const MoeGeom& g, int64_t T, int64_t k) {
   w.max_tiles = cdiv(P, 32) + g.E;
   uint64_t p = 0;
   auto take = [&](uint64_t bytes) { uint64_t o = p; p = align256(p + bytes); return o; };
-  w.counts = take(4 * g.E);
+  w.blkcnt = take(4 * cdiv(T, kRouteTokens) * g.E);
   w.offsets = take(4 * (g.E + 1));
   w.poffsets = take(4 * (g.E + 1));
   w.sorted_pairs = take(4 * P);
   w.ids = take(4 * P);
   w.w = take(4 * P);
   w.prow_pair = take(4 * w.nrows_alloc);
+  w.prow_tok = take(4 * w.nrows_alloc);
+  w.prow_w = take(4 * w.nrows_alloc);
   w.tiles = take(16 * w.max_tiles);
   w.ntiles = take(16);
   w.xq = take((uint64_t)T * 2 * g.nkt1 * kSlot);
-  w.xs = take((uint64_t)T * g.ngrp1 * kTerms * 8);
+  w.xs = take((uint64_t)T * 2 * g.nkt1 * 4);
   w.actq = take((uint64_t)(w.nrows_alloc / 32) * g.nkt2 * 64 * kSlot);
-  w.acts = take((uint64_t)(w.nrows_alloc / 32) * g.ngrp2 * 64 * kTerms * 4);
+  w.acts = take((uint64_t)(w.nrows_alloc / 32) * g.nkt2 * 64 * 4);
   w.obuf = take((uint64_t)P * g.H * 4);
   w.total = p;
   return w;
 }
+
+// Arguments of the grouped GEMM kernels (device pointers into the blob and the workspace).
+struct GemmArgs {
+  const uint8_t* wq;        // weight pieces of this GEMM
+  const uint8_t* ws;        // weight scale records
+  const uint16_t* bias;     // b13 or b2 (bf16) or NULL
+  const uint8_t* xq;        // first GEMM: per-token slots; second: activation slots by row group
+  const uint8_t* xs;        // matching scale pairs
+  const int32_t* prow_tok;  // padded row -> token
+  const int32_t* prow_pair; // padded row -> pair (-1 = padding)
+  const float* prow_w;      // padded row -> routing weight
+  const int4* tiles;
+  const int32_t* ntiles;
+  uint8_t* actq;            // first GEMM output
+  uint8_t* acts;
+  float* obuf;              // second GEMM output
+  MoeGeom g;
+};

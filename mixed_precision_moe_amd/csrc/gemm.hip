@@ -1,25 +1,35 @@
 // Grouped expert GEMMs of the MoE layer on gfx950 block-scaled MFMA
-// (v_mfma_scale_f32_32x32x64_f8f6f4), with the SwiGLU and the weighted scatter-combine fused into
-// their epilogues.
+// (v_mfma_scale_f32_32x32x64_f8f6f4), with the SwiGLU and the routing-weighted output fused into
+// their epilogues, and the final combine over the top-k experts of each token.
 //
 // [NS: grouped w13 GEMM, SwiGLU = silu(w1 half) * (w3 half), grouped w2 GEMM, weighted top-k combine;
 //  MXFP4 weights with E8M0 scales per 32 elements; P1 Implementation breakdown: the mixed-input fused
 //  MoE multiplies packed 4-bit weights with per-32 group scales by 16-bit activations]
 //
-// The MFMA has no bf16 operand, so a bf16 activation enters as three E2M3 (FP6) terms x = t0 + t1 + t2,
-// each with its own E8M0 scale per 32 elements, and every product is issued once per term against the
-// same FP4 weight registers.  FP6 x FP4 runs at the FP4 rate on gfx950.  Two terms keep only about
-// eight bits relative to the block maximum, which is not enough for the elementwise tolerance on
-// millions of outputs; three terms leave the bf16 rounding of the activation as the largest error.
+// The MFMA has no bf16 operand, so a bf16 activation enters as two E2M3 (FP6) terms x = t0 + t1, each
+// with its own E8M0 scale per 32 elements, and every product is issued once per term against the same
+// FP4 weight registers; FP6 x FP4 runs at the FP4 rate on gfx950.  The first GEMM's output (the SwiGLU
+// activation) stays fp32 until it is split into the second GEMM's two terms, and the second GEMM writes
+// fp32 rows that the combine sums in fp32, so the only bf16 rounding after the input is the output's.
 //
 // First GEMM, transposed: D[n][m] = sum_k W13[n][k] x[m][k], weights as the A operand (rows n = 32
-// gate or up rows of one 32-column tile), tokens as the B operand (columns m = 32 tokens gathered from
-// the sorted pair list).  Lane l of the 32x32 result holds token l%32 and rows 8*jj + 4*(l/32) + i, so
+// gate or up rows of one tile), tokens as the B operand (columns m = 32 tokens gathered through the
+// padded row order).  Lane l of the 32x32 result holds token l%32 and rows 8*jj + 4*(l/32) + i, so
 // gate and up of one column sit in the same lane (SwiGLU in registers) and a 32-element block of the
 // activation is split over the two lane halves (one exchange for the block maximum).
 //
 // Second GEMM, not transposed: D[m][n] = sum_k act[m][k] W2[n][k]; lane l holds output column l%32 and
-// rows 8*jj + 4*(l/32) + i, so each fp32 atomic instruction adds 2 x 32 consecutive floats.
+// rows 8*jj + 4*(l/32) + i, so each store instruction writes 2 x 32 consecutive floats of o_buf.
+//
+// Both GEMMs run one kernel template.  A workgroup of four waves (WR x WC) computes an M tile of
+// NRG = WR*RW row groups of 32 rows against NT = WC*CW weight tiles of 32 columns; wave (wr, wc) holds
+// RW x CW accumulators.  Per 64-wide K step the workgroup copies the step's operands global -> LDS
+// with LDS DMA (global_load_lds: no registers, no address math beyond the source) into a ring of D
+// stages: every wave issues the same number of copies per stage, waits for its own with vmcnt and one
+// barrier per step publishes the stage.  Operand fragments of step kt+1 are read from LDS while the
+// MFMAs of step kt run.  Work items (M tile, column position) are dealt to XCDs in contiguous ranges
+// so the column positions of one M tile (same gathered tokens) and consecutive tiles of one expert
+// (same weights) share an XCD's L2.
 #include <type_traits>
 
 #include "common.h"
@@ -27,33 +37,73 @@
 namespace {
 
 typedef decltype(__builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(bf16x32_t{}, 1.0f)) fp6x32_t;
-
-MX_DEV u32x4_t ld16(const uint8_t* p) { return *reinterpret_cast<const u32x4_t*>(p); }
-
-MX_DEV i32x8_t fp4_operand(u32x4_t v) {
-  return i32x8_t{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
-}
-// One operand slot (kSlot bytes): the three E2M3 terms, 6 dwords each, back to back.
-MX_DEV void fp6_term_operands(const uint8_t* p, i32x8_t* o) {
-  const u32x4_t a = ld16(p), b = ld16(p + 16), c = ld16(p + 32), d = ld16(p + 48), f = ld16(p + 64);
-  o[0] = i32x8_t{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], 0, 0};
-  o[1] = i32x8_t{(int)b[2], (int)b[3], (int)c[0], (int)c[1], (int)c[2], (int)c[3], 0, 0};
-  o[2] = i32x8_t{(int)d[0], (int)d[1], (int)d[2], (int)d[3], (int)f[0], (int)f[1], 0, 0};
-}
+typedef __attribute__((address_space(3))) void* lds_vptr_t;
 
 constexpr int kFp4 = 4, kFp6 = 2;  // MFMA operand format codes (E2M1, E2M3)
+constexpr int kXcds = 8;           // workgroup b runs on XCD b % 8
 
-template <int MT>
-struct G1Acc {
-  f32x16_t g[MT], u[MT];
-};
+MX_DEV u32x4_t ld16(const uint8_t* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+MX_DEV u32x2_t ld8(const uint8_t* p) { return *reinterpret_cast<const u32x2_t*>(p); }
+
+// LDS DMA: lane i copies 16 (or 4) bytes from its global address to lds_wave_base + i * 16 (or 4).
+// (Sub-dword copies still occupy a dword per lane in LDS, so every copied record here is a dword or
+// a multiple of 16 bytes.)
+MX_DEV void dma16(const void* g, uint8_t* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_vptr_t)lds_wave_base, 16, 0, 0);
+}
+MX_DEV void dma4(const void* g, uint8_t* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_vptr_t)lds_wave_base, 4, 0, 0);
+}
+
+// f(integral_constant<int, i>) for i = 0 .. N-1 (operand selectors of the MFMA must be literals).
+template <int I, int N, typename F>
+MX_DEV void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+template <int N>
+MX_DEV void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+MX_DEV void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Barrier without the implied full vmcnt wait of __syncthreads: the LDS DMA copies are waited for
+// explicitly, so only LDS and compiler ordering are needed here.
+MX_DEV void block_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 MX_DEV float silu(float g) { return g / (1.0f + __expf(-g)); }
 
+// ------------------------------------------------------------------------------------------------
+// Kernel configuration.  LDS stage: [NT weight pieces of 1 KB][1 KB weight scale records of the
+// column block][NRG x 3 KB activation slots, lane-major][NRG x 256 B activation scale dwords].
+template <int WR, int WC, int RW, int CW, int D>
+struct Cfg {
+  static constexpr int NRG = WR * RW, NT = WC * CW;
+  static_assert(WR * WC == 4, "four waves");
+  static_assert(NT == 8 || NT == 16, "a workgroup covers a column block or half of one");
+  static_assert(CW % 4 == 0, "weight scales are read four tiles per dword");
+  static_assert(D >= 3 && D <= 6, "ring depth");  // stages issued D - 1 steps ahead
+  static constexpr int oW = 0, oWS = NT * 1024, oX = oWS + 1024, oXS = oX + NRG * 3072;
+  static constexpr int kStage = oXS + NRG * 256;
+  static constexpr int nW = NT / 4;              // weight pieces copied per wave
+  static constexpr int nX = (3 * NRG + 3) / 4;   // 1 KB activation copies per wave (last one repeated)
+  static constexpr int nXS = (NRG + 3) / 4;      // activation scale copies per wave
+  static constexpr int kOps = nW + 1 + nX + nXS; // copies per wave per stage
+};
+
+
 // First GEMM epilogue for one (32-column activation tile `it`, row group `rg`) result held by one
-// wave: bias, SwiGLU in fp32, then the three-term E2M3 split of each 32-element block (one block = the
+// wave: bias, SwiGLU in fp32, then the two-term E2M3 split of each 32-element block (one block = the
 // two lane halves of a token column; each block maximum needs one exchange across the halves), written
-// in the second GEMM's operand layout.  The last K tile of the second GEMM is completed with a zero
+// in the second GEMM's operand layout.  The last K step of the second GEMM is completed with a zero
 // block when I/32 is odd.
 MX_DEV void g1_epilogue_tile(const f32x16_t& accg, const f32x16_t& accu, const uint16_t* __restrict__ b13,
                              uint8_t* __restrict__ actq, uint8_t* __restrict__ acts, const MoeGeom& g, int e, int64_t it,
@@ -71,10 +121,10 @@ MX_DEV void g1_epilogue_tile(const f32x16_t& accg, const f32x16_t& accu, const u
     cur[q] = silu(accg[q] + b1) * (accu[q] + b3);
   }
   const int64_t kt2 = it >> 1, kb = it & 1;
-  uint8_t* chunk = actq + ((rg * g.nkt2 + kt2) * 64 + kb * 32 + m) * kSlot;
-  uint8_t* sc = acts + ((rg * g.ngrp2 + (kt2 >> 2)) * 64 + kb * 32 + m) * (kTerms * 4) + (kt2 & 3);
-  // Each term quantizes the bf16 rounding of the fp32 remainder; the remainder itself stays fp32
-  // (subtracting a term, a multiple of the remainder's ulp within one grid step, is exact in fp32).
+  const int64_t slot = (rg * g.nkt2 + kt2) * 64 + kb * 32 + m;
+  uint8_t* chunk = actq + slot * kSlot;
+  uint32_t scales = 0;
+  // Each term quantizes the bf16 rounding of the fp32 remainder; the remainder itself stays fp32.
 #pragma unroll
   for (int term = 0; term < kTerms; term++) {
     uint32_t rb[16];
@@ -98,813 +148,262 @@ MX_DEV void g1_epilogue_tile(const f32x16_t& accg, const f32x16_t& accu, const u
     tp[0] = codes[0];
     tp[1] = codes[1];
     tp[2] = codes[2];
-    if (h == 0) sc[term * 4] = (uint8_t)ex;
+    scales |= ex << (8 * term);
     if (term + 1 < kTerms) {
       const auto deq = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(codes, sv);
 #pragma unroll
       for (int q = 0; q < 16; q++) cur[q] = cur[q] - deq[q];
     }
   }
+  if (h == 0) reinterpret_cast<uint32_t*>(acts)[slot] = scales;
   if ((it == g.nit - 1) && (g.nit & 1)) {
-    uint32_t* zp = reinterpret_cast<uint32_t*>(actq + ((rg * g.nkt2 + kt2) * 64 + 32 + m) * kSlot + h * (kSlot / 2));
+    const int64_t zslot = (rg * g.nkt2 + kt2) * 64 + 32 + m;
+    uint32_t* zp = reinterpret_cast<uint32_t*>(actq + zslot * kSlot + h * (kSlot / 2));
 #pragma unroll
     for (int q = 0; q < kSlot / 8; q++) zp[q] = 0;
-    if (h == 0) {
-      uint8_t* zs = acts + ((rg * g.ngrp2 + (kt2 >> 2)) * 64 + 32 + m) * (kTerms * 4) + (kt2 & 3);
-#pragma unroll
-      for (int term = 0; term < kTerms; term++) zs[term * 4] = 0;
-    }
-  }
-}
-
-template <int MT>
-MX_DEV void g1_epilogue(const G1Acc<MT>& acc, const uint16_t* __restrict__ b13, uint8_t* __restrict__ actq,
-                        uint8_t* __restrict__ acts, const MoeGeom& g, int e, int64_t it, int prow0, int nvg, int lane) {
-#pragma unroll
-  for (int mt = 0; mt < MT; mt++)
-    if (mt < nvg) g1_epilogue_tile(acc.g[mt], acc.u[mt], b13, actq, acts, g, e, it, (prow0 >> 5) + mt, lane);
-}
-
-// ------------------------------------------------------------------------------------------------
-// First GEMM + SwiGLU + three-term split of the activation.
-//
-// Workgroup: NW waves; wave w owns the 32 activation columns of tile it = blockIdx.x*NW + w (its gate
-// and up weight rows, 2 x 32) against the MT*32 tokens of one M tile.  The token operand of each 64-K
-// step is shared by all waves, so the workgroup stages it in LDS (double-buffered): thread t copies
-// 16-byte pieces of the gathered three-term rows, and each wave then reads its MFMA operands (one slot per lane)
-// from LDS.  The weight operand is private to the wave and is loaded straight from global memory one
-// K step ahead.  One barrier per K step.  grid: x = column tiles / NW, y = M tiles (strided loop).
-template <int MT, int NW>
-struct G1Smem {
-  uint8_t b[2][MT * 64 * kSlot];
-  int32_t tok[MT * 32];
-};
-
-// DEEP (used for single-row-group tiles, i.e. decode shapes): the weight operand of the next group of
-// four K steps is requested while the current group computes, so each wave keeps 8 KB of weights in
-// flight -- the weight stream is the bound there.  Otherwise one K step ahead (fewer registers).
-template <int MT, int NW, bool DEEP>
-__global__ __launch_bounds__(NW * 64) void gemm1_kernel(const uint8_t* __restrict__ w13q, const uint32_t* __restrict__ w13s,
-                                                         const uint16_t* __restrict__ b13, const uint8_t* __restrict__ xq,
-                                                         const uint8_t* __restrict__ xs,
-                                                         const int32_t* __restrict__ prow_pair,
-                                                         const int4* __restrict__ tiles, const int32_t* __restrict__ ntiles,
-                                                         uint8_t* __restrict__ actq, uint8_t* __restrict__ acts, MoeGeom g,
-                                                         int k) {
-  __shared__ G1Smem<MT, NW> sm;
-  constexpr int kThreads = NW * 64;
-  constexpr int kChunks = MT * 64 * (kSlot / 16);  // 16-byte pieces of one staged token tile
-  constexpr int kPer = (kChunks + kThreads - 1) / kThreads;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t it_raw = (int64_t)blockIdx.x * NW + wave;
-  const bool active = it_raw < g.nit;  // wave-uniform; inactive waves only help with loads and barriers
-  const int64_t it = active ? it_raw : 0;
-  const int64_t nblk1 = 2 * g.nkt1;
-  const int nt_all = *ntiles;
-
-  for (int tile = blockIdx.y; tile < nt_all; tile += gridDim.y) {
-    const int4 td = tiles[tile];
-    const int e = td.x, prow0 = td.y, nrows = td.z;
-    const int nvg = (nrows + 31) >> 5;
-    __syncthreads();  // the previous tile's readers are done with sm
-    for (int r = tid; r < MT * 32; r += kThreads) {
-      int tok = 0;
-      if (r < nrows) {
-        const int pair = prow_pair[prow0 + r];
-        if (pair >= 0) tok = pair / k;
-      }
-      sm.tok[r] = tok;
-    }
-    __syncthreads();
-
-    const uint8_t* src[kPer];
-    int dst[kPer];
-    bool live[kPer];
-#pragma unroll
-    for (int i = 0; i < kPer; i++) {
-      const int c = tid + i * kThreads;
-      const int slot = c / (kSlot / 16), part = c - (kSlot / 16) * slot;
-      const int mt = slot >> 6, ln = slot & 63;
-      live[i] = c < kChunks && mt < nvg;
-      const int tok = live[i] ? sm.tok[mt * 32 + (ln & 31)] : 0;
-      src[i] = xq + ((int64_t)tok * nblk1 + (ln >> 5)) * kSlot + part * 16;
-      dst[i] = slot * kSlot + part * 16;
-    }
-    const uint8_t* xsrow[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; mt++)
-      xsrow[mt] = xs + (int64_t)sm.tok[mt * 32 + (lane & 31)] * g.ngrp1 * (kTerms * 8) + (lane >> 5) * 4;
-    const uint8_t* wa = w13q + ((int64_t)e * g.nit + it) * g.nkt1 * 2048 + lane * 16;
-    const uint32_t* wsa = w13s + ((int64_t)e * g.nit + it) * g.ngrp1 * 128 + lane;
-
-    G1Acc<MT> acc;
-#pragma unroll
-    for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-      for (int i = 0; i < 16; i++) { acc.g[mt][i] = 0.f; acc.u[mt][i] = 0.f; }
-
-    // prologue: K step 0
-    {
-      u32x4_t stage[kPer];
-#pragma unroll
-      for (int i = 0; i < kPer; i++)
-        if (live[i]) stage[i] = ld16(src[i]);
-#pragma unroll
-      for (int i = 0; i < kPer; i++)
-        if (live[i]) *reinterpret_cast<u32x4_t*>(&sm.b[0][dst[i]]) = stage[i];
-    }
-    u32x4_t ag = {0u, 0u, 0u, 0u}, au = {0u, 0u, 0u, 0u};
-    u32x4_t cg[4], cu[4];  // DEEP: weights of the current group of K steps
-    if (active) {
-      if constexpr (DEEP) {
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-          if (j < g.nkt1) {
-            cg[j] = ld16(wa + j * 2048);
-            cu[j] = ld16(wa + j * 2048 + 1024);
-          }
-        }
-      } else {
-        ag = ld16(wa);
-        au = ld16(wa + 1024);
-      }
-    }
-    __syncthreads();
-
-    for (int64_t grp = 0; grp < g.ngrp1; grp++) {
-      u32x4_t ng[4], nu[4];
-      if constexpr (DEEP) {
-        if (active && grp + 1 < g.ngrp1) {
-#pragma unroll
-          for (int j = 0; j < 4; j++) {
-            const int64_t kn = (grp + 1) * 4 + j;
-            if (kn < g.nkt1) {
-              ng[j] = ld16(wa + kn * 2048);
-              nu[j] = ld16(wa + kn * 2048 + 1024);
-            }
-          }
-        }
-      }
-      uint32_t sg = 0, su = 0;
-      uint32_t sx[MT][kTerms];
-      if (active) {
-        sg = wsa[grp * 128];
-        su = wsa[grp * 128 + 64];
-#pragma unroll
-        for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-          for (int term = 0; term < kTerms; term++)
-            sx[mt][term] = *reinterpret_cast<const uint32_t*>(xsrow[mt] + grp * (kTerms * 8) + term * 8);
-      }
-      auto step = [&](auto jc) {
-        constexpr int J = decltype(jc)::value;
-        const int64_t kt = grp * 4 + J;
-        const bool more = kt + 1 < g.nkt1;
-        u32x4_t stage[kPer];
-        u32x4_t ag_n = ag, au_n = au;
-        if (more) {
-#pragma unroll
-          for (int i = 0; i < kPer; i++)
-            if (live[i]) stage[i] = ld16(src[i] + (kt + 1) * (2 * kSlot));
-          if constexpr (!DEEP) {
-            if (active) {
-              ag_n = ld16(wa + (kt + 1) * 2048);
-              au_n = ld16(wa + (kt + 1) * 2048 + 1024);
-            }
-          }
-        }
-        if (active) {
-          const i32x8_t a_g = fp4_operand(DEEP ? cg[J] : ag), a_u = fp4_operand(DEEP ? cu[J] : au);
-          const uint8_t* bb = sm.b[kt & 1];
-#pragma unroll
-          for (int mt = 0; mt < MT; mt++) {
-            if (mt < nvg) {
-              i32x8_t bt[kTerms];
-              fp6_term_operands(bb + (mt * 64 + lane) * kSlot, bt);
-#pragma unroll
-              for (int term = 0; term < kTerms; term++) {
-                acc.g[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a_g, bt[term], acc.g[mt], kFp4, kFp6, J, sg, J,
-                                                                            sx[mt][term]);
-                acc.u[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a_u, bt[term], acc.u[mt], kFp4, kFp6, J, su, J,
-                                                                            sx[mt][term]);
-              }
-            }
-          }
-        }
-        if (more) {
-#pragma unroll
-          for (int i = 0; i < kPer; i++)
-            if (live[i]) *reinterpret_cast<u32x4_t*>(&sm.b[(kt + 1) & 1][dst[i]]) = stage[i];
-        }
-        __syncthreads();
-        ag = ag_n;
-        au = au_n;
-      };
-      step(std::integral_constant<int, 0>{});
-      if (grp * 4 + 1 < g.nkt1) step(std::integral_constant<int, 1>{});
-      if (grp * 4 + 2 < g.nkt1) step(std::integral_constant<int, 2>{});
-      if (grp * 4 + 3 < g.nkt1) step(std::integral_constant<int, 3>{});
-      if constexpr (DEEP) {
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-          cg[j] = ng[j];
-          cu[j] = nu[j];
-        }
-      }
-    }
-    if (active) g1_epilogue<MT>(acc, b13, actq, acts, g, e, it, prow0, nvg, lane);
+    if (h == 0) reinterpret_cast<uint32_t*>(acts)[zslot] = 0;
   }
 }
 
 // ------------------------------------------------------------------------------------------------
-// Second GEMM + bias + routing weight.  Workgroup: NW waves over NW column tiles of 32 (of H) and one
-// M tile; the activation tile (MT row groups, contiguous 3 KB per row group and K step) is staged in
-// LDS, double-buffered; the weight operand is private per wave and prefetched one K step ahead.  The
-// epilogue writes w * (o + b2) as bf16 to o_buf[pair][H] (token-major), and combine_kernel sums the k
-// rows of each token: no atomics, a fixed summation order.
-template <int MT, int NW, bool DEEP>
-__global__ __launch_bounds__(NW * 64) void gemm2_kernel(const uint8_t* __restrict__ w2q, const uint32_t* __restrict__ w2s,
-                                                         const uint16_t* __restrict__ b2, const uint8_t* __restrict__ actq,
-                                                         const uint8_t* __restrict__ acts,
-                                                         const int32_t* __restrict__ prow_pair,
-                                                         const float* __restrict__ topw, const int4* __restrict__ tiles,
-                                                         const int32_t* __restrict__ ntiles, float* __restrict__ obuf,
-                                                         MoeGeom g, int k) {
-  constexpr int kTileBytes = 64 * kSlot;  // one row group's operand for one K step
-  __shared__ uint8_t sa[2][MT * kTileBytes];
-  __shared__ int32_t s_pair[MT * 32];
-  __shared__ float s_w[MT * 32];
-  constexpr int kThreads = NW * 64;
-  constexpr int kChunks = MT * (kTileBytes / 16);
-  constexpr int kPer = (kChunks + kThreads - 1) / kThreads;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t nt_raw = (int64_t)blockIdx.x * NW + wave;
-  const bool active = nt_raw < g.nht;
-  const int64_t nt = active ? nt_raw : 0;
-  const int nt_all = *ntiles;
+// The grouped GEMM.  G1: first GEMM (A = weights, B = gathered token terms, SwiGLU epilogue);
+// otherwise the second GEMM (A = activation terms, B = weights, weighted fp32 rows to o_buf).
+template <bool G1, int WR, int WC, int RW, int CW, int D>
+__global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
+  using C = Cfg<WR, WC, RW, CW, D>;
+  constexpr int NRG = C::NRG, NT = C::NT;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[D * C::kStage];
+  const MoeGeom& g = a.g;
+  const int tid = threadIdx.x;
+  const int64_t nkt = G1 ? g.nkt1 : g.nkt2;
+  const int64_t ncb = G1 ? g.ncb1 : g.ncb2;
+  const int nx = (int)(ncb * kCB / NT);
+  const int64_t nblk = 2 * g.nkt1;  // token slots per row of xq (first GEMM)
 
-  for (int tile = blockIdx.y; tile < nt_all; tile += gridDim.y) {
-    const int4 td = tiles[tile];
-    const int e = td.x, prow0 = td.y, nrows = td.z;
-    const int nvg = (nrows + 31) >> 5;
-    const int64_t rg0 = prow0 >> 5;
-    __syncthreads();  // the previous tile's readers are done with sa, s_pair, s_w
-    for (int r = tid; r < MT * 32; r += kThreads) {
-      int pair = -1;
-      float wt = 0.f;
-      if (r < nrows) {
-        pair = prow_pair[prow0 + r];
-        if (pair >= 0) wt = topw[pair];
-      }
-      s_pair[r] = pair;
-      s_w[r] = wt;
-    }
-
-    const uint8_t* src[kPer];
-    int dst[kPer];
-    bool live[kPer];
-#pragma unroll
-    for (int i = 0; i < kPer; i++) {
-      const int c = tid + i * kThreads;
-      const int mt = c / (kTileBytes / 16), off = (c - (kTileBytes / 16) * mt) * 16;
-      live[i] = c < kChunks && mt < nvg;
-      src[i] = actq + (rg0 + (live[i] ? mt : 0)) * g.nkt2 * kTileBytes + off;
-      dst[i] = mt * kTileBytes + off;
-    }
-    const uint8_t* sarow[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; mt++) sarow[mt] = acts + ((rg0 + mt) * g.ngrp2 * 64 + lane) * (kTerms * 4);
-    const uint8_t* wb = w2q + ((int64_t)e * g.nht + nt) * g.nkt2 * 1024 + lane * 16;
-    const uint32_t* wsb = w2s + ((int64_t)e * g.nht + nt) * g.ngrp2 * 64 + lane;
-
-    f32x16_t acc[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-      for (int i = 0; i < 16; i++) acc[mt][i] = 0.f;
-
-    {
-      u32x4_t stage[kPer];
-#pragma unroll
-      for (int i = 0; i < kPer; i++)
-        if (live[i]) stage[i] = ld16(src[i]);
-#pragma unroll
-      for (int i = 0; i < kPer; i++)
-        if (live[i]) *reinterpret_cast<u32x4_t*>(&sa[0][dst[i]]) = stage[i];
-    }
-    u32x4_t wv = {0u, 0u, 0u, 0u};
-    u32x4_t cw[4];  // DEEP: weights of the current group of K steps
-    if (active) {
-      if constexpr (DEEP) {
-#pragma unroll
-        for (int j = 0; j < 4; j++)
-          if (j < g.nkt2) cw[j] = ld16(wb + j * 1024);
-      } else {
-        wv = ld16(wb);
-      }
-    }
-    __syncthreads();
-
-    for (int64_t grp = 0; grp < g.ngrp2; grp++) {
-      u32x4_t nw[4];
-      if constexpr (DEEP) {
-        if (active && grp + 1 < g.ngrp2) {
-#pragma unroll
-          for (int j = 0; j < 4; j++) {
-            const int64_t kn = (grp + 1) * 4 + j;
-            if (kn < g.nkt2) nw[j] = ld16(wb + kn * 1024);
-          }
-        }
-      }
-      uint32_t sb = 0;
-      uint32_t sa_t[MT][kTerms];
-      if (active) {
-        sb = wsb[grp * 64];
-#pragma unroll
-        for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-          for (int term = 0; term < kTerms; term++)
-            sa_t[mt][term] = mt < nvg ? *reinterpret_cast<const uint32_t*>(sarow[mt] + grp * (64 * kTerms * 4) + term * 4) : 0u;
-      }
-      auto step = [&](auto jc) {
-        constexpr int J = decltype(jc)::value;
-        const int64_t kt = grp * 4 + J;
-        const bool more = kt + 1 < g.nkt2;
-        u32x4_t stage[kPer];
-        u32x4_t wv_n = wv;
-        if (more) {
-#pragma unroll
-          for (int i = 0; i < kPer; i++)
-            if (live[i]) stage[i] = ld16(src[i] + (kt + 1) * kTileBytes);
-          if constexpr (!DEEP) {
-            if (active) wv_n = ld16(wb + (kt + 1) * 1024);
-          }
-        }
-        if (active) {
-          const i32x8_t bw = fp4_operand(DEEP ? cw[J] : wv);
-          const uint8_t* ab = sa[kt & 1];
-#pragma unroll
-          for (int mt = 0; mt < MT; mt++) {
-            if (mt < nvg) {
-              i32x8_t at[kTerms];
-              fp6_term_operands(ab + mt * kTileBytes + lane * kSlot, at);
-#pragma unroll
-              for (int term = 0; term < kTerms; term++)
-                acc[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(at[term], bw, acc[mt], kFp6, kFp4, J, sa_t[mt][term],
-                                                                          J, sb);
-            }
-          }
-        }
-        if (more) {
-#pragma unroll
-          for (int i = 0; i < kPer; i++)
-            if (live[i]) *reinterpret_cast<u32x4_t*>(&sa[(kt + 1) & 1][dst[i]]) = stage[i];
-        }
-        __syncthreads();
-        wv = wv_n;
-      };
-      step(std::integral_constant<int, 0>{});
-      if (grp * 4 + 1 < g.nkt2) step(std::integral_constant<int, 1>{});
-      if (grp * 4 + 2 < g.nkt2) step(std::integral_constant<int, 2>{});
-      if (grp * 4 + 3 < g.nkt2) step(std::integral_constant<int, 3>{});
-      if constexpr (DEEP) {
-#pragma unroll
-        for (int j = 0; j < 4; j++) cw[j] = nw[j];
-      }
-    }
-
-    if (active) {
-      const int64_t col = nt * 32 + (lane & 31);
-      const float bias = b2 ? bf16_bits_to_f32(b2[(int64_t)e * g.H + col]) : 0.f;
-      const int h = lane >> 5;
-#pragma unroll
-      for (int mt = 0; mt < MT; mt++) {
-        if (mt >= nvg) continue;
-#pragma unroll
-        for (int q = 0; q < 16; q++) {
-          const int r = mt * 32 + 8 * (q >> 2) + 4 * h + (q & 3);
-          const int pair = s_pair[r];
-          if (pair >= 0) obuf[(int64_t)pair * g.H + col] = s_w[r] * (acc[mt][q] + bias);
-        }
-      }
-    }
-  }
-}
-
-// ------------------------------------------------------------------------------------------------
-// Row-split kernels for M tiles of WM row groups (prefill shapes).  Wave w owns row group w of the
-// tile; the workgroup shares the weight tiles of each 64-K step.  Every operand of a K step -- the
-// weight tiles and their scale registers, each wave's activation slots and their scale registers --
-// is copied global -> LDS by the gfx950 direct loads (global_load_lds_dwordx4 / _dword: lane i of a
-// wave writes base + i*size), into a ring of D stages, so D-1 steps of loads are in flight while a
-// step computes and no registers are spent on staging.  Each wave waits for its own copies with an
-// exact vmcnt (the same number of copies per wave and step, dummy-but-valid addresses included), then
-// one workgroup barrier makes every wave's copies of that step visible and frees the stage read in
-// the previous step, which is refilled right after the barrier.  Every weight fragment read from LDS
-// feeds three MFMAs (one per activation term), every activation fragment feeds all weight tiles.
-
-typedef __attribute__((address_space(3))) void* lds_vptr_t;
-
-MX_DEV void dma16(const void* g, uint8_t* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_vptr_t)lds_wave_base, 16, 0, 0);
-}
-MX_DEV void dma4(const void* g, uint8_t* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_vptr_t)lds_wave_base, 4, 0, 0);
-}
-// s_waitcnt with vmcnt <= N and no wait on the other counters (gfx9 encoding: vmcnt in bits 3:0 and
-// 15:14, expcnt 6:4 = 7, lgkmcnt 11:8 = 15).
-template <int N>
-MX_DEV void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x70 | 0xF00);
-}
-MX_DEV void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-// Workgroup barrier without the release/acquire fence of __syncthreads (which would wait for every
-// outstanding copy); the asm statements keep the compiler from moving LDS accesses across it.
-MX_DEV void block_sync() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-// Wait until at most c (0..D-2) later stages of kOps copies each are still in flight.
-template <int kOps, int D>
-MX_DEV void wait_stage(int c) {
-  static_assert(D >= 2 && D <= 5, "ring depth");
-  if (c >= 3) wait_vmcnt<kOps * (D - 2 >= 3 ? 3 : 0)>();
-  else if (c == 2) wait_vmcnt<kOps * (D - 2 >= 2 ? 2 : 0)>();
-  else if (c == 1) wait_vmcnt<kOps>();
-  else wait_vmcnt<0>();
-}
-
-// XCD-aware work split for the row-split kernels.  Workgroups are dispatched round-robin over the
-// MI355X's 8 XCDs (workgroup b runs on XCD b % 8) and each XCD has its own L2.  The (M tile, column
-// block) items are given to XCDs in contiguous ranges, column block fastest, so the column blocks of
-// one M tile (which read the same gathered activations) and the M tiles of one expert (which read the
-// same weights) run on the same XCD at about the same time.  Returns false when this workgroup has no
-// item.  The grid must hold at least 8 * ceil(max_tiles * nx / 8) workgroups.
-constexpr int kXcds = 8;
-MX_DEV bool xcd_item(int nt_all, int nx, int& tile, int& x) {
-  const int64_t total = (int64_t)nt_all * nx;
+  const int64_t total = (int64_t)(*a.ntiles) * nx;
   const int64_t chunk = (total + kXcds - 1) / kXcds;
-  const int64_t b = blockIdx.x;
-  const int64_t local = b / kXcds;
-  const int64_t p = (b % kXcds) * chunk + local;
-  if (local >= chunk || p >= total) return false;
-  tile = (int)(p / nx);
-  x = (int)(p % nx);
-  return true;
-}
+  const int64_t xcd = blockIdx.x % kXcds, per_xcd = gridDim.x / kXcds;
 
-// First GEMM: the workgroup covers NACT activation tiles (2*NACT gate/up weight tiles of 32 rows).
-template <int WM, int NACT, int D>
-__global__ __launch_bounds__(WM * 64) void gemm1_rows_kernel(
-    const uint8_t* __restrict__ w13q, const uint32_t* __restrict__ w13s, const uint16_t* __restrict__ b13,
-    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const int32_t* __restrict__ prow_pair,
-    const int4* __restrict__ tiles, const int32_t* __restrict__ ntiles, uint8_t* __restrict__ actq,
-    uint8_t* __restrict__ acts, MoeGeom g, int k) {
-  constexpr int NWT = 2 * NACT;  // weight tiles: 2i = gate of activation tile i, 2i+1 = its up
-  static_assert(NWT % WM == 0, "weight tiles split evenly over waves");
-  constexpr int WPW = NWT / WM;
-  constexpr int kParts = kSlot / 16;
-  constexpr int oW = 0, oWS = NWT * 1024, oX = oWS + NWT * 256, oXS = oX + WM * kParts * 1024;
-  constexpr int kStage = oXS + WM * kTerms * 256;
-  constexpr int kOps = 2 * WPW + kParts + kTerms;  // copies per wave per K step
-  __shared__ __attribute__((aligned(16))) uint8_t smem[D * kStage];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t nblk1 = 2 * g.nkt1;
-  const int64_t nkt = g.nkt1;
-  int tile, xb;
-  if (!xcd_item(*ntiles, (int)((g.nit + NACT - 1) / NACT), tile, xb)) return;
-  const int64_t it0 = (int64_t)xb * NACT;
-  {
-    const int4 td = tiles[tile];
+  for (int64_t p = blockIdx.x / kXcds; p < chunk; p += per_xcd) {
+    const int64_t item = xcd * chunk + p;
+    if (item >= total) break;
+    // Lane and wave indices are re-derived per item through volatile asm so that nothing computed from
+    // them is hoisted out of the item loop and kept live across the K loop.
+    int lane, wave;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+    asm volatile("s_lshr_b32 %0, %1, 6" : "=s"(wave) : "s"(__builtin_amdgcn_readfirstlane(tid)));
+    const int wr = wave / WC, wc = wave % WC;
+    const int tile = (int)(item / nx), x = (int)(item % nx);
+    const int4 td = a.tiles[tile];
     const int e = td.x, prow0 = td.y, nrows = td.z;
-    const bool valid = wave * 32 < nrows;  // wave-uniform
-    // Copies of the wave's 32 gathered rows go by contiguous runs: per K step a row holds two slots
-    // (160 B, kParts*2 chunks of 16 B) and 6 scale words (24 B), so chunk c of the wave's step data is
-    // row c / (2*kParts), part c % (2*kParts), and lane l of copy i takes chunk i*64 + l.  The LDS
-    // image is row-major: slot of (row m, block parity kb) at (m*2*kParts + kb*kParts)*16.
-    const uint8_t* xsrc[kParts];
-    const uint8_t* xssrc[kTerms];
+    const int64_t cb = (int64_t)x * NT / kCB;
+    const int jj0 = (x * NT) % kCB;
+
+    // ---- copy sources of this item (step 0; each stage advances by a fixed stride)
+    const uint8_t* wsrc = a.wq + ((e * ncb + cb) * nkt) * (kCB * 1024) + (jj0 + wave * C::nW) * 1024 + lane * 16;
+    const uint8_t* wssrc = a.ws + ((e * ncb + cb) * nkt) * 1024 + wave * 256 + lane * 4;
+    const uint8_t* xsrc[C::nX];
+    int xdst[C::nX];
 #pragma unroll
-    for (int i = 0; i < kParts; i++) {
-      const int c = i * 64 + lane;
-      const int rr = wave * 32 + c / (2 * kParts);
-      int tk = 0;
-      if (rr < nrows) {
-        const int pair = prow_pair[prow0 + rr];
-        if (pair >= 0) tk = pair / k;
+    for (int q = 0; q < C::nX; q++) {
+      int o = wave + 4 * q;
+      o = o < 3 * NRG ? o : 3 * NRG - 1;
+      const int rg = o / 3, pp = o % 3;
+      xdst[q] = C::oX + o * 1024;
+      if (G1) {
+        const int c = pp * 64 + lane, s = c / 3, part = c % 3;
+        const int tok = a.prow_tok[prow0 + rg * 32 + (s & 31)];
+        xsrc[q] = a.xq + ((int64_t)tok * nblk + (s >> 5)) * kSlot + part * 16;
+      } else {
+        xsrc[q] = a.xq + (((int64_t)(prow0 >> 5) + rg) * nkt * 64) * kSlot + (pp * 64 + lane) * 16;
       }
-      xsrc[i] = xq + (int64_t)tk * nblk1 * kSlot + (c % (2 * kParts)) * 16;
     }
+    const uint8_t* xssrc[C::nXS];
+    int xsdst[C::nXS];
 #pragma unroll
-    for (int i = 0; i < kTerms; i++) {
-      const int c = i * 64 + lane;
-      const int rr = wave * 32 + c / (2 * kTerms);
-      int tk = 0;
-      if (rr < nrows) {
-        const int pair = prow_pair[prow0 + rr];
-        if (pair >= 0) tk = pair / k;
+    for (int q = 0; q < C::nXS; q++) {
+      int o = wave + 4 * q;
+      o = o < NRG ? o : NRG - 1;
+      xsdst[q] = C::oXS + o * 256;
+      if (G1) {
+        const int tok = a.prow_tok[prow0 + o * 32 + (lane & 31)];
+        xssrc[q] = a.xs + ((int64_t)tok * nblk + (lane >> 5)) * 4;
+      } else {
+        xssrc[q] = a.xs + ((((int64_t)(prow0 >> 5) + o) * nkt) * 64 + lane) * 4;
       }
-      xssrc[i] = xs + (int64_t)tk * g.ngrp1 * (kTerms * 8) + (c % (2 * kTerms)) * 4;
     }
-    const uint8_t* wsrc[WPW];
-    const uint32_t* wssrc[WPW];
+    const int64_t xstep = G1 ? 2 * kSlot : 64 * kSlot;  // bytes per K step of an activation copy
+    const int64_t xsstep = G1 ? 8 : 256;
+
+    auto issue = [&](int64_t s, int slot) __attribute__((always_inline)) {
+      const int64_t kt = s < nkt ? s : nkt - 1;  // past the end: repeat the last stage (never read)
+      uint8_t* base = smem + slot * C::kStage;
 #pragma unroll
-    for (int i = 0; i < WPW; i++) {
-      const int j = wave * WPW + i;
-      const int64_t itj = it0 + (j >> 1);
-      const int64_t itc = itj < g.nit ? itj : it0;  // valid address; the tile's MFMAs are skipped
-      wsrc[i] = w13q + (((int64_t)e * g.nit + itc) * g.nkt1 * 2 + (j & 1)) * 1024 + lane * 16;
-      wssrc[i] = w13s + ((int64_t)e * g.nit + itc) * g.ngrp1 * 128 + (j & 1) * 64 + lane;
-    }
-    auto issue = [&](int64_t kt, int stage) {
-      uint8_t* base = smem + stage * kStage;
+      for (int i = 0; i < C::nW; i++) dma16(wsrc + kt * (kCB * 1024) + i * 1024, base + C::oW + (wave * C::nW + i) * 1024);
+      dma4(wssrc + kt * 1024, base + C::oWS + wave * 256);
 #pragma unroll
-      for (int i = 0; i < WPW; i++) dma16(wsrc[i] + kt * 2048, base + oW + (wave * WPW + i) * 1024);
+      for (int q = 0; q < C::nX; q++) dma16(xsrc[q] + kt * xstep, base + xdst[q]);
 #pragma unroll
-      for (int i = 0; i < WPW; i++) dma4(wssrc[i] + (kt >> 2) * 128, base + oWS + (wave * WPW + i) * 256);
-#pragma unroll
-      for (int i = 0; i < kParts; i++) dma16(xsrc[i] + kt * (2 * kSlot), base + oX + (wave * kParts + i) * 1024);
-#pragma unroll
-      for (int i = 0; i < kTerms; i++) dma4(xssrc[i] + (kt >> 2) * (kTerms * 8), base + oXS + (wave * kTerms + i) * 256);
+      for (int q = 0; q < C::nXS; q++) dma4(xssrc[q] + kt * xsstep, base + xsdst[q]);
     };
 
-    f32x16_t acc[NWT];
+    wait_vmcnt<0>();  // nothing of the previous item in flight
+    block_sync();     // every wave is done with the ring
 #pragma unroll
-    for (int j = 0; j < NWT; j++)
-#pragma unroll
-      for (int i = 0; i < 16; i++) acc[j][i] = 0.f;
+    for (int s = 0; s < D - 1; s++) issue(s, s);
 
-    wait_vmcnt<0>();  // nothing of the previous tile still in flight
-    block_sync();     // every wave is done reading the ring
+    // Each E2M3 term operand (6 dwords) is read by its own two LDS loads (16 + 8 bytes for term 0 at
+    // slot offset 0, 8 + 16 bytes for term 1 at offset 24), so every MFMA operand tuple is written in
+    // place by its loads.  Activation fragments are double-buffered across steps; a weight fragment is
+    // reloaded for the next step right after the last MFMA that uses it.
+    // xop[P]: activation operands (two buffers selected by a compile-time parity), w/wsc: weights.
+    i32x8_t xop[2][RW][kTerms];
+    uint32_t xsc[2][RW];
+    u32x4_t w[CW];
+    uint32_t wsc[CW / 4];
+    auto load_x = [&](const uint8_t* base, auto pc) __attribute__((always_inline)) {
+      constexpr int P = decltype(pc)::value;
 #pragma unroll
-    for (int s = 0; s < D - 1; s++)
-      if (s < nkt) issue(s, s);
-
-    // Operand fragments of one K step, read from LDS one step ahead of the MFMAs that use them.
-    struct Frag {
-      u32x4_t a[NWT];
-      uint32_t sa[NWT];
-      u32x4_t x[kParts];
-      uint32_t sx[kTerms];
-    };
-    auto load_frag = [&](int64_t kt, Frag& f) {
-      const uint8_t* base = smem + (kt % D) * kStage;
-      const uint8_t* xb = base + oX + wave * kParts * 1024 + ((lane & 31) * 2 * kParts + (lane >> 5) * kParts) * 16;
-#pragma unroll
-      for (int q = 0; q < kParts; q++) f.x[q] = ld16(xb + q * 16);
-#pragma unroll
-      for (int t = 0; t < kTerms; t++)
-        f.sx[t] = *reinterpret_cast<const uint32_t*>(base + oXS + (wave * kTerms) * 256 +
-                                                     ((lane & 31) * 2 * kTerms + t * 2 + (lane >> 5)) * 4);
-#pragma unroll
-      for (int j = 0; j < NWT; j++) {
-        f.a[j] = ld16(base + oW + j * 1024 + lane * 16);
-        f.sa[j] = *reinterpret_cast<const uint32_t*>(base + oWS + j * 256 + lane * 4);
+      for (int r = 0; r < RW; r++) {
+        const uint8_t* xp = base + C::oX + (wr * RW + r) * 3072 + lane * kSlot;
+        const u32x4_t a4 = ld16(xp);
+        const u32x2_t a2 = ld8(xp + 16);
+        const u32x2_t b2 = ld8(xp + 24);
+        const u32x4_t b4 = ld16(xp + 32);
+        xop[P][r][0] = i32x8_t{(int)a4[0], (int)a4[1], (int)a4[2], (int)a4[3], (int)a2[0], (int)a2[1], 0, 0};
+        xop[P][r][1] = i32x8_t{(int)b2[0], (int)b2[1], (int)b4[0], (int)b4[1], (int)b4[2], (int)b4[3], 0, 0};
+        xsc[P][r] = *reinterpret_cast<const uint32_t*>(base + C::oXS + (wr * RW + r) * 256 + lane * 4);
       }
     };
-    // Make stage kt visible to every wave (own copies counted by vmcnt, then the barrier), after which
-    // the ring slot of stage kt - 1 is free: refill it with stage kt + D - 1.
-    auto arrive = [&](int64_t kt) {
-      const int64_t ahead = nkt - 1 - kt;
-      wait_stage<kOps, D>((int)(ahead < D - 2 ? ahead : D - 2));
-      wait_lgkmcnt0();
+    auto load_w = [&](const uint8_t* base, int j) __attribute__((always_inline)) { w[j] = ld16(base + C::oW + (wc * CW + j) * 1024 + lane * 16); };
+    auto load_ws = [&](const uint8_t* base, int j4) __attribute__((always_inline)) {
+      wsc[j4] = *reinterpret_cast<const uint32_t*>(base + C::oWS + lane * 16 + jj0 + wc * CW + j4 * 4);
+    };
+
+    f32x16_t acc[RW][CW];
+#pragma unroll
+    for (int r = 0; r < RW; r++)
+#pragma unroll
+      for (int j = 0; j < CW; j++)
+#pragma unroll
+        for (int i = 0; i < 16; i++) acc[r][j][i] = 0.f;
+
+    // MFMAs of weight tiles [J0, J0 + JG): term-major, then row group, then tile, so an accumulator is
+    // reused RW * JG instructions later.
+    constexpr int JG = 2;
+    auto mfma_group = [&](auto jc, auto pc) __attribute__((always_inline)) {
+      constexpr int J0 = decltype(jc)::value * JG;
+      constexpr int P = decltype(pc)::value;
+      static_for<0, kTerms>([&](auto tc) __attribute__((always_inline)) {
+        constexpr int t = decltype(tc)::value;
+#pragma unroll
+        for (int r = 0; r < RW; r++) {
+          const i32x8_t xo = xop[P][r][t];
+          static_for<J0, J0 + JG>([&](auto jc2) __attribute__((always_inline)) {
+            constexpr int j = decltype(jc2)::value;
+            const i32x8_t wo = i32x8_t{(int)w[j][0], (int)w[j][1], (int)w[j][2], (int)w[j][3], 0, 0, 0, 0};
+            if constexpr (G1)
+              acc[r][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wo, xo, acc[r][j], kFp4, kFp6, j & 3,
+                                                                          wsc[j >> 2], t, xsc[P][r]);
+            else
+              acc[r][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(xo, wo, acc[r][j], kFp6, kFp4, t, xsc[P][r],
+                                                                          j & 3, wsc[j >> 2]);
+          });
+        }
+      });
+    };
+
+    // One K step.  Stage kt+1 (my copies landed) becomes everyone's at the barrier; every wave has by
+    // then finished all reads of stage kt-1 (they fed the MFMAs of step kt-1), so that slot takes stage
+    // kt + D - 1.  The activation fragments of step kt+1 are read into `xn` at the start, the weight
+    // fragments of step kt+1 after their last use in this step.
+    auto step = [&](int64_t kt, auto pc) __attribute__((always_inline)) {
+      constexpr int P = decltype(pc)::value;
+      wait_vmcnt<C::kOps * (D - 3)>();
       block_sync();
-      if (kt + D - 1 < nkt) issue(kt + D - 1, (int)((kt + D - 1) % D));
+      const int64_t kn = kt + 1 < nkt ? kt + 1 : kt;
+      const uint8_t* nb = smem + (kn % D) * C::kStage;
+      load_x(nb, std::integral_constant<int, 1 - P>{});
+      issue(kt + D - 1, (int)((kt + D - 1) % D));
+      static_for<0, CW / JG>([&](auto gc) __attribute__((always_inline)) {
+        constexpr int J0 = decltype(gc)::value * JG;
+        mfma_group(gc, pc);
+#pragma unroll
+        for (int j = J0; j < J0 + JG; j++) load_w(nb, j);
+        if constexpr ((J0 + JG) % 4 == 0) load_ws(nb, (J0 + JG) / 4 - 1);
+      });
     };
 
-    auto kloop = [&](auto fullc) {
-      constexpr bool FULL = decltype(fullc)::value;
-      // Waves without rows (a short last M tile) run the same instruction stream on harmless data and
-      // skip the epilogue: keeping the loop free of divergent branches lets the compiler wait for exactly
-      // the LDS reads each MFMA needs instead of draining all of them.
-      Frag cur, nxt;
-      arrive(0);
-      load_frag(0, cur);
-      for (int64_t grp = 0; grp < g.ngrp1; grp++) {
-        auto step = [&](auto jc) {
-          constexpr int J = decltype(jc)::value;
-          const int64_t kt = grp * 4 + J;
-          const bool more = kt + 1 < nkt;
-          // The MFMAs of step kt follow the reads of step kt + 1 in the same basic block, so they do not
-          // wait for those reads.
-          auto mfmas = [&]() {
-          {
-            i32x8_t bt[kTerms];
-            bt[0] = i32x8_t{(int)cur.x[0][0], (int)cur.x[0][1], (int)cur.x[0][2], (int)cur.x[0][3], (int)cur.x[1][0],
-                            (int)cur.x[1][1], 0, 0};
-            bt[1] = i32x8_t{(int)cur.x[1][2], (int)cur.x[1][3], (int)cur.x[2][0], (int)cur.x[2][1], (int)cur.x[2][2],
-                            (int)cur.x[2][3], 0, 0};
-            bt[2] = i32x8_t{(int)cur.x[3][0], (int)cur.x[3][1], (int)cur.x[3][2], (int)cur.x[3][3], (int)cur.x[4][0],
-                            (int)cur.x[4][1], 0, 0};
-            // term-major: consecutive MFMAs use different accumulators
+    // stage 0 visible: D - 2 later stages may still be in flight
+    wait_vmcnt<C::kOps * (D - 2)>();
+    block_sync();
+    {
+      const uint8_t* b0 = smem;
+      load_x(b0, std::integral_constant<int, 0>{});
 #pragma unroll
-            for (int t = 0; t < kTerms; t++)
+      for (int j = 0; j < CW; j++) load_w(b0, j);
 #pragma unroll
-              for (int j = 0; j < NWT; j++)
-                if (FULL || it0 + (j >> 1) < g.nit)
-                  acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp4_operand(cur.a[j]), bt[t], acc[j], kFp4, kFp6,
-                                                                           J, cur.sa[j], J, cur.sx[t]);
-          }
-          };
-          if (more) {
-            arrive(kt + 1);
-            load_frag(kt + 1, nxt);
-            mfmas();
-            cur = nxt;
-          } else {
-            mfmas();
-          }
-        };
-        step(std::integral_constant<int, 0>{});
-        if (grp * 4 + 1 < nkt) step(std::integral_constant<int, 1>{});
-        if (grp * 4 + 2 < nkt) step(std::integral_constant<int, 2>{});
-        if (grp * 4 + 3 < nkt) step(std::integral_constant<int, 3>{});
-      }
-    };
-    if (it0 + NACT <= g.nit) kloop(std::true_type{});
-    else kloop(std::false_type{});
-    if (valid) {
-#pragma unroll
-      for (int i = 0; i < NACT; i++)
-        if (it0 + i < g.nit)
-          g1_epilogue_tile(acc[2 * i], acc[2 * i + 1], b13, actq, acts, g, e, it0 + i, (prow0 >> 5) + wave, lane);
+      for (int j4 = 0; j4 < CW / 4; j4++) load_ws(b0, j4);
     }
-  }
-}
-
-// Second GEMM: the workgroup covers NB column tiles of 32 (of H); w * (o + b2) goes to o_buf in fp32.
-template <int WM, int NB, int D>
-__global__ __launch_bounds__(WM * 64) void gemm2_rows_kernel(
-    const uint8_t* __restrict__ w2q, const uint32_t* __restrict__ w2s, const uint16_t* __restrict__ b2,
-    const uint8_t* __restrict__ actq, const uint8_t* __restrict__ acts, const int32_t* __restrict__ prow_pair,
-    const float* __restrict__ topw, const int4* __restrict__ tiles, const int32_t* __restrict__ ntiles,
-    float* __restrict__ obuf, MoeGeom g, int k) {
-  static_assert(NB % WM == 0, "weight tiles split evenly over waves");
-  constexpr int WPW = NB / WM;
-  constexpr int kParts = kSlot / 16;
-  constexpr int oW = 0, oWS = NB * 1024, oA = oWS + NB * 256, oAS = oA + WM * kParts * 1024;
-  constexpr int kStage = oAS + WM * kTerms * 256;
-  constexpr int kOps = 2 * WPW + kParts + kTerms;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[D * kStage];
-  __shared__ int32_t s_pair[WM * 32];
-  __shared__ float s_w[WM * 32];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t nkt = g.nkt2;
-  int tile, xb;
-  if (!xcd_item(*ntiles, (int)((g.nht + NB - 1) / NB), tile, xb)) return;
-  const int64_t nt0 = (int64_t)xb * NB;
-  {
-    const int4 td = tiles[tile];
-    const int e = td.x, prow0 = td.y, nrows = td.z;
-    const bool valid = wave * 32 < nrows;
-    const int64_t rg = (prow0 >> 5) + wave;  // inside the allocation even when not valid
-    // The row group's operand chunk of a K step is contiguous (64 lane slots), so copy i takes bytes
-    // [i*1024, (i+1)*1024) of it and the LDS image is the chunk itself; likewise the scale words.
-    const uint8_t* achunk = actq + rg * g.nkt2 * 64 * kSlot + lane * 16;
-    const uint8_t* schunk = acts + rg * g.ngrp2 * 64 * (kTerms * 4) + lane * 4;
-    const uint8_t* wsrc[WPW];
-    const uint32_t* wssrc[WPW];
-#pragma unroll
-    for (int i = 0; i < WPW; i++) {
-      const int j = wave * WPW + i;
-      const int64_t ntj = nt0 + j;
-      const int64_t ntc = ntj < g.nht ? ntj : nt0;
-      wsrc[i] = w2q + (((int64_t)e * g.nht + ntc) * g.nkt2) * 1024 + lane * 16;
-      wssrc[i] = w2s + ((int64_t)e * g.nht + ntc) * g.ngrp2 * 64 + lane;
+    int64_t kt = 0;
+    for (; kt + 2 <= nkt; kt += 2) {  // two steps per iteration keep both buffers in place
+      step(kt, std::integral_constant<int, 0>{});
+      step(kt + 1, std::integral_constant<int, 1>{});
     }
-    auto issue = [&](int64_t kt, int stage) {
-      uint8_t* base = smem + stage * kStage;
-#pragma unroll
-      for (int i = 0; i < WPW; i++) dma16(wsrc[i] + kt * 1024, base + oW + (wave * WPW + i) * 1024);
-#pragma unroll
-      for (int i = 0; i < WPW; i++) dma4(wssrc[i] + (kt >> 2) * 64, base + oWS + (wave * WPW + i) * 256);
-#pragma unroll
-      for (int i = 0; i < kParts; i++) dma16(achunk + kt * (64 * kSlot) + i * 1024, base + oA + (wave * kParts + i) * 1024);
-#pragma unroll
-      for (int i = 0; i < kTerms; i++)
-        dma4(schunk + (kt >> 2) * (64 * kTerms * 4) + i * 256, base + oAS + (wave * kTerms + i) * 256);
-    };
+    if (kt < nkt) step(kt, std::integral_constant<int, 0>{});
 
-    f32x16_t acc[NB];
+    // ---- epilogue (one tile at a time: the scheduling barriers keep each tile's values short-lived)
+    if constexpr (G1) {
 #pragma unroll
-    for (int j = 0; j < NB; j++)
+      for (int r = 0; r < RW; r++) {
+        const int rgl = wr * RW + r;
+        if (rgl * 32 >= nrows) continue;
 #pragma unroll
-      for (int i = 0; i < 16; i++) acc[j][i] = 0.f;
-
-    wait_vmcnt<0>();
-    block_sync();  // every wave is done with the ring, s_pair and s_w of the previous tile
-    for (int rr = tid; rr < WM * 32; rr += WM * 64) {
-      int pair = -1;
-      float wt = 0.f;
-      if (rr < nrows) {
-        pair = prow_pair[prow0 + rr];
-        if (pair >= 0) wt = topw[pair];
+        for (int i = 0; i < CW / 2; i++) {
+          const int64_t it = ((int64_t)x * NT + wc * CW) / 2 + i;
+          if (it < g.nit)
+            g1_epilogue_tile(acc[r][2 * i], acc[r][2 * i + 1], a.bias, a.actq, a.acts, g, e, it, (prow0 >> 5) + rgl, lane);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
-      s_pair[rr] = pair;
-      s_w[rr] = wt;
-    }
+    } else {
+      const int m0 = 4 * (lane >> 5);
 #pragma unroll
-    for (int s = 0; s < D - 1; s++)
-      if (s < nkt) issue(s, s);
-
-    struct Frag {
-      u32x4_t b[NB];
-      uint32_t sb[NB];
-      u32x4_t x[kParts];
-      uint32_t sa[kTerms];
-    };
-    auto load_frag = [&](int64_t kt, Frag& f) {
-      const uint8_t* base = smem + (kt % D) * kStage;
-      const uint8_t* ab = base + oA + wave * kParts * 1024 + lane * kSlot;
+      for (int r = 0; r < RW; r++) {
+        const int rgl = wr * RW + r;
+        if (rgl * 32 >= nrows) continue;
+        // rows 8*jj + m0 + i of the row group: four runs of four consecutive rows
+        int32_t pr[16];
+        float wt[16];
 #pragma unroll
-      for (int q = 0; q < kParts; q++) f.x[q] = ld16(ab + q * 16);
+        for (int jj = 0; jj < 4; jj++) {
+          const int row = rgl * 32 + 8 * jj + m0;
+          const int4 p4 = *reinterpret_cast<const int4*>(a.prow_pair + prow0 + row);
+          const f32x4_t w4 = *reinterpret_cast<const f32x4_t*>(a.prow_w + prow0 + row);
+          pr[4 * jj] = row < nrows ? p4.x : -1;
+          pr[4 * jj + 1] = row + 1 < nrows ? p4.y : -1;
+          pr[4 * jj + 2] = row + 2 < nrows ? p4.z : -1;
+          pr[4 * jj + 3] = row + 3 < nrows ? p4.w : -1;
 #pragma unroll
-      for (int t = 0; t < kTerms; t++)
-        f.sa[t] = *reinterpret_cast<const uint32_t*>(base + oAS + (wave * kTerms) * 256 + lane * (kTerms * 4) + t * 4);
+          for (int i = 0; i < 4; i++) wt[4 * jj + i] = w4[i];
+        }
 #pragma unroll
-      for (int j = 0; j < NB; j++) {
-        f.b[j] = ld16(base + oW + j * 1024 + lane * 16);
-        f.sb[j] = *reinterpret_cast<const uint32_t*>(base + oWS + j * 256 + lane * 4);
-      }
-    };
-    auto arrive = [&](int64_t kt) {
-      const int64_t ahead = nkt - 1 - kt;
-      wait_stage<kOps, D>((int)(ahead < D - 2 ? ahead : D - 2));
-      wait_lgkmcnt0();
-      block_sync();
-      if (kt + D - 1 < nkt) issue(kt + D - 1, (int)((kt + D - 1) % D));
-    };
-
-    auto kloop = [&](auto fullc) {
-      constexpr bool FULL = decltype(fullc)::value;
-      // Waves without rows (a short last M tile) run the same instruction stream on harmless data and
-      // skip the epilogue: keeping the loop free of divergent branches lets the compiler wait for exactly
-      // the LDS reads each MFMA needs instead of draining all of them.
-      Frag cur, nxt;
-      arrive(0);
-      load_frag(0, cur);
-      for (int64_t grp = 0; grp < g.ngrp2; grp++) {
-        auto step = [&](auto jc) {
-          constexpr int J = decltype(jc)::value;
-          const int64_t kt = grp * 4 + J;
-          const bool more = kt + 1 < nkt;
-          auto mfmas = [&]() {
-          {
-            i32x8_t at[kTerms];
-            at[0] = i32x8_t{(int)cur.x[0][0], (int)cur.x[0][1], (int)cur.x[0][2], (int)cur.x[0][3], (int)cur.x[1][0],
-                            (int)cur.x[1][1], 0, 0};
-            at[1] = i32x8_t{(int)cur.x[1][2], (int)cur.x[1][3], (int)cur.x[2][0], (int)cur.x[2][1], (int)cur.x[2][2],
-                            (int)cur.x[2][3], 0, 0};
-            at[2] = i32x8_t{(int)cur.x[3][0], (int)cur.x[3][1], (int)cur.x[3][2], (int)cur.x[3][3], (int)cur.x[4][0],
-                            (int)cur.x[4][1], 0, 0};
+        for (int j = 0; j < CW; j++) {
+          const int64_t nt = (int64_t)x * NT + wc * CW + j;
+          if (nt < g.nht) {
+            const int64_t col = nt * 32 + (lane & 31);
+            const float bb = a.bias ? bf16_bits_to_f32(a.bias[(int64_t)e * g.H + col]) : 0.f;
 #pragma unroll
-            for (int t = 0; t < kTerms; t++)
-#pragma unroll
-              for (int j = 0; j < NB; j++)
-                if (FULL || nt0 + j < g.nht)
-                  acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(at[t], fp4_operand(cur.b[j]), acc[j], kFp6, kFp4, J,
-                                                                           cur.sa[t], J, cur.sb[j]);
+            for (int q = 0; q < 16; q++)
+              if (pr[q] >= 0) a.obuf[(int64_t)pr[q] * g.H + col] = wt[q] * (acc[r][j][q] + bb);
           }
-          };
-          if (more) {
-            arrive(kt + 1);
-            load_frag(kt + 1, nxt);
-            mfmas();
-            cur = nxt;
-          } else {
-            mfmas();
-          }
-        };
-        step(std::integral_constant<int, 0>{});
-        if (grp * 4 + 1 < nkt) step(std::integral_constant<int, 1>{});
-        if (grp * 4 + 2 < nkt) step(std::integral_constant<int, 2>{});
-        if (grp * 4 + 3 < nkt) step(std::integral_constant<int, 3>{});
-      }
-    };
-    if (nt0 + NB <= g.nht) kloop(std::true_type{});
-    else kloop(std::false_type{});
-
-    if (valid) {
-      const int h = lane >> 5;
-#pragma unroll
-      for (int j = 0; j < NB; j++) {
-        if (nt0 + j >= g.nht) continue;
-        const int64_t col = (nt0 + j) * 32 + (lane & 31);
-        const float bias = b2 ? bf16_bits_to_f32(b2[(int64_t)e * g.H + col]) : 0.f;
-#pragma unroll
-        for (int q = 0; q < 16; q++) {
-          const int rr = wave * 32 + 8 * (q >> 2) + 4 * h + (q & 3);
-          const int pair = s_pair[rr];
-          if (pair >= 0) obuf[(int64_t)pair * g.H + col] = s_w[rr] * (acc[j][q] + bias);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
   }
 }
 
-// y[t] = sum_j o_buf[t*k + j], fp32 sum in j order, bf16 out; eight columns per thread.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ obuf, uint16_t* __restrict__ y,
                                                       int64_t H8, int k, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
@@ -912,8 +411,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
     const f32x4_t* src = reinterpret_cast<const f32x4_t*>(obuf) + ((t * k) * H8 + c) * 2;
     for (int j = 0; j < k; j++) {
-      s0 += src[j * H8 * 2];
-      s1 += src[j * H8 * 2 + 1];
+      s0 += __builtin_nontemporal_load(src + j * H8 * 2);
+      s1 += __builtin_nontemporal_load(src + j * H8 * 2 + 1);
     }
     u32x4_t o;
     o[0] = f32_to_bf16_bits(s0[0]) | (f32_to_bf16_bits(s0[1]) << 16);
@@ -924,71 +423,41 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
 }
 
-
-}  // namespace
-
-static unsigned tiles_grid_y(int64_t max_tiles) { return (unsigned)(max_tiles < 65535 ? max_tiles : 65535); }
-
-// 1-D grid of the row-split kernels: every (tile, column block) item, rounded up to whole XCD rounds.
-static unsigned rows_grid(int64_t max_tiles, int64_t nx) { return (unsigned)(kXcds * cdiv(max_tiles * nx, kXcds)); }
-
-constexpr int kNW = 4;    // waves per workgroup of the column-split kernels (single row group tiles)
-constexpr int kNACT = 4;  // activation tiles per workgroup of the row-split first GEMM
-constexpr int kNB = 8;    // column tiles per workgroup of the row-split second GEMM
-
-int launch_gemm1(int MT, const MoeGeom& g, const uint8_t* blob, const BlobOffsets& o, bool bias, const uint8_t* xq,
-                 const uint8_t* xs, const int32_t* prow_pair, const void* tiles, const int32_t* ntiles, int64_t max_tiles,
-                 uint8_t* actq, uint8_t* acts, int k, hipStream_t stream) {
-  const uint16_t* b13 = bias ? (const uint16_t*)(blob + o.b13) : nullptr;
-  const uint8_t* wq = blob + o.w13q;
-  const uint32_t* ws = (const uint32_t*)(blob + o.w13s);
-  const int4* tl = (const int4*)tiles;
-  const unsigned gy = tiles_grid_y(max_tiles);
-  switch (MT) {
-    case 1:
-      hipLaunchKernelGGL((gemm1_kernel<1, kNW, true>), dim3((unsigned)cdiv(g.nit, kNW), gy), dim3(kNW * 64), 0, stream,
-                         wq, ws, b13, xq, xs, prow_pair, tl, ntiles, actq, acts, g, k);
-      break;
-    case 2:
-      hipLaunchKernelGGL((gemm1_rows_kernel<2, kNACT, 4>), dim3(rows_grid(max_tiles, cdiv(g.nit, kNACT))), dim3(2 * 64), 0, stream,
-                         wq, ws, b13, xq, xs, prow_pair, tl, ntiles, actq, acts, g, k);
-      break;
-    case 4:
-      hipLaunchKernelGGL((gemm1_rows_kernel<4, kNACT, 4>), dim3(rows_grid(max_tiles, cdiv(g.nit, kNACT))), dim3(4 * 64), 0, stream,
-                         wq, ws, b13, xq, xs, prow_pair, tl, ntiles, actq, acts, g, k);
-      break;
-    default:
-      return MXFP4_ERR_SHAPE;
-  }
+template <bool G1, int WR, int WC, int RW, int CW, int D>
+int launch_cfg(const GemmArgs& a, int64_t max_tiles, int wg_per_cu, hipStream_t stream) {
+  using C = Cfg<WR, WC, RW, CW, D>;
+  const int64_t nx = (G1 ? a.g.ncb1 : a.g.ncb2) * kCB / C::NT;
+  int64_t items = max_tiles * nx;
+  int64_t grid = 256 * wg_per_cu;
+  if (items < grid) grid = items;
+  grid = kXcds * cdiv(grid, kXcds);
+  if (grid < kXcds) grid = kXcds;
+  hipLaunchKernelGGL((grouped_gemm_kernel<G1, WR, WC, RW, CW, D>), dim3((unsigned)grid), dim3(256), 0, stream, a);
   return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
 }
 
-int launch_gemm2(int MT, const MoeGeom& g, const uint8_t* blob, const BlobOffsets& o, bool bias, const uint8_t* actq,
-                 const uint8_t* acts, const int32_t* prow_pair, const float* topw, const void* tiles,
-                 const int32_t* ntiles, int64_t max_tiles, float* obuf, int64_t T, int k, hipStream_t stream) {
-  (void)T;
-  const uint16_t* b2 = bias ? (const uint16_t*)(blob + o.b2) : nullptr;
-  const uint8_t* wq = blob + o.w2q;
-  const uint32_t* ws = (const uint32_t*)(blob + o.w2s);
-  const int4* tl = (const int4*)tiles;
-  const unsigned gy = tiles_grid_y(max_tiles);
-  switch (MT) {
-    case 1:
-      hipLaunchKernelGGL((gemm2_kernel<1, kNW, true>), dim3((unsigned)cdiv(g.nht, kNW), gy), dim3(kNW * 64), 0, stream,
-                         wq, ws, b2, actq, acts, prow_pair, topw, tl, ntiles, obuf, g, k);
-      break;
-    case 2:
-      hipLaunchKernelGGL((gemm2_rows_kernel<2, kNB, 4>), dim3(rows_grid(max_tiles, cdiv(g.nht, kNB))), dim3(2 * 64), 0, stream,
-                         wq, ws, b2, actq, acts, prow_pair, topw, tl, ntiles, obuf, g, k);
-      break;
-    case 4:
-      hipLaunchKernelGGL((gemm2_rows_kernel<4, kNB, 4>), dim3(rows_grid(max_tiles, cdiv(g.nht, kNB))), dim3(4 * 64), 0, stream,
-                         wq, ws, b2, actq, acts, prow_pair, topw, tl, ntiles, obuf, g, k);
-      break;
-    default:
-      return MXFP4_ERR_SHAPE;
+}  // namespace
+
+// Tile configurations by rows per M tile (32 * NRG): 1 row group for decode-like loads, 2 or 4 for
+// larger ones.  The first GEMM covers a whole column block per workgroup; the 128-row second GEMM
+// covers half of one so that two workgroups share a CU and one's output stores overlap the other's
+// MFMAs.
+int launch_gemm1(int NRG, const GemmArgs& a, int64_t max_tiles, hipStream_t stream) {
+  switch (NRG) {
+    case 1: return launch_cfg<true, 1, 4, 1, 4, 3>(a, max_tiles, 2, stream);
+    case 2: return launch_cfg<true, 1, 4, 2, 4, 3>(a, max_tiles, 2, stream);
+    case 4: return launch_cfg<true, 2, 2, 2, 8, 5>(a, max_tiles, 1, stream);
+    default: return MXFP4_ERR_SHAPE;
   }
-  return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
+}
+
+int launch_gemm2(int NRG, const GemmArgs& a, int64_t max_tiles, hipStream_t stream) {
+  switch (NRG) {
+    case 1: return launch_cfg<false, 1, 4, 1, 4, 3>(a, max_tiles, 2, stream);
+    case 2: return launch_cfg<false, 1, 4, 2, 4, 3>(a, max_tiles, 2, stream);
+    case 4: return launch_cfg<false, 2, 2, 2, 4, 3>(a, max_tiles, 2, stream);
+    default: return MXFP4_ERR_SHAPE;
+  }
 }
 
 int launch_combine(const float* obuf, void* y, int64_t T, int64_t H, int k, hipStream_t stream) {

@@ -21,67 +21,81 @@ __global__ void write_header_kernel(uint8_t* out, BlobHeader h) {
   for (int i = sizeof(BlobHeader) + threadIdx.x; i < 256; i += blockDim.x) out[i] = 0;
 }
 
-// w13 q: one 16-byte chunk per (e, it, kt, gu, lane)
+// Coordinates of a 16-byte weight chunk (e, c, kt, j, lane) and of a 16-byte scale record
+// (e, c, kt, lane) of the column-block layout.
+struct ChunkIdx {
+  int64_t e, c, kt;
+  int j, lane;
+};
+MX_DEV ChunkIdx chunk_idx(int64_t i, int64_t nkt, int64_t ncb) {
+  ChunkIdx r;
+  r.lane = (int)(i & 63); i >>= 6;
+  r.j = (int)(i % kCB); i /= kCB;
+  r.kt = i % nkt; i /= nkt;
+  r.c = i % ncb; r.e = i / ncb;
+  return r;
+}
+MX_DEV ChunkIdx record_idx(int64_t i, int64_t nkt, int64_t ncb) {
+  ChunkIdx r;
+  r.lane = (int)(i & 63); i >>= 6;
+  r.j = 0;
+  r.kt = i % nkt; i /= nkt;
+  r.c = i % ncb; r.e = i / ncb;
+  return r;
+}
+
+// First GEMM tile j of column block c: source row of w13 ([w1; w3] stacked), or -1 past I.
+MX_DEV int64_t w13_row(const MoeGeom& g, int64_t c, int j, int lane) {
+  const int64_t it = 8 * c + (j >> 1);
+  if (it >= g.nit) return -1;
+  return (j & 1) * g.I + it * 32 + (lane & 31);
+}
+
+// w13 q: one 16-byte chunk per (e, c, kt, j, lane)
 __global__ void pack_w13q_kernel(const uint8_t* __restrict__ src, u32x4_t* __restrict__ dst, MoeGeom g, int64_t n) {
   GRID_STRIDE(i, n) {
-    int64_t t = i;
-    const int lane = (int)(t & 63); t >>= 6;
-    const int gu = (int)(t & 1); t >>= 1;
-    const int64_t kt = t % g.nkt1; t /= g.nkt1;
-    const int64_t it = t % g.nit; const int64_t e = t / g.nit;
-    const int64_t row = gu * g.I + it * 32 + (lane & 31);
-    const int64_t blk = 2 * kt + (lane >> 5);
+    const ChunkIdx x = chunk_idx(i, g.nkt1, g.ncb1);
+    const int64_t row = w13_row(g, x.c, x.j, x.lane);
+    const int64_t blk = 2 * x.kt + (x.lane >> 5);
     u32x4_t v = {0u, 0u, 0u, 0u};
-    if (blk < g.H / 32)
-      v = *reinterpret_cast<const u32x4_t*>(src + (e * 2 * g.I + row) * (g.H / 2) + blk * 16);
+    if (row >= 0 && blk < g.H / 32)
+      v = *reinterpret_cast<const u32x4_t*>(src + (x.e * 2 * g.I + row) * (g.H / 2) + blk * 16);
     dst[i] = v;
   }
 }
 
 __global__ void unpack_w13q_kernel(const u32x4_t* __restrict__ src, uint8_t* __restrict__ dst, MoeGeom g, int64_t n) {
   GRID_STRIDE(i, n) {
-    int64_t t = i;
-    const int lane = (int)(t & 63); t >>= 6;
-    const int gu = (int)(t & 1); t >>= 1;
-    const int64_t kt = t % g.nkt1; t /= g.nkt1;
-    const int64_t it = t % g.nit; const int64_t e = t / g.nit;
-    const int64_t row = gu * g.I + it * 32 + (lane & 31);
-    const int64_t blk = 2 * kt + (lane >> 5);
-    if (blk < g.H / 32)
-      *reinterpret_cast<u32x4_t*>(dst + (e * 2 * g.I + row) * (g.H / 2) + blk * 16) = src[i];
+    const ChunkIdx x = chunk_idx(i, g.nkt1, g.ncb1);
+    const int64_t row = w13_row(g, x.c, x.j, x.lane);
+    const int64_t blk = 2 * x.kt + (x.lane >> 5);
+    if (row >= 0 && blk < g.H / 32)
+      *reinterpret_cast<u32x4_t*>(dst + (x.e * 2 * g.I + row) * (g.H / 2) + blk * 16) = src[i];
   }
 }
 
-// w13 s: one dword per (e, it, grp, gu, lane); byte j = scale of K block 2*(4*grp + j) + lane/32
-__global__ void pack_w13s_kernel(const uint8_t* __restrict__ src, uint32_t* __restrict__ dst, MoeGeom g, int64_t n) {
+// w13 s: one 16-byte record per (e, c, kt, lane); byte j = scale of tile j's row, K block 2*kt + lane/32
+__global__ void pack_w13s_kernel(const uint8_t* __restrict__ src, u32x4_t* __restrict__ dst, MoeGeom g, int64_t n) {
   GRID_STRIDE(i, n) {
-    int64_t t = i;
-    const int lane = (int)(t & 63); t >>= 6;
-    const int gu = (int)(t & 1); t >>= 1;
-    const int64_t grp = t % g.ngrp1; t /= g.ngrp1;
-    const int64_t it = t % g.nit; const int64_t e = t / g.nit;
-    const int64_t row = gu * g.I + it * 32 + (lane & 31);
-    uint32_t word = 0;
-    for (int j = 0; j < 4; j++) {
-      const int64_t blk = 2 * (4 * grp + j) + (lane >> 5);
-      if (blk < g.H / 32) word |= (uint32_t)src[(e * 2 * g.I + row) * (g.H / 32) + blk] << (8 * j);
+    const ChunkIdx x = record_idx(i, g.nkt1, g.ncb1);
+    const int64_t blk = 2 * x.kt + (x.lane >> 5);
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    for (int j = 0; j < kCB; j++) {
+      const int64_t row = w13_row(g, x.c, j, x.lane);
+      if (row >= 0 && blk < g.H / 32) w[j >> 2] |= (uint32_t)src[(x.e * 2 * g.I + row) * (g.H / 32) + blk] << (8 * (j & 3));
     }
-    dst[i] = word;
+    dst[i] = u32x4_t{w[0], w[1], w[2], w[3]};
   }
 }
 
-__global__ void unpack_w13s_kernel(const uint32_t* __restrict__ src, uint8_t* __restrict__ dst, MoeGeom g, int64_t n) {
+__global__ void unpack_w13s_kernel(const u32x4_t* __restrict__ src, uint8_t* __restrict__ dst, MoeGeom g, int64_t n) {
   GRID_STRIDE(i, n) {
-    int64_t t = i;
-    const int lane = (int)(t & 63); t >>= 6;
-    const int gu = (int)(t & 1); t >>= 1;
-    const int64_t grp = t % g.ngrp1; t /= g.ngrp1;
-    const int64_t it = t % g.nit; const int64_t e = t / g.nit;
-    const int64_t row = gu * g.I + it * 32 + (lane & 31);
-    const uint32_t word = src[i];
-    for (int j = 0; j < 4; j++) {
-      const int64_t blk = 2 * (4 * grp + j) + (lane >> 5);
-      if (blk < g.H / 32) dst[(e * 2 * g.I + row) * (g.H / 32) + blk] = (uint8_t)(word >> (8 * j));
+    const ChunkIdx x = record_idx(i, g.nkt1, g.ncb1);
+    const int64_t blk = 2 * x.kt + (x.lane >> 5);
+    const u32x4_t v = src[i];
+    for (int j = 0; j < kCB; j++) {
+      const int64_t row = w13_row(g, x.c, j, x.lane);
+      if (row >= 0 && blk < g.H / 32) dst[(x.e * 2 * g.I + row) * (g.H / 32) + blk] = (uint8_t)(v[j >> 2] >> (8 * (j & 3)));
     }
   }
 }
@@ -99,62 +113,57 @@ MX_DEV u32x4_t unperm_w2_block(u32x4_t d) {
   return u32x4_t{w0 | (w1 << 16), w2 | (w3 << 16), w4 | (w5 << 16), w6 | (w7 << 16)};
 }
 
-// w2 q: one 16-byte chunk per (e, nt, kt, lane)
+// Second GEMM tile j of column block c: source row of w2, or -1 past H.
+MX_DEV int64_t w2_row(const MoeGeom& g, int64_t c, int j, int lane) {
+  const int64_t nt = kCB * c + j;
+  if (nt >= g.nht) return -1;
+  return nt * 32 + (lane & 31);
+}
+
+// w2 q: one 16-byte chunk per (e, c, kt, j, lane)
 __global__ void pack_w2q_kernel(const uint8_t* __restrict__ src, u32x4_t* __restrict__ dst, MoeGeom g, int64_t n) {
   GRID_STRIDE(i, n) {
-    int64_t t = i;
-    const int lane = (int)(t & 63); t >>= 6;
-    const int64_t kt = t % g.nkt2; t /= g.nkt2;
-    const int64_t nt = t % g.nht; const int64_t e = t / g.nht;
-    const int64_t row = nt * 32 + (lane & 31);
-    const int64_t blk = 2 * kt + (lane >> 5);
+    const ChunkIdx x = chunk_idx(i, g.nkt2, g.ncb2);
+    const int64_t row = w2_row(g, x.c, x.j, x.lane);
+    const int64_t blk = 2 * x.kt + (x.lane >> 5);
     u32x4_t v = {0u, 0u, 0u, 0u};
-    if (blk < g.I / 32)
-      v = perm_w2_block(*reinterpret_cast<const u32x4_t*>(src + (e * g.H + row) * (g.I / 2) + blk * 16));
+    if (row >= 0 && blk < g.I / 32)
+      v = perm_w2_block(*reinterpret_cast<const u32x4_t*>(src + (x.e * g.H + row) * (g.I / 2) + blk * 16));
     dst[i] = v;
   }
 }
 
 __global__ void unpack_w2q_kernel(const u32x4_t* __restrict__ src, uint8_t* __restrict__ dst, MoeGeom g, int64_t n) {
   GRID_STRIDE(i, n) {
-    int64_t t = i;
-    const int lane = (int)(t & 63); t >>= 6;
-    const int64_t kt = t % g.nkt2; t /= g.nkt2;
-    const int64_t nt = t % g.nht; const int64_t e = t / g.nht;
-    const int64_t row = nt * 32 + (lane & 31);
-    const int64_t blk = 2 * kt + (lane >> 5);
-    if (blk < g.I / 32)
-      *reinterpret_cast<u32x4_t*>(dst + (e * g.H + row) * (g.I / 2) + blk * 16) = unperm_w2_block(src[i]);
+    const ChunkIdx x = chunk_idx(i, g.nkt2, g.ncb2);
+    const int64_t row = w2_row(g, x.c, x.j, x.lane);
+    const int64_t blk = 2 * x.kt + (x.lane >> 5);
+    if (row >= 0 && blk < g.I / 32)
+      *reinterpret_cast<u32x4_t*>(dst + (x.e * g.H + row) * (g.I / 2) + blk * 16) = unperm_w2_block(src[i]);
   }
 }
 
-__global__ void pack_w2s_kernel(const uint8_t* __restrict__ src, uint32_t* __restrict__ dst, MoeGeom g, int64_t n) {
+__global__ void pack_w2s_kernel(const uint8_t* __restrict__ src, u32x4_t* __restrict__ dst, MoeGeom g, int64_t n) {
   GRID_STRIDE(i, n) {
-    int64_t t = i;
-    const int lane = (int)(t & 63); t >>= 6;
-    const int64_t grp = t % g.ngrp2; t /= g.ngrp2;
-    const int64_t nt = t % g.nht; const int64_t e = t / g.nht;
-    const int64_t row = nt * 32 + (lane & 31);
-    uint32_t word = 0;
-    for (int j = 0; j < 4; j++) {
-      const int64_t blk = 2 * (4 * grp + j) + (lane >> 5);
-      if (blk < g.I / 32) word |= (uint32_t)src[(e * g.H + row) * (g.I / 32) + blk] << (8 * j);
+    const ChunkIdx x = record_idx(i, g.nkt2, g.ncb2);
+    const int64_t blk = 2 * x.kt + (x.lane >> 5);
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    for (int j = 0; j < kCB; j++) {
+      const int64_t row = w2_row(g, x.c, j, x.lane);
+      if (row >= 0 && blk < g.I / 32) w[j >> 2] |= (uint32_t)src[(x.e * g.H + row) * (g.I / 32) + blk] << (8 * (j & 3));
     }
-    dst[i] = word;
+    dst[i] = u32x4_t{w[0], w[1], w[2], w[3]};
   }
 }
 
-__global__ void unpack_w2s_kernel(const uint32_t* __restrict__ src, uint8_t* __restrict__ dst, MoeGeom g, int64_t n) {
+__global__ void unpack_w2s_kernel(const u32x4_t* __restrict__ src, uint8_t* __restrict__ dst, MoeGeom g, int64_t n) {
   GRID_STRIDE(i, n) {
-    int64_t t = i;
-    const int lane = (int)(t & 63); t >>= 6;
-    const int64_t grp = t % g.ngrp2; t /= g.ngrp2;
-    const int64_t nt = t % g.nht; const int64_t e = t / g.nht;
-    const int64_t row = nt * 32 + (lane & 31);
-    const uint32_t word = src[i];
-    for (int j = 0; j < 4; j++) {
-      const int64_t blk = 2 * (4 * grp + j) + (lane >> 5);
-      if (blk < g.I / 32) dst[(e * g.H + row) * (g.I / 32) + blk] = (uint8_t)(word >> (8 * j));
+    const ChunkIdx x = record_idx(i, g.nkt2, g.ncb2);
+    const int64_t blk = 2 * x.kt + (x.lane >> 5);
+    const u32x4_t v = src[i];
+    for (int j = 0; j < kCB; j++) {
+      const int64_t row = w2_row(g, x.c, j, x.lane);
+      if (row >= 0 && blk < g.I / 32) dst[(x.e * g.H + row) * (g.I / 32) + blk] = (uint8_t)(v[j >> 2] >> (8 * (j & 3)));
     }
   }
 }
@@ -249,10 +258,10 @@ int launch_repack_gfx950(const MoeGeom& g, const BlobOffsets& o, bool bias, cons
   h.off_w13q = o.w13q; h.off_w13s = o.w13s; h.off_w2q = o.w2q; h.off_w2s = o.w2s;
   h.off_b13 = o.b13; h.off_b2 = o.b2; h.total = o.total;
   hipLaunchKernelGGL(write_header_kernel, dim3(1), dim3(64), 0, stream, base, h);
-  LAUNCH1D(pack_w13q_kernel, g.E * g.nit * g.nkt1 * 2 * 64, (const uint8_t*)w13_q, (u32x4_t*)(base + o.w13q), g);
-  LAUNCH1D(pack_w13s_kernel, g.E * g.nit * g.ngrp1 * 2 * 64, (const uint8_t*)w13_s, (uint32_t*)(base + o.w13s), g);
-  LAUNCH1D(pack_w2q_kernel, g.E * g.nht * g.nkt2 * 64, (const uint8_t*)w2_q, (u32x4_t*)(base + o.w2q), g);
-  LAUNCH1D(pack_w2s_kernel, g.E * g.nht * g.ngrp2 * 64, (const uint8_t*)w2_s, (uint32_t*)(base + o.w2s), g);
+  LAUNCH1D(pack_w13q_kernel, g.E * g.ncb1 * g.nkt1 * kCB * 64, (const uint8_t*)w13_q, (u32x4_t*)(base + o.w13q), g);
+  LAUNCH1D(pack_w13s_kernel, g.E * g.ncb1 * g.nkt1 * 64, (const uint8_t*)w13_s, (u32x4_t*)(base + o.w13s), g);
+  LAUNCH1D(pack_w2q_kernel, g.E * g.ncb2 * g.nkt2 * kCB * 64, (const uint8_t*)w2_q, (u32x4_t*)(base + o.w2q), g);
+  LAUNCH1D(pack_w2s_kernel, g.E * g.ncb2 * g.nkt2 * 64, (const uint8_t*)w2_s, (u32x4_t*)(base + o.w2s), g);
   if (bias) {
     LAUNCH1D(bias_kernel, g.E * 2 * g.I, b13, (uint16_t*)(base + o.b13), bias_is_fp32, g.E, 2 * g.I, 0);
     LAUNCH1D(bias_kernel, g.E * g.H, b2, (uint16_t*)(base + o.b2), bias_is_fp32, g.E, g.H, 0);
@@ -263,10 +272,10 @@ int launch_repack_gfx950(const MoeGeom& g, const BlobOffsets& o, bool bias, cons
 int launch_unpack_gfx950(const MoeGeom& g, const BlobOffsets& o, bool bias, const void* packed, void* w13_q,
                          void* w13_s, void* w2_q, void* w2_s, void* b13, void* b2, hipStream_t stream) {
   const uint8_t* base = (const uint8_t*)packed;
-  LAUNCH1D(unpack_w13q_kernel, g.E * g.nit * g.nkt1 * 2 * 64, (const u32x4_t*)(base + o.w13q), (uint8_t*)w13_q, g);
-  LAUNCH1D(unpack_w13s_kernel, g.E * g.nit * g.ngrp1 * 2 * 64, (const uint32_t*)(base + o.w13s), (uint8_t*)w13_s, g);
-  LAUNCH1D(unpack_w2q_kernel, g.E * g.nht * g.nkt2 * 64, (const u32x4_t*)(base + o.w2q), (uint8_t*)w2_q, g);
-  LAUNCH1D(unpack_w2s_kernel, g.E * g.nht * g.ngrp2 * 64, (const uint32_t*)(base + o.w2s), (uint8_t*)w2_s, g);
+  LAUNCH1D(unpack_w13q_kernel, g.E * g.ncb1 * g.nkt1 * kCB * 64, (const u32x4_t*)(base + o.w13q), (uint8_t*)w13_q, g);
+  LAUNCH1D(unpack_w13s_kernel, g.E * g.ncb1 * g.nkt1 * 64, (const u32x4_t*)(base + o.w13s), (uint8_t*)w13_s, g);
+  LAUNCH1D(unpack_w2q_kernel, g.E * g.ncb2 * g.nkt2 * kCB * 64, (const u32x4_t*)(base + o.w2q), (uint8_t*)w2_q, g);
+  LAUNCH1D(unpack_w2s_kernel, g.E * g.ncb2 * g.nkt2 * 64, (const u32x4_t*)(base + o.w2s), (uint8_t*)w2_s, g);
   if (bias) {
     if (b13) LAUNCH1D(bias_kernel, g.E * 2 * g.I, base + o.b13, (uint16_t*)b13, 0, g.E, 2 * g.I, 0);
     if (b2) LAUNCH1D(bias_kernel, g.E * g.H, base + o.b2, (uint16_t*)b2, 0, g.E, g.H, 0);

@@ -1,8 +1,14 @@
-// MoE front and back: activation preparation, top-k routing, the stable counting sort of
-// (token, expert) pairs with the GEMM tile schedule, and the final fp32 -> bf16 combine output.
+// MoE front: activation preparation, top-k routing, and the stable counting sort of (token, expert)
+// pairs that lays out the grouped GEMMs' rows and tile schedule.
 //
 // [NS: top-k routing of softmax(router logits) renormalized over the selected experts; the router
-//  sort/permute/gather step; the weighted top-k combine]
+//  sort/permute/gather step]
+//
+// Routing runs without global atomics in three launches: route_kernel (top-k per token and a
+// per-block expert histogram of kRouteTokens tokens), scan_kernel (one workgroup: prefix sums over
+// blocks and experts, the expert offsets, the padded row offsets and the M-tile list), scatter_kernel
+// (each block ranks its pairs per expert in token order and writes them to their rows).  The
+// resulting order is stable: pairs of one expert appear in increasing token order.
 #include "common.h"
 
 namespace {
@@ -11,15 +17,6 @@ namespace {
 
 typedef decltype(__builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(bf16x32_t{}, 1.0f)) fp6x32_t;
 
-// Split 32 bf16 values into kTerms E2M3 terms x = t0 + t1 + t2: each term is the current remainder
-// quantized with its own E8M0 scale from the 0.75 round-up rule (block maximum / scale < 7 <= 7.5, the
-// E2M3 maximum, so no term saturates), and the next remainder is exact in bf16 (a term is a multiple
-// of the remainder's ulp within one grid step of it).
-struct Fp6Split {
-  fp6x32_t t[kTerms];
-  uint32_t e[kTerms];
-};
-
 MX_DEV uint32_t amax_bits32(const uint32_t* w) {  // 16 words = 32 bf16 -> largest magnitude bits
   uint32_t m = 0;
 #pragma unroll
@@ -27,70 +24,56 @@ MX_DEV uint32_t amax_bits32(const uint32_t* w) {  // 16 words = 32 bf16 -> large
   return m;
 }
 
-MX_DEV Fp6Split split_fp6(const uint32_t* w /* 16 words */) {
-  Fp6Split p;
-  uint32_t cur[16];
-#pragma unroll
-  for (int i = 0; i < 16; i++) cur[i] = w[i];
-#pragma unroll
-  for (int term = 0; term < kTerms; term++) {
-    bf16x32_t v;
-#pragma unroll
-    for (int i = 0; i < 16; i++) {
-      bf16x2_t two = __builtin_bit_cast(bf16x2_t, cur[i]);
-      v[2 * i] = two[0];
-      v[2 * i + 1] = two[1];
-    }
-    p.e[term] = e8m0_from_amax_bits(amax_bits32(cur) << 16);
-    const float sc = e8m0_as_scale_operand(p.e[term]);
-    p.t[term] = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(v, sc);
-    if (term + 1 < kTerms) {
-      const auto deq = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(p.t[term], sc);
-#pragma unroll
-      for (int i = 0; i < 16; i++) {
-        const float a = bf16_bits_to_f32(cur[i] & 0xFFFFu) - deq[2 * i];
-        const float b = bf16_bits_to_f32(cur[i] >> 16) - deq[2 * i + 1];
-        cur[i] = f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
-      }
-    }
-  }
-  return p;
-}
-
-// x [T, ldx] bf16 -> xq/xs (three E2M3 terms per 32-element block, K padded to a multiple of 64 with
-// zero blocks); also clears the per-expert pair counters.
+// x [T, ldx] bf16 -> xq/xs: per 32-element block the two E2M3 terms x = t0 + t1.  Each term is the
+// current remainder quantized with its own E8M0 scale from the 0.75 round-up rule (block maximum /
+// scale < 7 <= 7.5, the E2M3 maximum, so no term saturates).  The remainder x - t0 is exact in bf16
+// (a bf16 value minus its own rounding to a coarser grid).  K is padded to a multiple of 64 with zero
+// blocks.
 __global__ __launch_bounds__(256) void xprep_kernel(const uint16_t* __restrict__ x, int64_t ldx, int64_t H, int64_t nblk,
-                                                    int64_t ngrp, uint8_t* __restrict__ xq, uint8_t* __restrict__ xs,
-                                                    int32_t* __restrict__ counts, int E,
-                                                    int64_t n) {
-  if (blockIdx.x == 0)
-    for (int i = threadIdx.x; i < E; i += blockDim.x) counts[i] = 0;
+                                                    uint8_t* __restrict__ xq, uint8_t* __restrict__ xs, int64_t n) {
   GRID_STRIDE(i, n) {
     const int64_t t = i / nblk, b = i % nblk;
     uint32_t w[16];
-    const bool in = b < H / 32;
-    if (in) {
+    if (b < H / 32) {
       const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + t * ldx + b * 32);
 #pragma unroll
       for (int j = 0; j < 4; j++) {
-        u32x4_t v = src[j];
+        const u32x4_t v = __builtin_nontemporal_load(src + j);
         w[4 * j] = v[0]; w[4 * j + 1] = v[1]; w[4 * j + 2] = v[2]; w[4 * j + 3] = v[3];
       }
     } else {
 #pragma unroll
       for (int j = 0; j < 16; j++) w[j] = 0;
     }
-    const Fp6Split p = split_fp6(w);
-    u32x4_t* dst = reinterpret_cast<u32x4_t*>(xq + (t * nblk + b) * kSlot);
-    dst[0] = u32x4_t{p.t[0][0], p.t[0][1], p.t[0][2], p.t[0][3]};
-    dst[1] = u32x4_t{p.t[0][4], p.t[0][5], p.t[1][0], p.t[1][1]};
-    dst[2] = u32x4_t{p.t[1][2], p.t[1][3], p.t[1][4], p.t[1][5]};
-    dst[3] = u32x4_t{p.t[2][0], p.t[2][1], p.t[2][2], p.t[2][3]};
-    dst[4] = u32x4_t{p.t[2][4], p.t[2][5], 0u, 0u};
-    const int64_t grp = b >> 3, j = (b & 7) >> 1, par = b & 1;
-    uint8_t* s = xs + (t * ngrp + grp) * (kTerms * 8) + par * 4 + j;
+    fp6x32_t tq[kTerms];
+    uint32_t te[kTerms];
 #pragma unroll
-    for (int term = 0; term < kTerms; term++) s[term * 8] = (uint8_t)p.e[term];
+    for (int term = 0; term < kTerms; term++) {
+      bf16x32_t v;
+#pragma unroll
+      for (int j = 0; j < 16; j++) {
+        const bf16x2_t two = __builtin_bit_cast(bf16x2_t, w[j]);
+        v[2 * j] = two[0];
+        v[2 * j + 1] = two[1];
+      }
+      te[term] = e8m0_from_amax_bits(amax_bits32(w) << 16);
+      const float sc = e8m0_as_scale_operand(te[term]);
+      tq[term] = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(v, sc);
+      if (term + 1 < kTerms) {
+        const auto deq = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(tq[term], sc);
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+          const float a = bf16_bits_to_f32(w[j] & 0xFFFFu) - deq[2 * j];
+          const float c = bf16_bits_to_f32(w[j] >> 16) - deq[2 * j + 1];
+          w[j] = f32_to_bf16_bits(a) | (f32_to_bf16_bits(c) << 16);
+        }
+      }
+    }
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(xq + i * kSlot);
+    dst[0] = u32x4_t{tq[0][0], tq[0][1], tq[0][2], tq[0][3]};
+    dst[1] = u32x4_t{tq[0][4], tq[0][5], tq[1][0], tq[1][1]};
+    dst[2] = u32x4_t{tq[1][2], tq[1][3], tq[1][4], tq[1][5]};
+    reinterpret_cast<uint32_t*>(xs)[i] = te[0] | (te[1] << 8);
   }
 }
 
@@ -101,146 +84,212 @@ MX_DEV uint32_t logit_key(float l) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-constexpr int kMaxPerLane = 16;  // E <= 1024
+constexpr int kRouteWaves = 16;                                // waves per routing workgroup
+constexpr int kTokPerWave = kRouteTokens / kRouteWaves;        // tokens each wave routes
 
-// One wave per token: k rounds of a wave-wide arg-max over 64-bit keys (logit key, inverted expert
-// index), so equal logits go to the lower expert index; softmax weights of the selected experts.
-__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int64_t T, int E, int k,
-                                                    int renormalize, int32_t* __restrict__ ids, float* __restrict__ wts,
-                                                    int32_t* __restrict__ counts) {
-  const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;  // uniform per wave
-  const float* lt = logits + t * E;
-  uint64_t key[kMaxPerLane];
-  float val[kMaxPerLane];
+// Workgroup b routes tokens [b*kRouteTokens, (b+1)*kRouteTokens): each wave takes kTokPerWave tokens
+// (their logits are loaded together), and for each runs k rounds of a wave-wide arg-max over 64-bit
+// keys (logit key, inverted expert index), so equal logits go to the lower expert index; softmax
+// weights of the selected experts (renormalized over them, or over all experts).  The block's pair
+// count per expert goes to blkcnt[b][e].  NPL logits per lane (E <= 64 * NPL).
+template <int NPL>
+__global__ __launch_bounds__(1024) void route_kernel(const float* __restrict__ logits, int64_t T, int E, int k,
+                                                     int renormalize, int32_t* __restrict__ ids, float* __restrict__ wts,
+                                                     int32_t* __restrict__ blkcnt) {
+  __shared__ int hist[64 * NPL];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < E; i += blockDim.x) hist[i] = 0;
+  __syncthreads();
+  float val[kTokPerWave][NPL];
 #pragma unroll
-  for (int j = 0; j < kMaxPerLane; j++) {
-    const int idx = lane + 64 * j;
-    if (idx < E) {
-      val[j] = lt[idx];
-      key[j] = ((uint64_t)logit_key(val[j]) << 32) | (uint32_t)(~idx);
-    } else {
-      val[j] = 0.f;
-      key[j] = 0;
+  for (int q = 0; q < kTokPerWave; q++) {
+    const int64_t t = (int64_t)blockIdx.x * kRouteTokens + wave * kTokPerWave + q;
+#pragma unroll
+    for (int j = 0; j < NPL; j++) {
+      const int idx = lane + 64 * j;
+      val[q][j] = (t < T && idx < E) ? logits[t * E + idx] : 0.f;
     }
   }
-  int my_id = 0;
-  float my_l = 0.f, lmax = 0.f;
-  for (int r = 0; r < k; r++) {
-    uint64_t best = 0;
 #pragma unroll
-    for (int j = 0; j < kMaxPerLane; j++) best = key[j] > best ? key[j] : best;
+  for (int q = 0; q < kTokPerWave; q++) {
+    const int64_t t = (int64_t)blockIdx.x * kRouteTokens + wave * kTokPerWave + q;
+    if (t >= T) break;  // uniform per wave
+    uint64_t key[NPL];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)best, off);
-      const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(best >> 32), off);
-      const uint64_t o = ((uint64_t)hi << 32) | lo;
-      best = o > best ? o : best;
+    for (int j = 0; j < NPL; j++) {
+      const int idx = lane + 64 * j;
+      key[j] = idx < E ? ((uint64_t)logit_key(val[q][j]) << 32) | (uint32_t)(~idx) : 0;
     }
-    const int id = (int)(~(uint32_t)best);
-    // owner lane clears the winner and broadcasts its logit
-    float wl = 0.f;
+    int my_id = 0;
+    float my_l = 0.f, lmax = 0.f;
+    for (int r = 0; r < k; r++) {
+      uint64_t best = 0;
 #pragma unroll
-    for (int j = 0; j < kMaxPerLane; j++) {
-      if (lane + 64 * j == id) {
-        wl = val[j];
-        key[j] = 0;
+      for (int j = 0; j < NPL; j++) best = key[j] > best ? key[j] : best;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)best, off);
+        const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(best >> 32), off);
+        const uint64_t o = ((uint64_t)hi << 32) | lo;
+        best = o > best ? o : best;
+      }
+      const int id = (int)(~(uint32_t)best);
+      float wl = 0.f;  // the owner lane clears the winner and broadcasts its logit
+#pragma unroll
+      for (int j = 0; j < NPL; j++) {
+        if (lane + 64 * j == id) {
+          wl = val[q][j];
+          key[j] = 0;
+        }
+      }
+      wl = __shfl(wl, id & 63);
+      if (r == 0) lmax = wl;
+      if (lane == r) {
+        my_id = id;
+        my_l = wl;
       }
     }
-    wl = __shfl(wl, id & 63);
-    if (r == 0) lmax = wl;
-    if (lane == r) {
-      my_id = id;
-      my_l = wl;
+    const float ex = lane < k ? __expf(my_l - lmax) : 0.f;
+    float den = 0.f;
+    if (renormalize) {
+      den = ex;
+    } else {
+#pragma unroll
+      for (int j = 0; j < NPL; j++)
+        if (lane + 64 * j < E) den += __expf(val[q][j] - lmax);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
+    if (lane < k) {
+      ids[t * k + lane] = my_id;
+      wts[t * k + lane] = ex / den;
+      atomicAdd(&hist[my_id], 1);
     }
   }
-  const float ex = lane < k ? __expf(my_l - lmax) : 0.f;
-  float den = 0.f;
-  if (renormalize) {
-    den = ex;
-  } else {
-#pragma unroll
-    for (int j = 0; j < kMaxPerLane; j++)
-      if (lane + 64 * j < E) den += __expf(val[j] - lmax);
+  __syncthreads();
+  for (int i = threadIdx.x; i < E; i += blockDim.x) blkcnt[(int64_t)blockIdx.x * E + i] = hist[i];
+}
+
+// One workgroup of 1024 threads.  (1) Per expert, the total pair count and the exclusive prefix of
+// blkcnt over blocks (rewritten in place); (2) exclusive scans over experts of the counts, of the
+// counts padded to 32 and of the M tiles of BM rows; (3) offsets, padded offsets, the tile list, and
+// the padding rows of every expert plus 128 slack rows after the last one (pair -1, token 0,
+// weight 0), so a GEMM tile may read up to 128 rows past its expert's start.
+__global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ blkcnt, int nb, int E, int BM,
+                                                    int32_t* __restrict__ offsets, int32_t* __restrict__ poffsets,
+                                                    int4* __restrict__ tiles, int32_t* __restrict__ ntiles,
+                                                    int32_t* __restrict__ prow_pair, int32_t* __restrict__ prow_tok,
+                                                    float* __restrict__ prow_w) {
+  __shared__ int part[1024];
+  __shared__ int pin[1024];
+  __shared__ int wsum[3][16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int es = 64;  // expert stride: power of two >= E, at least one wave
+  while (es < E) es <<= 1;
+  const int G = 1024 / es;  // block groups
+  const int e = tid % es, grp = tid / es;
+  const int per = (nb + G - 1) / G;
+  const int b0 = min(nb, grp * per), b1 = min(nb, b0 + per);
+  int s = 0;
+  if (e < E)
+    for (int b = b0; b < b1; b++) s += blkcnt[(int64_t)b * E + e];
+  part[tid] = s;
+  __syncthreads();
+  int base = 0, total = 0;
+  for (int q = 0; q < G; q++) {
+    const int v = part[q * es + e];
+    if (q < grp) base += v;
+    total += v;
   }
+  if (e < E)
+    for (int b = b0; b < b1; b++) {
+      const int v = blkcnt[(int64_t)b * E + e];
+      blkcnt[(int64_t)b * E + e] = base;
+      base += v;
+    }
+  // scans over experts: thread e of group 0 (tid == e) holds expert e, every other thread zeros
+  int v0 = 0, v1 = 0, v2 = 0;
+  if (grp == 0 && e < E) {
+    v0 = total;
+    v1 = (total + 31) & ~31;
+    v2 = (total + BM - 1) / BM;
+  }
+  // inclusive wave scans, then across waves
+  int x0 = v0, x1 = v1, x2 = v2;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
-  if (lane < k) {
-    ids[t * k + lane] = my_id;
-    wts[t * k + lane] = ex / den;
-    atomicAdd(&counts[my_id], 1);
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y0 = __shfl_up(x0, off), y1 = __shfl_up(x1, off), y2 = __shfl_up(x2, off);
+    if (lane >= off) { x0 += y0; x1 += y1; x2 += y2; }
+  }
+  if (lane == 63) { wsum[0][wave] = x0; wsum[1][wave] = x1; wsum[2][wave] = x2; }
+  __syncthreads();
+  int p0 = 0, p1 = 0, p2 = 0;
+  for (int q = 0; q < wave; q++) { p0 += wsum[0][q]; p1 += wsum[1][q]; p2 += wsum[2][q]; }
+  x0 += p0; x1 += p1; x2 += p2;  // inclusive scans over threads 0..tid
+  pin[tid] = x1;
+  __syncthreads();
+  if (grp == 0 && e < E) {
+    const int off = x0 - v0, poff = x1 - v1, toff = x2 - v2;
+    offsets[e] = off;
+    poffsets[e] = poff;
+    for (int i = 0; i < v2; i++) tiles[toff + i] = make_int4(e, poff + i * BM, min(BM, total - i * BM), 0);
+    for (int r = poff + total; r < poff + v1; r++) {
+      prow_pair[r] = -1;
+      prow_tok[r] = 0;
+      prow_w[r] = 0.f;
+    }
+    if (e == E - 1) {
+      offsets[E] = x0;
+      poffsets[E] = x1;
+      *ntiles = x2;
+    }
+  }
+  // slack rows after the last expert
+  const int ptot = pin[E - 1];
+  if (tid < 128) {
+    prow_pair[ptot + tid] = -1;
+    prow_tok[ptot + tid] = 0;
+    prow_w[ptot + tid] = 0.f;
   }
 }
 
-// One workgroup per expert: prefix sums of the counts of lower experts (compact and padded offsets,
-// M-tile offset), the tile list of this expert, and a stable scatter of its pairs in token order.
-__global__ __launch_bounds__(256) void place_kernel(const int32_t* __restrict__ ids, const int32_t* __restrict__ counts,
-                                                    int64_t T, int k, int E, int BM, int32_t* __restrict__ offsets,
-                                                    int32_t* __restrict__ poffsets, int32_t* __restrict__ sorted_pairs,
-                                                    int32_t* __restrict__ prow_pair, int4* __restrict__ tiles,
-                                                    int32_t* __restrict__ ntiles) {
-  const int e = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  __shared__ int red[4][3];
-  __shared__ int wsum[4];
-  int s0 = 0, s1 = 0, s2 = 0;
-  for (int i = tid; i < e; i += 256) {
-    const int c = counts[i];
-    s0 += c;
-    s1 += (c + 31) & ~31;
-    s2 += (c + BM - 1) / BM;
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    s0 += __shfl_xor(s0, off);
-    s1 += __shfl_xor(s1, off);
-    s2 += __shfl_xor(s2, off);
-  }
-  if (lane == 0) { red[wave][0] = s0; red[wave][1] = s1; red[wave][2] = s2; }
+// One wave per block of kRouteTokens tokens (lane = token): rank of each pair among the pairs of its
+// expert in token order = (pairs of that expert in earlier blocks) + (earlier lanes of this block with
+// that expert), from a 64-bit lane mask per expert.  Writes the compact order (sorted_pairs, may be
+// NULL) and the padded rows (pair, token, routing weight).
+__global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__ ids, const float* __restrict__ wts,
+                                                     const int32_t* __restrict__ blkcnt, int64_t T, int k, int E,
+                                                     const int32_t* __restrict__ offsets,
+                                                     const int32_t* __restrict__ poffsets,
+                                                     int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ prow_pair,
+                                                     int32_t* __restrict__ prow_tok, float* __restrict__ prow_w) {
+  __shared__ uint32_t mlo[1024], mhi[1024];
+  const int lane = threadIdx.x;
+  const int64_t b = blockIdx.x;
+  for (int i = lane; i < E; i += 64) { mlo[i] = 0; mhi[i] = 0; }
   __syncthreads();
-  const int off = red[0][0] + red[1][0] + red[2][0] + red[3][0];
-  const int poff = red[0][1] + red[1][1] + red[2][1] + red[3][1];
-  const int toff = red[0][2] + red[1][2] + red[2][2] + red[3][2];
-  const int n = counts[e];
-  const int npad = (n + 31) & ~31;
-  const int nt = (n + BM - 1) / BM;
-  if (tid == 0) {
-    offsets[e] = off;
-    poffsets[e] = poff;
-    if (e == E - 1) {
-      offsets[E] = off + n;
-      poffsets[E] = poff + npad;
-      *ntiles = toff + nt;
+  const int64_t t = b * kRouteTokens + lane;
+  const bool live = t < T;
+  if (live)
+    for (int j = 0; j < k; j++) {
+      const int ex = ids[t * k + j];
+      if (lane < 32) atomicOr(&mlo[ex], 1u << lane);
+      else atomicOr(&mhi[ex], 1u << (lane - 32));
     }
-  }
-  for (int i = tid; i < nt; i += 256) tiles[toff + i] = make_int4(e, poff + i * BM, min(BM, n - i * BM), 0);
-  for (int i = n + tid; i < npad; i += 256) prow_pair[poff + i] = -1;
-  if (n == 0) return;
-  int base = 0;
-  for (int64_t t0 = 0; t0 < T; t0 += 256) {
-    const int64_t t = t0 + tid;
-    int j = -1;
-    if (t < T)
-      for (int jj = 0; jj < k; jj++)
-        if (ids[t * k + jj] == e) j = jj;
-    const bool f = j >= 0;
-    const uint64_t bal = __ballot(f);
-    const int before = __popcll(bal & ((1ull << lane) - 1ull));
-    __syncthreads();
-    if (lane == 0) wsum[wave] = __popcll(bal);
-    __syncthreads();
-    int wbase = 0;
-    for (int q = 0; q < wave; q++) wbase += wsum[q];
-    const int total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-    if (f) {
-      const int pos = base + wbase + before;
+  __syncthreads();
+  if (live) {
+    const uint64_t lt = (1ull << lane) - 1ull;
+    for (int j = 0; j < k; j++) {
+      const int ex = ids[t * k + j];
+      const uint64_t m = ((uint64_t)mhi[ex] << 32) | mlo[ex];
+      const int rank = blkcnt[b * E + ex] + __popcll(m & lt);
       const int32_t pair = (int32_t)(t * k + j);
-      sorted_pairs[off + pos] = pair;
-      prow_pair[poff + pos] = pair;
+      if (sorted_pairs) sorted_pairs[offsets[ex] + rank] = pair;
+      const int r = poffsets[ex] + rank;
+      prow_pair[r] = pair;
+      prow_tok[r] = (int32_t)t;
+      prow_w[r] = wts[pair];
     }
-    base += total;
-    if (base >= n) break;  // uniform: every thread sees the same total
   }
 }
 
@@ -253,37 +302,41 @@ inline unsigned grid_for(int64_t n, int threads = 256) {
 
 }  // namespace
 
-int launch_xprep(const void* x, int64_t T, int64_t ldx, const MoeGeom& g, void* xq, void* xs, int32_t* counts,
-                 hipStream_t stream) {
+int launch_xprep(const void* x, int64_t T, int64_t ldx, const MoeGeom& g, void* xq, void* xs, hipStream_t stream) {
   const int64_t nblk = 2 * g.nkt1;
   const int64_t n = T * nblk;
-  hipLaunchKernelGGL(xprep_kernel, dim3(grid_for(n)), dim3(256), 0, stream, (const uint16_t*)x, ldx, g.H, nblk,
-                     g.ngrp1, (uint8_t*)xq, (uint8_t*)xs, counts, (int)g.E, n);
-  return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
-}
-
-__global__ void zero_i32_kernel(int32_t* p, int n) {
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
-}
-
-int launch_zero_i32(int32_t* p, int n, hipStream_t stream) {
-  if (n > 0) hipLaunchKernelGGL(zero_i32_kernel, dim3(grid_for(n)), dim3(256), 0, stream, p, n);
+  if (n > 0)
+    hipLaunchKernelGGL(xprep_kernel, dim3(grid_for(n)), dim3(256), 0, stream, (const uint16_t*)x, ldx, g.H, nblk,
+                       (uint8_t*)xq, (uint8_t*)xs, n);
   return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
 }
 
 int launch_route(const float* logits, int64_t T, int E, int k, int renormalize, int32_t* ids, float* w,
-                 int32_t* counts, hipStream_t stream) {
-  if (T > 0)
-    hipLaunchKernelGGL(route_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream, logits, T, E, k,
-                       renormalize, ids, w, counts);
+                 int32_t* blkcnt, hipStream_t stream) {
+  const unsigned nb = (unsigned)cdiv(T, kRouteTokens);
+  if (T > 0) {
+    if (E <= 64)
+      hipLaunchKernelGGL(route_kernel<1>, dim3(nb), dim3(1024), 0, stream, logits, T, E, k, renormalize, ids, w, blkcnt);
+    else if (E <= 128)
+      hipLaunchKernelGGL(route_kernel<2>, dim3(nb), dim3(1024), 0, stream, logits, T, E, k, renormalize, ids, w, blkcnt);
+    else if (E <= 256)
+      hipLaunchKernelGGL(route_kernel<4>, dim3(nb), dim3(1024), 0, stream, logits, T, E, k, renormalize, ids, w, blkcnt);
+    else if (E <= 512)
+      hipLaunchKernelGGL(route_kernel<8>, dim3(nb), dim3(1024), 0, stream, logits, T, E, k, renormalize, ids, w, blkcnt);
+    else
+      hipLaunchKernelGGL(route_kernel<16>, dim3(nb), dim3(1024), 0, stream, logits, T, E, k, renormalize, ids, w, blkcnt);
+  }
   return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
 }
 
-int launch_place(const int32_t* ids, const int32_t* counts, int64_t T, int k, int E, int BM, int32_t* offsets,
-                 int32_t* poffsets, int32_t* sorted_pairs, int32_t* prow_pair, void* tiles, int32_t* ntiles,
-                 hipStream_t stream) {
-  hipLaunchKernelGGL(place_kernel, dim3((unsigned)E), dim3(256), 0, stream, ids, counts, T, k, E, BM, offsets,
-                     poffsets, sorted_pairs, prow_pair, (int4*)tiles, ntiles);
+int launch_place(const int32_t* ids, const float* w, int32_t* blkcnt, int64_t T, int k, int E, int BM, int32_t* offsets,
+                 int32_t* poffsets, int32_t* sorted_pairs, int32_t* prow_pair, int32_t* prow_tok, float* prow_w,
+                 void* tiles, int32_t* ntiles, hipStream_t stream) {
+  const int nb = (int)cdiv(T, kRouteTokens);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream, blkcnt, nb, E, BM, offsets, poffsets, (int4*)tiles,
+                     ntiles, prow_pair, prow_tok, prow_w);
+  if (nb > 0)
+    hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)nb), dim3(64), 0, stream, ids, w, blkcnt, T, k, E, offsets,
+                       poffsets, sorted_pairs, prow_pair, prow_tok, prow_w);
   return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
 }
-
