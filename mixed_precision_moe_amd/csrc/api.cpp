@@ -20,15 +20,18 @@ int launch_unpack_gfx950(const MoeGeom& g, const BlobOffsets& o, bool bias, cons
 int launch_repack_standard(const MoeGeom& g, bool bias, const void* w13_q, const void* w13_s, const void* w2_q,
                            const void* w2_s, const void* b13, const void* b2, int bias_is_fp32, bool swap, bool tiled,
                            const size_t off[6], void* out, hipStream_t stream);
-int launch_xprep(const void* x, int64_t T, int64_t ldx, const MoeGeom& g, void* xq, void* xs, hipStream_t stream);
+int launch_xprep(const void* x, int64_t T, int64_t ldx, const MoeGeom& g, void* xq, void* xs, int32_t* zero,
+                 int64_t nzero, hipStream_t stream);
+int launch_zero_i32(int32_t* p, int64_t n, hipStream_t stream);
 int launch_route(const float* logits, int64_t T, int E, int k, int renormalize, int32_t* ids, float* w,
                  int32_t* blkcnt, hipStream_t stream);
 int launch_place(const int32_t* ids, const float* w, int32_t* blkcnt, int64_t T, int k, int E, int BM, int32_t* offsets,
                  int32_t* poffsets, int32_t* sorted_pairs, int32_t* prow_pair, int32_t* prow_tok, float* prow_w,
-                 void* tiles, int32_t* ntiles, hipStream_t stream);
+                 int32_t* pair_prow, void* tiles, int32_t* ntiles, hipStream_t stream);
 int launch_gemm1(int NRG, const GemmArgs& a, int64_t max_tiles, hipStream_t stream);
 int launch_gemm2(int NRG, const GemmArgs& a, int64_t max_tiles, hipStream_t stream);
-int launch_combine(const float* obuf, void* y, int64_t T, int64_t H, int k, hipStream_t stream);
+int launch_combine(const uint16_t* o16, const uint8_t* osc, const int32_t* pair_prow, void* y, int64_t T, int64_t H, int k,
+                   hipStream_t stream);
 
 namespace {
 
@@ -249,10 +252,11 @@ MX_API int moe_mxfp4_route(const float* router_logits, int64_t T, int32_t E, int
   if (workspace_bytes < w.total) return MXFP4_ERR_WORKSPACE;
   uint8_t* ws = (uint8_t*)workspace;
   int32_t* blkcnt = (int32_t*)(ws + w.blkcnt);
+  if ((st = launch_zero_i32(blkcnt, cdiv(T, kRouteTokens) * E, S(stream)))) return st;
   if ((st = launch_route(router_logits, T, E, top_k, renormalize, topk_ids, topk_w, blkcnt, S(stream)))) return st;
   return launch_place(topk_ids, topk_w, blkcnt, T, top_k, E, 32, expert_offsets, (int32_t*)(ws + w.poffsets),
                       sorted_pairs, (int32_t*)(ws + w.prow_pair), (int32_t*)(ws + w.prow_tok), (float*)(ws + w.prow_w),
-                      ws + w.tiles, (int32_t*)(ws + w.ntiles), S(stream));
+                      nullptr, ws + w.tiles, (int32_t*)(ws + w.ntiles), S(stream));
 }
 
 MX_API size_t moe_mxfp4_workspace_bytes(const mxfp4_moe_dims* d, int64_t T, int32_t top_k) {
@@ -282,7 +286,6 @@ static int forward_impl(const mxfp4_moe_dims* d, const void* packed_gfx950, cons
   const int64_t P = T * top_k;
   int32_t* ids = topk_ids ? topk_ids : (int32_t*)(ws + w.ids);
   float* wts = topk_w ? topk_w : (float*)(ws + w.w);
-  float* obuf = (float*)(ws + w.obuf);
   const int NRG = choose_nrg(P, g.E);
   int ev = 0;
   auto mark = [&]() -> int {
@@ -291,21 +294,25 @@ static int forward_impl(const mxfp4_moe_dims* d, const void* packed_gfx950, cons
     return MXFP4_OK;
   };
   if ((st = mark())) return st;
-  if ((st = launch_xprep(x_bf16, T, ldx, g, ws + w.xq, ws + w.xs, s)) || (st = mark())) return st;
+  if ((st = launch_xprep(x_bf16, T, ldx, g, ws + w.xq, ws + w.xs, (int32_t*)(ws + w.blkcnt), cdiv(T, kRouteTokens) * g.E,
+                         s)) ||
+      (st = mark()))
+    return st;
   if ((st = launch_route(router_logits, T, (int)g.E, top_k, renormalize, ids, wts, (int32_t*)(ws + w.blkcnt), s)) ||
       (st = mark()))
     return st;
   if ((st = launch_place(ids, wts, (int32_t*)(ws + w.blkcnt), T, top_k, (int)g.E, 32 * NRG, (int32_t*)(ws + w.offsets),
                          (int32_t*)(ws + w.poffsets), nullptr, (int32_t*)(ws + w.prow_pair),
-                         (int32_t*)(ws + w.prow_tok), (float*)(ws + w.prow_w), ws + w.tiles,
-                         (int32_t*)(ws + w.ntiles), s)) ||
+                         (int32_t*)(ws + w.prow_tok), (float*)(ws + w.prow_w), (int32_t*)(ws + w.pair_prow),
+                         ws + w.tiles, (int32_t*)(ws + w.ntiles), s)) ||
       (st = mark()))
     return st;
   const uint8_t* blob = (const uint8_t*)packed_gfx950;
   GemmArgs a1 = {blob + o.w13q, blob + o.w13s, d->has_bias ? (const uint16_t*)(blob + o.b13) : nullptr,
                  ws + w.xq, ws + w.xs, (const int32_t*)(ws + w.prow_tok), (const int32_t*)(ws + w.prow_pair),
                  (const float*)(ws + w.prow_w), (const int4*)(ws + w.tiles), (const int32_t*)(ws + w.ntiles),
-                 ws + w.actq, ws + w.acts, nullptr, g};
+                 ws + w.actq, ws + w.acts, nullptr, nullptr, (int32_t)g.nkt1, (int32_t)g.ncb1, (int32_t)g.nit,
+                 (int32_t)g.nkt2, (int32_t)(2 * g.nkt1), (int32_t)g.I, (int32_t)g.H};
   if ((st = launch_gemm1(NRG, a1, w.max_tiles, s)) || (st = mark())) return st;
   GemmArgs a2 = a1;
   a2.wq = blob + o.w2q;
@@ -313,9 +320,16 @@ static int forward_impl(const mxfp4_moe_dims* d, const void* packed_gfx950, cons
   a2.bias = d->has_bias ? (const uint16_t*)(blob + o.b2) : nullptr;
   a2.xq = ws + w.actq;
   a2.xs = ws + w.acts;
-  a2.obuf = obuf;
+  a2.o16 = (uint16_t*)(ws + w.o16);
+  a2.osc = ws + w.osc;
+  a2.nkt = (int32_t)g.nkt2;
+  a2.ncb = (int32_t)g.ncb2;
+  a2.ntl = (int32_t)g.nht;
   if ((st = launch_gemm2(NRG, a2, w.max_tiles, s)) || (st = mark())) return st;
-  if ((st = launch_combine(obuf, y_bf16, T, g.H, top_k, s)) || (st = mark())) return st;
+  if ((st = launch_combine((const uint16_t*)(ws + w.o16), ws + w.osc, (const int32_t*)(ws + w.pair_prow), y_bf16, T, g.H,
+                           top_k, s)) ||
+      (st = mark()))
+    return st;
   return MXFP4_OK;
 }
 

@@ -139,12 +139,16 @@ constexpr int kSlot = 48;
 //         K block l/32)
 //   acts: [row group][nkt2][64 lanes][4]
 //   tiles: int4 (expert, first padded row, valid rows, 0) per M tile of the GEMMs
-//   obuf: fp32 [T*k][H], row t*k + j = topk_w[t][j] * (expert output + b2) of the token's j-th expert
+//   pair_prow: [T*k] padded row of each (token, slot) pair
+//   o16 : fp16 [padded rows][H], row r = w * (expert output + b2) of the pair at row r, divided by the
+//         power of two 2^(osc - 127) of its block
+//   osc : [padded rows / 32][2][H] bytes, the block exponents: one per (32-row group, row parity
+//         (r / 4) % 2, column), i.e. per 16 rows of one column as one lane of the second GEMM holds them
 constexpr int kRouteTokens = 64;
 
 struct FwdWs {
-  uint64_t blkcnt, offsets, poffsets, sorted_pairs, ids, w, prow_pair, prow_tok, prow_w, tiles, ntiles, xq, xs, actq,
-      acts, obuf, total;
+  uint64_t blkcnt, offsets, poffsets, sorted_pairs, ids, w, prow_pair, prow_tok, prow_w, pair_prow, tiles, ntiles, xq, xs,
+      actq, acts, o16, osc, total;
   int64_t nrows_alloc, max_tiles;
 };
 
@@ -164,24 +168,27 @@ static inline FwdWs fwd_ws(const MoeGeom& g, int64_t T, int64_t k) {
   w.prow_pair = take(4 * w.nrows_alloc);
   w.prow_tok = take(4 * w.nrows_alloc);
   w.prow_w = take(4 * w.nrows_alloc);
+  w.pair_prow = take(4 * P);
   w.tiles = take(16 * w.max_tiles);
   w.ntiles = take(16);
   w.xq = take((uint64_t)T * 2 * g.nkt1 * kSlot);
   w.xs = take((uint64_t)T * 2 * g.nkt1 * 4);
   w.actq = take((uint64_t)(w.nrows_alloc / 32) * g.nkt2 * 64 * kSlot);
   w.acts = take((uint64_t)(w.nrows_alloc / 32) * g.nkt2 * 64 * 4);
-  w.obuf = take((uint64_t)P * g.H * 4);
+  w.o16 = take((uint64_t)w.nrows_alloc * g.H * 2);
+  w.osc = take((uint64_t)(w.nrows_alloc / 32) * 2 * g.H);
   w.total = p;
   return w;
 }
 
-// Arguments of the grouped GEMM kernels (device pointers into the blob and the workspace).
+// Arguments of the grouped GEMM kernels (device pointers into the blob and the workspace, and the
+// 32-bit sizes the kernels index with).
 struct GemmArgs {
   const uint8_t* wq;        // weight pieces of this GEMM
   const uint8_t* ws;        // weight scale records
   const uint16_t* bias;     // b13 or b2 (bf16) or NULL
   const uint8_t* xq;        // first GEMM: per-token slots; second: activation slots by row group
-  const uint8_t* xs;        // matching scale pairs
+  const uint8_t* xs;        // matching scale dwords
   const int32_t* prow_tok;  // padded row -> token
   const int32_t* prow_pair; // padded row -> pair (-1 = padding)
   const float* prow_w;      // padded row -> routing weight
@@ -189,6 +196,11 @@ struct GemmArgs {
   const int32_t* ntiles;
   uint8_t* actq;            // first GEMM output
   uint8_t* acts;
-  float* obuf;              // second GEMM output
-  MoeGeom g;
+  uint16_t* o16;            // second GEMM output (fp16, padded-row order) and its block exponents
+  uint8_t* osc;
+  int32_t nkt, ncb;         // K steps and column blocks of this GEMM
+  int32_t ntl;              // output column tiles of this GEMM (I/32 activation tiles, or H/32)
+  int32_t nkt2;             // K steps of the second GEMM (layout of the activation)
+  int32_t nblk;             // 32-element blocks per token row of xq (2 * K steps of the first GEMM)
+  int32_t I, H;
 };

@@ -9,8 +9,9 @@
 // The MFMA has no bf16 operand, so a bf16 activation enters as two E2M3 (FP6) terms x = t0 + t1, each
 // with its own E8M0 scale per 32 elements, and every product is issued once per term against the same
 // FP4 weight registers; FP6 x FP4 runs at the FP4 rate on gfx950.  The first GEMM's output (the SwiGLU
-// activation) stays fp32 until it is split into the second GEMM's two terms, and the second GEMM writes
-// fp32 rows that the combine sums in fp32, so the only bf16 rounding after the input is the output's.
+// activation) stays fp32 until it is split into the second GEMM's two terms, and the second GEMM's rows
+// are block-scaled fp16 that the combine sums in fp32, so the only bf16 rounding after the input is the
+// output's.
 //
 // First GEMM, transposed: D[n][m] = sum_k W13[n][k] x[m][k], weights as the A operand (rows n = 32
 // gate or up rows of one tile), tokens as the B operand (columns m = 32 tokens gathered through the
@@ -19,7 +20,9 @@
 // activation is split over the two lane halves (one exchange for the block maximum).
 //
 // Second GEMM, not transposed: D[m][n] = sum_k act[m][k] W2[n][k]; lane l holds output column l%32 and
-// rows 8*jj + 4*(l/32) + i, so each store instruction writes 2 x 32 consecutive floats of o_buf.
+// rows 8*jj + 4*(l/32) + i.  Its rows go to o16 (fp16 with a power-of-two exponent per 16 rows of a
+// column, which keeps about eleven significant bits of every value that matters for the sum) in the
+// padded row order; the combine gathers each token's k rows.
 //
 // Both GEMMs run one kernel template.  A workgroup of four waves (WR x WC) computes an M tile of
 // NRG = WR*RW row groups of 32 rows against NT = WC*CW weight tiles of 32 columns; wave (wr, wc) holds
@@ -79,7 +82,7 @@ MX_DEV void block_sync() {
   asm volatile("" ::: "memory");
 }
 
-MX_DEV float silu(float g) { return g / (1.0f + __expf(-g)); }
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------------------------------------------
 // Kernel configuration.  LDS stage: [NT weight pieces of 1 KB][1 KB weight scale records of the
@@ -105,49 +108,59 @@ struct Cfg {
 // two lane halves of a token column; each block maximum needs one exchange across the halves), written
 // in the second GEMM's operand layout.  The last K step of the second GEMM is completed with a zero
 // block when I/32 is odd.
-MX_DEV void g1_epilogue_tile(const f32x16_t& accg, const f32x16_t& accu, const uint16_t* __restrict__ b13,
-                             uint8_t* __restrict__ actq, uint8_t* __restrict__ acts, const MoeGeom& g, int e, int64_t it,
-                             int64_t rg, int lane) {
+MX_DEV void g1_epilogue_tile(const f32x16_t& accg, const f32x16_t& accu, const GemmArgs& a, int e, int it, int rg,
+                             int lane) {
+  const uint16_t* __restrict__ b13 = a.bias;
   const int m = lane & 31, h = lane >> 5;
   float cur[16];
 #pragma unroll
-  for (int q = 0; q < 16; q++) {
-    const int n = 8 * (q >> 2) + 4 * h + (q & 3);
-    float b1 = 0.f, b3 = 0.f;
+  for (int jj = 0; jj < 4; jj++) {
+    // accumulator 4*jj + i holds row 8*jj + 4*h + i of the tile: four consecutive bias entries
+    float b1[4] = {0.f, 0.f, 0.f, 0.f}, b3[4] = {0.f, 0.f, 0.f, 0.f};
     if (b13) {
-      b1 = bf16_bits_to_f32(b13[(int64_t)e * 2 * g.I + it * 32 + n]);
-      b3 = bf16_bits_to_f32(b13[(int64_t)e * 2 * g.I + g.I + it * 32 + n]);
+      const uint16_t* bp = b13 + (int64_t)e * 2 * a.I + it * 32 + 8 * jj + 4 * h;
+      const u32x2_t v1 = *reinterpret_cast<const u32x2_t*>(bp);
+      const u32x2_t v3 = *reinterpret_cast<const u32x2_t*>(bp + a.I);
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        b1[i] = bf16_bits_to_f32((v1[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+        b3[i] = bf16_bits_to_f32((v3[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+      }
     }
-    cur[q] = silu(accg[q] + b1) * (accu[q] + b3);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const float gt = accg[4 * jj + i] + b1[i];
+      // silu(g) = g / (1 + exp(-g)) with the hardware exponential and reciprocal (exp overflow gives 0)
+      cur[4 * jj + i] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * (accu[4 * jj + i] + b3[i]);
+    }
   }
-  const int64_t kt2 = it >> 1, kb = it & 1;
-  const int64_t slot = (rg * g.nkt2 + kt2) * 64 + kb * 32 + m;
-  uint8_t* chunk = actq + slot * kSlot;
+  const int kt2 = it >> 1, kb = it & 1;
+  const int slot = (rg * a.nkt2 + kt2) * 64 + kb * 32 + m;
+  uint32_t* chunk = reinterpret_cast<uint32_t*>(a.actq + (int64_t)slot * kSlot + h * 12);
   uint32_t scales = 0;
-  // Each term quantizes the bf16 rounding of the fp32 remainder; the remainder itself stays fp32.
+  // Each term quantizes the bf16 rounding of the fp32 remainder (the remainder itself stays fp32).
+  // Rounding is monotonic, so the largest bf16 magnitude is the rounding of the largest fp32 one.
 #pragma unroll
   for (int term = 0; term < kTerms; term++) {
-    uint32_t rb[16];
-    uint32_t amax = 0;
-#pragma unroll
-    for (int q = 0; q < 16; q++) {
-      rb[q] = f32_to_bf16_bits(cur[q]);
-      amax = max(amax, rb[q] & 0x7FFFu);
-    }
-    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32));
-    const uint32_t ex = e8m0_from_amax_bits(amax << 16);
-    const float sv = e8m0_as_scale_operand(ex);
+    float amax = 0.f;
     bf16x32_t v;
 #pragma unroll
-    for (int q = 0; q < 16; q++) {
-      v[q] = __builtin_bit_cast(__bf16, (uint16_t)rb[q]);
+    for (int q = 0; q < 16; q += 2) {
+      amax = fmaxf(amax, fmaxf(fabsf(cur[q]), fabsf(cur[q + 1])));
+      const bf16x2_t two = __builtin_convertvector((f32x2_t){cur[q], cur[q + 1]}, bf16x2_t);
+      v[q] = two[0];
+      v[q + 1] = two[1];
       v[16 + q] = __builtin_bit_cast(__bf16, (uint16_t)0);
+      v[17 + q] = __builtin_bit_cast(__bf16, (uint16_t)0);
     }
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    const bf16x2_t am = __builtin_convertvector((f32x2_t){amax, 0.f}, bf16x2_t);
+    const uint32_t ex = e8m0_from_amax_bits((uint32_t)__builtin_bit_cast(uint16_t, am[0]) << 16);
+    const float sv = e8m0_as_scale_operand(ex);
     const fp6x32_t codes = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(v, sv);
-    uint32_t* tp = reinterpret_cast<uint32_t*>(chunk + term * 24 + h * 12);
-    tp[0] = codes[0];
-    tp[1] = codes[1];
-    tp[2] = codes[2];
+    chunk[term * 6] = codes[0];
+    chunk[term * 6 + 1] = codes[1];
+    chunk[term * 6 + 2] = codes[2];
     scales |= ex << (8 * term);
     if (term + 1 < kTerms) {
       const auto deq = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(codes, sv);
@@ -155,37 +168,35 @@ MX_DEV void g1_epilogue_tile(const f32x16_t& accg, const f32x16_t& accu, const u
       for (int q = 0; q < 16; q++) cur[q] = cur[q] - deq[q];
     }
   }
-  if (h == 0) reinterpret_cast<uint32_t*>(acts)[slot] = scales;
-  if ((it == g.nit - 1) && (g.nit & 1)) {
-    const int64_t zslot = (rg * g.nkt2 + kt2) * 64 + 32 + m;
-    uint32_t* zp = reinterpret_cast<uint32_t*>(actq + zslot * kSlot + h * (kSlot / 2));
+  if (h == 0) reinterpret_cast<uint32_t*>(a.acts)[slot] = scales;
+  if ((it == a.ntl - 1) && (a.ntl & 1)) {
+    const int zslot = (rg * a.nkt2 + kt2) * 64 + 32 + m;
+    uint32_t* zp = reinterpret_cast<uint32_t*>(a.actq + (int64_t)zslot * kSlot + h * (kSlot / 2));
 #pragma unroll
     for (int q = 0; q < kSlot / 8; q++) zp[q] = 0;
-    if (h == 0) reinterpret_cast<uint32_t*>(acts)[zslot] = 0;
+    if (h == 0) reinterpret_cast<uint32_t*>(a.acts)[zslot] = 0;
   }
 }
 
 // ------------------------------------------------------------------------------------------------
 // The grouped GEMM.  G1: first GEMM (A = weights, B = gathered token terms, SwiGLU epilogue);
 // otherwise the second GEMM (A = activation terms, B = weights, weighted fp32 rows to o_buf).
-template <bool G1, int WR, int WC, int RW, int CW, int D>
-__global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
+template <bool G1, int WR, int WC, int RW, int CW, int D, int OCC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void grouped_gemm_kernel(GemmArgs a) {
   using C = Cfg<WR, WC, RW, CW, D>;
   constexpr int NRG = C::NRG, NT = C::NT;
   __shared__ __attribute__((aligned(16))) uint8_t smem[D * C::kStage];
-  const MoeGeom& g = a.g;
   const int tid = threadIdx.x;
-  const int64_t nkt = G1 ? g.nkt1 : g.nkt2;
-  const int64_t ncb = G1 ? g.ncb1 : g.ncb2;
-  const int nx = (int)(ncb * kCB / NT);
-  const int64_t nblk = 2 * g.nkt1;  // token slots per row of xq (first GEMM)
+  const int nkt = a.nkt, ncb = a.ncb;
+  const int nx = ncb * kCB / NT;
+  const int nblk = a.nblk;  // token slots per row of xq (first GEMM)
 
-  const int64_t total = (int64_t)(*a.ntiles) * nx;
-  const int64_t chunk = (total + kXcds - 1) / kXcds;
-  const int64_t xcd = blockIdx.x % kXcds, per_xcd = gridDim.x / kXcds;
+  const int total = *a.ntiles * nx;
+  const int chunk = (total + kXcds - 1) / kXcds;
+  const int xcd = blockIdx.x % kXcds, per_xcd = gridDim.x / kXcds;
 
-  for (int64_t p = blockIdx.x / kXcds; p < chunk; p += per_xcd) {
-    const int64_t item = xcd * chunk + p;
+  for (int p = blockIdx.x / kXcds; p < chunk; p += per_xcd) {
+    const int item = xcd * chunk + p;
     if (item >= total) break;
     // Lane and wave indices are re-derived per item through volatile asm so that nothing computed from
     // them is hoisted out of the item loop and kept live across the K loop.
@@ -193,15 +204,16 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
     asm volatile("s_lshr_b32 %0, %1, 6" : "=s"(wave) : "s"(__builtin_amdgcn_readfirstlane(tid)));
     const int wr = wave / WC, wc = wave % WC;
-    const int tile = (int)(item / nx), x = (int)(item % nx);
+    const int tile = item / nx, x = item % nx;
     const int4 td = a.tiles[tile];
     const int e = td.x, prow0 = td.y, nrows = td.z;
-    const int64_t cb = (int64_t)x * NT / kCB;
+    const int cb = x * NT / kCB;
     const int jj0 = (x * NT) % kCB;
 
     // ---- copy sources of this item (step 0; each stage advances by a fixed stride)
-    const uint8_t* wsrc = a.wq + ((e * ncb + cb) * nkt) * (kCB * 1024) + (jj0 + wave * C::nW) * 1024 + lane * 16;
-    const uint8_t* wssrc = a.ws + ((e * ncb + cb) * nkt) * 1024 + wave * 256 + lane * 4;
+    const int64_t wstep0 = (int64_t)(e * ncb + cb) * nkt;  // first K step of this (expert, column block)
+    const uint8_t* wsrc = a.wq + wstep0 * (kCB * 1024) + (jj0 + wave * C::nW) * 1024 + lane * 16;
+    const uint8_t* wssrc = a.ws + wstep0 * 1024 + wave * 256 + lane * 4;
     const uint8_t* xsrc[C::nX];
     int xdst[C::nX];
 #pragma unroll
@@ -215,7 +227,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
         const int tok = a.prow_tok[prow0 + rg * 32 + (s & 31)];
         xsrc[q] = a.xq + ((int64_t)tok * nblk + (s >> 5)) * kSlot + part * 16;
       } else {
-        xsrc[q] = a.xq + (((int64_t)(prow0 >> 5) + rg) * nkt * 64) * kSlot + (pp * 64 + lane) * 16;
+        xsrc[q] = a.xq + (int64_t)((prow0 >> 5) + rg) * nkt * (64 * kSlot) + (pp * 64 + lane) * 16;
       }
     }
     const uint8_t* xssrc[C::nXS];
@@ -229,14 +241,14 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
         const int tok = a.prow_tok[prow0 + o * 32 + (lane & 31)];
         xssrc[q] = a.xs + ((int64_t)tok * nblk + (lane >> 5)) * 4;
       } else {
-        xssrc[q] = a.xs + ((((int64_t)(prow0 >> 5) + o) * nkt) * 64 + lane) * 4;
+        xssrc[q] = a.xs + (int64_t)((prow0 >> 5) + o) * nkt * 256 + lane * 4;
       }
     }
-    const int64_t xstep = G1 ? 2 * kSlot : 64 * kSlot;  // bytes per K step of an activation copy
-    const int64_t xsstep = G1 ? 8 : 256;
+    constexpr int xstep = G1 ? 2 * kSlot : 64 * kSlot;  // bytes per K step of an activation copy
+    constexpr int xsstep = G1 ? 8 : 256;
 
-    auto issue = [&](int64_t s, int slot) __attribute__((always_inline)) {
-      const int64_t kt = s < nkt ? s : nkt - 1;  // past the end: repeat the last stage (never read)
+    auto issue = [&](int s, int slot) __attribute__((always_inline)) {
+      const int kt = s < nkt ? s : nkt - 1;  // past the end: repeat the last stage (never read)
       uint8_t* base = smem + slot * C::kStage;
 #pragma unroll
       for (int i = 0; i < C::nW; i++) dma16(wsrc + kt * (kCB * 1024) + i * 1024, base + C::oW + (wave * C::nW + i) * 1024);
@@ -317,14 +329,14 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
     // then finished all reads of stage kt-1 (they fed the MFMAs of step kt-1), so that slot takes stage
     // kt + D - 1.  The activation fragments of step kt+1 are read into `xn` at the start, the weight
     // fragments of step kt+1 after their last use in this step.
-    auto step = [&](int64_t kt, auto pc) __attribute__((always_inline)) {
+    auto step = [&](int kt, auto pc) __attribute__((always_inline)) {
       constexpr int P = decltype(pc)::value;
       wait_vmcnt<C::kOps * (D - 3)>();
       block_sync();
-      const int64_t kn = kt + 1 < nkt ? kt + 1 : kt;
+      const int kn = kt + 1 < nkt ? kt + 1 : kt;
       const uint8_t* nb = smem + (kn % D) * C::kStage;
       load_x(nb, std::integral_constant<int, 1 - P>{});
-      issue(kt + D - 1, (int)((kt + D - 1) % D));
+      issue(kt + D - 1, (kt + D - 1) % D);
       static_for<0, CW / JG>([&](auto gc) __attribute__((always_inline)) {
         constexpr int J0 = decltype(gc)::value * JG;
         mfma_group(gc, pc);
@@ -345,7 +357,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int j4 = 0; j4 < CW / 4; j4++) load_ws(b0, j4);
     }
-    int64_t kt = 0;
+    int kt = 0;
     for (; kt + 2 <= nkt; kt += 2) {  // two steps per iteration keep both buffers in place
       step(kt, std::integral_constant<int, 0>{});
       step(kt + 1, std::integral_constant<int, 1>{});
@@ -360,42 +372,51 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
         if (rgl * 32 >= nrows) continue;
 #pragma unroll
         for (int i = 0; i < CW / 2; i++) {
-          const int64_t it = ((int64_t)x * NT + wc * CW) / 2 + i;
-          if (it < g.nit)
-            g1_epilogue_tile(acc[r][2 * i], acc[r][2 * i + 1], a.bias, a.actq, a.acts, g, e, it, (prow0 >> 5) + rgl, lane);
+          const int it = (x * NT + wc * CW) / 2 + i;
+          if (it < a.ntl) g1_epilogue_tile(acc[r][2 * i], acc[r][2 * i + 1], a, e, it, (prow0 >> 5) + rgl, lane);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
     } else {
-      const int m0 = 4 * (lane >> 5);
+      // Rows 8*jj + 4*h + i (h = lane / 32) of each row group, column lane % 32 of each tile: the lane's
+      // 16 values of one tile form one block with a power-of-two scale (largest magnitude in
+      // [2^14, 2^15) after scaling), stored as fp16 plus the exponent byte.
+      const int h = lane >> 5;
 #pragma unroll
       for (int r = 0; r < RW; r++) {
         const int rgl = wr * RW + r;
         if (rgl * 32 >= nrows) continue;
-        // rows 8*jj + m0 + i of the row group: four runs of four consecutive rows
-        int32_t pr[16];
         float wt[16];
 #pragma unroll
         for (int jj = 0; jj < 4; jj++) {
-          const int row = rgl * 32 + 8 * jj + m0;
-          const int4 p4 = *reinterpret_cast<const int4*>(a.prow_pair + prow0 + row);
-          const f32x4_t w4 = *reinterpret_cast<const f32x4_t*>(a.prow_w + prow0 + row);
-          pr[4 * jj] = row < nrows ? p4.x : -1;
-          pr[4 * jj + 1] = row + 1 < nrows ? p4.y : -1;
-          pr[4 * jj + 2] = row + 2 < nrows ? p4.z : -1;
-          pr[4 * jj + 3] = row + 3 < nrows ? p4.w : -1;
+          const f32x4_t w4 = *reinterpret_cast<const f32x4_t*>(a.prow_w + prow0 + rgl * 32 + 8 * jj + 4 * h);
 #pragma unroll
-          for (int i = 0; i < 4; i++) wt[4 * jj + i] = w4[i];
+          for (int i = 0; i < 4; i++) wt[4 * jj + i] = rgl * 32 + 8 * jj + 4 * h + i < nrows ? w4[i] : 0.f;
         }
+        uint16_t* orow = a.o16 + (int64_t)(prow0 + rgl * 32 + 4 * h) * a.H;
+        uint8_t* srow = a.osc + (int64_t)(((prow0 >> 5) + rgl) * 2 + h) * a.H;
 #pragma unroll
         for (int j = 0; j < CW; j++) {
-          const int64_t nt = (int64_t)x * NT + wc * CW + j;
-          if (nt < g.nht) {
-            const int64_t col = nt * 32 + (lane & 31);
-            const float bb = a.bias ? bf16_bits_to_f32(a.bias[(int64_t)e * g.H + col]) : 0.f;
+          const int nt = x * NT + wc * CW + j;
+          if (nt < a.ntl) {
+            const int col = nt * 32 + (lane & 31);
+            const float bb = a.bias ? bf16_bits_to_f32(a.bias[(int64_t)e * a.H + col]) : 0.f;
+            float v[16];
+            float amax = 0.f;
 #pragma unroll
-            for (int q = 0; q < 16; q++)
-              if (pr[q] >= 0) a.obuf[(int64_t)pr[q] * g.H + col] = wt[q] * (acc[r][j][q] + bb);
+            for (int q = 0; q < 16; q++) {
+              v[q] = wt[q] * (acc[r][j][q] + bb);
+              amax = fmaxf(amax, fabsf(v[q]));
+            }
+            int ex = amax > 0.f ? __builtin_amdgcn_frexp_expf(amax) - 15 : 0;
+            ex = ex < -127 ? -127 : (ex > 127 ? 127 : ex);
+#pragma unroll
+            for (int q = 0; q < 16; q++) {
+              const int row = rgl * 32 + 8 * (q >> 2) + 4 * h + (q & 3);
+              const _Float16 hv = (_Float16)__builtin_ldexpf(v[q], -ex);
+              if (row < nrows) orow[(8 * (q >> 2) + (q & 3)) * a.H + col] = __builtin_bit_cast(uint16_t, hv);
+            }
+            srow[col] = (uint8_t)(ex + 127);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -404,35 +425,44 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
   }
 }
 
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ obuf, uint16_t* __restrict__ y,
-                                                      int64_t H8, int k, int64_t n) {
+// y[t] = sum over the token's k pairs of the fp16 rows (times their block powers of two), fp32 sum in
+// slot order, bf16 output.  One thread per 8 output columns of a token.
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ o16, const uint8_t* __restrict__ osc,
+                                                      const int32_t* __restrict__ pair_prow, uint16_t* __restrict__ y,
+                                                      int64_t H, int k, int64_t n) {
+  const int64_t H8 = H / 8;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t t = i / H8, c = i - t * H8;
-    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-    const f32x4_t* src = reinterpret_cast<const f32x4_t*>(obuf) + ((t * k) * H8 + c) * 2;
+    const int64_t t = i / H8, c = (i - t * H8) * 8;
+    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < k; j++) {
-      s0 += __builtin_nontemporal_load(src + j * H8 * 2);
-      s1 += __builtin_nontemporal_load(src + j * H8 * 2 + 1);
+      const int64_t r = pair_prow[t * k + j];
+      const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(o16 + r * H + c));
+      const u32x2_t e = *reinterpret_cast<const u32x2_t*>(osc + (((r >> 5) * 2 + ((r >> 2) & 1)) * H + c));
+#pragma unroll
+      for (int q = 0; q < 8; q++) {
+        const uint16_t hb = (uint16_t)(v[q >> 1] >> (16 * (q & 1)));
+        const int ex = (int)((e[q >> 2] >> (8 * (q & 3))) & 0xFFu) - 127;
+        s[q] += __builtin_ldexpf((float)__builtin_bit_cast(_Float16, hb), ex);
+      }
     }
     u32x4_t o;
-    o[0] = f32_to_bf16_bits(s0[0]) | (f32_to_bf16_bits(s0[1]) << 16);
-    o[1] = f32_to_bf16_bits(s0[2]) | (f32_to_bf16_bits(s0[3]) << 16);
-    o[2] = f32_to_bf16_bits(s1[0]) | (f32_to_bf16_bits(s1[1]) << 16);
-    o[3] = f32_to_bf16_bits(s1[2]) | (f32_to_bf16_bits(s1[3]) << 16);
+#pragma unroll
+    for (int q = 0; q < 4; q++) o[q] = f32_to_bf16_bits(s[2 * q]) | (f32_to_bf16_bits(s[2 * q + 1]) << 16);
     reinterpret_cast<u32x4_t*>(y)[i] = o;
   }
 }
 
-template <bool G1, int WR, int WC, int RW, int CW, int D>
-int launch_cfg(const GemmArgs& a, int64_t max_tiles, int wg_per_cu, hipStream_t stream) {
+template <bool G1, int WR, int WC, int RW, int CW, int D, int OCC>
+int launch_cfg(const GemmArgs& a, int64_t max_tiles, hipStream_t stream) {
+  const int wg_per_cu = OCC;
   using C = Cfg<WR, WC, RW, CW, D>;
-  const int64_t nx = (G1 ? a.g.ncb1 : a.g.ncb2) * kCB / C::NT;
+  const int64_t nx = (int64_t)a.ncb * kCB / C::NT;
   int64_t items = max_tiles * nx;
   int64_t grid = 256 * wg_per_cu;
   if (items < grid) grid = items;
   grid = kXcds * cdiv(grid, kXcds);
   if (grid < kXcds) grid = kXcds;
-  hipLaunchKernelGGL((grouped_gemm_kernel<G1, WR, WC, RW, CW, D>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((grouped_gemm_kernel<G1, WR, WC, RW, CW, D, OCC>), dim3((unsigned)grid), dim3(256), 0, stream, a);
   return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
 }
 
@@ -444,27 +474,29 @@ int launch_cfg(const GemmArgs& a, int64_t max_tiles, int wg_per_cu, hipStream_t 
 // MFMAs.
 int launch_gemm1(int NRG, const GemmArgs& a, int64_t max_tiles, hipStream_t stream) {
   switch (NRG) {
-    case 1: return launch_cfg<true, 1, 4, 1, 4, 3>(a, max_tiles, 2, stream);
-    case 2: return launch_cfg<true, 1, 4, 2, 4, 3>(a, max_tiles, 2, stream);
-    case 4: return launch_cfg<true, 2, 2, 2, 8, 5>(a, max_tiles, 1, stream);
+    case 1: return launch_cfg<true, 1, 4, 1, 4, 3, 2>(a, max_tiles, stream);
+    case 2: return launch_cfg<true, 1, 4, 2, 4, 3, 2>(a, max_tiles, stream);
+    case 4: return launch_cfg<true, 2, 2, 2, 8, 5, 1>(a, max_tiles, stream);
     default: return MXFP4_ERR_SHAPE;
   }
 }
 
 int launch_gemm2(int NRG, const GemmArgs& a, int64_t max_tiles, hipStream_t stream) {
   switch (NRG) {
-    case 1: return launch_cfg<false, 1, 4, 1, 4, 3>(a, max_tiles, 2, stream);
-    case 2: return launch_cfg<false, 1, 4, 2, 4, 3>(a, max_tiles, 2, stream);
-    case 4: return launch_cfg<false, 2, 2, 2, 4, 3>(a, max_tiles, 2, stream);
+    case 1: return launch_cfg<false, 1, 4, 1, 4, 3, 2>(a, max_tiles, stream);
+    case 2: return launch_cfg<false, 1, 4, 2, 4, 3, 2>(a, max_tiles, stream);
+    case 4: return launch_cfg<false, 2, 2, 2, 4, 3, 2>(a, max_tiles, stream);
     default: return MXFP4_ERR_SHAPE;
   }
 }
 
-int launch_combine(const float* obuf, void* y, int64_t T, int64_t H, int k, hipStream_t stream) {
+int launch_combine(const uint16_t* o16, const uint8_t* osc, const int32_t* pair_prow, void* y, int64_t T, int64_t H, int k,
+                   hipStream_t stream) {
   const int64_t n = T * (H / 8);
   int64_t blocks = (n + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   if (n > 0)
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, obuf, (uint16_t*)y, H / 8, k, n);
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, o16, osc, pair_prow, (uint16_t*)y, H,
+                       k, n);
   return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
 }

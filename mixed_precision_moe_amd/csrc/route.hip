@@ -4,8 +4,8 @@
 // [NS: top-k routing of softmax(router logits) renormalized over the selected experts; the router
 //  sort/permute/gather step]
 //
-// Routing runs without global atomics in three launches: route_kernel (top-k per token and a
-// per-block expert histogram of kRouteTokens tokens), scan_kernel (one workgroup: prefix sums over
+// Routing runs in three launches: route_kernel (top-k per token, counted into a per-block expert
+// histogram of kRouteTokens tokens), scan_kernel (one workgroup: prefix sums over
 // blocks and experts, the expert offsets, the padded row offsets and the M-tile list), scatter_kernel
 // (each block ranks its pairs per expert in token order and writes them to their rows).  The
 // resulting order is stable: pairs of one expert appear in increasing token order.
@@ -28,9 +28,11 @@ MX_DEV uint32_t amax_bits32(const uint32_t* w) {  // 16 words = 32 bf16 -> large
 // current remainder quantized with its own E8M0 scale from the 0.75 round-up rule (block maximum /
 // scale < 7 <= 7.5, the E2M3 maximum, so no term saturates).  The remainder x - t0 is exact in bf16
 // (a bf16 value minus its own rounding to a coarser grid).  K is padded to a multiple of 64 with zero
-// blocks.
+// blocks.  Also clears `zero` (nzero ints).
 __global__ __launch_bounds__(256) void xprep_kernel(const uint16_t* __restrict__ x, int64_t ldx, int64_t H, int64_t nblk,
-                                                    uint8_t* __restrict__ xq, uint8_t* __restrict__ xs, int64_t n) {
+                                                    uint8_t* __restrict__ xq, uint8_t* __restrict__ xs,
+                                                    int32_t* __restrict__ zero, int64_t nzero, int64_t n) {
+  GRID_STRIDE(i, nzero) zero[i] = 0;  // the routing histogram, cleared for the next launch
   GRID_STRIDE(i, n) {
     const int64_t t = i / nblk, b = i % nblk;
     uint32_t w[16];
@@ -83,91 +85,93 @@ MX_DEV uint32_t logit_key(float l) {
   if (u == 0x80000000u) u = 0;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+MX_DEV float key_logit(uint32_t k) { return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k); }
 
-constexpr int kRouteWaves = 16;                                // waves per routing workgroup
-constexpr int kTokPerWave = kRouteTokens / kRouteWaves;        // tokens each wave routes
+// Wave-wide maximum of a 64-bit value, uniform result: DPP exchanges inside each row of 16 lanes (xor 1,
+// xor 2, rotate 4, rotate 8), then the four row maxima through scalar lane reads.
+MX_DEV uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+#define DPP_U64(v, ctrl)                                                                                  \
+  (((uint64_t)(uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)((v) >> 32), ctrl, 0xF, 0xF, false) << 32) | \
+   (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v), ctrl, 0xF, 0xF, false))
+MX_DEV uint64_t wave_max_u64(uint64_t v) {
+  v = max_u64(v, DPP_U64(v, 0xB1));   // quad_perm [1,0,3,2]
+  v = max_u64(v, DPP_U64(v, 0x4E));   // quad_perm [2,3,0,1]
+  v = max_u64(v, DPP_U64(v, 0x124));  // row_ror:4
+  v = max_u64(v, DPP_U64(v, 0x128));  // row_ror:8
+  uint64_t r = 0;
+#pragma unroll
+  for (int row = 0; row < 4; row++) {
+    const uint64_t x = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 16 * row) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 16 * row);
+    r = max_u64(r, x);
+  }
+  return r;
+}
+MX_DEV float wave_sum_f32(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+  float r = 0.f;
+#pragma unroll
+  for (int row = 0; row < 4; row++) r += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16 * row));
+  return r;
+}
 
-// Workgroup b routes tokens [b*kRouteTokens, (b+1)*kRouteTokens): each wave takes kTokPerWave tokens
-// (their logits are loaded together), and for each runs k rounds of a wave-wide arg-max over 64-bit
-// keys (logit key, inverted expert index), so equal logits go to the lower expert index; softmax
-// weights of the selected experts (renormalized over them, or over all experts).  The block's pair
-// count per expert goes to blkcnt[b][e].  NPL logits per lane (E <= 64 * NPL).
+// One wave per token: k rounds of a wave-wide arg-max over 64-bit keys (logit key, inverted expert
+// index), so equal logits go to the lower expert index; the winner's logit is read back from its key.
+// Softmax weights of the selected experts (renormalized over them, or over all experts).  Each pair
+// also counts into blkcnt[token / kRouteTokens][expert] (zeroed beforehand), the per-block histogram of
+// the counting sort.  NPL logits per lane (E <= 64 * NPL).
 template <int NPL>
-__global__ __launch_bounds__(1024) void route_kernel(const float* __restrict__ logits, int64_t T, int E, int k,
-                                                     int renormalize, int32_t* __restrict__ ids, float* __restrict__ wts,
-                                                     int32_t* __restrict__ blkcnt) {
-  __shared__ int hist[64 * NPL];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int i = threadIdx.x; i < E; i += blockDim.x) hist[i] = 0;
-  __syncthreads();
-  float val[kTokPerWave][NPL];
+__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int64_t T, int E, int k,
+                                                    int renormalize, int32_t* __restrict__ ids, float* __restrict__ wts,
+                                                    int32_t* __restrict__ blkcnt) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;  // uniform per wave
+  float val[NPL];
+  uint64_t key[NPL];
 #pragma unroll
-  for (int q = 0; q < kTokPerWave; q++) {
-    const int64_t t = (int64_t)blockIdx.x * kRouteTokens + wave * kTokPerWave + q;
+  for (int j = 0; j < NPL; j++) {
+    const int idx = lane + 64 * j;
+    val[j] = idx < E ? logits[t * E + idx] : 0.f;
+    key[j] = idx < E ? ((uint64_t)logit_key(val[j]) << 32) | (uint32_t)(~idx) : 0;
+  }
+  int my_id = 0;
+  float my_l = 0.f, lmax = 0.f;
+  for (int r = 0; r < k; r++) {
+    uint64_t best = 0;
 #pragma unroll
-    for (int j = 0; j < NPL; j++) {
-      const int idx = lane + 64 * j;
-      val[q][j] = (t < T && idx < E) ? logits[t * E + idx] : 0.f;
+    for (int j = 0; j < NPL; j++) best = max_u64(best, key[j]);
+    best = wave_max_u64(best);
+    const int id = (int)(~(uint32_t)best);
+    const float wl = key_logit((uint32_t)(best >> 32));
+#pragma unroll
+    for (int j = 0; j < NPL; j++)
+      if (lane + 64 * j == id) key[j] = 0;
+    if (r == 0) lmax = wl;
+    if (lane == r) {
+      my_id = id;
+      my_l = wl;
     }
   }
+  const float ex = lane < k ? __expf(my_l - lmax) : 0.f;
+  float den;
+  if (renormalize) {
+    den = wave_sum_f32(ex);
+  } else {
+    float part = 0.f;
 #pragma unroll
-  for (int q = 0; q < kTokPerWave; q++) {
-    const int64_t t = (int64_t)blockIdx.x * kRouteTokens + wave * kTokPerWave + q;
-    if (t >= T) break;  // uniform per wave
-    uint64_t key[NPL];
-#pragma unroll
-    for (int j = 0; j < NPL; j++) {
-      const int idx = lane + 64 * j;
-      key[j] = idx < E ? ((uint64_t)logit_key(val[q][j]) << 32) | (uint32_t)(~idx) : 0;
-    }
-    int my_id = 0;
-    float my_l = 0.f, lmax = 0.f;
-    for (int r = 0; r < k; r++) {
-      uint64_t best = 0;
-#pragma unroll
-      for (int j = 0; j < NPL; j++) best = key[j] > best ? key[j] : best;
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)best, off);
-        const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(best >> 32), off);
-        const uint64_t o = ((uint64_t)hi << 32) | lo;
-        best = o > best ? o : best;
-      }
-      const int id = (int)(~(uint32_t)best);
-      float wl = 0.f;  // the owner lane clears the winner and broadcasts its logit
-#pragma unroll
-      for (int j = 0; j < NPL; j++) {
-        if (lane + 64 * j == id) {
-          wl = val[q][j];
-          key[j] = 0;
-        }
-      }
-      wl = __shfl(wl, id & 63);
-      if (r == 0) lmax = wl;
-      if (lane == r) {
-        my_id = id;
-        my_l = wl;
-      }
-    }
-    const float ex = lane < k ? __expf(my_l - lmax) : 0.f;
-    float den = 0.f;
-    if (renormalize) {
-      den = ex;
-    } else {
-#pragma unroll
-      for (int j = 0; j < NPL; j++)
-        if (lane + 64 * j < E) den += __expf(val[q][j] - lmax);
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
-    if (lane < k) {
-      ids[t * k + lane] = my_id;
-      wts[t * k + lane] = ex / den;
-      atomicAdd(&hist[my_id], 1);
-    }
+    for (int j = 0; j < NPL; j++)
+      if (lane + 64 * j < E) part += __expf(val[j] - lmax);
+    den = wave_sum_f32(part);
   }
-  __syncthreads();
-  for (int i = threadIdx.x; i < E; i += blockDim.x) blkcnt[(int64_t)blockIdx.x * E + i] = hist[i];
+  if (lane < k) {
+    ids[t * k + lane] = my_id;
+    wts[t * k + lane] = ex / den;
+    atomicAdd(&blkcnt[(t / kRouteTokens) * E + my_id], 1);
+  }
 }
 
 // One workgroup of 1024 threads.  (1) Per expert, the total pair count and the exclusive prefix of
@@ -190,9 +194,17 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ blkcnt
   const int e = tid % es, grp = tid / es;
   const int per = (nb + G - 1) / G;
   const int b0 = min(nb, grp * per), b1 = min(nb, b0 + per);
+  // block counts of this thread, 16 independent loads at a time
+  constexpr int kBatch = 16;
   int s = 0;
   if (e < E)
-    for (int b = b0; b < b1; b++) s += blkcnt[(int64_t)b * E + e];
+    for (int b = b0; b < b1; b += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; i++) v[i] = b + i < b1 ? blkcnt[(int64_t)(b + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kBatch; i++) s += v[i];
+    }
   part[tid] = s;
   __syncthreads();
   int base = 0, total = 0;
@@ -202,10 +214,15 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ blkcnt
     total += v;
   }
   if (e < E)
-    for (int b = b0; b < b1; b++) {
-      const int v = blkcnt[(int64_t)b * E + e];
-      blkcnt[(int64_t)b * E + e] = base;
-      base += v;
+    for (int b = b0; b < b1; b += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; i++) v[i] = b + i < b1 ? blkcnt[(int64_t)(b + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kBatch; i++) {
+        if (b + i < b1) blkcnt[(int64_t)(b + i) * E + e] = base;
+        base += v[i];
+      }
     }
   // scans over experts: thread e of group 0 (tid == e) holds expert e, every other thread zeros
   int v0 = 0, v1 = 0, v2 = 0;
@@ -256,13 +273,15 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ blkcnt
 // One wave per block of kRouteTokens tokens (lane = token): rank of each pair among the pairs of its
 // expert in token order = (pairs of that expert in earlier blocks) + (earlier lanes of this block with
 // that expert), from a 64-bit lane mask per expert.  Writes the compact order (sorted_pairs, may be
-// NULL) and the padded rows (pair, token, routing weight).
+// NULL), the padded rows (pair, token, routing weight) and each pair's padded row (pair_prow, may be
+// NULL).
 __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__ ids, const float* __restrict__ wts,
                                                      const int32_t* __restrict__ blkcnt, int64_t T, int k, int E,
                                                      const int32_t* __restrict__ offsets,
                                                      const int32_t* __restrict__ poffsets,
                                                      int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ prow_pair,
-                                                     int32_t* __restrict__ prow_tok, float* __restrict__ prow_w) {
+                                                     int32_t* __restrict__ prow_tok, float* __restrict__ prow_w,
+                                                     int32_t* __restrict__ pair_prow) {
   __shared__ uint32_t mlo[1024], mhi[1024];
   const int lane = threadIdx.x;
   const int64_t b = blockIdx.x;
@@ -289,6 +308,7 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__
       prow_pair[r] = pair;
       prow_tok[r] = (int32_t)t;
       prow_w[r] = wts[pair];
+      if (pair_prow) pair_prow[pair] = r;
     }
   }
 }
@@ -302,41 +322,49 @@ inline unsigned grid_for(int64_t n, int threads = 256) {
 
 }  // namespace
 
-int launch_xprep(const void* x, int64_t T, int64_t ldx, const MoeGeom& g, void* xq, void* xs, hipStream_t stream) {
+int launch_xprep(const void* x, int64_t T, int64_t ldx, const MoeGeom& g, void* xq, void* xs, int32_t* zero,
+                 int64_t nzero, hipStream_t stream) {
   const int64_t nblk = 2 * g.nkt1;
   const int64_t n = T * nblk;
-  if (n > 0)
-    hipLaunchKernelGGL(xprep_kernel, dim3(grid_for(n)), dim3(256), 0, stream, (const uint16_t*)x, ldx, g.H, nblk,
-                       (uint8_t*)xq, (uint8_t*)xs, n);
+  if (n > 0 || nzero > 0)
+    hipLaunchKernelGGL(xprep_kernel, dim3(grid_for(n > nzero ? n : nzero)), dim3(256), 0, stream, (const uint16_t*)x,
+                       ldx, g.H, nblk, (uint8_t*)xq, (uint8_t*)xs, zero, nzero, n);
+  return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
+}
+
+__global__ void zero_i32_kernel(int32_t* p, int64_t n) { GRID_STRIDE(i, n) p[i] = 0; }
+
+int launch_zero_i32(int32_t* p, int64_t n, hipStream_t stream) {
+  if (n > 0) hipLaunchKernelGGL(zero_i32_kernel, dim3(grid_for(n)), dim3(256), 0, stream, p, n);
   return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
 }
 
 int launch_route(const float* logits, int64_t T, int E, int k, int renormalize, int32_t* ids, float* w,
                  int32_t* blkcnt, hipStream_t stream) {
-  const unsigned nb = (unsigned)cdiv(T, kRouteTokens);
+  const dim3 grid((unsigned)cdiv(T, 4)), block(256);
   if (T > 0) {
     if (E <= 64)
-      hipLaunchKernelGGL(route_kernel<1>, dim3(nb), dim3(1024), 0, stream, logits, T, E, k, renormalize, ids, w, blkcnt);
+      hipLaunchKernelGGL(route_kernel<1>, grid, block, 0, stream, logits, T, E, k, renormalize, ids, w, blkcnt);
     else if (E <= 128)
-      hipLaunchKernelGGL(route_kernel<2>, dim3(nb), dim3(1024), 0, stream, logits, T, E, k, renormalize, ids, w, blkcnt);
+      hipLaunchKernelGGL(route_kernel<2>, grid, block, 0, stream, logits, T, E, k, renormalize, ids, w, blkcnt);
     else if (E <= 256)
-      hipLaunchKernelGGL(route_kernel<4>, dim3(nb), dim3(1024), 0, stream, logits, T, E, k, renormalize, ids, w, blkcnt);
+      hipLaunchKernelGGL(route_kernel<4>, grid, block, 0, stream, logits, T, E, k, renormalize, ids, w, blkcnt);
     else if (E <= 512)
-      hipLaunchKernelGGL(route_kernel<8>, dim3(nb), dim3(1024), 0, stream, logits, T, E, k, renormalize, ids, w, blkcnt);
+      hipLaunchKernelGGL(route_kernel<8>, grid, block, 0, stream, logits, T, E, k, renormalize, ids, w, blkcnt);
     else
-      hipLaunchKernelGGL(route_kernel<16>, dim3(nb), dim3(1024), 0, stream, logits, T, E, k, renormalize, ids, w, blkcnt);
+      hipLaunchKernelGGL(route_kernel<16>, grid, block, 0, stream, logits, T, E, k, renormalize, ids, w, blkcnt);
   }
   return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
 }
 
 int launch_place(const int32_t* ids, const float* w, int32_t* blkcnt, int64_t T, int k, int E, int BM, int32_t* offsets,
                  int32_t* poffsets, int32_t* sorted_pairs, int32_t* prow_pair, int32_t* prow_tok, float* prow_w,
-                 void* tiles, int32_t* ntiles, hipStream_t stream) {
+                 int32_t* pair_prow, void* tiles, int32_t* ntiles, hipStream_t stream) {
   const int nb = (int)cdiv(T, kRouteTokens);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream, blkcnt, nb, E, BM, offsets, poffsets, (int4*)tiles,
                      ntiles, prow_pair, prow_tok, prow_w);
   if (nb > 0)
     hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)nb), dim3(64), 0, stream, ids, w, blkcnt, T, k, E, offsets,
-                       poffsets, sorted_pairs, prow_pair, prow_tok, prow_w);
+                       poffsets, sorted_pairs, prow_pair, prow_tok, prow_w, pair_prow);
   return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
 }
