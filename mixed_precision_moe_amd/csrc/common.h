@@ -142,8 +142,7 @@ constexpr int kSlot = 48;
 //   pair_prow: [T*k] padded row of each (token, slot) pair
 //   o16 : fp16 [padded rows][H], row r = w * (expert output + b2) of the pair at row r, divided by the
 //         power of two 2^(osc - 127) of its block
-//   osc : [padded rows / 32][2][H] bytes, the block exponents: one per (32-row group, row parity
-//         (r / 4) % 2, column), i.e. per 16 rows of one column as one lane of the second GEMM holds them
+//   osc : [padded rows][H / 16] bytes, the block exponents: one per 16 consecutive columns of a row
 constexpr int kRouteTokens = 64;
 
 struct FwdWs {
@@ -176,7 +175,7 @@ static inline FwdWs fwd_ws(const MoeGeom& g, int64_t T, int64_t k) {
   w.actq = take((uint64_t)(w.nrows_alloc / 32) * g.nkt2 * 64 * kSlot);
   w.acts = take((uint64_t)(w.nrows_alloc / 32) * g.nkt2 * 64 * 4);
   w.o16 = take((uint64_t)w.nrows_alloc * g.H * 2);
-  w.osc = take((uint64_t)(w.nrows_alloc / 32) * 2 * g.H);
+  w.osc = take((uint64_t)w.nrows_alloc * (g.H / 16));
   w.total = p;
   return w;
 }

@@ -13,16 +13,16 @@
 // are block-scaled fp16 that the combine sums in fp32, so the only bf16 rounding after the input is the
 // output's.
 //
-// First GEMM, transposed: D[n][m] = sum_k W13[n][k] x[m][k], weights as the A operand (rows n = 32
-// gate or up rows of one tile), tokens as the B operand (columns m = 32 tokens gathered through the
-// padded row order).  Lane l of the 32x32 result holds token l%32 and rows 8*jj + 4*(l/32) + i, so
-// gate and up of one column sit in the same lane (SwiGLU in registers) and a 32-element block of the
-// activation is split over the two lane halves (one exchange for the block maximum).
-//
-// Second GEMM, not transposed: D[m][n] = sum_k act[m][k] W2[n][k]; lane l holds output column l%32 and
-// rows 8*jj + 4*(l/32) + i.  Its rows go to o16 (fp16 with a power-of-two exponent per 16 rows of a
-// column, which keeps about eleven significant bits of every value that matters for the sum) in the
-// padded row order; the combine gathers each token's k rows.
+// Both GEMMs are computed transposed, D[n][m] = sum_k W[n][k] act[m][k]: the weights are the A operand
+// (rows n = 32 output columns of one tile), the tokens the B operand (columns m = 32 rows of the padded
+// row order).  Lane l of a 32x32 result holds token l%32 and tile rows 8*jj + 4*(l/32) + i.
+//  - First GEMM: gate and up of a token sit in the same lane (SwiGLU in registers); the 32-element
+//    blocks of two adjacent activation tiles are spread over both lane halves, and one exchange of
+//    halves leaves each lane one whole block, which it splits into the second GEMM's two E2M3 terms.
+//  - Second GEMM: one exchange of halves leaves each lane 16 consecutive output columns of its token,
+//    stored as fp16 with one power-of-two exponent per 16 columns (about eleven significant bits of
+//    every value that matters for the sum) in the padded row order; the combine gathers each token's
+//    k rows.
 //
 // Both GEMMs run one kernel template.  A workgroup of four waves (WR x WC) computes an M tile of
 // NRG = WR*RW row groups of 32 rows against NT = WC*CW weight tiles of 32 columns; wave (wr, wc) holds
@@ -83,6 +83,15 @@ MX_DEV void block_sync() {
 }
 
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// Reads an accumulator element where the epilogue needs it: the operand stays in its AGPR until this
+// point, so the accumulator tiles are not all copied to VGPRs when the K loop ends.
+MX_DEV float acc_read(float v) {
+  float r;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(v));
+  return r;
+}
 
 // ------------------------------------------------------------------------------------------------
 // Kernel configuration.  LDS stage: [NT weight pieces of 1 KB][1 KB weight scale records of the
@@ -103,40 +112,72 @@ struct Cfg {
 };
 
 
-// First GEMM epilogue for one (32-column activation tile `it`, row group `rg`) result held by one
-// wave: bias, SwiGLU in fp32, then the two-term E2M3 split of each 32-element block (one block = the
-// two lane halves of a token column; each block maximum needs one exchange across the halves), written
-// in the second GEMM's operand layout.  The last K step of the second GEMM is completed with a zero
-// block when I/32 is odd.
-MX_DEV void g1_epilogue_tile(const f32x16_t& accg, const f32x16_t& accu, const GemmArgs& a, int e, int it, int rg,
-                             int lane) {
-  const uint16_t* __restrict__ b13 = a.bias;
-  const int m = lane & 31, h = lane >> 5;
-  float cur[16];
+typedef const __attribute__((address_space(3))) uint16_t lds_u16;
+typedef const __attribute__((address_space(3))) uint8_t* lds_u8;
+typedef const __attribute__((address_space(3))) int32_t lds_i32;
+typedef const __attribute__((address_space(3))) float lds_f32;
+
+// Exchanges lane halves: returns {lanes 0-31 of x, then lanes 0-31 of y} and {lanes 32-63 of x, then
+// lanes 32-63 of y} (one v_permlane32_swap).
+MX_DEV void swap_halves(float& x, float& y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, y), false,
+                                                  false);
+  x = __builtin_bit_cast(float, (unsigned)r[0]);
+  y = __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+// Four consecutive bf16 entries of an LDS bias table (8-byte aligned) as fp32.
+MX_DEV void bias4(lds_u16* p, float* out) {
+  const u32x2_t v = *reinterpret_cast<const __attribute__((address_space(3))) u32x2_t*>(p);
+  out[0] = __uint_as_float(v[0] << 16);
+  out[1] = __uint_as_float(v[0] & 0xFFFF0000u);
+  out[2] = __uint_as_float(v[1] << 16);
+  out[3] = __uint_as_float(v[1] & 0xFFFF0000u);
+}
+
+// First GEMM epilogue for the activation tiles `it` (even) and it + 1 of one row group, which together
+// are one K step (kt2 = it / 2) of the second GEMM: bias, SwiGLU in fp32, then one exchange of lane
+// halves after which lane l holds the whole 32-element block of token l % 32 in tile it + l / 32, split
+// into two E2M3 terms and written as one 48-byte operand slot of the second GEMM (lane l of the step) and
+// its scale dword.  When tile it + 1 is past I / 32 its half is a zero block.
+// g0/u0, g1/u1: gate and up accumulators of the two tiles; bg/bu: the 64 gate / up biases of the pair
+// (bf16, LDS), read when BIAS.
+template <bool BIAS>
+MX_DEV void g1_epilogue_pair(const f32x16_t& g0, const f32x16_t& u0, const f32x16_t& g1, const f32x16_t& u1,
+                             const GemmArgs& a, lds_u16* bg, lds_u16* bu, bool second, int kt2, int rg, int lane) {
+  const int h = lane >> 5;
+  // lo[q], hi[q]: block positions q and 16 + q after the exchange (position p of a block holds the
+  // tile's row 8 * ((p & 15) >> 2) + 4 * (p >> 4) + (p & 3), the order the second GEMM's weights use)
+  float lo[16], hi[16];
 #pragma unroll
   for (int jj = 0; jj < 4; jj++) {
-    // accumulator 4*jj + i holds row 8*jj + 4*h + i of the tile: four consecutive bias entries
-    float b1[4] = {0.f, 0.f, 0.f, 0.f}, b3[4] = {0.f, 0.f, 0.f, 0.f};
-    if (b13) {
-      const uint16_t* bp = b13 + (int64_t)e * 2 * a.I + it * 32 + 8 * jj + 4 * h;
-      const u32x2_t v1 = *reinterpret_cast<const u32x2_t*>(bp);
-      const u32x2_t v3 = *reinterpret_cast<const u32x2_t*>(bp + a.I);
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        b1[i] = bf16_bits_to_f32((v1[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
-        b3[i] = bf16_bits_to_f32((v3[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
-      }
+    // accumulator 4*jj + i holds row 8*jj + 4*h + i of its tile: four consecutive bias entries
+    float b1a[4] = {0.f, 0.f, 0.f, 0.f}, b3a[4] = {0.f, 0.f, 0.f, 0.f};
+    float b1b[4] = {0.f, 0.f, 0.f, 0.f}, b3b[4] = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (BIAS) {
+      const int o = 8 * jj + 4 * h;
+      bias4(bg + o, b1a);
+      bias4(bu + o, b3a);
+      bias4(bg + 32 + o, b1b);
+      bias4(bu + 32 + o, b3b);
     }
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      const float gt = accg[4 * jj + i] + b1[i];
+      const int q = 4 * jj + i;
       // silu(g) = g / (1 + exp(-g)) with the hardware exponential and reciprocal (exp overflow gives 0)
-      cur[4 * jj + i] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * (accu[4 * jj + i] + b3[i]);
+      const float ga = acc_read(g0[q]) + b1a[i];
+      float va = ga * __builtin_amdgcn_rcpf(1.0f + __expf(-ga)) * (acc_read(u0[q]) + b3a[i]);
+      const float gb = acc_read(g1[q]) + b1b[i];
+      float vb = gb * __builtin_amdgcn_rcpf(1.0f + __expf(-gb)) * (acc_read(u1[q]) + b3b[i]);
+      vb = second ? vb : 0.f;
+      swap_halves(va, vb);
+      lo[q] = va;
+      hi[q] = vb;
     }
   }
-  const int kt2 = it >> 1, kb = it & 1;
-  const int slot = (rg * a.nkt2 + kt2) * 64 + kb * 32 + m;
-  uint32_t* chunk = reinterpret_cast<uint32_t*>(a.actq + (int64_t)slot * kSlot + h * 12);
+  const int slot = (rg * a.nkt2 + kt2) * 64 + lane;
+  u32x4_t* dst = reinterpret_cast<u32x4_t*>(a.actq + (int64_t)slot * kSlot);
+  uint32_t out[12];
   uint32_t scales = 0;
   // Each term quantizes the bf16 rounding of the fp32 remainder (the remainder itself stays fp32).
   // Rounding is monotonic, so the largest bf16 magnitude is the rounding of the largest fp32 one.
@@ -146,46 +187,65 @@ MX_DEV void g1_epilogue_tile(const f32x16_t& accg, const f32x16_t& accu, const G
     bf16x32_t v;
 #pragma unroll
     for (int q = 0; q < 16; q += 2) {
-      amax = fmaxf(amax, fmaxf(fabsf(cur[q]), fabsf(cur[q + 1])));
-      const bf16x2_t two = __builtin_convertvector((f32x2_t){cur[q], cur[q + 1]}, bf16x2_t);
-      v[q] = two[0];
-      v[q + 1] = two[1];
-      v[16 + q] = __builtin_bit_cast(__bf16, (uint16_t)0);
-      v[17 + q] = __builtin_bit_cast(__bf16, (uint16_t)0);
+      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(lo[q]), fabsf(lo[q + 1])), fmaxf(fabsf(hi[q]), fabsf(hi[q + 1]))));
+      const bf16x2_t l2 = __builtin_convertvector((f32x2_t){lo[q], lo[q + 1]}, bf16x2_t);
+      const bf16x2_t h2 = __builtin_convertvector((f32x2_t){hi[q], hi[q + 1]}, bf16x2_t);
+      v[q] = l2[0];
+      v[q + 1] = l2[1];
+      v[16 + q] = h2[0];
+      v[17 + q] = h2[1];
     }
-    amax = fmaxf(amax, __shfl_xor(amax, 32));
     const bf16x2_t am = __builtin_convertvector((f32x2_t){amax, 0.f}, bf16x2_t);
     const uint32_t ex = e8m0_from_amax_bits((uint32_t)__builtin_bit_cast(uint16_t, am[0]) << 16);
     const float sv = e8m0_as_scale_operand(ex);
     const fp6x32_t codes = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(v, sv);
-    chunk[term * 6] = codes[0];
-    chunk[term * 6 + 1] = codes[1];
-    chunk[term * 6 + 2] = codes[2];
+#pragma unroll
+    for (int d = 0; d < 6; d++) out[term * 6 + d] = codes[d];
     scales |= ex << (8 * term);
     if (term + 1 < kTerms) {
       const auto deq = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(codes, sv);
 #pragma unroll
-      for (int q = 0; q < 16; q++) cur[q] = cur[q] - deq[q];
+      for (int q = 0; q < 16; q++) {
+        lo[q] = lo[q] - deq[q];
+        hi[q] = hi[q] - deq[16 + q];
+      }
     }
   }
-  if (h == 0) reinterpret_cast<uint32_t*>(a.acts)[slot] = scales;
-  if ((it == a.ntl - 1) && (a.ntl & 1)) {
-    const int zslot = (rg * a.nkt2 + kt2) * 64 + 32 + m;
-    uint32_t* zp = reinterpret_cast<uint32_t*>(a.actq + (int64_t)zslot * kSlot + h * (kSlot / 2));
-#pragma unroll
-    for (int q = 0; q < kSlot / 8; q++) zp[q] = 0;
-    if (h == 0) reinterpret_cast<uint32_t*>(a.acts)[zslot] = 0;
-  }
+  dst[0] = u32x4_t{out[0], out[1], out[2], out[3]};
+  dst[1] = u32x4_t{out[4], out[5], out[6], out[7]};
+  dst[2] = u32x4_t{out[8], out[9], out[10], out[11]};
+  reinterpret_cast<uint32_t*>(a.acts)[slot] = scales;
 }
 
 // ------------------------------------------------------------------------------------------------
 // The grouped GEMM.  G1: first GEMM (A = weights, B = gathered token terms, SwiGLU epilogue);
-// otherwise the second GEMM (A = activation terms, B = weights, weighted fp32 rows to o_buf).
-template <bool G1, int WR, int WC, int RW, int CW, int D, int OCC>
+// otherwise the second GEMM (A = activation terms, B = weights, weighted fp16 rows to o16).
+//
+// A workgroup processes the items (M tile, column position) dealt to it in turn; the first D - 1
+// stages of the next item are copied before the current item's epilogue runs, so the ring refills
+// while the epilogue computes and stores.  The first GEMM gathers the next item's token rows through a
+// table of its token indices, which one copy per wave brings into LDS at the start of the current item.
+template <int NX, int NXS>
+struct ItemSrc {
+  int64_t wb;       // byte offset of this wave's first weight piece of step 0 (uniform)
+  int64_t wsb;      // byte offset of this wave's quarter of the step-0 scale records (uniform)
+  uint32_t x[NX];   // byte offsets of this lane's activation copies of step 0
+  uint32_t xs[NXS]; // byte offsets of this lane's activation scale copies of step 0
+};
+
+template <bool G1, bool BIAS, int WR, int WC, int RW, int CW, int D, int OCC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void grouped_gemm_kernel(GemmArgs a) {
   using C = Cfg<WR, WC, RW, CW, D>;
   constexpr int NRG = C::NRG, NT = C::NT;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[D * C::kStage];
+  constexpr int kTab = NRG * 32 > 64 ? NRG * 32 : 64;  // row table entries (one dword copy covers 64)
+  constexpr int kBias = G1 ? NT / 2 * 32 : NT * 32;   // bias entries of one half (first GEMM) or of the tile
+  // The ring, then the per-item tables (double-buffered by item parity, copied with LDS DMA one item
+  // ahead): the first GEMM's row tokens and gate / up biases, the second GEMM's row weights and biases.
+  // One LDS object holds both, so the compiler's tracking of LDS DMA writes sees a single buffer.
+  constexpr int kTabRow = 2 * kTab * 4, kTabB = 2 * (G1 ? 2 : 1) * kBias * 2;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[D * C::kStage + kTabRow + kTabB];
+  int32_t(*t_row)[kTab] = reinterpret_cast<int32_t(*)[kTab]>(smem + D * C::kStage);
+  uint16_t(*t_b)[G1 ? 2 : 1][kBias] = reinterpret_cast<uint16_t(*)[G1 ? 2 : 1][kBias]>(smem + D * C::kStage + kTabRow);
   const int tid = threadIdx.x;
   const int nkt = a.nkt, ncb = a.ncb;
   const int nx = ncb * kCB / NT;
@@ -194,161 +254,214 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
   const int total = *a.ntiles * nx;
   const int chunk = (total + kXcds - 1) / kXcds;
   const int xcd = blockIdx.x % kXcds, per_xcd = gridDim.x / kXcds;
+  const int p0 = blockIdx.x / kXcds;
+  // items of this workgroup: q = 0 .. nq - 1 -> item xcd * chunk + p0 + q * per_xcd
+  int nq = 0;
+  if (p0 < chunk) {
+    const int last = min(chunk, total - xcd * chunk);  // local positions of this XCD's items
+    if (last > p0) nq = (last - p0 + per_xcd - 1) / per_xcd;
+  }
+  if (nq == 0) return;
 
-  for (int p = blockIdx.x / kXcds; p < chunk; p += per_xcd) {
-    const int item = xcd * chunk + p;
-    if (item >= total) break;
-    // Lane and wave indices are re-derived per item through volatile asm so that nothing computed from
-    // them is hoisted out of the item loop and kept live across the K loop.
-    int lane, wave;
-    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
-    asm volatile("s_lshr_b32 %0, %1, 6" : "=s"(wave) : "s"(__builtin_amdgcn_readfirstlane(tid)));
-    const int wr = wave / WC, wc = wave % WC;
+  int lane, wave;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+  asm volatile("s_lshr_b32 %0, %1, 6" : "=s"(wave) : "s"(__builtin_amdgcn_readfirstlane(tid)));
+  const int wr = wave / WC, wc = wave % WC;
+
+  auto item_of = [&](int q) __attribute__((always_inline)) { return xcd * chunk + p0 + q * per_xcd; };
+
+  // Copy sources of an item.  G1 takes the tokens of the item's rows from `tab` (LDS) when given, else
+  // from global memory.
+  using Src = ItemSrc<C::nX, C::nXS>;
+  auto make_src = [&](int item, int tb, Src& sr) __attribute__((always_inline)) {
     const int tile = item / nx, x = item % nx;
     const int4 td = a.tiles[tile];
-    const int e = td.x, prow0 = td.y, nrows = td.z;
-    const int cb = x * NT / kCB;
-    const int jj0 = (x * NT) % kCB;
-
-    // ---- copy sources of this item (step 0; each stage advances by a fixed stride)
-    const int64_t wstep0 = (int64_t)(e * ncb + cb) * nkt;  // first K step of this (expert, column block)
-    const uint8_t* wsrc = a.wq + wstep0 * (kCB * 1024) + (jj0 + wave * C::nW) * 1024 + lane * 16;
-    const uint8_t* wssrc = a.ws + wstep0 * 1024 + wave * 256 + lane * 4;
-    const uint8_t* xsrc[C::nX];
-    int xdst[C::nX];
+    const int e = td.x, prow0 = td.y;
+    const int cb = x * NT / kCB, jj0 = (x * NT) % kCB;
+    const int64_t wstep0 = (int64_t)(e * ncb + cb) * nkt;
+    sr.wb = wstep0 * (kCB * 1024) + (jj0 + wave * C::nW) * 1024;
+    sr.wsb = wstep0 * 1024 + wave * 256;
 #pragma unroll
     for (int q = 0; q < C::nX; q++) {
       int o = wave + 4 * q;
       o = o < 3 * NRG ? o : 3 * NRG - 1;
       const int rg = o / 3, pp = o % 3;
-      xdst[q] = C::oX + o * 1024;
       if (G1) {
         const int c = pp * 64 + lane, s = c / 3, part = c % 3;
-        const int tok = a.prow_tok[prow0 + rg * 32 + (s & 31)];
-        xsrc[q] = a.xq + ((int64_t)tok * nblk + (s >> 5)) * kSlot + part * 16;
+        const int row = rg * 32 + (s & 31);
+        const int tok = tb >= 0 ? t_row[tb][row] : a.prow_tok[prow0 + row];
+        sr.x[q] = (uint32_t)((tok * nblk + (s >> 5)) * kSlot + part * 16);
       } else {
-        xsrc[q] = a.xq + (int64_t)((prow0 >> 5) + rg) * nkt * (64 * kSlot) + (pp * 64 + lane) * 16;
+        sr.x[q] = (uint32_t)(((prow0 >> 5) + rg) * nkt * (64 * kSlot) + (pp * 64 + lane) * 16);
       }
     }
-    const uint8_t* xssrc[C::nXS];
-    int xsdst[C::nXS];
 #pragma unroll
     for (int q = 0; q < C::nXS; q++) {
       int o = wave + 4 * q;
       o = o < NRG ? o : NRG - 1;
-      xsdst[q] = C::oXS + o * 256;
       if (G1) {
-        const int tok = a.prow_tok[prow0 + o * 32 + (lane & 31)];
-        xssrc[q] = a.xs + ((int64_t)tok * nblk + (lane >> 5)) * 4;
+        const int row = o * 32 + (lane & 31);
+        const int tok = tb >= 0 ? t_row[tb][row] : a.prow_tok[prow0 + row];
+        sr.xs[q] = (uint32_t)((tok * nblk + (lane >> 5)) * 4);
       } else {
-        xssrc[q] = a.xs + (int64_t)((prow0 >> 5) + o) * nkt * 256 + lane * 4;
+        sr.xs[q] = (uint32_t)(((prow0 >> 5) + o) * nkt * 256 + lane * 4);
       }
     }
-    constexpr int xstep = G1 ? 2 * kSlot : 64 * kSlot;  // bytes per K step of an activation copy
-    constexpr int xsstep = G1 ? 8 : 256;
+  };
+  constexpr int xstep = G1 ? 2 * kSlot : 64 * kSlot;  // bytes per K step of an activation copy
+  constexpr int xsstep = G1 ? 8 : 256;
+  // Stage `kt` of the item with sources `sr` into ring slot `slot`: kOps copies per wave.
+  auto issue = [&](const Src& sr, int kt, int slot) __attribute__((always_inline)) {
+    uint8_t* base = smem + slot * C::kStage;
+#pragma unroll
+    for (int i = 0; i < C::nW; i++)
+      dma16(a.wq + (sr.wb + kt * (kCB * 1024) + i * 1024) + lane * 16, base + C::oW + (wave * C::nW + i) * 1024);
+    dma4(a.ws + (sr.wsb + kt * 1024) + lane * 4, base + C::oWS + wave * 256);
+#pragma unroll
+    for (int q = 0; q < C::nX; q++) {
+      int o = wave + 4 * q;
+      o = o < 3 * NRG ? o : 3 * NRG - 1;
+      dma16(a.xq + (sr.x[q] + (uint32_t)(kt * xstep)), base + C::oX + o * 1024);
+    }
+#pragma unroll
+    for (int q = 0; q < C::nXS; q++) {
+      int o = wave + 4 * q;
+      o = o < NRG ? o : NRG - 1;
+      dma4(a.xs + (sr.xs[q] + (uint32_t)(kt * xsstep)), base + C::oXS + o * 256);
+    }
+  };
+  // The tables of item `item` into buffer `tb`: rows (tokens or weights, kTab dwords) and, with biases,
+  // the item's bias entries; 256-byte dword copies spread over the waves (repeats are harmless).
+  auto issue_tab = [&](int item, int tb) __attribute__((always_inline)) {
+    const int tile = item / nx, x = item % nx;
+    const int4 td = a.tiles[tile];
+    const int prow0 = td.y;
+    constexpr int kRowOps = kTab / 64;
+    const uint8_t* rsrc = G1 ? reinterpret_cast<const uint8_t*>(a.prow_tok) : reinterpret_cast<const uint8_t*>(a.prow_w);
+    {
+      const int o = wave < kRowOps ? wave : 0;
+      dma4(rsrc + (int64_t)(prow0 + o * 64) * 4 + lane * 4, reinterpret_cast<uint8_t*>(&t_row[tb][o * 64]));
+    }
+    if constexpr (BIAS) {
+      constexpr int kBOps = kBias * 2 / 256;  // copies per bias half
+      // entries past the end of the bias row (columns beyond I or H, never used) re-read its last pair
+      const int len = G1 ? a.I : a.H;
+      const uint16_t* brow = a.bias + (int64_t)td.x * (G1 ? 2 * a.I : a.H);
+#pragma unroll
+      for (int i = 0; i < (G1 ? 2 : 1) * kBOps; i += 4) {
+        int o = wave + i;
+        o = o < (G1 ? 2 : 1) * kBOps ? o : (G1 ? 2 : 1) * kBOps - 1;
+        const int half = o / kBOps, part = o % kBOps;
+        int el = x * kBias + part * 128 + lane * 2;  // first of this lane's two entries
+        el = el < len - 2 ? el : len - 2;
+        dma4(brow + half * len + el, reinterpret_cast<uint8_t*>(&t_b[tb][half][0]) + part * 256);
+      }
+    }
+  };
 
-    auto issue = [&](int s, int slot) __attribute__((always_inline)) {
-      const int kt = s < nkt ? s : nkt - 1;  // past the end: repeat the last stage (never read)
-      uint8_t* base = smem + slot * C::kStage;
+  // Each E2M3 term operand (6 dwords) is read by its own two LDS loads (16 + 8 bytes for term 0 at
+  // slot offset 0, 8 + 16 bytes for term 1 at offset 24), so every MFMA operand tuple is written in
+  // place by its loads.  The loads are volatile: that keeps the compiler from merging the two adjacent
+  // 8-byte loads into one 16-byte load whose halves would then have to be copied (and waited for) to
+  // form the two tuples.  Activation fragments are double-buffered across steps (xop[P], P a
+  // compile-time parity); a weight fragment is reloaded for the next step right after the last MFMA
+  // that uses it.
+  typedef const volatile __attribute__((address_space(3))) u32x4_t* vl16_t;
+  typedef const volatile __attribute__((address_space(3))) u32x2_t* vl8_t;
+  typedef const volatile __attribute__((address_space(3))) uint32_t* vl4_t;
+  i32x8_t xop[2][RW][kTerms];
+  uint32_t xsc[2][RW];
+  u32x4_t w[CW];
+  uint32_t wsc[CW / 4];
+  f32x16_t acc[RW][CW];
+  int jj0 = 0;
+  auto load_x = [&](const uint8_t* base, auto pc) __attribute__((always_inline)) {
+    constexpr int P = decltype(pc)::value;
 #pragma unroll
-      for (int i = 0; i < C::nW; i++) dma16(wsrc + kt * (kCB * 1024) + i * 1024, base + C::oW + (wave * C::nW + i) * 1024);
-      dma4(wssrc + kt * 1024, base + C::oWS + wave * 256);
-#pragma unroll
-      for (int q = 0; q < C::nX; q++) dma16(xsrc[q] + kt * xstep, base + xdst[q]);
-#pragma unroll
-      for (int q = 0; q < C::nXS; q++) dma4(xssrc[q] + kt * xsstep, base + xsdst[q]);
-    };
+    for (int r = 0; r < RW; r++) {
+      lds_u8 xp = (lds_u8)(base + C::oX + (wr * RW + r) * 3072 + lane * kSlot);
+      const u32x4_t a4 = *(vl16_t)xp;
+      const u32x2_t a2 = *(vl8_t)(xp + 16);
+      const u32x2_t b2 = *(vl8_t)(xp + 24);
+      const u32x4_t b4 = *(vl16_t)(xp + 32);
+      xop[P][r][0] = i32x8_t{(int)a4[0], (int)a4[1], (int)a4[2], (int)a4[3], (int)a2[0], (int)a2[1], 0, 0};
+      xop[P][r][1] = i32x8_t{(int)b2[0], (int)b2[1], (int)b4[0], (int)b4[1], (int)b4[2], (int)b4[3], 0, 0};
+      xsc[P][r] = *(vl4_t)(lds_u8)(base + C::oXS + (wr * RW + r) * 256 + lane * 4);
+    }
+  };
+  auto load_w = [&](const uint8_t* base, int j) __attribute__((always_inline)) {
+    w[j] = *(vl16_t)(lds_u8)(base + C::oW + (wc * CW + j) * 1024 + lane * 16);
+  };
+  auto load_ws = [&](const uint8_t* base, int j4) __attribute__((always_inline)) {
+    wsc[j4] = *(vl4_t)(lds_u8)(base + C::oWS + lane * 16 + jj0 + wc * CW + j4 * 4);
+  };
 
-    wait_vmcnt<0>();  // nothing of the previous item in flight
-    block_sync();     // every wave is done with the ring
-#pragma unroll
-    for (int s = 0; s < D - 1; s++) issue(s, s);
-
-    // Each E2M3 term operand (6 dwords) is read by its own two LDS loads (16 + 8 bytes for term 0 at
-    // slot offset 0, 8 + 16 bytes for term 1 at offset 24), so every MFMA operand tuple is written in
-    // place by its loads.  Activation fragments are double-buffered across steps; a weight fragment is
-    // reloaded for the next step right after the last MFMA that uses it.
-    // xop[P]: activation operands (two buffers selected by a compile-time parity), w/wsc: weights.
-    i32x8_t xop[2][RW][kTerms];
-    uint32_t xsc[2][RW];
-    u32x4_t w[CW];
-    uint32_t wsc[CW / 4];
-    auto load_x = [&](const uint8_t* base, auto pc) __attribute__((always_inline)) {
-      constexpr int P = decltype(pc)::value;
+  // MFMAs of weight tiles [J0, J0 + JG): term-major, then row group, then tile, so an accumulator is
+  // reused RW * JG instructions later.
+  constexpr int JG = 2;
+  auto mfma_group = [&](auto jc, auto pc) __attribute__((always_inline)) {
+    constexpr int J0 = decltype(jc)::value * JG;
+    constexpr int P = decltype(pc)::value;
+    static_for<0, kTerms>([&](auto tc) __attribute__((always_inline)) {
+      constexpr int t = decltype(tc)::value;
 #pragma unroll
       for (int r = 0; r < RW; r++) {
-        const uint8_t* xp = base + C::oX + (wr * RW + r) * 3072 + lane * kSlot;
-        const u32x4_t a4 = ld16(xp);
-        const u32x2_t a2 = ld8(xp + 16);
-        const u32x2_t b2 = ld8(xp + 24);
-        const u32x4_t b4 = ld16(xp + 32);
-        xop[P][r][0] = i32x8_t{(int)a4[0], (int)a4[1], (int)a4[2], (int)a4[3], (int)a2[0], (int)a2[1], 0, 0};
-        xop[P][r][1] = i32x8_t{(int)b2[0], (int)b2[1], (int)b4[0], (int)b4[1], (int)b4[2], (int)b4[3], 0, 0};
-        xsc[P][r] = *reinterpret_cast<const uint32_t*>(base + C::oXS + (wr * RW + r) * 256 + lane * 4);
+        const i32x8_t xo = xop[P][r][t];
+        static_for<J0, J0 + JG>([&](auto jc2) __attribute__((always_inline)) {
+          constexpr int j = decltype(jc2)::value;
+          const i32x8_t wo = i32x8_t{(int)w[j][0], (int)w[j][1], (int)w[j][2], (int)w[j][3], 0, 0, 0, 0};
+          acc[r][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wo, xo, acc[r][j], kFp4, kFp6, j & 3, wsc[j >> 2],
+                                                                      t, xsc[P][r]);
+        });
       }
-    };
-    auto load_w = [&](const uint8_t* base, int j) __attribute__((always_inline)) { w[j] = ld16(base + C::oW + (wc * CW + j) * 1024 + lane * 16); };
-    auto load_ws = [&](const uint8_t* base, int j4) __attribute__((always_inline)) {
-      wsc[j4] = *reinterpret_cast<const uint32_t*>(base + C::oWS + lane * 16 + jj0 + wc * CW + j4 * 4);
-    };
-
-    f32x16_t acc[RW][CW];
+    });
+    // Pin the group here: the MFMAs are pure, and without an ordered use the compiler may sink them
+    // past the next step's wait, barrier and copies (across basic blocks, where scheduling barriers
+    // do not reach).
 #pragma unroll
     for (int r = 0; r < RW; r++)
 #pragma unroll
-      for (int j = 0; j < CW; j++)
-#pragma unroll
-        for (int i = 0; i < 16; i++) acc[r][j][i] = 0.f;
+      for (int j = J0; j < J0 + JG; j++) asm volatile("" : "+a"(acc[r][j]));
+  };
 
-    // MFMAs of weight tiles [J0, J0 + JG): term-major, then row group, then tile, so an accumulator is
-    // reused RW * JG instructions later.
-    constexpr int JG = 2;
-    auto mfma_group = [&](auto jc, auto pc) __attribute__((always_inline)) {
-      constexpr int J0 = decltype(jc)::value * JG;
-      constexpr int P = decltype(pc)::value;
-      static_for<0, kTerms>([&](auto tc) __attribute__((always_inline)) {
-        constexpr int t = decltype(tc)::value;
-#pragma unroll
-        for (int r = 0; r < RW; r++) {
-          const i32x8_t xo = xop[P][r][t];
-          static_for<J0, J0 + JG>([&](auto jc2) __attribute__((always_inline)) {
-            constexpr int j = decltype(jc2)::value;
-            const i32x8_t wo = i32x8_t{(int)w[j][0], (int)w[j][1], (int)w[j][2], (int)w[j][3], 0, 0, 0, 0};
-            if constexpr (G1)
-              acc[r][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wo, xo, acc[r][j], kFp4, kFp6, j & 3,
-                                                                          wsc[j >> 2], t, xsc[P][r]);
-            else
-              acc[r][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(xo, wo, acc[r][j], kFp6, kFp4, t, xsc[P][r],
-                                                                          j & 3, wsc[j >> 2]);
-          });
-        }
+  // Waits until at most n (0 <= n <= N) of this wave's most recent stages may still be in flight
+  // (younger copies and stores count too, which only makes the wait longer).
+  auto wait_stages = [&](int n, auto nc) __attribute__((always_inline)) {
+    constexpr int N = decltype(nc)::value;
+    if (n >= N) {
+      wait_vmcnt<C::kOps * N>();
+    } else {
+      static_for<0, N>([&](auto ic) __attribute__((always_inline)) {
+        if (n == decltype(ic)::value) wait_vmcnt<C::kOps * decltype(ic)::value>();
       });
-    };
+    }
+  };
 
-    // One K step.  Stage kt+1 (my copies landed) becomes everyone's at the barrier; every wave has by
-    // then finished all reads of stage kt-1 (they fed the MFMAs of step kt-1), so that slot takes stage
-    // kt + D - 1.  The activation fragments of step kt+1 are read into `xn` at the start, the weight
-    // fragments of step kt+1 after their last use in this step.
-    auto step = [&](int kt, auto pc) __attribute__((always_inline)) {
-      constexpr int P = decltype(pc)::value;
-      wait_vmcnt<C::kOps * (D - 3)>();
-      block_sync();
-      const int kn = kt + 1 < nkt ? kt + 1 : kt;
-      const uint8_t* nb = smem + (kn % D) * C::kStage;
-      load_x(nb, std::integral_constant<int, 1 - P>{});
-      issue(kt + D - 1, (kt + D - 1) % D);
-      static_for<0, CW / JG>([&](auto gc) __attribute__((always_inline)) {
-        constexpr int J0 = decltype(gc)::value * JG;
-        mfma_group(gc, pc);
+  Src cur;
+  int q = 0;
+  int item = item_of(0);
+  make_src(item, -1, cur);
+  issue_tab(item, 0);
+  wait_vmcnt<0>();
+  block_sync();
 #pragma unroll
-        for (int j = J0; j < J0 + JG; j++) load_w(nb, j);
-        if constexpr ((J0 + JG) % 4 == 0) load_ws(nb, (J0 + JG) / 4 - 1);
-      });
-    };
+  for (int s = 0; s < D - 1; s++)
+    if (s < nkt) issue(cur, s, s);
 
-    // stage 0 visible: D - 2 later stages may still be in flight
-    wait_vmcnt<C::kOps * (D - 2)>();
+  while (true) {
+    const int tile = item / nx, x = item % nx;
+    const int4 td = a.tiles[tile];
+    const int prow0 = td.y, nrows = td.z;
+    jj0 = (x * NT) % kCB;
+    const bool has_next = q + 1 < nq;
+    const int tb = q & 1;
+
+    // stage 0 visible: the later stages of the prologue (and younger stores) may be in flight; after
+    // the barrier every wave is done with the previous item's tables, so the next item's tables can
+    // go to the other buffer.
+    wait_stages(nkt - 1, std::integral_constant<int, D - 2>{});
     block_sync();
+    if (has_next) issue_tab(item_of(q + 1), tb ^ 1);
     {
       const uint8_t* b0 = smem;
       load_x(b0, std::integral_constant<int, 0>{});
@@ -357,6 +470,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
 #pragma unroll
       for (int j4 = 0; j4 < CW / 4; j4++) load_ws(b0, j4);
     }
+#pragma unroll
+    for (int r = 0; r < RW; r++)
+#pragma unroll
+      for (int j = 0; j < CW; j++)
+#pragma unroll
+        for (int i = 0; i < 16; i++) acc[r][j][i] = 0.f;
+
+    // One K step.  Stage kt+1 (my copies landed) becomes everyone's at the barrier; every wave has by
+    // then finished all reads of stage kt-1 (they fed the MFMAs of step kt-1), so that slot takes the
+    // stage D - 1 steps ahead, if there is one.  Stages kt+2 .. min(kt+D-2, nkt-1) may stay in flight.
+    auto step = [&](int kt, auto pc) __attribute__((always_inline)) {
+      constexpr int P = decltype(pc)::value;
+      // (the scheduling barriers keep the fragment loads and copies where they are placed among the
+      // MFMAs)
+      __builtin_amdgcn_sched_barrier(0);
+      wait_stages(nkt - kt - 2, std::integral_constant<int, D - 3>{});
+      block_sync();
+      __builtin_amdgcn_sched_barrier(0);
+      const int kn = kt + 1 < nkt ? kt + 1 : kt;
+      const uint8_t* nb = smem + (kn % D) * C::kStage;
+      const int s = kt + D - 1;
+      // MFMA group g, then the reloads of its weight fragments for the next step; the next step's
+      // activation fragments and this step's copies go out under the first group's MFMAs.
+      static_for<0, CW / JG>([&](auto gc) __attribute__((always_inline)) {
+        constexpr int J0 = decltype(gc)::value * JG;
+        mfma_group(gc, pc);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (J0 == 0) load_x(nb, std::integral_constant<int, 1 - P>{});
+#pragma unroll
+        for (int j = J0; j < J0 + JG; j++) load_w(nb, j);
+        if constexpr ((J0 + JG) % 4 == 0) load_ws(nb, (J0 + JG) / 4 - 1);
+        if constexpr (J0 == 0) {
+          if (s < nkt) issue(cur, s, s % D);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    };
     int kt = 0;
     for (; kt + 2 <= nkt; kt += 2) {  // two steps per iteration keep both buffers in place
       step(kt, std::integral_constant<int, 0>{});
@@ -364,64 +515,102 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
     }
     if (kt < nkt) step(kt, std::integral_constant<int, 0>{});
 
-    // ---- epilogue (one tile at a time: the scheduling barriers keep each tile's values short-lived)
+    // ---- next item's first D - 1 stages go out before this item's epilogue, so their latency hides
+    // under it.  The last step waited for every copy (the next item's tables included); the barrier
+    // makes sure every wave is done reading the ring.
+    if (has_next) {
+      block_sync();
+      make_src(item_of(q + 1), tb ^ 1, cur);
+#pragma unroll
+      for (int s = 0; s < D - 1; s++)
+        if (s < nkt) issue(cur, s, s);
+    }
+
+    // ---- epilogue (one tile or tile pair at a time: the scheduling barriers keep each one's values
+    // short-lived)
     if constexpr (G1) {
 #pragma unroll
       for (int r = 0; r < RW; r++) {
         const int rgl = wr * RW + r;
         if (rgl * 32 >= nrows) continue;
 #pragma unroll
-        for (int i = 0; i < CW / 2; i++) {
-          const int it = (x * NT + wc * CW) / 2 + i;
-          if (it < a.ntl) g1_epilogue_tile(acc[r][2 * i], acc[r][2 * i + 1], a, e, it, (prow0 >> 5) + rgl, lane);
+        for (int p = 0; p < CW / 4; p++) {
+          const int it = (x * NT + wc * CW) / 2 + 2 * p;  // even: a K step of the second GEMM
+          const int il = (wc * CW) / 2 + 2 * p;           // activation tile within the item
+          if (it < a.ntl)
+            g1_epilogue_pair<BIAS>(acc[r][4 * p], acc[r][4 * p + 1], acc[r][4 * p + 2], acc[r][4 * p + 3], a,
+                                   (lds_u16*)&t_b[tb][0][il * 32], (lds_u16*)&t_b[tb][G1 ? 1 : 0][il * 32],
+                                   it + 1 < a.ntl, it >> 1, (prow0 >> 5) + rgl, lane);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
     } else {
-      // Rows 8*jj + 4*h + i (h = lane / 32) of each row group, column lane % 32 of each tile: the lane's
-      // 16 values of one tile form one block with a power-of-two scale (largest magnitude in
-      // [2^14, 2^15) after scaling), stored as fp16 plus the exponent byte.
-      const int h = lane >> 5;
+      // Lane l holds token row l % 32 of its row group and output columns 8*jj + 4*(l/32) + i of each
+      // tile; after one exchange of lane halves, half h holds the 16 consecutive columns 16h .. 16h+15
+      // of the row: one block with a power-of-two scale (largest magnitude in [2^14, 2^15) after
+      // scaling), stored as 32 bytes of fp16 plus the exponent byte.  Rows of a row group past the
+      // expert's pairs are padding rows of that expert (weight 0), written like the others.
+      const int m = lane & 31, h = lane >> 5;
 #pragma unroll
       for (int r = 0; r < RW; r++) {
         const int rgl = wr * RW + r;
         if (rgl * 32 >= nrows) continue;
-        float wt[16];
-#pragma unroll
-        for (int jj = 0; jj < 4; jj++) {
-          const f32x4_t w4 = *reinterpret_cast<const f32x4_t*>(a.prow_w + prow0 + rgl * 32 + 8 * jj + 4 * h);
-#pragma unroll
-          for (int i = 0; i < 4; i++) wt[4 * jj + i] = rgl * 32 + 8 * jj + 4 * h + i < nrows ? w4[i] : 0.f;
-        }
-        uint16_t* orow = a.o16 + (int64_t)(prow0 + rgl * 32 + 4 * h) * a.H;
-        uint8_t* srow = a.osc + (int64_t)(((prow0 >> 5) + rgl) * 2 + h) * a.H;
+        const float wt = __builtin_bit_cast(float, t_row[tb][rgl * 32 + m]);
+        const int64_t prow = prow0 + rgl * 32 + m;
+        uint16_t* orow = a.o16 + prow * a.H;
+        uint8_t* srow = a.osc + prow * (a.H / 16);
 #pragma unroll
         for (int j = 0; j < CW; j++) {
           const int nt = x * NT + wc * CW + j;
           if (nt < a.ntl) {
-            const int col = nt * 32 + (lane & 31);
-            const float bb = a.bias ? bf16_bits_to_f32(a.bias[(int64_t)e * a.H + col]) : 0.f;
+            // v[c]: column 16h + c of the tile after the exchange
             float v[16];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+              float x0 = acc_read(acc[r][j][i]), x2 = acc_read(acc[r][j][8 + i]);
+              float x1 = acc_read(acc[r][j][4 + i]), x3 = acc_read(acc[r][j][12 + i]);
+              swap_halves(x0, x2);  // half 0: cols i | 4 + i;  half 1: cols 16 + i | 20 + i
+              swap_halves(x1, x3);  // half 0: cols 8 + i | 12 + i;  half 1: cols 24 + i | 28 + i
+              v[i] = x0;
+              v[4 + i] = x2;
+              v[8 + i] = x1;
+              v[12 + i] = x3;
+            }
+            if constexpr (BIAS) {
+              lds_u16* bp = (lds_u16*)&t_b[tb][0][(wc * CW + j) * 32 + 16 * h];
+              float b[16];
+#pragma unroll
+              for (int c = 0; c < 4; c++) bias4(bp + 4 * c, b + 4 * c);
+#pragma unroll
+              for (int c = 0; c < 16; c++) v[c] += b[c];
+            }
+            // The block maximum of w * v is |w| times that of v (rounding is monotonic), and scaling by a
+            // power of two commutes with rounding, so w * 2^-ex is applied as one factor.
             float amax = 0.f;
 #pragma unroll
-            for (int q = 0; q < 16; q++) {
-              v[q] = wt[q] * (acc[r][j][q] + bb);
-              amax = fmaxf(amax, fabsf(v[q]));
-            }
+            for (int c = 0; c < 16; c++) amax = fmaxf(amax, fabsf(v[c]));
+            amax *= fabsf(wt);
             int ex = amax > 0.f ? __builtin_amdgcn_frexp_expf(amax) - 15 : 0;
             ex = ex < -127 ? -127 : (ex > 127 ? 127 : ex);
+            const float f = __builtin_ldexpf(wt, -ex);
+            uint32_t hv[8];
 #pragma unroll
-            for (int q = 0; q < 16; q++) {
-              const int row = rgl * 32 + 8 * (q >> 2) + 4 * h + (q & 3);
-              const _Float16 hv = (_Float16)__builtin_ldexpf(v[q], -ex);
-              if (row < nrows) orow[(8 * (q >> 2) + (q & 3)) * a.H + col] = __builtin_bit_cast(uint16_t, hv);
+            for (int c = 0; c < 8; c++) {
+              const f16x2_t e = __builtin_convertvector((f32x2_t){v[2 * c] * f, v[2 * c + 1] * f}, f16x2_t);
+              hv[c] = __builtin_bit_cast(uint32_t, e);
             }
-            srow[col] = (uint8_t)(ex + 127);
+            u32x4_t* op = reinterpret_cast<u32x4_t*>(orow + nt * 32 + 16 * h);
+            op[0] = u32x4_t{hv[0], hv[1], hv[2], hv[3]};
+            op[1] = u32x4_t{hv[4], hv[5], hv[6], hv[7]};
+            srow[nt * 2 + h] = (uint8_t)(ex + 127);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
+
+    if (++q >= nq) break;
+    item = item_of(q);
   }
 }
 
@@ -437,11 +626,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
     for (int j = 0; j < k; j++) {
       const int64_t r = pair_prow[t * k + j];
       const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(o16 + r * H + c));
-      const u32x2_t e = *reinterpret_cast<const u32x2_t*>(osc + (((r >> 5) * 2 + ((r >> 2) & 1)) * H + c));
+      const int ex = (int)osc[r * (H / 16) + c / 16] - 127;
 #pragma unroll
       for (int q = 0; q < 8; q++) {
         const uint16_t hb = (uint16_t)(v[q >> 1] >> (16 * (q & 1)));
-        const int ex = (int)((e[q >> 2] >> (8 * (q & 3))) & 0xFFu) - 127;
         s[q] += __builtin_ldexpf((float)__builtin_bit_cast(_Float16, hb), ex);
       }
     }
@@ -462,7 +650,10 @@ int launch_cfg(const GemmArgs& a, int64_t max_tiles, hipStream_t stream) {
   if (items < grid) grid = items;
   grid = kXcds * cdiv(grid, kXcds);
   if (grid < kXcds) grid = kXcds;
-  hipLaunchKernelGGL((grouped_gemm_kernel<G1, WR, WC, RW, CW, D, OCC>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+  if (a.bias)
+    hipLaunchKernelGGL((grouped_gemm_kernel<G1, true, WR, WC, RW, CW, D, OCC>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((grouped_gemm_kernel<G1, false, WR, WC, RW, CW, D, OCC>), dim3((unsigned)grid), dim3(256), 0, stream, a);
   return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
 }
 
