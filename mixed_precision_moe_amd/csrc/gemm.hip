@@ -50,13 +50,23 @@ MX_DEV u32x2_t ld8(const uint8_t* p) { return *reinterpret_cast<const u32x2_t*>(
 
 // LDS DMA: lane i copies 16 (or 4) bytes from its global address to lds_wave_base + i * 16 (or 4).
 // (Sub-dword copies still occupy a dword per lane in LDS, so every copied record here is a dword or
-// a multiple of 16 bytes.)
+// a multiple of 16 bytes.)  The copies are issued as inline assembly with M0 set explicitly: the
+// compiler's wait-count tracking treats its own global_load_lds as a FLAT access to both memories and
+// would then wait for every LDS load (lgkmcnt(0)) before any use of one.  Every wait for these copies
+// is therefore explicit (vmcnt, counted per stage) and each LDS consumer follows such a wait and a
+// barrier.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // M0 is listed as clobbered; nothing else here uses it
+MX_DEV uint32_t lds_addr_of(const void* lds_ptr) { return (uint32_t)(uintptr_t)(lds_vptr_t)lds_ptr; }
 MX_DEV void dma16(const void* g, uint8_t* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_vptr_t)lds_wave_base, 16, 0, 0);
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr_of(lds_wave_base));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(m0) : "memory", "m0");
 }
 MX_DEV void dma4(const void* g, uint8_t* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_vptr_t)lds_wave_base, 4, 0, 0);
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr_of(lds_wave_base));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(g), "s"(m0) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // f(integral_constant<int, i>) for i = 0 .. N-1 (operand selectors of the MFMA must be literals).
 template <int I, int N, typename F>
@@ -109,6 +119,58 @@ struct Cfg {
   static constexpr int nX = (3 * NRG + 3) / 4;   // 1 KB activation copies per wave (last one repeated)
   static constexpr int nXS = (NRG + 3) / 4;      // activation scale copies per wave
   static constexpr int kOps = nW + 1 + nX + nXS; // copies per wave per stage
+};
+
+// Order of the work of one K step of a wave: its NM MFMAs in a fixed order (groups of two weight
+// tiles; within a group term-major, then row group, then tile, so an accumulator is reused 2 * RW
+// MFMAs later), and after MFMA m up to kCap of the other tasks of the step, so that their instructions
+// issue while the matrix core works:
+//   kDef + i : weight fragment CW - 2 + i of this step, from the current stage (the last group's
+//              fragments are reloaded at the start of the step that uses them)
+//   kX + r   : activation fragments and scale of row group r for the next step, from the next stage
+//   kWs      : weight scale dwords for the next step
+//   kRel + j : weight fragment j (< CW - 2) for the next step, after the last MFMA that uses it
+//   kDma + i : copy i of the stage D - 1 steps ahead
+struct StepTask {
+  static constexpr int kNone = -1, kDef = 0, kX = 10, kWs = 20, kRel = 30, kDma = 100;
+};
+template <int RW, int CW, int KOPS>
+struct StepPlan {
+  static constexpr int G = CW / 2, NM = 4 * RW * G, kCap = 6, kPer = 2;
+  int t[NM][kCap];
+  constexpr void place(int task, int earliest) {
+    int m = earliest < NM ? earliest : NM - 1;
+    while (m < NM - 1 && n_at(m) >= kPer) m++;
+    int c = n_at(m);
+    t[m][c < kCap ? c : kCap - 1] = task;
+  }
+  constexpr int n_at(int m) const {
+    int c = 0;
+    while (c < kCap && t[m][c] != StepTask::kNone) c++;
+    return c;
+  }
+  constexpr StepPlan() : t{} {
+    for (int m = 0; m < NM; m++)
+      for (int c = 0; c < kCap; c++) t[m][c] = StepTask::kNone;
+    for (int r = 0; r < RW; r++) place(StepTask::kX + r, 0);
+    place(StepTask::kWs, 0);
+    for (int j = 0; j < CW - 2; j++) place(StepTask::kRel + j, (j / 2 + 1) * 4 * RW - 1);
+    for (int i = 0; i < KOPS; i++) place(StepTask::kDma + i, 4 * RW + i * (NM - 4 * RW) / KOPS);
+    // the last group's fragments shortly before that group, so few loads are younger than them
+    place(StepTask::kDef + 0, (G - 1) * 4 * RW - 4 > 0 ? (G - 1) * 4 * RW - 4 : 0);
+    place(StepTask::kDef + 1, (G - 1) * 4 * RW - 4 > 0 ? (G - 1) * 4 * RW - 4 : 0);
+  }
+  // every task placed exactly once, the last group's fragments before that group
+  constexpr bool valid() const {
+    int n = 0, def_last = 0;
+    for (int m = 0; m < NM; m++)
+      for (int c = 0; c < kCap; c++)
+        if (t[m][c] != StepTask::kNone) {
+          n++;
+          if (t[m][c] < StepTask::kX) def_last = m;
+        }
+    return n == 2 + RW + 1 + (CW - 2) + KOPS && def_last < (G - 1) * 4 * RW && n_at(NM - 1) < kCap;
+  }
 };
 
 
@@ -310,25 +372,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
   };
   constexpr int xstep = G1 ? 2 * kSlot : 64 * kSlot;  // bytes per K step of an activation copy
   constexpr int xsstep = G1 ? 8 : 256;
-  // Stage `kt` of the item with sources `sr` into ring slot `slot`: kOps copies per wave.
-  auto issue = [&](const Src& sr, int kt, int slot) __attribute__((always_inline)) {
+  // Copy i (of kOps per wave) of stage `kt` of the item with sources `sr` into ring slot `slot`.
+  auto issue_op = [&](const Src& sr, int kt, int slot, auto ic) __attribute__((always_inline)) {
+    constexpr int i = decltype(ic)::value;
     uint8_t* base = smem + slot * C::kStage;
-#pragma unroll
-    for (int i = 0; i < C::nW; i++)
+    if constexpr (i < C::nW) {
       dma16(a.wq + (sr.wb + kt * (kCB * 1024) + i * 1024) + lane * 16, base + C::oW + (wave * C::nW + i) * 1024);
-    dma4(a.ws + (sr.wsb + kt * 1024) + lane * 4, base + C::oWS + wave * 256);
-#pragma unroll
-    for (int q = 0; q < C::nX; q++) {
+    } else if constexpr (i == C::nW) {
+      dma4(a.ws + (sr.wsb + kt * 1024) + lane * 4, base + C::oWS + wave * 256);
+    } else if constexpr (i < C::nW + 1 + C::nX) {
+      constexpr int q = i - C::nW - 1;
       int o = wave + 4 * q;
       o = o < 3 * NRG ? o : 3 * NRG - 1;
       dma16(a.xq + (sr.x[q] + (uint32_t)(kt * xstep)), base + C::oX + o * 1024);
-    }
-#pragma unroll
-    for (int q = 0; q < C::nXS; q++) {
+    } else {
+      constexpr int q = i - C::nW - 1 - C::nX;
       int o = wave + 4 * q;
       o = o < NRG ? o : NRG - 1;
       dma4(a.xs + (sr.xs[q] + (uint32_t)(kt * xsstep)), base + C::oXS + o * 256);
     }
+  };
+  auto issue = [&](const Src& sr, int kt, int slot) __attribute__((always_inline)) {
+    static_for<0, C::kOps>([&](auto ic) __attribute__((always_inline)) { issue_op(sr, kt, slot, ic); });
   };
   // The tables of item `item` into buffer `tb`: rows (tokens or weights, kTab dwords) and, with biases,
   // the item's bias entries; 256-byte dword copies spread over the waves (repeats are harmless).
@@ -361,73 +426,66 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
 
   // Each E2M3 term operand (6 dwords) is read by its own two LDS loads (16 + 8 bytes for term 0 at
   // slot offset 0, 8 + 16 bytes for term 1 at offset 24), so every MFMA operand tuple is written in
-  // place by its loads.  The loads are volatile: that keeps the compiler from merging the two adjacent
-  // 8-byte loads into one 16-byte load whose halves would then have to be copied (and waited for) to
-  // form the two tuples.  Activation fragments are double-buffered across steps (xop[P], P a
-  // compile-time parity); a weight fragment is reloaded for the next step right after the last MFMA
-  // that uses it.
-  typedef const volatile __attribute__((address_space(3))) u32x4_t* vl16_t;
-  typedef const volatile __attribute__((address_space(3))) u32x2_t* vl8_t;
-  typedef const volatile __attribute__((address_space(3))) uint32_t* vl4_t;
+  // place by its loads.  Each row group's and each term's loads take their base address through an
+  // opaque copy: that keeps the compiler from merging adjacent 8-byte loads (of the two terms, or of
+  // two row groups) into wider loads whose parts would then have to be copied (and waited for) to
+  // form the tuples.  Activation fragments and
+  // weight scales are double-buffered across steps ([P], P a compile-time parity); a weight fragment
+  // is reloaded for the next step after the last MFMA that uses it.
+  typedef const __attribute__((address_space(3))) u32x4_t* vl16_t;
+  typedef const __attribute__((address_space(3))) u32x2_t* vl8_t;
+  typedef const __attribute__((address_space(3))) uint32_t* vl4_t;
+  using Plan = StepPlan<RW, CW, C::kOps>;
+  static constexpr Plan plan{};
+  static_assert(plan.valid(), "step plan");
   i32x8_t xop[2][RW][kTerms];
   uint32_t xsc[2][RW];
   u32x4_t w[CW];
-  uint32_t wsc[CW / 4];
+  uint32_t wsc[2][CW / 4];
   f32x16_t acc[RW][CW];
   int jj0 = 0;
-  auto load_x = [&](const uint8_t* base, auto pc) __attribute__((always_inline)) {
+  auto load_x = [&](const uint8_t* base, int r, auto pc) __attribute__((always_inline)) {
     constexpr int P = decltype(pc)::value;
-#pragma unroll
-    for (int r = 0; r < RW; r++) {
-      lds_u8 xp = (lds_u8)(base + C::oX + (wr * RW + r) * 3072 + lane * kSlot);
-      const u32x4_t a4 = *(vl16_t)xp;
-      const u32x2_t a2 = *(vl8_t)(xp + 16);
-      const u32x2_t b2 = *(vl8_t)(xp + 24);
-      const u32x4_t b4 = *(vl16_t)(xp + 32);
-      xop[P][r][0] = i32x8_t{(int)a4[0], (int)a4[1], (int)a4[2], (int)a4[3], (int)a2[0], (int)a2[1], 0, 0};
-      xop[P][r][1] = i32x8_t{(int)b2[0], (int)b2[1], (int)b4[0], (int)b4[1], (int)b4[2], (int)b4[3], 0, 0};
-      xsc[P][r] = *(vl4_t)(lds_u8)(base + C::oXS + (wr * RW + r) * 256 + lane * 4);
-    }
+    lds_u8 xp = (lds_u8)(base + C::oX + (wr * RW + r) * 3072 + lane * kSlot);
+    asm("" : "+v"(xp));
+    lds_u8 xp1 = xp + 24;
+    asm("" : "+v"(xp1));
+    const u32x4_t a4 = *(vl16_t)xp;
+    const u32x2_t a2 = *(vl8_t)(xp + 16);
+    const u32x2_t b2 = *(vl8_t)xp1;
+    const u32x4_t b4 = *(vl16_t)(xp1 + 8);
+    xop[P][r][0] = i32x8_t{(int)a4[0], (int)a4[1], (int)a4[2], (int)a4[3], (int)a2[0], (int)a2[1], 0, 0};
+    xop[P][r][1] = i32x8_t{(int)b2[0], (int)b2[1], (int)b4[0], (int)b4[1], (int)b4[2], (int)b4[3], 0, 0};
+    xsc[P][r] = *(vl4_t)(lds_u8)(base + C::oXS + (wr * RW + r) * 256 + lane * 4);
   };
   auto load_w = [&](const uint8_t* base, int j) __attribute__((always_inline)) {
     w[j] = *(vl16_t)(lds_u8)(base + C::oW + (wc * CW + j) * 1024 + lane * 16);
   };
-  auto load_ws = [&](const uint8_t* base, int j4) __attribute__((always_inline)) {
-    wsc[j4] = *(vl4_t)(lds_u8)(base + C::oWS + lane * 16 + jj0 + wc * CW + j4 * 4);
+  auto load_ws = [&](const uint8_t* base, auto pc) __attribute__((always_inline)) {
+    constexpr int P = decltype(pc)::value;
+#pragma unroll
+    for (int j4 = 0; j4 < CW / 4; j4++)
+      wsc[P][j4] = *(vl4_t)(lds_u8)(base + C::oWS + lane * 16 + jj0 + wc * CW + j4 * 4);
   };
 
-  // MFMAs of weight tiles [J0, J0 + JG): term-major, then row group, then tile, so an accumulator is
-  // reused RW * JG instructions later.
-  constexpr int JG = 2;
-  auto mfma_group = [&](auto jc, auto pc) __attribute__((always_inline)) {
-    constexpr int J0 = decltype(jc)::value * JG;
-    constexpr int P = decltype(pc)::value;
-    static_for<0, kTerms>([&](auto tc) __attribute__((always_inline)) {
-      constexpr int t = decltype(tc)::value;
-#pragma unroll
-      for (int r = 0; r < RW; r++) {
-        const i32x8_t xo = xop[P][r][t];
-        static_for<J0, J0 + JG>([&](auto jc2) __attribute__((always_inline)) {
-          constexpr int j = decltype(jc2)::value;
-          const i32x8_t wo = i32x8_t{(int)w[j][0], (int)w[j][1], (int)w[j][2], (int)w[j][3], 0, 0, 0, 0};
-          acc[r][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wo, xo, acc[r][j], kFp4, kFp6, j & 3, wsc[j >> 2],
-                                                                      t, xsc[P][r]);
-        });
-      }
-    });
-    // Pin the group here: the MFMAs are pure, and without an ordered use the compiler may sink them
-    // past the next step's wait, barrier and copies (across basic blocks, where scheduling barriers
-    // do not reach).
-#pragma unroll
-    for (int r = 0; r < RW; r++)
-#pragma unroll
-      for (int j = J0; j < J0 + JG; j++) asm volatile("" : "+a"(acc[r][j]));
+  // MFMA m of a step (the order of StepPlan).  Each is pinned by an ordered use of its accumulator:
+  // the MFMAs are pure, and the compiler would otherwise sink them past later waits and barriers
+  // (across basic blocks, where scheduling barriers do not reach).
+  auto mfma_one = [&](auto mc, auto pc) __attribute__((always_inline)) {
+    constexpr int m = decltype(mc)::value, P = decltype(pc)::value;
+    constexpr int g = m / (4 * RW), u = m % (4 * RW);
+    constexpr int t = u / (2 * RW), r = (u % (2 * RW)) / 2, j = 2 * g + (u % 2);
+    const i32x8_t wo = i32x8_t{(int)w[j][0], (int)w[j][1], (int)w[j][2], (int)w[j][3], 0, 0, 0, 0};
+    acc[r][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wo, xop[P][r][t], acc[r][j], kFp4, kFp6, j & 3,
+                                                                wsc[P][j >> 2], t, xsc[P][r]);
+    asm volatile("" : "+a"(acc[r][j]));
   };
 
   // Waits until at most n (0 <= n <= N) of this wave's most recent stages may still be in flight
   // (younger copies and stores count too, which only makes the wait longer).
   auto wait_stages = [&](int n, auto nc) __attribute__((always_inline)) {
     constexpr int N = decltype(nc)::value;
+    if (n < 0) n = 0;
     if (n >= N) {
       wait_vmcnt<C::kOps * N>();
     } else {
@@ -464,11 +522,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
     if (has_next) issue_tab(item_of(q + 1), tb ^ 1);
     {
       const uint8_t* b0 = smem;
-      load_x(b0, std::integral_constant<int, 0>{});
 #pragma unroll
-      for (int j = 0; j < CW; j++) load_w(b0, j);
+      for (int r = 0; r < RW; r++) load_x(b0, r, std::integral_constant<int, 0>{});
 #pragma unroll
-      for (int j4 = 0; j4 < CW / 4; j4++) load_ws(b0, j4);
+      for (int j = 0; j < CW - 2; j++) load_w(b0, j);
+      load_ws(b0, std::integral_constant<int, 0>{});
     }
 #pragma unroll
     for (int r = 0; r < RW; r++)
@@ -480,40 +538,58 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
     // One K step.  Stage kt+1 (my copies landed) becomes everyone's at the barrier; every wave has by
     // then finished all reads of stage kt-1 (they fed the MFMAs of step kt-1), so that slot takes the
     // stage D - 1 steps ahead, if there is one.  Stages kt+2 .. min(kt+D-2, nkt-1) may stay in flight.
-    auto step = [&](int kt, auto pc) __attribute__((always_inline)) {
+    // MAIN steps (kt + D - 1 < nkt) interleave their copies with the MFMAs; the last steps of an item
+    // issue any copy up front and wait by a runtime count.
+    auto step = [&](int kt, auto pc, auto mc) __attribute__((always_inline)) {
       constexpr int P = decltype(pc)::value;
-      // (the scheduling barriers keep the fragment loads and copies where they are placed among the
-      // MFMAs)
+      constexpr bool MAIN = decltype(mc)::value;
       __builtin_amdgcn_sched_barrier(0);
-      wait_stages(nkt - kt - 2, std::integral_constant<int, D - 3>{});
+      if constexpr (MAIN)
+        wait_vmcnt<C::kOps * (D - 3)>();
+      else
+        wait_stages(nkt - kt - 2, std::integral_constant<int, D - 3>{});
       block_sync();
       __builtin_amdgcn_sched_barrier(0);
       const int kn = kt + 1 < nkt ? kt + 1 : kt;
+      const uint8_t* cb = smem + (kt % D) * C::kStage;
       const uint8_t* nb = smem + (kn % D) * C::kStage;
       const int s = kt + D - 1;
-      // MFMA group g, then the reloads of its weight fragments for the next step; the next step's
-      // activation fragments and this step's copies go out under the first group's MFMAs.
-      static_for<0, CW / JG>([&](auto gc) __attribute__((always_inline)) {
-        constexpr int J0 = decltype(gc)::value * JG;
-        mfma_group(gc, pc);
+      if constexpr (!MAIN) {
+        if (s < nkt) issue(cur, s, s % D);
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (J0 == 0) load_x(nb, std::integral_constant<int, 1 - P>{});
-#pragma unroll
-        for (int j = J0; j < J0 + JG; j++) load_w(nb, j);
-        if constexpr ((J0 + JG) % 4 == 0) load_ws(nb, (J0 + JG) / 4 - 1);
-        if constexpr (J0 == 0) {
-          if (s < nkt) issue(cur, s, s % D);
-        }
+      }
+      static_for<0, Plan::NM>([&](auto mi) __attribute__((always_inline)) {
+        constexpr int m = decltype(mi)::value;
+        mfma_one(mi, pc);
+        static_for<0, Plan::kCap>([&](auto ci) __attribute__((always_inline)) {
+          constexpr int task = plan.t[m][decltype(ci)::value];
+          if constexpr (task >= StepTask::kDma) {
+            if constexpr (MAIN) issue_op(cur, s, s % D, std::integral_constant<int, task - StepTask::kDma>{});
+          } else if constexpr (task >= StepTask::kRel) {
+            load_w(nb, task - StepTask::kRel);
+          } else if constexpr (task == StepTask::kWs) {
+            load_ws(nb, std::integral_constant<int, 1 - P>{});
+          } else if constexpr (task >= StepTask::kX) {
+            load_x(nb, task - StepTask::kX, std::integral_constant<int, 1 - P>{});
+          } else if constexpr (task >= StepTask::kDef) {
+            load_w(cb, CW - 2 + task - StepTask::kDef);
+          }
+        });
         __builtin_amdgcn_sched_barrier(0);
       });
-      __builtin_amdgcn_sched_barrier(0);
     };
+    // main steps in pairs (an even count, so the buffers are back in place), then the rest
+    const int nmain = nkt > D - 1 ? ((nkt - (D - 1)) & ~1) : 0;
     int kt = 0;
-    for (; kt + 2 <= nkt; kt += 2) {  // two steps per iteration keep both buffers in place
-      step(kt, std::integral_constant<int, 0>{});
-      step(kt + 1, std::integral_constant<int, 1>{});
+    for (; kt < nmain; kt += 2) {
+      step(kt, std::integral_constant<int, 0>{}, std::true_type{});
+      step(kt + 1, std::integral_constant<int, 1>{}, std::true_type{});
     }
-    if (kt < nkt) step(kt, std::integral_constant<int, 0>{});
+    for (; kt + 2 <= nkt; kt += 2) {
+      step(kt, std::integral_constant<int, 0>{}, std::false_type{});
+      step(kt + 1, std::integral_constant<int, 1>{}, std::false_type{});
+    }
+    if (kt < nkt) step(kt, std::integral_constant<int, 0>{}, std::false_type{});
 
     // ---- next item's first D - 1 stages go out before this item's epilogue, so their latency hides
     // under it.  The last step waited for every copy (the next item's tables included); the barrier
