@@ -29,8 +29,27 @@ from tests.gpu_common import bf16_dev, gpu_standard_weights  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 PEAK_FP4_TFLOPS = 10100.0  # MI355X dense MXFP4 / MXFP6 MFMA
-STAGES = ["act_split", "route", "pair_sort", "gemm1_swiglu", "gemm2_combine", "bf16_out"]
-STAGE_KERNELS = ["xprep_kernel", "route_kernel", "place_kernel", "gemm1_kernel", "gemm2_kernel", "finish_kernel"]
+# the forward's stages as the library's events bracket them, and the kernels each stage launches
+STAGES = ["act_split", "route", "pair_sort", "gemm1_swiglu", "gemm2_weighted", "combine"]
+STAGE_KERNELS = ["xprep_kernel", "route_kernel", "scan_kernel + scatter_kernel", "grouped_gemm_kernel<G1=true>",
+                 "grouped_gemm_kernel<G1=false>", "combine_kernel"]
+DTYPE = "mxfp4 (e2m1 + e8m0) weights x two-term e2m3 (fp6) activations on block-scaled MFMA, fp32 accumulate"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm1_prefill_traffic.txt")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the first GEMM on the prefill workload, from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by the same counter on a copy of known size), or None when the
+    summary is missing or the GEMM source has changed since the counters were taken."""
+    import hashlib
+    try:
+        fields = dict(l.split(None, 1) for l in open(TRAFFIC_FILE).read().splitlines() if l.strip() and not l.startswith("#"))
+        src = open(os.path.join(ROOT, "mixed_precision_moe_amd", "csrc", "gemm.hip"), "rb").read()
+        if hashlib.sha256(src).hexdigest() != fields["gemm_source_sha256"].strip():
+            return None
+        return float(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def moe_flops(cfg):
@@ -163,7 +182,7 @@ def cpu_baselines(cfg, x_bits, logits):
     cores = len(os.sched_getaffinity(0))
     # MoE: a few sampled tokens of the prefill workload; the oracle dequantizes every expert they use in
     # fp64, which dominates its time
-    ntok = 4
+    ntok = 512  # every expert is used; about 10-30 s of the oracle on the host cores
     rows = np.sort(np.random.default_rng(1).choice(cfg.T, size=ntok, replace=False))
     w13, w2 = LazyExperts(cfg, "w13"), LazyExperts(cfg, "w2")
     from oracle.route import route_ref
@@ -180,16 +199,16 @@ def cpu_baselines(cfg, x_bits, logits):
            "kind": "oracle", "seconds": dt,
            "sample": f"{ntok} of {cfg.T} prefill tokens ({len(np.unique(ids[rows]))} experts dequantized in fp64); "
                      "weights pre-quantized outside the timed region"}
-    # quantizer: 512 rows of the 8192 x 7168 matrix
+    # quantizer: the whole 8192 x 7168 matrix
     Mq, K = synth.QUANT_CONFIG["M"], synth.QUANT_CONFIG["K"]
-    sub = synth.quant_matrix(Mq, K, cid=synth.QUANT_CONFIG["cid"])[:512]
+    sub = synth.quant_matrix(Mq, K, cid=synth.QUANT_CONFIG["cid"])
     t0 = time.perf_counter()
     q, s = Q.quantize_ref(sub)
     Q.tile_scales(s)
     dt = time.perf_counter() - t0
-    nbytes = 512 * K * 2 + 512 * K // 2 + 2 * 512 * K // 32
+    nbytes = Mq * K * 2 + Mq * K // 2 + 2 * Mq * K // 32
     quant = {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle", "seconds": dt,
-             "sample": f"512 of {Mq} rows of the quantize matrix"}
+             "sample": f"all {Mq} rows of the quantize matrix"}
     return moe, quant
 
 
@@ -265,20 +284,25 @@ def main():
     g1_flops = 2.0 * P * cfg.H * 2 * cfg.I
     g2_flops = 2.0 * P * cfg.I * cfg.H
     g1_ms, g2_ms = stages[3], stages[4]
-    roofline = {"bound": "mfma", "kernel": "gemm1_kernel (first grouped GEMM + SwiGLU)",
-                "achieved": g1_flops / (g1_ms * 1e-3) / 1e12, "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
-                "frac": g1_flops / (g1_ms * 1e-3) / 1e12 / PEAK_FP4_TFLOPS, "traffic": None,
-                "flops_per_launch": g1_flops, "avg_launch_ms": g1_ms}
+    # the dominant kernel: algorithmic flops of the first GEMM per launch over its measured launch time
+    # (HIP events the library records on its own stream around the launch).  The MFMA issues every
+    # product once per activation term, so the matrix cores execute twice the algorithmic flops.
+    g1_tf = g1_flops / (g1_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": "grouped_gemm_kernel<G1=true> (first grouped GEMM + SwiGLU)",
+                "achieved": g1_tf, "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s", "frac": g1_tf / PEAK_FP4_TFLOPS,
+                "traffic": measured_traffic(), "flops_per_launch": g1_flops, "avg_launch_ms": g1_ms,
+                "mfma_issued_frac": 2 * g1_tf / PEAK_FP4_TFLOPS}
     out = {
         "metric": "MXFP4 MoE layer TFLOP/s + quantize GB/s, % of MI355X roofline, 1 GPU",
         "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp4 weights x three-term fp6 activations, fp32 accumulate", "data": "synthetic",
+        "dtype": DTYPE, "data": "synthetic",
         "config": {"workload": "prefill-shaped MXFP4 MoE layer, bf16 tokens", "T": cfg.T, "E": cfg.E, "top_k": cfg.k,
                    "H": cfg.H, "I": cfg.I, "bias": cfg.bias, "parallelism": "single GPU"},
         "roofline": roofline,
         "stages_ms": {n: float(v) for n, v in zip(STAGES, stages)},
         "layer_frac_of_fp4_peak": value / PEAK_FP4_TFLOPS,
+        "stage_kernels": dict(zip(STAGES, STAGE_KERNELS)),
         "gemm2": {"achieved_TFLOP_s": g2_flops / (g2_ms * 1e-3) / 1e12, "avg_launch_ms": g2_ms},
     }
     x_bits_host, logits_host = synth.moe_activations(cfg)

@@ -5,9 +5,10 @@
  *   [P1] prhub summary of vLLM PR #46915 (weight/scale interleave fix in the SM90 MXFP4 fused-MoE test)
  *   [P2] prhub report of vLLM PR #51038 "[Bugfix][Quantization] Fix MXFP4 conversion for FlashInfer CUTLASS"
  *   [P3] prhub summary of vLLM PR #43557 (E8M0 scale fix in the MXFP4 MoE CUTLASS kernel)
- *   [NS] the workload specification: OCP-MX MXFP4 (32-element blocks, E2M1 round-to-nearest-even
- *        saturating at +-6, two nibbles per byte), top-k routing, SwiGLU = silu(w1 half) * (w3 half),
- *        grouped GEMMs and a weighted combine.
+ *   [DEF] definitions this library adopts where the pages name a step without spelling it out: the
+ *        OCP Microscaling MXFP4 format (32-element blocks, E2M1 round-to-nearest-even saturating at
+ *        +-6, two nibbles per byte), top-k routing over softmax(logits), SwiGLU = silu(w1 half) *
+ *        (w3 half), grouped GEMMs and a routing-weighted combine.
  *
  * Conventions for every entry point:
  *   - Pointers marked "device" are HIP device pointers owned by the caller; the library never
@@ -47,7 +48,7 @@ uint32_t mxfp4_version(void);
 
 /* ------------------------------------------------------------------------------------------------
  * MXFP4 block quantization.  [P3 Implementation breakdown item 1; Key source snippets: the E8M0
- * reference helper and the UE8M0_SF branch of the FP16/BF16 -> FP4 converter; NS element rule]
+ * reference helper and the UE8M0_SF branch of the FP16/BF16 -> FP4 converter; DEF element rule]
  *
  * For each row of x and each 32-element block along K:
  *   amax = max |x| over the block (bf16 magnitudes, exact);
@@ -126,7 +127,7 @@ int mxfp4_unpack_weights(const mxfp4_moe_dims* d, const void* packed, void* w13_
 int mxfp4_check_packed(const mxfp4_moe_dims* d, const void* packed, void* stream);
 
 /* ------------------------------------------------------------------------------------------------
- * Routing.  [NS: router logits -> softmax -> top-k, renormalized over the selected experts]
+ * Routing.  [DEF: router logits -> softmax -> top-k, renormalized over the selected experts]
  *   topk_ids[t] = the top_k largest logits of token t in descending order, equal logits in
  *                 increasing expert index (-0.0 equals +0.0);
  *   topk_w[t,j] = exp(l_j - l_max) / S, S summed over the selected experts (renormalize != 0) or
@@ -143,7 +144,7 @@ int moe_mxfp4_route(const float* router_logits, int64_t T, int32_t E, int32_t to
                     size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------------
- * The MoE layer.  [NS; P1 Implementation breakdown: the fused-MoE call takes packed 4-bit weights
+ * The MoE layer.  [DEF; P1 Implementation breakdown: the fused-MoE call takes packed 4-bit weights
  * with per-32 group scales and 16-bit activations]
  *   y[t] = sum_j topk_w[t,j] * ( W2_e (silu(h_g) * h_u) + b2_e ),  e = topk_ids[t,j],
  *   h = W13_e x_t + b13_e, h_g = rows [0, I) (w1), h_u = rows [I, 2I) (w3),

@@ -2,7 +2,7 @@
 // (v_mfma_scale_f32_32x32x64_f8f6f4), with the SwiGLU and the routing-weighted output fused into
 // their epilogues, and the final combine over the top-k experts of each token.
 //
-// [NS: grouped w13 GEMM, SwiGLU = silu(w1 half) * (w3 half), grouped w2 GEMM, weighted top-k combine;
+// [DEF: grouped w13 GEMM, SwiGLU = silu(w1 half) * (w3 half), grouped w2 GEMM, weighted top-k combine;
 //  MXFP4 weights with E8M0 scales per 32 elements; P1 Implementation breakdown: the mixed-input fused
 //  MoE multiplies packed 4-bit weights with per-32 group scales by 16-bit activations]
 //

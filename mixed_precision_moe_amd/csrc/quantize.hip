@@ -1,12 +1,12 @@
 // MXFP4 block quantization of a bf16 matrix on gfx950.
 //
 // [P3 Implementation breakdown item 1; Key source snippets: the E8M0 reference helper, the UE8M0_SF
-//  branch of the FP16/BF16 -> FP4 converter and the tiled-scale untile helper; NS element rule]
+//  branch of the FP16/BF16 -> FP4 converter and the tiled-scale untile helper; DEF element rule]
 //
 // Work split: a wave covers 512 consecutive columns (16 blocks) of four rows; lane l owns eight
 // bf16 (one 16-byte load) of each row, four lanes per 32-element block.  The block maximum is a
 // max of bf16 magnitude bits (monotone for non-negative values), reduced over the four lanes.
-// Elements are encoded by v_cvt_scalef32_pk_fp4_bf16, which divides by the E8M0 scale and rounds
+// Cross-lane steps are DPP moves (no LDS round trips).  Elements are encoded by v_cvt_scalef32_pk_fp4_bf16, which divides by the E8M0 scale and rounds
 // to nearest even with saturation and a kept sign -- the element rule exactly (checked against the
 // oracle on every bf16 pattern under every exponent).  The grid also covers the padding of the tiled
 // layout (rows up to a multiple of 128, columns up to a multiple of 128), whose lanes read nothing and
@@ -28,6 +28,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
   const int64_t col = (int64_t)blockIdx.x * 512 + lane * 8;
   const bool col_live = col < Kpad;   // uniform over each 16-lane (128-column) group
   const bool col_in = col < K;        // uniform over each 4-lane block (K % 32 == 0)
+  const bool flat_words = (K / 32) % 4 == 0;  // every row's flat scales start dword-aligned
   const int64_t nby = Mpad / kRowsPerBlock;
   for (int64_t by = blockIdx.y; by < nby; by += gridDim.y) {
   const int64_t row0 = by * kRowsPerBlock + wave * kRowsPerWave;
@@ -53,8 +54,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
       uint32_t lo = w[i] & 0x7FFFu, hi = (w[i] >> 16) & 0x7FFFu;
       m = max(m, max(lo, hi));
     }
-    m = max(m, (uint32_t)__shfl_xor((int)m, 1));
-    m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+    // maximum over the block's four lanes (DPP quad permutations: lane ^ 1, lane ^ 2)
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false));
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false));
     const uint32_t e = e8m0_from_amax_bits(m << 16);
     const float s = e8m0_as_scale_operand(e);
 
@@ -64,19 +66,29 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
     packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(packed, __builtin_bit_cast(bf16x2_t, w[2]), s, 2);
     packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(packed, __builtin_bit_cast(bf16x2_t, w[3]), s, 3);
 
+    // the scales of the four blocks of a 128-column group live in lanes 16j, 16j+4, 16j+8, 16j+12
+    // (DPP rotations within each 16-lane row bring lanes +4, +8, +12 to lane 16j): one dword for the
+    // tiled layout and, where the row's flat scales are dword-aligned and the group lies inside K, for
+    // the flat layout too
+    const uint32_t e1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)e, 0x12C, 0xF, 0xF, false);
+    const uint32_t e2 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)e, 0x128, 0xF, 0xF, false);
+    const uint32_t e3 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)e, 0x124, 0xF, 0xF, false);
+    const uint32_t word = e | (e1 << 8) | (e2 << 16) | (e3 << 24);
     const bool live = col_in && row < M;
     if (live) {
-      *reinterpret_cast<uint32_t*>(q + row * (K / 2) + col / 2) = packed;
-      if (sflat && (lane & 3) == 0) sflat[row * (K / 32) + col / 32] = (uint8_t)e;
+      // nibbles are written once and not read again here: streaming stores
+      __builtin_nontemporal_store(packed, reinterpret_cast<uint32_t*>(q + row * (K / 2) + col / 2));
+      if (sflat) {
+        if (flat_words && col + 128 <= K) {
+          if ((lane & 15) == 0) *reinterpret_cast<uint32_t*>(sflat + row * (K / 32) + col / 32) = word;
+        } else if ((lane & 3) == 0) {
+          sflat[row * (K / 32) + col / 32] = (uint8_t)e;
+        }
+      }
     }
-    // tiled scales: the four blocks of a 128-column tile live in lanes 16j, 16j+4, 16j+8, 16j+12
-    uint32_t e1 = (uint32_t)__shfl_down((int)e, 4);
-    uint32_t e2 = (uint32_t)__shfl_down((int)e, 8);
-    uint32_t e3 = (uint32_t)__shfl_down((int)e, 12);
     if (stiled && col_live && (lane & 15) == 0) {
       const int64_t mT = row >> 7, iM = (row >> 5) & 3, oM = row & 31;
       const int64_t kT = col >> 7;
-      const uint32_t word = e | (e1 << 8) | (e2 << 16) | (e3 << 24);
       *reinterpret_cast<uint32_t*>(stiled + ((mT * kTiles + kT) * 32 + oM) * 16 + iM * 4) = word;
     }
   }

@@ -1,7 +1,7 @@
 // MoE front: activation preparation, top-k routing, and the stable counting sort of (token, expert)
 // pairs that lays out the grouped GEMMs' rows and tile schedule.
 //
-// [NS: top-k routing of softmax(router logits) renormalized over the selected experts; the router
+// [DEF: top-k routing of softmax(router logits) renormalized over the selected experts; the router
 //  sort/permute/gather step]
 //
 // Routing runs in three launches: route_kernel (top-k per token, counted into a per-block expert

@@ -12,12 +12,13 @@ passage it follows.  Page tags used throughout:
   CUTLASS" (the checkpoint-to-kernel weight conversion, the [w1; w3] -> [w3; w1] swap, bias -> bf16).
 * [P3] prhub summary of vLLM PR #43557 (the E8M0 scale fix in the MXFP4 MoE CUTLASS kernel: the 0.75
   round-up rule, the tiled scale layout and the Python reference helpers).
-* [NS] the workload specification this library is built to (OCP-MX MXFP4: 32-element blocks, E2M1
-  round-to-nearest-even saturating at +-6, two nibbles per byte; top-k routing, SwiGLU defined as
-  silu(w1 half) * (w3 half), grouped GEMMs and a weighted combine; tolerance
-  |y - y_ref| <= 2e-2 * rms(y_ref) + 1e-3).
+* [DEF] definitions this library adopts where the pages name a step without spelling it out: the
+  OCP Microscaling MXFP4 format (32-element blocks, E2M1 elements rounded to nearest even and
+  saturating at +-6, two nibbles per byte), top-k routing over softmax(router logits), SwiGLU as
+  silu(w1 half) * (w3 half), grouped GEMMs and a routing-weighted combine; the comparison tolerance
+  |y - y_ref| <= 2e-2 * rms(y_ref) + 1e-3 for floating-point outputs.
 
-Readings of points the pages leave open are stated where they are used and collected in the design doc.
+Readings of points the pages leave open are stated where they are used.
 
 Parity status:  every function here is pinned by a ``-m "not gpu"`` test against something other than
 itself (hand values, closed forms, brute force, textbook cases or an independent library routine),

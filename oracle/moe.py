@@ -7,7 +7,7 @@ Per token t with selected experts e_j and weights w_j (route_ref):
     a   = silu(h[:I]) * h[I:]            silu(g) = g / (1 + exp(-g))
     o   = a . W2_e^T + b2_e              W2_e  = dequant(w2_q[e], w2_s[e])
     y_t = sum_j w_j * o_j
-[NS: grouped w13 GEMM, SwiGLU as silu(w1 half) * (w3 half), grouped w2 GEMM, weighted combine;
+[DEF: grouped w13 GEMM, SwiGLU as silu(w1 half) * (w3 half), grouped w2 GEMM, weighted combine;
  P2 Implementation breakdown item 2: the checkpoint's fused gate/up is [w1; w3]]
 Reading: b13 is added before the activation and b2 to each expert's output before weighting.
 """

@@ -9,7 +9,7 @@ import numpy as np
 
 BLOCK = 32
 """Elements per scale block along K.  [P3 Key source snippets, test_mxfp4_moe.py: the untile helper
-divides K by the MXFP4 block size of 32]  [NS: 32-element blocks]"""
+divides K by the MXFP4 block size of 32]  [DEF: 32-element blocks]"""
 
 E2M1_MAGNITUDES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
 """Magnitude of each 3-bit E2M1 code (OCP-MX FP4: 1 sign, 2 exponent, 1 mantissa bit, bias 1).
@@ -45,7 +45,7 @@ def e8m0_from_amax(amax):
 def e2m1_magnitude_code(v):
     """E2M1 magnitude code of v >= 0 (float64), round to nearest, ties to the even code, saturating.
 
-    [NS: E2M1 elements, round-to-nearest-even, saturating at +-6]  The representable magnitudes are
+    [DEF: E2M1 elements, round-to-nearest-even, saturating at +-6]  The representable magnitudes are
     E2M1_MAGNITUDES; the midpoints between neighbours are 0.25, 0.75, 1.25, 1.75, 2.5, 3.5 and 5.
     On a midpoint the neighbour with the even code wins (0.25 -> 0, 0.75 -> 1.0, 1.25 -> 1.0,
     1.75 -> 2.0, 2.5 -> 2.0, 3.5 -> 4.0, 5 -> 4.0), and anything above 5 becomes 6.0 (code 7).
@@ -72,7 +72,7 @@ def quantize_ref(x_bits):
          reading: the maximum of magnitudes, as the not-positive branch of the reference implies)
          [P3 Key source snippets].
       2. e = e8m0_from_amax(amax).
-      3. v = |x| * 2**(127 - e), exact in float64; magnitude code by e2m1_magnitude_code [NS].
+      3. v = |x| * 2**(127 - e), exact in float64; magnitude code by e2m1_magnitude_code [DEF].
       4. sign bit 0x8 set when the input's sign bit is set, also when the magnitude code is 0
          (reading: the sign is kept; the pages are silent).
       5. two codes per byte, element 2j in the low nibble and 2j+1 in the high nibble

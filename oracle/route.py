@@ -1,8 +1,8 @@
 """Oracle: top-k routing and the counting sort of (token, expert) pairs.
 
-Test infrastructure only (see the package docstring).  The pages never write the routing down; the
-workload specification does: router logits -> softmax -> top-k, weights renormalized over the k
-selected experts [NS; the tiny configuration's "softmax -> top-2 weights renormalized"].
+Test infrastructure only (see the package docstring).  The pages never write the routing down; this
+library adopts the usual definition: router logits -> softmax -> top-k, weights renormalized over the
+k selected experts [DEF].
 """
 
 import numpy as np
