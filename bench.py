@@ -34,20 +34,23 @@ STAGES = ["act_split", "route", "pair_sort", "gemm1_swiglu", "gemm2_weighted", "
 STAGE_KERNELS = ["xprep_kernel", "route_kernel", "scan_kernel + scatter_kernel", "grouped_gemm_kernel<G1=true>",
                  "grouped_gemm_kernel<G1=false>", "combine_kernel"]
 DTYPE = "mxfp4 (e2m1 + e8m0) weights x two-term e2m3 (fp6) activations on block-scaled MFMA, fp32 accumulate"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm1_prefill_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_prefill_gemm1_and_quantize.txt")
 
 
-def measured_traffic():
-    """HBM bytes per launch of the first GEMM on the prefill workload, from the committed counter summary
-    (FETCH_SIZE + WRITE_SIZE, each scaled by the same counter on a copy of known size), or None when the
-    summary is missing or the GEMM source has changed since the counters were taken."""
+def measured_traffic(which):
+    """HBM bytes per launch of `which` ("gemm" = the first GEMM on the prefill workload, or "quantize")
+    from the committed counter summary (FETCH_SIZE + WRITE_SIZE, each scaled by the same counter on a
+    copy of known size), or None when the summary is missing or the kernel's source file has changed
+    since the counters were taken."""
     import hashlib
+    key = {"gemm": ("traffic_bytes_per_launch", "gemm_source_sha256", "gemm.hip"),
+           "quantize": ("quantize_traffic_bytes_per_launch", "quantize_source_sha256", "quantize.hip")}[which]
     try:
         fields = dict(l.split(None, 1) for l in open(TRAFFIC_FILE).read().splitlines() if l.strip() and not l.startswith("#"))
-        src = open(os.path.join(ROOT, "mixed_precision_moe_amd", "csrc", "gemm.hip"), "rb").read()
-        if hashlib.sha256(src).hexdigest() != fields["gemm_source_sha256"].strip():
+        src = open(os.path.join(ROOT, "mixed_precision_moe_amd", "csrc", key[2]), "rb").read()
+        if hashlib.sha256(src).hexdigest() != fields[key[1]].strip():
             return None
-        return float(fields["traffic_bytes_per_launch"])
+        return float(fields[key[0]])
     except (OSError, KeyError, ValueError):
         return None
 
@@ -147,25 +150,29 @@ def bench_quantize(steps, warmup, rotations=4):
     L = lib()
     import ctypes
     st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    args = [(ctypes.c_void_p(xs[r].data_ptr()), ctypes.c_void_p(qs[r].data_ptr()), ctypes.c_void_p(sfs[r].data_ptr()),
+             ctypes.c_void_p(sts[r].data_ptr())) for r in range(rotations)]
 
     def one(i):
-        r = i % rotations
-        check("mxfp4_quantize", L.mxfp4_quantize(ctypes.c_void_p(xs[r].data_ptr()), M, K, K,
-                                                 ctypes.c_void_p(qs[r].data_ptr()), ctypes.c_void_p(sfs[r].data_ptr()),
-                                                 ctypes.c_void_p(sts[r].data_ptr()), st))
+        a = args[i % rotations]
+        check("mxfp4_quantize", L.mxfp4_quantize(a[0], M, K, K, a[1], a[2], a[3], st))
     for i in range(warmup):
         one(i)
     n = max(steps, 20)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    # The launches are queued behind a GPU-side sleep, so the host has enqueued all of them before the
+    # first runs: the interval between the two events is n launches back to back on the stream they
+    # run on, without gaps from host-side launch overhead.
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     torch.cuda.synchronize()
+    torch.cuda._sleep(20_000_000)
     ev[0].record()
     for i in range(n):
         one(i)
-        ev[i + 1].record()
+    ev[1].record()
     torch.cuda.synchronize()
-    ms = np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(n)])
+    ms = float(ev[0].elapsed_time(ev[1])) / n
     nbytes = M * K * 2 + M * K // 2 + 2 * (M * K // 32)  # bf16 in, nibbles, flat + tiled scales (no padding here)
-    return {"workload": f"quantize bf16 {M}x{K} -> E2M1 nibbles + E8M0 flat and tiled scales", "ms": float(ms),
+    return {"workload": f"quantize bf16 {M}x{K} -> E2M1 nibbles + E8M0 flat and tiled scales", "ms": ms,
             "bytes": nbytes, "GB_s": nbytes / (ms * 1e-3) / 1e9, "launches": n}
 
 
@@ -216,7 +223,7 @@ def run_quantize(args):
     log("[bench] timing quantize")
     qr = bench_quantize(args.steps, args.warmup)
     qr["roofline"] = {"bound": "hbm", "kernel": "quantize_kernel", "achieved": qr["GB_s"], "peak": PEAK_HBM_GBS,
-                      "unit": "GB/s", "frac": qr["GB_s"] / PEAK_HBM_GBS, "traffic": None}
+                      "unit": "GB/s", "frac": qr["GB_s"] / PEAK_HBM_GBS, "traffic": measured_traffic("quantize")}
     return qr
 
 
@@ -290,7 +297,7 @@ def main():
     g1_tf = g1_flops / (g1_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": "grouped_gemm_kernel<G1=true> (first grouped GEMM + SwiGLU)",
                 "achieved": g1_tf, "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s", "frac": g1_tf / PEAK_FP4_TFLOPS,
-                "traffic": measured_traffic(), "flops_per_launch": g1_flops, "avg_launch_ms": g1_ms,
+                "traffic": measured_traffic("gemm"), "flops_per_launch": g1_flops, "avg_launch_ms": g1_ms,
                 "mfma_issued_frac": 2 * g1_tf / PEAK_FP4_TFLOPS}
     out = {
         "metric": "MXFP4 MoE layer TFLOP/s + quantize GB/s, % of MI355X roofline, 1 GPU",
