@@ -134,7 +134,9 @@ struct Cfg {
 struct StepTask {
   static constexpr int kNone = -1, kDef = 0, kX = 10, kWs = 20, kRel = 30, kDma = 100;
 };
-template <int RW, int CW, int KOPS>
+// COPIES_FIRST puts the copies right after the step's first MFMAs (for a latency-bound GEMM with few
+// K steps per item); otherwise they are spread over the MFMAs after the first group.
+template <int RW, int CW, int KOPS, bool COPIES_FIRST>
 struct StepPlan {
   static constexpr int G = CW / 2, NM = 4 * RW * G, kCap = 6, kPer = 2;
   int t[NM][kCap];
@@ -152,13 +154,21 @@ struct StepPlan {
   constexpr StepPlan() : t{} {
     for (int m = 0; m < NM; m++)
       for (int c = 0; c < kCap; c++) t[m][c] = StepTask::kNone;
+    // the last group's fragments shortly before that group, so few loads are younger than them
+    const int def_at = (G - 1) * 4 * RW - 4 > 0 ? (G - 1) * 4 * RW - 4 : 0;
+    if (COPIES_FIRST) {
+      place(StepTask::kDef + 0, def_at);
+      place(StepTask::kDef + 1, def_at);
+      for (int i = 0; i < KOPS; i++) place(StepTask::kDma + i, 0);
+    }
     for (int r = 0; r < RW; r++) place(StepTask::kX + r, 0);
     place(StepTask::kWs, 0);
     for (int j = 0; j < CW - 2; j++) place(StepTask::kRel + j, (j / 2 + 1) * 4 * RW - 1);
-    for (int i = 0; i < KOPS; i++) place(StepTask::kDma + i, 4 * RW + i * (NM - 4 * RW) / KOPS);
-    // the last group's fragments shortly before that group, so few loads are younger than them
-    place(StepTask::kDef + 0, (G - 1) * 4 * RW - 4 > 0 ? (G - 1) * 4 * RW - 4 : 0);
-    place(StepTask::kDef + 1, (G - 1) * 4 * RW - 4 > 0 ? (G - 1) * 4 * RW - 4 : 0);
+    if (!COPIES_FIRST) {
+      for (int i = 0; i < KOPS; i++) place(StepTask::kDma + i, 4 * RW + i * (NM - 4 * RW) / KOPS);
+      place(StepTask::kDef + 0, def_at);
+      place(StepTask::kDef + 1, def_at);
+    }
   }
   // every task placed exactly once, the last group's fragments before that group
   constexpr bool valid() const {
@@ -435,7 +445,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
   typedef const __attribute__((address_space(3))) u32x4_t* vl16_t;
   typedef const __attribute__((address_space(3))) u32x2_t* vl8_t;
   typedef const __attribute__((address_space(3))) uint32_t* vl4_t;
-  using Plan = StepPlan<RW, CW, C::kOps>;
+  using Plan = StepPlan<RW, CW, C::kOps, !G1>;
   static constexpr Plan plan{};
   static_assert(plan.valid(), "step plan");
   i32x8_t xop[2][RW][kTerms];
@@ -691,7 +701,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
 }
 
 // y[t] = sum over the token's k pairs of the fp16 rows (times their block powers of two), fp32 sum in
-// slot order, bf16 output.  One thread per 8 output columns of a token.
+// slot order, bf16 output.  One thread per 8 output columns of a token; the rows of four pairs are
+// loaded before any is added, so four gathers per thread are in flight.
+MX_DEV void combine_add(float* s, const u32x4_t& v, int ex) {
+  const float f = __builtin_ldexpf(1.0f, ex);  // exact power of two (ex in [-127, 127])
+#pragma unroll
+  for (int q = 0; q < 8; q++) {
+    const uint16_t hb = (uint16_t)(v[q >> 1] >> (16 * (q & 1)));
+    s[q] += (float)__builtin_bit_cast(_Float16, hb) * f;
+  }
+}
+
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ o16, const uint8_t* __restrict__ osc,
                                                       const int32_t* __restrict__ pair_prow, uint16_t* __restrict__ y,
                                                       int64_t H, int k, int64_t n) {
@@ -699,15 +719,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t t = i / H8, c = (i - t * H8) * 8;
     float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; j++) {
+    int j = 0;
+    for (; j + 4 <= k; j += 4) {
+      u32x4_t v[4];
+      int ex[4];
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const int64_t r = pair_prow[t * k + j + u];
+        v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(o16 + r * H + c));
+        ex[u] = (int)osc[r * (H / 16) + c / 16] - 127;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; u++) combine_add(s, v[u], ex[u]);
+    }
+    for (; j < k; j++) {
       const int64_t r = pair_prow[t * k + j];
       const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(o16 + r * H + c));
-      const int ex = (int)osc[r * (H / 16) + c / 16] - 127;
-#pragma unroll
-      for (int q = 0; q < 8; q++) {
-        const uint16_t hb = (uint16_t)(v[q >> 1] >> (16 * (q & 1)));
-        s[q] += __builtin_ldexpf((float)__builtin_bit_cast(_Float16, hb), ex);
-      }
+      combine_add(s, v, (int)osc[r * (H / 16) + c / 16] - 127);
     }
     u32x4_t o;
 #pragma unroll
