@@ -29,23 +29,42 @@ MX_DEV uint32_t amax_bits32(const uint32_t* w) {  // 16 words = 32 bf16 -> large
 // scale < 7 <= 7.5, the E2M3 maximum, so no term saturates).  The remainder x - t0 is exact in bf16
 // (a bf16 value minus its own rounding to a coarser grid).  K is padded to a multiple of 64 with zero
 // blocks.  Also clears `zero` (nzero ints).
+//
+// A wave handles 64 consecutive blocks (block gi = token * nblk + b), lane l computing block l.  Its
+// global accesses are staged through LDS so that every load and store instruction covers 1 KB of
+// consecutive bytes: 16-byte chunk c = 64 j + l of the wave's 4 KB of x is loaded by lane l in load j and
+// written to LDS, lane l then reads its block's four chunks; the 48-byte slots go to LDS and leave as
+// three 1 KB stores (the slots of consecutive blocks are consecutive in xq).
+typedef float xf32x2_t __attribute__((ext_vector_type(2)));
+
 __global__ __launch_bounds__(256) void xprep_kernel(const uint16_t* __restrict__ x, int64_t ldx, int64_t H, int64_t nblk,
                                                     uint8_t* __restrict__ xq, uint8_t* __restrict__ xs,
                                                     int32_t* __restrict__ zero, int64_t nzero, int64_t n) {
+  __shared__ __attribute__((aligned(16))) uint8_t stage_in[4][4096];
+  __shared__ __attribute__((aligned(16))) uint8_t stage_out[4][64 * kSlot];
   GRID_STRIDE(i, nzero) zero[i] = 0;  // the routing histogram, cleared for the next launch
-  GRID_STRIDE(i, n) {
-    const int64_t t = i / nblk, b = i % nblk;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t hb = H / 32;  // real blocks per token
+  const int64_t nwaves = (n + 63) / 64;
+  for (int64_t wv = (int64_t)blockIdx.x * 4 + wave; wv < nwaves; wv += (int64_t)gridDim.x * 4) {
+    const int64_t g0 = wv * 64;
+    // coalesced loads: chunk c = 64 j + lane is part c % 4 of block c / 4
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int c = 64 * j + lane;
+      const int64_t gi = g0 + c / 4;
+      const int64_t t = gi / nblk, b = gi % nblk;
+      u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+      if (gi < n && b < hb)
+        v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(x + t * ldx + b * 32 + (c % 4) * 8));
+      *reinterpret_cast<u32x4_t*>(&stage_in[wave][c * 16]) = v;
+    }
+    __builtin_amdgcn_wave_barrier();  // the wave's LDS writes before its reads (single wave, in order)
     uint32_t w[16];
-    if (b < H / 32) {
-      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + t * ldx + b * 32);
 #pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const u32x4_t v = __builtin_nontemporal_load(src + j);
-        w[4 * j] = v[0]; w[4 * j + 1] = v[1]; w[4 * j + 2] = v[2]; w[4 * j + 3] = v[3];
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 16; j++) w[j] = 0;
+    for (int p = 0; p < 4; p++) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&stage_in[wave][lane * 64 + p * 16]);
+      w[4 * p] = v[0]; w[4 * p + 1] = v[1]; w[4 * p + 2] = v[2]; w[4 * p + 3] = v[3];
     }
     fp6x32_t tq[kTerms];
     uint32_t te[kTerms];
@@ -65,17 +84,28 @@ __global__ __launch_bounds__(256) void xprep_kernel(const uint16_t* __restrict__
         const auto deq = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(tq[term], sc);
 #pragma unroll
         for (int j = 0; j < 16; j++) {
+          // the remainder of a bf16 value is exact in fp32 (and in bf16); hardware conversion
           const float a = bf16_bits_to_f32(w[j] & 0xFFFFu) - deq[2 * j];
           const float c = bf16_bits_to_f32(w[j] >> 16) - deq[2 * j + 1];
-          w[j] = f32_to_bf16_bits(a) | (f32_to_bf16_bits(c) << 16);
+          w[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector((xf32x2_t){a, c}, bf16x2_t));
         }
       }
     }
-    u32x4_t* dst = reinterpret_cast<u32x4_t*>(xq + i * kSlot);
-    dst[0] = u32x4_t{tq[0][0], tq[0][1], tq[0][2], tq[0][3]};
-    dst[1] = u32x4_t{tq[0][4], tq[0][5], tq[1][0], tq[1][1]};
-    dst[2] = u32x4_t{tq[1][2], tq[1][3], tq[1][4], tq[1][5]};
-    reinterpret_cast<uint32_t*>(xs)[i] = te[0] | (te[1] << 8);
+    u32x4_t* sl = reinterpret_cast<u32x4_t*>(&stage_out[wave][lane * kSlot]);
+    sl[0] = u32x4_t{tq[0][0], tq[0][1], tq[0][2], tq[0][3]};
+    sl[1] = u32x4_t{tq[0][4], tq[0][5], tq[1][0], tq[1][1]};
+    sl[2] = u32x4_t{tq[1][2], tq[1][3], tq[1][4], tq[1][5]};
+    const int64_t gl = g0 + lane;
+    if (gl < n) reinterpret_cast<uint32_t*>(xs)[gl] = te[0] | (te[1] << 8);
+    __builtin_amdgcn_wave_barrier();
+    // coalesced stores: 16-byte chunk c = 64 j + lane of the wave's 3 KB of slots
+#pragma unroll
+    for (int j = 0; j < 3; j++) {
+      const int c = 64 * j + lane;
+      if (g0 + (c * 16) / kSlot < n)
+        *reinterpret_cast<u32x4_t*>(xq + g0 * kSlot + c * 16) = *reinterpret_cast<const u32x4_t*>(&stage_out[wave][c * 16]);
+    }
+    __builtin_amdgcn_wave_barrier();  // the next iteration's LDS writes after these reads
   }
 }
 
