@@ -57,13 +57,13 @@ MX_DEV u32x2_t ld8(const uint8_t* p) { return *reinterpret_cast<const u32x2_t*>(
 // barrier.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"  // M0 is listed as clobbered; nothing else here uses it
-MX_DEV uint32_t lds_addr_of(const void* lds_ptr) { return (uint32_t)(uintptr_t)(lds_vptr_t)lds_ptr; }
-MX_DEV void dma16(const void* g, uint8_t* lds_wave_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr_of(lds_wave_base));
+// lds_wave_base is an LDS byte address, uniform over the wave (it goes to M0).
+MX_DEV void dma16(const void* g, uint32_t lds_wave_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_wave_base);
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(m0) : "memory", "m0");
 }
-MX_DEV void dma4(const void* g, uint8_t* lds_wave_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr_of(lds_wave_base));
+MX_DEV void dma4(const void* g, uint32_t lds_wave_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_wave_base);
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(g), "s"(m0) : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -319,6 +319,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
   int32_t(*t_row)[kTab] = reinterpret_cast<int32_t(*)[kTab]>(smem + D * C::kStage);
   uint16_t(*t_b)[G1 ? 2 : 1][kBias] = reinterpret_cast<uint16_t(*)[G1 ? 2 : 1][kBias]>(smem + D * C::kStage + kTabRow);
   const int tid = threadIdx.x;
+  // LDS byte address of smem (address-space arithmetic from here on, no generic-pointer conversions)
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_vptr_t)smem;
   const int nkt = a.nkt, ncb = a.ncb;
   const int nx = ncb * kCB / NT;
   const int nblk = a.nblk;  // token slots per row of xq (first GEMM)
@@ -385,7 +387,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
   // Copy i (of kOps per wave) of stage `kt` of the item with sources `sr` into ring slot `slot`.
   auto issue_op = [&](const Src& sr, int kt, int slot, auto ic) __attribute__((always_inline)) {
     constexpr int i = decltype(ic)::value;
-    uint8_t* base = smem + slot * C::kStage;
+    const uint32_t base = smem_lds + slot * C::kStage;
     if constexpr (i < C::nW) {
       dma16(a.wq + (sr.wb + kt * (kCB * 1024) + i * 1024) + lane * 16, base + C::oW + (wave * C::nW + i) * 1024);
     } else if constexpr (i == C::nW) {
@@ -415,7 +417,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
     const uint8_t* rsrc = G1 ? reinterpret_cast<const uint8_t*>(a.prow_tok) : reinterpret_cast<const uint8_t*>(a.prow_w);
     {
       const int o = wave < kRowOps ? wave : 0;
-      dma4(rsrc + (int64_t)(prow0 + o * 64) * 4 + lane * 4, reinterpret_cast<uint8_t*>(&t_row[tb][o * 64]));
+      dma4(rsrc + (int64_t)(prow0 + o * 64) * 4 + lane * 4, smem_lds + D * C::kStage + (tb * kTab + o * 64) * 4);
     }
     if constexpr (BIAS) {
       constexpr int kBOps = kBias * 2 / 256;  // copies per bias half
@@ -429,7 +431,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
         const int half = o / kBOps, part = o % kBOps;
         int el = x * kBias + part * 128 + lane * 2;  // first of this lane's two entries
         el = el < len - 2 ? el : len - 2;
-        dma4(brow + half * len + el, reinterpret_cast<uint8_t*>(&t_b[tb][half][0]) + part * 256);
+        dma4(brow + half * len + el,
+             smem_lds + D * C::kStage + kTabRow + ((tb * (G1 ? 2 : 1) + half) * kBias) * 2 + part * 256);
       }
     }
   };
