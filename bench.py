@@ -31,7 +31,7 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 PEAK_FP4_TFLOPS = 10100.0  # MI355X dense MXFP4 / MXFP6 MFMA
 # the forward's stages as the library's events bracket them, and the kernels each stage launches
 STAGES = ["act_split", "route", "pair_sort", "gemm1_swiglu", "gemm2_weighted", "combine"]
-STAGE_KERNELS = ["xprep_kernel", "route_kernel", "scan_kernel + scatter_kernel", "grouped_gemm_kernel<G1=true>",
+STAGE_KERNELS = ["xprep_kernel", "route_kernel", "place_kernel", "grouped_gemm_kernel<G1=true>",
                  "grouped_gemm_kernel<G1=false>", "combine_kernel"]
 DTYPE = "mxfp4 (e2m1 + e8m0) weights x two-term e2m3 (fp6) activations on block-scaled MFMA, fp32 accumulate"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_prefill_gemm1_and_quantize.txt")

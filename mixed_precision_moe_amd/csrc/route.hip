@@ -4,11 +4,12 @@
 // [DEF: top-k routing of softmax(router logits) renormalized over the selected experts; the router
 //  sort/permute/gather step]
 //
-// Routing runs in three launches: route_kernel (top-k per token, counted into a per-block expert
-// histogram of kRouteTokens tokens), scan_kernel (one workgroup: prefix sums over
-// blocks and experts, the expert offsets, the padded row offsets and the M-tile list), scatter_kernel
-// (each block ranks its pairs per expert in token order and writes them to their rows).  The
-// resulting order is stable: pairs of one expert appear in increasing token order.
+// Routing runs in two launches: route_kernel (top-k per token, counted into a per-block expert
+// histogram of kRouteTokens tokens) and place_kernel (per block of tokens: prefix sums over blocks and
+// experts from the histogram, the block's pairs ranked per expert in token order and written to their
+// rows; the first workgroup also writes the expert offsets, the padded row offsets, the M-tile list and
+// the padding rows).  The resulting order is stable: pairs of one expert appear in increasing token
+// order.
 #include "common.h"
 
 namespace {
@@ -204,64 +205,69 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   }
 }
 
-// One workgroup of 1024 threads.  (1) Per expert, the total pair count and the exclusive prefix of
-// blkcnt over blocks (rewritten in place); (2) exclusive scans over experts of the counts, of the
-// counts padded to 32 and of the M tiles of BM rows; (3) offsets, padded offsets, the tile list, and
-// the padding rows of every expert plus 128 slack rows after the last one (pair -1, token 0,
-// weight 0), so a GEMM tile may read up to 128 rows past its expert's start.
-__global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ blkcnt, int nb, int E, int BM,
-                                                    int32_t* __restrict__ offsets, int32_t* __restrict__ poffsets,
-                                                    int4* __restrict__ tiles, int32_t* __restrict__ ntiles,
-                                                    int32_t* __restrict__ prow_pair, int32_t* __restrict__ prow_tok,
-                                                    float* __restrict__ prow_w) {
-  __shared__ int part[1024];
-  __shared__ int pin[1024];
+// Pair placement, one workgroup of 1024 threads per block of kRouteTokens tokens.  blkcnt[b][e] holds
+// the pairs of expert e among the tokens of block b (the routing histogram, read only here).
+//  (1) Every workgroup sums, per expert, the counts of the blocks before its own and of all blocks
+//      (threads split the blocks, partial sums meet in LDS), then scans over experts: the exclusive
+//      prefixes of the counts, of the counts padded to 32 and of the M tiles of BM rows.
+//  (2) Workgroup 0 also writes offsets, padded offsets, the tile list (expert, first padded row, valid
+//      rows) and the padding rows of every expert plus 128 slack rows after the last one (pair -1,
+//      token 0, weight 0), so a GEMM tile may read up to 128 rows past its expert's start.
+//  (3) The first wave (lane = token of the block) ranks each pair among the pairs of its expert in
+//      token order: (pairs of that expert in earlier blocks) + (earlier lanes of this block with that
+//      expert, from a 64-bit lane mask per expert), and writes the compact order (sorted_pairs, may be
+//      NULL), the padded rows (pair, token, routing weight) and each pair's padded row (pair_prow, may be
+//      NULL).  Padding rows and pair rows are disjoint, so the workgroups never write the same row.
+__global__ __launch_bounds__(1024) void place_kernel(const int32_t* __restrict__ ids, const float* __restrict__ wts,
+                                                     const int32_t* __restrict__ blkcnt, int64_t T, int nb, int k,
+                                                     int E, int BM, int32_t* __restrict__ offsets,
+                                                     int32_t* __restrict__ poffsets, int4* __restrict__ tiles,
+                                                     int32_t* __restrict__ ntiles, int32_t* __restrict__ sorted_pairs,
+                                                     int32_t* __restrict__ prow_pair, int32_t* __restrict__ prow_tok,
+                                                     float* __restrict__ prow_w, int32_t* __restrict__ pair_prow) {
+  __shared__ int part_pre[1024], part_tot[1024];
+  __shared__ int e_pre[1024], e_off[1024], e_poff[1024];
+  __shared__ uint32_t mlo[1024], mhi[1024];
   __shared__ int wsum[3][16];
+  __shared__ int slack0;  // first slack row (workgroup 0)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int blk = blockIdx.x;
   int es = 64;  // expert stride: power of two >= E, at least one wave
   while (es < E) es <<= 1;
   const int G = 1024 / es;  // block groups
   const int e = tid % es, grp = tid / es;
   const int per = (nb + G - 1) / G;
   const int b0 = min(nb, grp * per), b1 = min(nb, b0 + per);
-  // block counts of this thread, 16 independent loads at a time
+  for (int i = tid; i < E; i += 1024) { mlo[i] = 0; mhi[i] = 0; }
+  // (1) partial sums over this thread's blocks, 16 independent loads at a time
   constexpr int kBatch = 16;
-  int s = 0;
+  int s_pre = 0, s_tot = 0;
   if (e < E)
-    for (int b = b0; b < b1; b += kBatch) {
+    for (int bb = b0; bb < b1; bb += kBatch) {
       int v[kBatch];
 #pragma unroll
-      for (int i = 0; i < kBatch; i++) v[i] = b + i < b1 ? blkcnt[(int64_t)(b + i) * E + e] : 0;
-#pragma unroll
-      for (int i = 0; i < kBatch; i++) s += v[i];
-    }
-  part[tid] = s;
-  __syncthreads();
-  int base = 0, total = 0;
-  for (int q = 0; q < G; q++) {
-    const int v = part[q * es + e];
-    if (q < grp) base += v;
-    total += v;
-  }
-  if (e < E)
-    for (int b = b0; b < b1; b += kBatch) {
-      int v[kBatch];
-#pragma unroll
-      for (int i = 0; i < kBatch; i++) v[i] = b + i < b1 ? blkcnt[(int64_t)(b + i) * E + e] : 0;
+      for (int i = 0; i < kBatch; i++) v[i] = bb + i < b1 ? blkcnt[(int64_t)(bb + i) * E + e] : 0;
 #pragma unroll
       for (int i = 0; i < kBatch; i++) {
-        if (b + i < b1) blkcnt[(int64_t)(b + i) * E + e] = base;
-        base += v[i];
+        s_tot += v[i];
+        s_pre += bb + i < blk ? v[i] : 0;
       }
     }
-  // scans over experts: thread e of group 0 (tid == e) holds expert e, every other thread zeros
-  int v0 = 0, v1 = 0, v2 = 0;
+  part_pre[tid] = s_pre;
+  part_tot[tid] = s_tot;
+  __syncthreads();
+  int v0 = 0, v1 = 0, v2 = 0, pre = 0;
   if (grp == 0 && e < E) {
+    int total = 0;
+    for (int q = 0; q < G; q++) {
+      pre += part_pre[q * es + e];
+      total += part_tot[q * es + e];
+    }
     v0 = total;
     v1 = (total + 31) & ~31;
     v2 = (total + BM - 1) / BM;
   }
-  // inclusive wave scans, then across waves
+  // scans over experts: thread e of group 0 (tid == e) holds expert e, every other thread zeros
   int x0 = v0, x1 = v1, x2 = v2;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -273,10 +279,14 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ blkcnt
   int p0 = 0, p1 = 0, p2 = 0;
   for (int q = 0; q < wave; q++) { p0 += wsum[0][q]; p1 += wsum[1][q]; p2 += wsum[2][q]; }
   x0 += p0; x1 += p1; x2 += p2;  // inclusive scans over threads 0..tid
-  pin[tid] = x1;
-  __syncthreads();
   if (grp == 0 && e < E) {
-    const int off = x0 - v0, poff = x1 - v1, toff = x2 - v2;
+    e_pre[e] = pre;
+    e_off[e] = x0 - v0;
+    e_poff[e] = x1 - v1;
+  }
+  // (2) the tables, once
+  if (blk == 0 && grp == 0 && e < E) {
+    const int off = x0 - v0, poff = x1 - v1, toff = x2 - v2, total = v0;
     offsets[e] = off;
     poffsets[e] = poff;
     for (int i = 0; i < v2; i++) tiles[toff + i] = make_int4(e, poff + i * BM, min(BM, total - i * BM), 0);
@@ -289,56 +299,60 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ blkcnt
       offsets[E] = x0;
       poffsets[E] = x1;
       *ntiles = x2;
+      slack0 = x1;
     }
   }
-  // slack rows after the last expert
-  const int ptot = pin[E - 1];
-  if (tid < 128) {
-    prow_pair[ptot + tid] = -1;
-    prow_tok[ptot + tid] = 0;
-    prow_w[ptot + tid] = 0.f;
+  __syncthreads();
+  if (blk == 0 && tid < 128) {  // slack rows after the last expert
+    const int r = slack0 + tid;
+    prow_pair[r] = -1;
+    prow_tok[r] = 0;
+    prow_w[r] = 0.f;
   }
-}
-
-// One wave per block of kRouteTokens tokens (lane = token): rank of each pair among the pairs of its
-// expert in token order = (pairs of that expert in earlier blocks) + (earlier lanes of this block with
-// that expert), from a 64-bit lane mask per expert.  Writes the compact order (sorted_pairs, may be
-// NULL), the padded rows (pair, token, routing weight) and each pair's padded row (pair_prow, may be
-// NULL).
-__global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__ ids, const float* __restrict__ wts,
-                                                     const int32_t* __restrict__ blkcnt, int64_t T, int k, int E,
-                                                     const int32_t* __restrict__ offsets,
-                                                     const int32_t* __restrict__ poffsets,
-                                                     int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ prow_pair,
-                                                     int32_t* __restrict__ prow_tok, float* __restrict__ prow_w,
-                                                     int32_t* __restrict__ pair_prow) {
-  __shared__ uint32_t mlo[1024], mhi[1024];
-  const int lane = threadIdx.x;
-  const int64_t b = blockIdx.x;
-  for (int i = lane; i < E; i += 64) { mlo[i] = 0; mhi[i] = 0; }
   __syncthreads();
-  const int64_t t = b * kRouteTokens + lane;
-  const bool live = t < T;
-  if (live)
-    for (int j = 0; j < k; j++) {
-      const int ex = ids[t * k + j];
-      if (lane < 32) atomicOr(&mlo[ex], 1u << lane);
-      else atomicOr(&mhi[ex], 1u << (lane - 32));
-    }
-  __syncthreads();
-  if (live) {
-    const uint64_t lt = (1ull << lane) - 1ull;
-    for (int j = 0; j < k; j++) {
-      const int ex = ids[t * k + j];
-      const uint64_t m = ((uint64_t)mhi[ex] << 32) | mlo[ex];
-      const int rank = blkcnt[b * E + ex] + __popcll(m & lt);
-      const int32_t pair = (int32_t)(t * k + j);
-      if (sorted_pairs) sorted_pairs[offsets[ex] + rank] = pair;
-      const int r = poffsets[ex] + rank;
-      prow_pair[r] = pair;
-      prow_tok[r] = (int32_t)t;
-      prow_w[r] = wts[pair];
-      if (pair_prow) pair_prow[pair] = r;
+  // (3) ranks within the block (the pair loads go out four at a time: k is a runtime count)
+  if (wave == 0) {
+    const int64_t t = (int64_t)blk * kRouteTokens + lane;
+    const bool live = t < T;
+    if (live)
+      for (int j0 = 0; j0 < k; j0 += 4) {
+        int exs[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) exs[u] = j0 + u < k ? ids[t * k + j0 + u] : -1;
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+          if (exs[u] < 0) continue;
+          if (lane < 32) atomicOr(&mlo[exs[u]], 1u << lane);
+          else atomicOr(&mhi[exs[u]], 1u << (lane - 32));
+        }
+      }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+    if (live) {
+      const uint64_t lt = (1ull << lane) - 1ull;
+      for (int j0 = 0; j0 < k; j0 += 4) {
+        int exs[4];
+        float ws[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+          exs[u] = j0 + u < k ? ids[t * k + j0 + u] : -1;
+          ws[u] = j0 + u < k ? wts[t * k + j0 + u] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+          const int ex = exs[u];
+          if (ex < 0) continue;
+          const uint64_t m = ((uint64_t)mhi[ex] << 32) | mlo[ex];
+          const int rank = e_pre[ex] + __popcll(m & lt);
+          const int32_t pair = (int32_t)(t * k + j0 + u);
+          if (sorted_pairs) sorted_pairs[e_off[ex] + rank] = pair;
+          const int r = e_poff[ex] + rank;
+          prow_pair[r] = pair;
+          prow_tok[r] = (int32_t)t;
+          prow_w[r] = ws[u];
+          if (pair_prow) pair_prow[pair] = r;
+        }
+      }
     }
   }
 }
@@ -391,10 +405,8 @@ int launch_place(const int32_t* ids, const float* w, int32_t* blkcnt, int64_t T,
                  int32_t* poffsets, int32_t* sorted_pairs, int32_t* prow_pair, int32_t* prow_tok, float* prow_w,
                  int32_t* pair_prow, void* tiles, int32_t* ntiles, hipStream_t stream) {
   const int nb = (int)cdiv(T, kRouteTokens);
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream, blkcnt, nb, E, BM, offsets, poffsets, (int4*)tiles,
-                     ntiles, prow_pair, prow_tok, prow_w);
-  if (nb > 0)
-    hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)nb), dim3(64), 0, stream, ids, w, blkcnt, T, k, E, offsets,
-                       poffsets, sorted_pairs, prow_pair, prow_tok, prow_w, pair_prow);
+  // at least one workgroup, which writes the tables even when there are no tokens
+  hipLaunchKernelGGL(place_kernel, dim3((unsigned)(nb > 0 ? nb : 1)), dim3(1024), 0, stream, ids, w, blkcnt, T, nb, k, E,
+                     BM, offsets, poffsets, (int4*)tiles, ntiles, sorted_pairs, prow_pair, prow_tok, prow_w, pair_prow);
   return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
 }
