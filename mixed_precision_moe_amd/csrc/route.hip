@@ -118,24 +118,16 @@ MX_DEV uint32_t logit_key(float l) {
 }
 MX_DEV float key_logit(uint32_t k) { return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k); }
 
-// Wave-wide maximum of a 64-bit value, uniform result: DPP exchanges inside each row of 16 lanes (xor 1,
-// xor 2, rotate 4, rotate 8), then the four row maxima through scalar lane reads.
-MX_DEV uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-#define DPP_U64(v, ctrl)                                                                                  \
-  (((uint64_t)(uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)((v) >> 32), ctrl, 0xF, 0xF, false) << 32) | \
-   (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v), ctrl, 0xF, 0xF, false))
-MX_DEV uint64_t wave_max_u64(uint64_t v) {
-  v = max_u64(v, DPP_U64(v, 0xB1));   // quad_perm [1,0,3,2]
-  v = max_u64(v, DPP_U64(v, 0x4E));   // quad_perm [2,3,0,1]
-  v = max_u64(v, DPP_U64(v, 0x124));  // row_ror:4
-  v = max_u64(v, DPP_U64(v, 0x128));  // row_ror:8
-  uint64_t r = 0;
+// Wave-wide maximum, uniform result: DPP max inside each row of 16 lanes (xor 1, xor 2, rotate 4,
+// rotate 8), then the four row maxima through scalar lane reads.
+MX_DEV uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));  // row_ror:4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));  // row_ror:8
+  uint32_t r = 0;
 #pragma unroll
-  for (int row = 0; row < 4; row++) {
-    const uint64_t x = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 16 * row) << 32) |
-                       (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 16 * row);
-    r = max_u64(r, x);
-  }
+  for (int row = 0; row < 4; row++) r = max(r, (uint32_t)__builtin_amdgcn_readlane((int)v, 16 * row));
   return r;
 }
 MX_DEV float wave_sum_f32(float v) {
@@ -149,8 +141,9 @@ MX_DEV float wave_sum_f32(float v) {
   return r;
 }
 
-// One wave per token: k rounds of a wave-wide arg-max over 64-bit keys (logit key, inverted expert
-// index), so equal logits go to the lower expert index; the winner's logit is read back from its key.
+// One wave per token: k rounds of a wave-wide maximum of the logit keys, the winner being the lowest
+// expert index holding that key (a ballot per lane slot), so equal logits go to the lower expert
+// index; the winner's logit is read back from its key.
 // Softmax weights of the selected experts (renormalized over them, or over all experts).  Each pair
 // also counts into blkcnt[token / kRouteTokens][expert] (zeroed beforehand), the per-block histogram of
 // the counting sort.  NPL logits per lane (E <= 64 * NPL).
@@ -162,22 +155,27 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // uniform per wave
   float val[NPL];
-  uint64_t key[NPL];
+  uint32_t key[NPL];  // 0 = absent or already selected (no logit maps to 0)
 #pragma unroll
   for (int j = 0; j < NPL; j++) {
     const int idx = lane + 64 * j;
     val[j] = idx < E ? logits[t * E + idx] : 0.f;
-    key[j] = idx < E ? ((uint64_t)logit_key(val[j]) << 32) | (uint32_t)(~idx) : 0;
+    key[j] = idx < E ? logit_key(val[j]) : 0u;
   }
   int my_id = 0;
   float my_l = 0.f, lmax = 0.f;
   for (int r = 0; r < k; r++) {
-    uint64_t best = 0;
+    uint32_t best = 0;
 #pragma unroll
-    for (int j = 0; j < NPL; j++) best = max_u64(best, key[j]);
-    best = wave_max_u64(best);
-    const int id = (int)(~(uint32_t)best);
-    const float wl = key_logit((uint32_t)(best >> 32));
+    for (int j = 0; j < NPL; j++) best = max(best, key[j]);
+    best = wave_max_u32(best);
+    int id = -1;
+#pragma unroll
+    for (int j = 0; j < NPL; j++) {
+      const uint64_t hit = __ballot(key[j] == best);
+      if (id < 0 && hit != 0) id = 64 * j + __ffsll((unsigned long long)hit) - 1;
+    }
+    const float wl = key_logit(best);
 #pragma unroll
     for (int j = 0; j < NPL; j++)
       if (lane + 64 * j == id) key[j] = 0;
@@ -226,7 +224,7 @@ __global__ __launch_bounds__(1024) void place_kernel(const int32_t* __restrict__
                                                      int32_t* __restrict__ prow_pair, int32_t* __restrict__ prow_tok,
                                                      float* __restrict__ prow_w, int32_t* __restrict__ pair_prow) {
   __shared__ int part_pre[1024], part_tot[1024];
-  __shared__ int e_pre[1024], e_off[1024], e_poff[1024];
+  __shared__ int e_pre[1024], e_off[1024], e_poff[1024], e_tot[1024], e_toff[1024];
   __shared__ uint32_t mlo[1024], mhi[1024];
   __shared__ int wsum[3][16];
   __shared__ int slack0;  // first slack row (workgroup 0)
@@ -283,18 +281,14 @@ __global__ __launch_bounds__(1024) void place_kernel(const int32_t* __restrict__
     e_pre[e] = pre;
     e_off[e] = x0 - v0;
     e_poff[e] = x1 - v1;
+    e_tot[e] = v0;
+    e_toff[e] = x2 - v2;
   }
-  // (2) the tables, once
+  // (2) the tables, once: offsets by expert thread, then each wave takes experts wave, wave + 16, ...
+  // and writes their tiles and padding rows with one lane per tile or row
   if (blk == 0 && grp == 0 && e < E) {
-    const int off = x0 - v0, poff = x1 - v1, toff = x2 - v2, total = v0;
-    offsets[e] = off;
-    poffsets[e] = poff;
-    for (int i = 0; i < v2; i++) tiles[toff + i] = make_int4(e, poff + i * BM, min(BM, total - i * BM), 0);
-    for (int r = poff + total; r < poff + v1; r++) {
-      prow_pair[r] = -1;
-      prow_tok[r] = 0;
-      prow_w[r] = 0.f;
-    }
+    offsets[e] = x0 - v0;
+    poffsets[e] = x1 - v1;
     if (e == E - 1) {
       offsets[E] = x0;
       poffsets[E] = x1;
@@ -303,13 +297,25 @@ __global__ __launch_bounds__(1024) void place_kernel(const int32_t* __restrict__
     }
   }
   __syncthreads();
-  if (blk == 0 && tid < 128) {  // slack rows after the last expert
-    const int r = slack0 + tid;
-    prow_pair[r] = -1;
-    prow_tok[r] = 0;
-    prow_w[r] = 0.f;
+  if (blk == 0) {
+    for (int ee = wave; ee < E; ee += 16) {
+      const int poff = e_poff[ee], total = e_tot[ee], toff = e_toff[ee];
+      const int ntl = (total + BM - 1) / BM, pad = ((total + 31) & ~31) - total;
+      for (int i = lane; i < ntl; i += 64) tiles[toff + i] = make_int4(ee, poff + i * BM, min(BM, total - i * BM), 0);
+      if (lane < pad) {
+        const int r = poff + total + lane;
+        prow_pair[r] = -1;
+        prow_tok[r] = 0;
+        prow_w[r] = 0.f;
+      }
+    }
+    if (tid < 128) {  // slack rows after the last expert
+      const int r = slack0 + tid;
+      prow_pair[r] = -1;
+      prow_tok[r] = 0;
+      prow_w[r] = 0.f;
+    }
   }
-  __syncthreads();
   // (3) ranks within the block (the pair loads go out four at a time: k is a runtime count)
   if (wave == 0) {
     const int64_t t = (int64_t)blk * kRouteTokens + lane;
