@@ -155,9 +155,11 @@ int moe_mxfp4_route(const float* router_logits, int64_t T, int32_t E, int32_t to
  * router_logits device fp32 [T, E].  topk_ids / topk_w: optional device outputs [T, top_k].
  * workspace device, >= moe_mxfp4_workspace_bytes(d, T, top_k), 256-byte aligned.
  * Arithmetic: activations enter the block-scaled MFMA as two E2M3 (FP6) terms with E8M0 scales
- * per 32 elements (x = hi + lo), weights as E2M1 with their E8M0 scales, fp32 accumulation; the
- * SwiGLU output is rounded to bf16 and split the same way; the combine accumulates in fp32 with
- * atomics (summation order not fixed), then rounds to bf16.
+ * per 32 elements (x = t0 + t1, t1 the rounding of the remainder), weights as E2M1 with their E8M0
+ * scales, fp32 accumulation; the SwiGLU output stays fp32 and is split into two terms the same way;
+ * each pair's weighted expert output is kept as fp16 with a power-of-two scale per 16 columns, and the
+ * combine sums a token's k rows in fp32 in slot order, then rounds to bf16.  The result is
+ * deterministic: repeated calls give the same bits.
  */
 size_t moe_mxfp4_workspace_bytes(const mxfp4_moe_dims* d, int64_t T, int32_t top_k);
 int moe_mxfp4_forward(const mxfp4_moe_dims* d, const void* packed_gfx950, const void* x_bf16, int64_t T, int64_t ldx,
@@ -166,9 +168,9 @@ int moe_mxfp4_forward(const mxfp4_moe_dims* d, const void* packed_gfx950, const 
 
 /* Same as moe_mxfp4_forward, and records events[i] (hipEvent_t passed as void*, created by the caller)
  * on `stream` at stage boundaries: events[0] before the first launch, then after each stage in the
- * order activation split, routing, pair sort/tile schedule, first GEMM (+SwiGLU), second GEMM
- * (+combine), bf16 output -- 7 events in all.  Only the first n_events are recorded.  For per-stage
- * timing (measurement); the computation is identical. */
+ * order activation split, routing, pair placement/tile schedule, first GEMM (+SwiGLU), second GEMM
+ * (weighted rows), combine (bf16 output) -- 7 events in all.  Only the first n_events are recorded.
+ * For per-stage timing (measurement); the computation is identical. */
 int moe_mxfp4_forward_profiled(const mxfp4_moe_dims* d, const void* packed_gfx950, const void* x_bf16, int64_t T,
                                int64_t ldx, const float* router_logits, int32_t top_k, int32_t renormalize,
                                void* y_bf16, int32_t* topk_ids, float* topk_w, void* workspace, size_t workspace_bytes,

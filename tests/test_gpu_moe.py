@@ -49,9 +49,10 @@ def run_case(cfg, sample=None, ldx_pad=0, seed=0):
                             tokens=rows)
     ratio, _ = assert_moe_close(y_gpu, y_ref, rows, cfg.name)
     print(f"  max|err|/rms = {ratio:.3e}", flush=True)
-    # repeated calls on the same workspace give the same result up to the atomic summation order
+    # the path is deterministic (no atomics on values, a fixed summation order in the combine): a second
+    # call on the same workspace gives the same bits
     y2 = bf16_host_f64(layer(xd, ld))
-    assert_moe_close(y2, y_ref, rows, cfg.name + " (second call)")
+    np.testing.assert_array_equal(y2, y_gpu)
     return ratio
 
 
