@@ -638,13 +638,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
       // tile; after one exchange of lane halves, half h holds the 16 consecutive columns 16h .. 16h+15
       // of the row: one block with a power-of-two scale (largest magnitude in [2^14, 2^15) after
       // scaling), stored as 32 bytes of fp16 plus the exponent byte.  Rows of a row group past the
-      // expert's pairs are padding rows of that expert (weight 0), written like the others.
+      // expert's pairs are padding rows of that expert, which nothing reads: their lanes store nothing.
       const int m = lane & 31, h = lane >> 5;
 #pragma unroll
       for (int r = 0; r < RW; r++) {
         const int rgl = wr * RW + r;
         if (rgl * 32 >= nrows) continue;
         const float wt = __builtin_bit_cast(float, t_row[tb][rgl * 32 + m]);
+        const bool real = rgl * 32 + m < nrows;
         const int64_t prow = prow0 + rgl * 32 + m;
         uint16_t* orow = a.o16 + prow * a.H;
         uint8_t* srow = a.osc + prow * (a.H / 16);
@@ -688,10 +689,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
               const f16x2_t e = __builtin_convertvector((f32x2_t){v[2 * c] * f, v[2 * c + 1] * f}, f16x2_t);
               hv[c] = __builtin_bit_cast(uint32_t, e);
             }
-            u32x4_t* op = reinterpret_cast<u32x4_t*>(orow + nt * 32 + 16 * h);
-            op[0] = u32x4_t{hv[0], hv[1], hv[2], hv[3]};
-            op[1] = u32x4_t{hv[4], hv[5], hv[6], hv[7]};
-            srow[nt * 2 + h] = (uint8_t)(ex + 127);
+            if (real) {
+              u32x4_t* op = reinterpret_cast<u32x4_t*>(orow + nt * 32 + 16 * h);
+              op[0] = u32x4_t{hv[0], hv[1], hv[2], hv[3]};
+              op[1] = u32x4_t{hv[4], hv[5], hv[6], hv[7]};
+              srow[nt * 2 + h] = (uint8_t)(ex + 127);
+            }
           }
           __builtin_amdgcn_sched_barrier(0);
         }
