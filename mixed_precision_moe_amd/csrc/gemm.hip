@@ -30,7 +30,9 @@
 // with LDS DMA (global_load_lds: no registers, no address math beyond the source) into a ring of D
 // stages: every wave issues the same number of copies per stage, waits for its own with vmcnt and one
 // barrier per step publishes the stage.  Operand fragments of step kt+1 are read from LDS while the
-// MFMAs of step kt run.  Work items (M tile, column position) are dealt to XCDs in contiguous ranges
+// MFMAs of step kt run: a fixed plan (StepPlan) orders each step's MFMAs and puts after each MFMA its
+// share of the fragment loads and copies, so their instructions issue while the matrix core works.
+// Work items (M tile, column position) are dealt to XCDs in contiguous ranges
 // so the column positions of one M tile (same gathered tokens) and consecutive tiles of one expert
 // (same weights) share an XCD's L2.
 #include <type_traits>
@@ -45,8 +47,6 @@ typedef __attribute__((address_space(3))) void* lds_vptr_t;
 constexpr int kFp4 = 4, kFp6 = 2;  // MFMA operand format codes (E2M1, E2M3)
 constexpr int kXcds = 8;           // workgroup b runs on XCD b % 8
 
-MX_DEV u32x4_t ld16(const uint8_t* p) { return *reinterpret_cast<const u32x4_t*>(p); }
-MX_DEV u32x2_t ld8(const uint8_t* p) { return *reinterpret_cast<const u32x2_t*>(p); }
 
 // LDS DMA: lane i copies 16 (or 4) bytes from its global address to lds_wave_base + i * 16 (or 4).
 // (Sub-dword copies still occupy a dword per lane in LDS, so every copied record here is a dword or
@@ -186,8 +186,6 @@ struct StepPlan {
 
 typedef const __attribute__((address_space(3))) uint16_t lds_u16;
 typedef const __attribute__((address_space(3))) uint8_t* lds_u8;
-typedef const __attribute__((address_space(3))) int32_t lds_i32;
-typedef const __attribute__((address_space(3))) float lds_f32;
 
 // Exchanges lane halves: returns {lanes 0-31 of x, then lanes 0-31 of y} and {lanes 32-63 of x, then
 // lanes 32-63 of y} (one v_permlane32_swap).
@@ -445,9 +443,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
   // form the tuples.  Activation fragments and
   // weight scales are double-buffered across steps ([P], P a compile-time parity); a weight fragment
   // is reloaded for the next step after the last MFMA that uses it.
-  typedef const __attribute__((address_space(3))) u32x4_t* vl16_t;
-  typedef const __attribute__((address_space(3))) u32x2_t* vl8_t;
-  typedef const __attribute__((address_space(3))) uint32_t* vl4_t;
+  typedef const __attribute__((address_space(3))) u32x4_t* lds16_p;
+  typedef const __attribute__((address_space(3))) u32x2_t* lds8_p;
+  typedef const __attribute__((address_space(3))) uint32_t* lds4_p;
   using Plan = StepPlan<RW, CW, C::kOps, !G1>;
   static constexpr Plan plan{};
   static_assert(plan.valid(), "step plan");
@@ -463,22 +461,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
     asm("" : "+v"(xp));
     lds_u8 xp1 = xp + 24;
     asm("" : "+v"(xp1));
-    const u32x4_t a4 = *(vl16_t)xp;
-    const u32x2_t a2 = *(vl8_t)(xp + 16);
-    const u32x2_t b2 = *(vl8_t)xp1;
-    const u32x4_t b4 = *(vl16_t)(xp1 + 8);
+    const u32x4_t a4 = *(lds16_p)xp;
+    const u32x2_t a2 = *(lds8_p)(xp + 16);
+    const u32x2_t b2 = *(lds8_p)xp1;
+    const u32x4_t b4 = *(lds16_p)(xp1 + 8);
     xop[P][r][0] = i32x8_t{(int)a4[0], (int)a4[1], (int)a4[2], (int)a4[3], (int)a2[0], (int)a2[1], 0, 0};
     xop[P][r][1] = i32x8_t{(int)b2[0], (int)b2[1], (int)b4[0], (int)b4[1], (int)b4[2], (int)b4[3], 0, 0};
-    xsc[P][r] = *(vl4_t)(lds_u8)(base + C::oXS + (wr * RW + r) * 256 + lane * 4);
+    xsc[P][r] = *(lds4_p)(lds_u8)(base + C::oXS + (wr * RW + r) * 256 + lane * 4);
   };
   auto load_w = [&](const uint8_t* base, int j) __attribute__((always_inline)) {
-    w[j] = *(vl16_t)(lds_u8)(base + C::oW + (wc * CW + j) * 1024 + lane * 16);
+    w[j] = *(lds16_p)(lds_u8)(base + C::oW + (wc * CW + j) * 1024 + lane * 16);
   };
   auto load_ws = [&](const uint8_t* base, auto pc) __attribute__((always_inline)) {
     constexpr int P = decltype(pc)::value;
 #pragma unroll
     for (int j4 = 0; j4 < CW / 4; j4++)
-      wsc[P][j4] = *(vl4_t)(lds_u8)(base + C::oWS + lane * 16 + jj0 + wc * CW + j4 * 4);
+      wsc[P][j4] = *(lds4_p)(lds_u8)(base + C::oWS + lane * 16 + jj0 + wc * CW + j4 * 4);
   };
 
   // MFMA m of a step (the order of StepPlan).  Each is pinned by an ordered use of its accumulator:
