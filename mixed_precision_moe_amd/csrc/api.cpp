@@ -25,9 +25,10 @@ int launch_xprep(const void* x, int64_t T, int64_t ldx, const MoeGeom& g, void* 
 int launch_zero_i32(int32_t* p, int64_t n, hipStream_t stream);
 int launch_route(const float* logits, int64_t T, int E, int k, int renormalize, int32_t* ids, float* w,
                  int32_t* blkcnt, hipStream_t stream);
-int launch_place(const int32_t* ids, const float* w, int32_t* blkcnt, int64_t T, int k, int E, int BM, int32_t* offsets,
-                 int32_t* poffsets, int32_t* sorted_pairs, int32_t* prow_pair, int32_t* prow_tok, float* prow_w,
-                 int32_t* pair_prow, void* tiles, int32_t* ntiles, hipStream_t stream);
+int launch_place(const int32_t* ids, const float* w, int32_t* blkcnt, int64_t T, int k, int E, int BM, int BM2,
+                 int32_t* offsets, int32_t* poffsets, int32_t* sorted_pairs, int32_t* prow_pair, int32_t* prow_tok,
+                 float* prow_w, int32_t* pair_prow, void* tiles, int32_t* ntiles, void* tiles2, int32_t* ntiles2,
+                 hipStream_t stream);
 int launch_gemm1(int NRG, const GemmArgs& a, int64_t max_tiles, hipStream_t stream);
 int launch_gemm2(int NRG, const GemmArgs& a, int64_t max_tiles, hipStream_t stream);
 int launch_combine(const uint16_t* o16, const uint8_t* osc, const int32_t* pair_prow, void* y, int64_t T, int64_t H, int k,
@@ -81,12 +82,19 @@ size_t standard_offsets(const mxfp4_moe_dims* d, uint32_t layout, size_t off[6])
   return p;
 }
 
-// Row groups of 32 per GEMM M tile from the mean rows per expert.
-int choose_nrg(int64_t P, int64_t E) {
+// Row groups of 32 per M tile of the first GEMM, from the mean rows per expert.
+int choose_nrg1(int64_t P, int64_t E) {
   const int64_t avg = P / (E > 0 ? E : 1);
   if (avg < 48) return 1;
   if (avg < 160) return 2;
   return 4;
+}
+
+// The same for the second GEMM, whose 64-row tiles measured faster than 128-row ones at every load
+// tried (its items are short, 12 K steps at I = 768, and bound by copy latency).
+int choose_nrg2(int64_t P, int64_t E) {
+  const int64_t avg = P / (E > 0 ? E : 1);
+  return avg < 48 ? 1 : 2;
 }
 
 struct RouteWs {
@@ -254,9 +262,9 @@ MX_API int moe_mxfp4_route(const float* router_logits, int64_t T, int32_t E, int
   int32_t* blkcnt = (int32_t*)(ws + w.blkcnt);
   if ((st = launch_zero_i32(blkcnt, cdiv(T, kRouteTokens) * E, S(stream)))) return st;
   if ((st = launch_route(router_logits, T, E, top_k, renormalize, topk_ids, topk_w, blkcnt, S(stream)))) return st;
-  return launch_place(topk_ids, topk_w, blkcnt, T, top_k, E, 32, expert_offsets, (int32_t*)(ws + w.poffsets),
+  return launch_place(topk_ids, topk_w, blkcnt, T, top_k, E, 32, 32, expert_offsets, (int32_t*)(ws + w.poffsets),
                       sorted_pairs, (int32_t*)(ws + w.prow_pair), (int32_t*)(ws + w.prow_tok), (float*)(ws + w.prow_w),
-                      nullptr, ws + w.tiles, (int32_t*)(ws + w.ntiles), S(stream));
+                      nullptr, ws + w.tiles, (int32_t*)(ws + w.ntiles), nullptr, nullptr, S(stream));
 }
 
 MX_API size_t moe_mxfp4_workspace_bytes(const mxfp4_moe_dims* d, int64_t T, int32_t top_k) {
@@ -286,7 +294,7 @@ static int forward_impl(const mxfp4_moe_dims* d, const void* packed_gfx950, cons
   const int64_t P = T * top_k;
   int32_t* ids = topk_ids ? topk_ids : (int32_t*)(ws + w.ids);
   float* wts = topk_w ? topk_w : (float*)(ws + w.w);
-  const int NRG = choose_nrg(P, g.E);
+  const int NRG1 = choose_nrg1(P, g.E), NRG2 = choose_nrg2(P, g.E);
   int ev = 0;
   auto mark = [&]() -> int {
     if (ev < n_events && hipEventRecord((hipEvent_t)events[ev], s) != hipSuccess) return MXFP4_ERR_DEVICE;
@@ -301,10 +309,10 @@ static int forward_impl(const mxfp4_moe_dims* d, const void* packed_gfx950, cons
   if ((st = launch_route(router_logits, T, (int)g.E, top_k, renormalize, ids, wts, (int32_t*)(ws + w.blkcnt), s)) ||
       (st = mark()))
     return st;
-  if ((st = launch_place(ids, wts, (int32_t*)(ws + w.blkcnt), T, top_k, (int)g.E, 32 * NRG, (int32_t*)(ws + w.offsets),
-                         (int32_t*)(ws + w.poffsets), nullptr, (int32_t*)(ws + w.prow_pair),
+  if ((st = launch_place(ids, wts, (int32_t*)(ws + w.blkcnt), T, top_k, (int)g.E, 32 * NRG1, 32 * NRG2,
+                         (int32_t*)(ws + w.offsets), (int32_t*)(ws + w.poffsets), nullptr, (int32_t*)(ws + w.prow_pair),
                          (int32_t*)(ws + w.prow_tok), (float*)(ws + w.prow_w), (int32_t*)(ws + w.pair_prow),
-                         ws + w.tiles, (int32_t*)(ws + w.ntiles), s)) ||
+                         ws + w.tiles, (int32_t*)(ws + w.ntiles), ws + w.tiles2, (int32_t*)(ws + w.ntiles2), s)) ||
       (st = mark()))
     return st;
   const uint8_t* blob = (const uint8_t*)packed_gfx950;
@@ -313,7 +321,7 @@ static int forward_impl(const mxfp4_moe_dims* d, const void* packed_gfx950, cons
                  (const float*)(ws + w.prow_w), (const int4*)(ws + w.tiles), (const int32_t*)(ws + w.ntiles),
                  ws + w.actq, ws + w.acts, nullptr, nullptr, (int32_t)g.nkt1, (int32_t)g.ncb1, (int32_t)g.nit,
                  (int32_t)g.nkt2, (int32_t)(2 * g.nkt1), (int32_t)g.I, (int32_t)g.H};
-  if ((st = launch_gemm1(NRG, a1, w.max_tiles, s)) || (st = mark())) return st;
+  if ((st = launch_gemm1(NRG1, a1, w.max_tiles, s)) || (st = mark())) return st;
   GemmArgs a2 = a1;
   a2.wq = blob + o.w2q;
   a2.ws = blob + o.w2s;
@@ -325,7 +333,9 @@ static int forward_impl(const mxfp4_moe_dims* d, const void* packed_gfx950, cons
   a2.nkt = (int32_t)g.nkt2;
   a2.ncb = (int32_t)g.ncb2;
   a2.ntl = (int32_t)g.nht;
-  if ((st = launch_gemm2(NRG, a2, w.max_tiles, s)) || (st = mark())) return st;
+  a2.tiles = (const int4*)(ws + w.tiles2);
+  a2.ntiles = (const int32_t*)(ws + w.ntiles2);
+  if ((st = launch_gemm2(NRG2, a2, w.max_tiles, s)) || (st = mark())) return st;
   if ((st = launch_combine((const uint16_t*)(ws + w.o16), ws + w.osc, (const int32_t*)(ws + w.pair_prow), y_bf16, T, g.H,
                            top_k, s)) ||
       (st = mark()))

@@ -138,7 +138,8 @@ constexpr int kSlot = 48;
 //   actq: [row group of 32][nkt2][64 lanes][kSlot]  the second GEMM's A operand, lane (row l%32,
 //         K block l/32)
 //   acts: [row group][nkt2][64 lanes][4]
-//   tiles: int4 (expert, first padded row, valid rows, 0) per M tile of the GEMMs
+//   tiles, tiles2: int4 (expert, first padded row, valid rows, 0) per M tile of the first and of the
+//         second GEMM (their tile heights may differ)
 //   pair_prow: [T*k] padded row of each (token, slot) pair
 //   o16 : fp16 [padded rows][H], row r = w * (expert output + b2) of the pair at row r, divided by the
 //         power of two 2^(osc - 127) of its block
@@ -146,8 +147,8 @@ constexpr int kSlot = 48;
 constexpr int kRouteTokens = 64;
 
 struct FwdWs {
-  uint64_t blkcnt, offsets, poffsets, sorted_pairs, ids, w, prow_pair, prow_tok, prow_w, pair_prow, tiles, ntiles, xq, xs,
-      actq, acts, o16, osc, total;
+  uint64_t blkcnt, offsets, poffsets, sorted_pairs, ids, w, prow_pair, prow_tok, prow_w, pair_prow, tiles, ntiles, tiles2,
+      ntiles2, xq, xs, actq, acts, o16, osc, total;
   int64_t nrows_alloc, max_tiles;
 };
 
@@ -170,6 +171,8 @@ static inline FwdWs fwd_ws(const MoeGeom& g, int64_t T, int64_t k) {
   w.pair_prow = take(4 * P);
   w.tiles = take(16 * w.max_tiles);
   w.ntiles = take(16);
+  w.tiles2 = take(16 * w.max_tiles);
+  w.ntiles2 = take(16);
   w.xq = take((uint64_t)T * 2 * g.nkt1 * kSlot);
   w.xs = take((uint64_t)T * 2 * g.nkt1 * 4);
   w.actq = take((uint64_t)(w.nrows_alloc / 32) * g.nkt2 * 64 * kSlot);

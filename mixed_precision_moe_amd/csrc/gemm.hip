@@ -767,10 +767,10 @@ int launch_cfg(const GemmArgs& a, int64_t max_tiles, hipStream_t stream) {
 
 }  // namespace
 
-// Tile configurations by rows per M tile (32 * NRG): 1 row group for decode-like loads, 2 or 4 for
-// larger ones.  The first GEMM covers a whole column block per workgroup; the 128-row second GEMM
-// covers half of one so that two workgroups share a CU and one's output stores overlap the other's
-// MFMAs.
+// Tile configurations by rows per M tile (32 * NRG): 1 row group for decode-like loads, 2 or 4 (first
+// GEMM only) for larger ones.  The 128-row first GEMM covers a whole column block per workgroup, one
+// workgroup per CU; the others run two workgroups per CU so that one's stores and waits overlap the
+// other's MFMAs.
 int launch_gemm1(int NRG, const GemmArgs& a, int64_t max_tiles, hipStream_t stream) {
   switch (NRG) {
     case 1: return launch_cfg<true, 1, 4, 1, 4, 3, 2>(a, max_tiles, stream);
@@ -784,7 +784,6 @@ int launch_gemm2(int NRG, const GemmArgs& a, int64_t max_tiles, hipStream_t stre
   switch (NRG) {
     case 1: return launch_cfg<false, 1, 4, 1, 4, 3, 2>(a, max_tiles, stream);
     case 2: return launch_cfg<false, 1, 4, 2, 4, 3, 2>(a, max_tiles, stream);
-    case 4: return launch_cfg<false, 2, 2, 2, 4, 3, 2>(a, max_tiles, stream);
     default: return MXFP4_ERR_SHAPE;
   }
 }

@@ -207,10 +207,12 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
 // the pairs of expert e among the tokens of block b (the routing histogram, read only here).
 //  (1) Every workgroup sums, per expert, the counts of the blocks before its own and of all blocks
 //      (threads split the blocks, partial sums meet in LDS), then scans over experts: the exclusive
-//      prefixes of the counts, of the counts padded to 32 and of the M tiles of BM rows.
-//  (2) Workgroup 0 also writes offsets, padded offsets, the tile list (expert, first padded row, valid
-//      rows) and the padding rows of every expert plus 128 slack rows after the last one (pair -1,
-//      token 0, weight 0), so a GEMM tile may read up to 128 rows past its expert's start.
+//      prefixes of the counts, of the counts padded to 32 and of the M tiles of BM and of BM2 rows.
+//  (2) Workgroup 0 also writes offsets, padded offsets, two tile lists (expert, first padded row,
+//      valid rows) for M tiles of BM rows (first GEMM) and of BM2 rows (second GEMM; the list is
+//      skipped when tiles2 is NULL), and the padding rows of every expert plus 128 slack rows after the
+//      last one (pair -1, token 0, weight 0), so a GEMM tile may read up to 128 rows past its expert's
+//      start.
 //  (3) The first wave (lane = token of the block) ranks each pair among the pairs of its expert in
 //      token order: (pairs of that expert in earlier blocks) + (earlier lanes of this block with that
 //      expert, from a 64-bit lane mask per expert), and writes the compact order (sorted_pairs, may be
@@ -218,15 +220,16 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
 //      NULL).  Padding rows and pair rows are disjoint, so the workgroups never write the same row.
 __global__ __launch_bounds__(1024) void place_kernel(const int32_t* __restrict__ ids, const float* __restrict__ wts,
                                                      const int32_t* __restrict__ blkcnt, int64_t T, int nb, int k,
-                                                     int E, int BM, int32_t* __restrict__ offsets,
+                                                     int E, int BM, int BM2, int32_t* __restrict__ offsets,
                                                      int32_t* __restrict__ poffsets, int4* __restrict__ tiles,
-                                                     int32_t* __restrict__ ntiles, int32_t* __restrict__ sorted_pairs,
+                                                     int32_t* __restrict__ ntiles, int4* __restrict__ tiles2,
+                                                     int32_t* __restrict__ ntiles2, int32_t* __restrict__ sorted_pairs,
                                                      int32_t* __restrict__ prow_pair, int32_t* __restrict__ prow_tok,
                                                      float* __restrict__ prow_w, int32_t* __restrict__ pair_prow) {
   __shared__ int part_pre[1024], part_tot[1024];
-  __shared__ int e_pre[1024], e_off[1024], e_poff[1024], e_tot[1024], e_toff[1024];
+  __shared__ int e_pre[1024], e_off[1024], e_poff[1024], e_tot[1024], e_toff[1024], e_toff2[1024];
   __shared__ uint32_t mlo[1024], mhi[1024];
-  __shared__ int wsum[3][16];
+  __shared__ int wsum[4][16];
   __shared__ int slack0;  // first slack row (workgroup 0)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int blk = blockIdx.x;
@@ -254,7 +257,7 @@ __global__ __launch_bounds__(1024) void place_kernel(const int32_t* __restrict__
   part_pre[tid] = s_pre;
   part_tot[tid] = s_tot;
   __syncthreads();
-  int v0 = 0, v1 = 0, v2 = 0, pre = 0;
+  int v0 = 0, v1 = 0, v2 = 0, v3 = 0, pre = 0;
   if (grp == 0 && e < E) {
     int total = 0;
     for (int q = 0; q < G; q++) {
@@ -264,25 +267,27 @@ __global__ __launch_bounds__(1024) void place_kernel(const int32_t* __restrict__
     v0 = total;
     v1 = (total + 31) & ~31;
     v2 = (total + BM - 1) / BM;
+    v3 = (total + BM2 - 1) / BM2;
   }
   // scans over experts: thread e of group 0 (tid == e) holds expert e, every other thread zeros
-  int x0 = v0, x1 = v1, x2 = v2;
+  int x0 = v0, x1 = v1, x2 = v2, x3 = v3;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const int y0 = __shfl_up(x0, off), y1 = __shfl_up(x1, off), y2 = __shfl_up(x2, off);
-    if (lane >= off) { x0 += y0; x1 += y1; x2 += y2; }
+    const int y0 = __shfl_up(x0, off), y1 = __shfl_up(x1, off), y2 = __shfl_up(x2, off), y3 = __shfl_up(x3, off);
+    if (lane >= off) { x0 += y0; x1 += y1; x2 += y2; x3 += y3; }
   }
-  if (lane == 63) { wsum[0][wave] = x0; wsum[1][wave] = x1; wsum[2][wave] = x2; }
+  if (lane == 63) { wsum[0][wave] = x0; wsum[1][wave] = x1; wsum[2][wave] = x2; wsum[3][wave] = x3; }
   __syncthreads();
-  int p0 = 0, p1 = 0, p2 = 0;
-  for (int q = 0; q < wave; q++) { p0 += wsum[0][q]; p1 += wsum[1][q]; p2 += wsum[2][q]; }
-  x0 += p0; x1 += p1; x2 += p2;  // inclusive scans over threads 0..tid
+  int p0 = 0, p1 = 0, p2 = 0, p3 = 0;
+  for (int q = 0; q < wave; q++) { p0 += wsum[0][q]; p1 += wsum[1][q]; p2 += wsum[2][q]; p3 += wsum[3][q]; }
+  x0 += p0; x1 += p1; x2 += p2; x3 += p3;  // inclusive scans over threads 0..tid
   if (grp == 0 && e < E) {
     e_pre[e] = pre;
     e_off[e] = x0 - v0;
     e_poff[e] = x1 - v1;
     e_tot[e] = v0;
     e_toff[e] = x2 - v2;
+    e_toff2[e] = x3 - v3;
   }
   // (2) the tables, once: offsets by expert thread, then each wave takes experts wave, wave + 16, ...
   // and writes their tiles and padding rows with one lane per tile or row
@@ -293,6 +298,7 @@ __global__ __launch_bounds__(1024) void place_kernel(const int32_t* __restrict__
       offsets[E] = x0;
       poffsets[E] = x1;
       *ntiles = x2;
+      if (tiles2) *ntiles2 = x3;
       slack0 = x1;
     }
   }
@@ -302,6 +308,11 @@ __global__ __launch_bounds__(1024) void place_kernel(const int32_t* __restrict__
       const int poff = e_poff[ee], total = e_tot[ee], toff = e_toff[ee];
       const int ntl = (total + BM - 1) / BM, pad = ((total + 31) & ~31) - total;
       for (int i = lane; i < ntl; i += 64) tiles[toff + i] = make_int4(ee, poff + i * BM, min(BM, total - i * BM), 0);
+      if (tiles2) {
+        const int toff2 = e_toff2[ee], ntl2 = (total + BM2 - 1) / BM2;
+        for (int i = lane; i < ntl2; i += 64)
+          tiles2[toff2 + i] = make_int4(ee, poff + i * BM2, min(BM2, total - i * BM2), 0);
+      }
       if (lane < pad) {
         const int r = poff + total + lane;
         prow_pair[r] = -1;
@@ -407,12 +418,14 @@ int launch_route(const float* logits, int64_t T, int E, int k, int renormalize, 
   return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
 }
 
-int launch_place(const int32_t* ids, const float* w, int32_t* blkcnt, int64_t T, int k, int E, int BM, int32_t* offsets,
-                 int32_t* poffsets, int32_t* sorted_pairs, int32_t* prow_pair, int32_t* prow_tok, float* prow_w,
-                 int32_t* pair_prow, void* tiles, int32_t* ntiles, hipStream_t stream) {
+int launch_place(const int32_t* ids, const float* w, int32_t* blkcnt, int64_t T, int k, int E, int BM, int BM2,
+                 int32_t* offsets, int32_t* poffsets, int32_t* sorted_pairs, int32_t* prow_pair, int32_t* prow_tok,
+                 float* prow_w, int32_t* pair_prow, void* tiles, int32_t* ntiles, void* tiles2, int32_t* ntiles2,
+                 hipStream_t stream) {
   const int nb = (int)cdiv(T, kRouteTokens);
   // at least one workgroup, which writes the tables even when there are no tokens
   hipLaunchKernelGGL(place_kernel, dim3((unsigned)(nb > 0 ? nb : 1)), dim3(1024), 0, stream, ids, w, blkcnt, T, nb, k, E,
-                     BM, offsets, poffsets, (int4*)tiles, ntiles, sorted_pairs, prow_pair, prow_tok, prow_w, pair_prow);
+                     BM, BM2, offsets, poffsets, (int4*)tiles, ntiles, (int4*)tiles2, ntiles2, sorted_pairs, prow_pair,
+                     prow_tok, prow_w, pair_prow);
   return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
 }
