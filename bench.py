@@ -5,8 +5,9 @@ A step is one MoE layer forward on the prefill-shaped workload (8192 bf16 tokens
 hidden 2048, intermediate 768, MXFP4 weights): activation split, routing, pair sort, first grouped
 GEMM + SwiGLU, second grouped GEMM + weighted combine, bf16 output.  `value` is algorithmic TFLOP/s
 of that layer (2 * T * k * 3 * H * I flops per step).  The same run times the quantizer on the
-8192 x 7168 bf16 matrix (GB/s of algorithmic traffic) and the decode-shaped layer, and times the CPU
-oracle on a bounded sample as a reported baseline.  Inputs are synthetic and seeded; weights are
+8192 x 7168 bf16 matrix (GB/s of algorithmic traffic), the decode-shaped layer and the large-expert
+layer (4096 tokens, 384 experts, hidden 7168, intermediate 2048, Zipf-skewed routing), and times the
+CPU oracle on the same prefill workload as a reported baseline.  Inputs are synthetic and seeded; weights are
 quantized from random bf16 masters.  Prints one JSON line.
 """
 
@@ -64,11 +65,13 @@ def log(*a):
 
 
 class MoeBench:
-    def __init__(self, cfg, rotations):
+    def __init__(self, cfg, rotations, weight_copies=None):
         self.cfg = cfg
         w = gpu_standard_weights(cfg)
         self.packed = [mx.repack_weights(*w)]
-        for _ in range(1, rotations):  # extra weight copies so consecutive steps cannot hit in the 256 MB cache
+        # extra weight copies so consecutive steps cannot hit in the 256 MB cache (not needed once the
+        # weights alone are many times that size)
+        for _ in range(1, rotations if weight_copies is None else weight_copies):
             self.packed.append(self.packed[0].clone())
         del w
         x_bits, logits = synth.moe_activations(cfg)
@@ -187,10 +190,10 @@ def cpu_baselines(cfg, x_bits, logits):
     except Exception:  # pragma: no cover
         blas_threads = None
     cores = len(os.sched_getaffinity(0))
-    # MoE: a few sampled tokens of the prefill workload; the oracle dequantizes every expert they use in
-    # fp64, which dominates its time
-    ntok = 512  # every expert is used; about 10-30 s of the oracle on the host cores
-    rows = np.sort(np.random.default_rng(1).choice(cfg.T, size=ntok, replace=False))
+    # MoE: the whole prefill workload (every token); the oracle dequantizes every expert the routing
+    # uses in fp64, which dominates its time (about 5-25 s on 8-16 host cores)
+    ntok = cfg.T
+    rows = np.arange(ntok)
     w13, w2 = LazyExperts(cfg, "w13"), LazyExperts(cfg, "w2")
     from oracle.route import route_ref
     ids, _ = route_ref(logits, cfg.k)
@@ -204,7 +207,7 @@ def cpu_baselines(cfg, x_bits, logits):
     flops = 2.0 * ntok * cfg.k * 3 * cfg.H * cfg.I
     moe = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "blas_threads": blas_threads,
            "kind": "oracle", "seconds": dt,
-           "sample": f"{ntok} of {cfg.T} prefill tokens ({len(np.unique(ids[rows]))} experts dequantized in fp64); "
+           "sample": f"all {ntok} prefill tokens ({len(np.unique(ids[rows]))} experts used, dequantized in fp64); "
                      "weights pre-quantized outside the timed region"}
     # quantizer: the whole 8192 x 7168 matrix
     Mq, K = synth.QUANT_CONFIG["M"], synth.QUANT_CONFIG["K"]
@@ -227,17 +230,25 @@ def run_quantize(args):
     return qr
 
 
+def touched_experts(b):
+    """Number of distinct experts the workload's routing selects, from the library's own routing."""
+    ids = mx.route(b.logits[0], b.cfg.k, b.cfg.renormalize)[0]
+    return int(torch.unique(ids).numel())
+
+
+def expert_bytes(cfg):
+    """Packed MXFP4 bytes of one expert: w13 and w2 nibbles and E8M0 scales, plus bf16 biases."""
+    n = 2 * cfg.I * cfg.H // 2 + 2 * cfg.I * cfg.H // 32 + cfg.H * cfg.I // 2 + cfg.H * cfg.I // 32
+    return n + (2 * (2 * cfg.I + cfg.H) if cfg.bias else 0)
+
+
 def run_decode(args):
     dcfg = synth.MOE_CONFIGS["decode"]
     log("[bench] timing decode MoE")
     db = MoeBench(dcfg, rotations=2)
     dms, dstages = time_moe(db, max(args.steps, 50), args.warmup)
-    _, logits_d = synth.moe_activations(dcfg)
-    from oracle.route import route_ref  # only to count the experts the batch touches, for the byte count
-    touched = len(np.unique(route_ref(logits_d, dcfg.k)[0]))
-    per_expert = (2 * dcfg.I * dcfg.H // 2 + 2 * dcfg.I * dcfg.H // 32 + dcfg.H * dcfg.I // 2 +
-                  dcfg.H * dcfg.I // 32 + 2 * (2 * dcfg.I + dcfg.H))
-    nbytes = touched * per_expert + dcfg.T * dcfg.H * 4 + dcfg.T * dcfg.E * 4
+    touched = touched_experts(db)
+    nbytes = touched * expert_bytes(dcfg) + dcfg.T * dcfg.H * 4 + dcfg.T * dcfg.E * 4
     return {"workload": "decode-shaped MXFP4 MoE layer (T=64, E=128, top-8, H=2048, I=768, biases)",
             "ms": dms, "stages_ms": {n: float(v) for n, v in zip(STAGES, dstages)},
             "touched_experts": touched, "algorithmic_bytes": nbytes,
@@ -245,10 +256,30 @@ def run_decode(args):
             "TFLOP_s": moe_flops(dcfg) / (dms * 1e-3) / 1e12}
 
 
+def run_large(args):
+    lcfg = synth.MOE_CONFIGS["large"]
+    log(f"[bench] building large-expert workload T={lcfg.T} E={lcfg.E} k={lcfg.k} H={lcfg.H} I={lcfg.I}")
+    lb = MoeBench(lcfg, rotations=2, weight_copies=1)  # 9 GB of weights: nothing survives in the cache
+    log("[bench] timing large-expert MoE")
+    lms, lstages = time_moe(lb, args.steps, args.warmup)
+    touched = touched_experts(lb)
+    P = lcfg.T * lcfg.k
+    # touched weights, x, logits, y, and the SwiGLU activation written and read once in bf16
+    nbytes = touched * expert_bytes(lcfg) + lcfg.T * lcfg.H * 4 + lcfg.T * lcfg.E * 4 + P * lcfg.I * 4
+    tflops = moe_flops(lcfg) / (lms * 1e-3) / 1e12
+    return {"workload": "large-expert MXFP4 MoE layer (T=4096, E=384, top-8, H=7168, I=2048, Zipf(1.2) routing)",
+            "ms": lms, "stages_ms": {n: float(v) for n, v in zip(STAGES, lstages)},
+            "touched_experts": touched, "algorithmic_bytes": nbytes,
+            "GB_s": nbytes / (lms * 1e-3) / 1e9, "frac_of_hbm": nbytes / (lms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "TFLOP_s": tflops, "frac_of_fp4_peak": tflops / PEAK_FP4_TFLOPS}
+
+
 def only_secondary(args):
     out = {"metric": "MXFP4 MoE layer TFLOP/s + quantize GB/s, % of MI355X roofline, 1 GPU", "only": args.only}
     if args.only == "decode":
         out["decode"] = run_decode(args)
+    elif args.only == "large":
+        out["large"] = run_large(args)
     else:
         out["quantize"] = run_quantize(args)
     print(json.dumps(out), flush=True)
@@ -262,11 +293,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-quantize", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "quantize"], default=None,
+    ap.add_argument("--no-large", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode", "quantize", "large"], default=None,
                     help="time one workload only (for profiler runs); the JSON line then holds that workload")
     args = ap.parse_args()
     if args.only == "prefill":
-        args.no_decode = args.no_quantize = args.no_cpu_baseline = True
+        args.no_decode = args.no_quantize = args.no_large = args.no_cpu_baseline = True
     elif args.only == "decode":
         args.no_quantize = args.no_cpu_baseline = True
     elif args.only == "quantize":
@@ -279,7 +311,7 @@ def main():
     torch.cuda.set_device(0)
 
     cfg = synth.MOE_CONFIGS["prefill"]
-    if args.only in ("decode", "quantize"):
+    if args.only in ("decode", "quantize", "large"):
         return only_secondary(args)
     log(f"[bench] building prefill workload T={cfg.T} E={cfg.E} k={cfg.k} H={cfg.H} I={cfg.I}")
     b = MoeBench(cfg, rotations=2)
@@ -322,6 +354,10 @@ def main():
 
     if not args.no_decode:
         out["decode"] = run_decode(args)
+        torch.cuda.empty_cache()
+
+    if not args.no_large:
+        out["large"] = run_large(args)
         torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
