@@ -234,11 +234,17 @@ MX_DEV void g1_epilogue_pair(const f32x16_t& g0, const f32x16_t& u0, const f32x1
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const int q = 4 * jj + i;
-      // silu(g) = g / (1 + exp(-g)) with the hardware exponential and reciprocal (exp overflow gives 0)
-      const float ga = acc_read(g0[q]) + b1a[i];
-      float va = ga * __builtin_amdgcn_rcpf(1.0f + __expf(-ga)) * (acc_read(u0[q]) + b3a[i]);
-      const float gb = acc_read(g1[q]) + b1b[i];
-      float vb = gb * __builtin_amdgcn_rcpf(1.0f + __expf(-gb)) * (acc_read(u1[q]) + b3b[i]);
+      // silu(g) = g / (1 + exp(-g)) with the hardware exponential and reciprocal (exp overflow gives 0);
+      // without biases nothing is added (x + 0 is not foldable: it turns -0 into +0)
+      float ga = acc_read(g0[q]), ua = acc_read(u0[q]), gb = acc_read(g1[q]), ub = acc_read(u1[q]);
+      if constexpr (BIAS) {
+        ga += b1a[i];
+        ua += b3a[i];
+        gb += b1b[i];
+        ub += b3b[i];
+      }
+      float va = ga * __builtin_amdgcn_rcpf(1.0f + __expf(-ga)) * ua;
+      float vb = gb * __builtin_amdgcn_rcpf(1.0f + __expf(-gb)) * ub;
       vb = second ? vb : 0.f;
       swap_halves(va, vb);
       lo[q] = va;
@@ -249,26 +255,29 @@ MX_DEV void g1_epilogue_pair(const f32x16_t& g0, const f32x16_t& u0, const f32x1
   u32x4_t* dst = reinterpret_cast<u32x4_t*>(a.actq + (int64_t)slot * kSlot);
   uint32_t out[12];
   uint32_t scales = 0;
-  // Each term quantizes the bf16 rounding of the fp32 remainder (the remainder itself stays fp32).
-  // Rounding is monotonic, so the largest bf16 magnitude is the rounding of the largest fp32 one.
+  // Each term is the fp32 remainder rounded to E2M3 (nearest even) under its block's scale.  The
+  // fp32-input conversion takes the block's even positions from its first source and the odd ones
+  // from its second (code 2j <- ev[j], code 2j + 1 <- od[j]).
 #pragma unroll
   for (int term = 0; term < kTerms; term++) {
     float amax = 0.f;
-    bf16x32_t v;
+    f32x16_t ev, od;
 #pragma unroll
     for (int q = 0; q < 16; q += 2) {
       amax = fmaxf(amax, fmaxf(fmaxf(fabsf(lo[q]), fabsf(lo[q + 1])), fmaxf(fabsf(hi[q]), fabsf(hi[q + 1]))));
-      const bf16x2_t l2 = __builtin_convertvector((f32x2_t){lo[q], lo[q + 1]}, bf16x2_t);
-      const bf16x2_t h2 = __builtin_convertvector((f32x2_t){hi[q], hi[q + 1]}, bf16x2_t);
-      v[q] = l2[0];
-      v[q + 1] = l2[1];
-      v[16 + q] = h2[0];
-      v[17 + q] = h2[1];
+      ev[q / 2] = lo[q];
+      od[q / 2] = lo[q + 1];
+      ev[8 + q / 2] = hi[q];
+      od[8 + q / 2] = hi[q + 1];
     }
-    const bf16x2_t am = __builtin_convertvector((f32x2_t){amax, 0.f}, bf16x2_t);
-    const uint32_t ex = e8m0_from_amax_bits((uint32_t)__builtin_bit_cast(uint16_t, am[0]) << 16);
+    const uint32_t ex = e8m0_from_amax_bits(__float_as_uint(amax));
     const float sv = e8m0_as_scale_operand(ex);
-    const fp6x32_t codes = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(v, sv);
+    // The conversion reads its sources over several passes while it writes its six result registers,
+    // so the result must not share a register with any source; the builtin carries no such
+    // constraint (the compiler gave the result the scale operand's register, which corrupted the
+    // codes), so the instruction is issued with an early-clobber output.
+    fp6x32_t codes;
+    asm("v_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, %3" : "=&v"(codes) : "v"(ev), "v"(od), "v"(sv));
 #pragma unroll
     for (int d = 0; d < 6; d++) out[term * 6 + d] = codes[d];
     scales |= ex << (8 * term);
