@@ -211,11 +211,22 @@ MX_DEV void bias4(lds_u16* p, float* out) {
 // into two E2M3 terms and written as one 48-byte operand slot of the second GEMM (lane l of the step) and
 // its scale dword.  When tile it + 1 is past I / 32 its half is a zero block.
 // g0/u0, g1/u1: gate and up accumulators of the two tiles; bg/bu: the 64 gate / up biases of the pair
-// (bf16, LDS), read when BIAS.
-template <bool BIAS>
+// (bf16, LDS), read when BIAS.  SECOND is false only for the last pair of an odd tile count.
+template <bool BIAS, bool SECOND>
 MX_DEV void g1_epilogue_pair(const f32x16_t& g0, const f32x16_t& u0, const f32x16_t& g1, const f32x16_t& u1,
-                             const GemmArgs& a, lds_u16* bg, lds_u16* bu, bool second, int kt2, int rg, int lane) {
+                             const GemmArgs& a, lds_u16* bg, lds_u16* bu, int kt2, int rg, int lane) {
   const int h = lane >> 5;
+  // All 64 accumulator values are read first: each read is a volatile asm statement, which the
+  // scheduler treats as a region boundary, so reading them up front leaves the SwiGLU arithmetic of the
+  // whole pair as one region whose 32 independent exp / reciprocal chains can interleave.
+  float ra[4][16];
+#pragma unroll
+  for (int q = 0; q < 16; q++) {
+    ra[0][q] = acc_read(g0[q]);
+    ra[1][q] = acc_read(u0[q]);
+    ra[2][q] = acc_read(g1[q]);
+    ra[3][q] = acc_read(u1[q]);
+  }
   // lo[q], hi[q]: block positions q and 16 + q after the exchange (position p of a block holds the
   // tile's row 8 * ((p & 15) >> 2) + 4 * (p >> 4) + (p & 3), the order the second GEMM's weights use)
   float lo[16], hi[16];
@@ -236,7 +247,7 @@ MX_DEV void g1_epilogue_pair(const f32x16_t& g0, const f32x16_t& u0, const f32x1
       const int q = 4 * jj + i;
       // silu(g) = g / (1 + exp(-g)) with the hardware exponential and reciprocal (exp overflow gives 0);
       // without biases nothing is added (x + 0 is not foldable: it turns -0 into +0)
-      float ga = acc_read(g0[q]), ua = acc_read(u0[q]), gb = acc_read(g1[q]), ub = acc_read(u1[q]);
+      float ga = ra[0][q], ua = ra[1][q], gb = ra[2][q], ub = ra[3][q];
       if constexpr (BIAS) {
         ga += b1a[i];
         ua += b3a[i];
@@ -245,7 +256,7 @@ MX_DEV void g1_epilogue_pair(const f32x16_t& g0, const f32x16_t& u0, const f32x1
       }
       float va = ga * __builtin_amdgcn_rcpf(1.0f + __expf(-ga)) * ua;
       float vb = gb * __builtin_amdgcn_rcpf(1.0f + __expf(-gb)) * ub;
-      vb = second ? vb : 0.f;
+      if constexpr (!SECOND) vb = 0.f;
       swap_halves(va, vb);
       lo[q] = va;
       hi[q] = vb;
@@ -260,16 +271,19 @@ MX_DEV void g1_epilogue_pair(const f32x16_t& g0, const f32x16_t& u0, const f32x1
   // from its second (code 2j <- ev[j], code 2j + 1 <- od[j]).
 #pragma unroll
   for (int term = 0; term < kTerms; term++) {
-    float amax = 0.f;
+    // block maximum of magnitudes: four independent chains of three-operand maxima
+    float m4[4] = {0.f, 0.f, 0.f, 0.f};
     f32x16_t ev, od;
 #pragma unroll
     for (int q = 0; q < 16; q += 2) {
-      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(lo[q]), fabsf(lo[q + 1])), fmaxf(fabsf(hi[q]), fabsf(hi[q + 1]))));
+      m4[(q / 2) & 1] = fmaxf(fmaxf(m4[(q / 2) & 1], fabsf(lo[q])), fabsf(lo[q + 1]));
+      m4[2 + ((q / 2) & 1)] = fmaxf(fmaxf(m4[2 + ((q / 2) & 1)], fabsf(hi[q])), fabsf(hi[q + 1]));
       ev[q / 2] = lo[q];
       od[q / 2] = lo[q + 1];
       ev[8 + q / 2] = hi[q];
       od[8 + q / 2] = hi[q + 1];
     }
+    const float amax = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
     const uint32_t ex = e8m0_from_amax_bits(__float_as_uint(amax));
     const float sv = e8m0_as_scale_operand(ex);
     // The conversion reads its sources over several passes while it writes its six result registers,
@@ -633,10 +647,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
         for (int p = 0; p < CW / 4; p++) {
           const int it = (x * NT + wc * CW) / 2 + 2 * p;  // even: a K step of the second GEMM
           const int il = (wc * CW) / 2 + 2 * p;           // activation tile within the item
-          if (it < a.ntl)
-            g1_epilogue_pair<BIAS>(acc[r][4 * p], acc[r][4 * p + 1], acc[r][4 * p + 2], acc[r][4 * p + 3], a,
-                                   (lds_u16*)&t_b[tb][0][il * 32], (lds_u16*)&t_b[tb][G1 ? 1 : 0][il * 32],
-                                   it + 1 < a.ntl, it >> 1, (prow0 >> 5) + rgl, lane);
+          if (it + 1 < a.ntl)
+            g1_epilogue_pair<BIAS, true>(acc[r][4 * p], acc[r][4 * p + 1], acc[r][4 * p + 2], acc[r][4 * p + 3], a,
+                                         (lds_u16*)&t_b[tb][0][il * 32], (lds_u16*)&t_b[tb][G1 ? 1 : 0][il * 32],
+                                         it >> 1, (prow0 >> 5) + rgl, lane);
+          else if (it < a.ntl)
+            g1_epilogue_pair<BIAS, false>(acc[r][4 * p], acc[r][4 * p + 1], acc[r][4 * p + 2], acc[r][4 * p + 3], a,
+                                          (lds_u16*)&t_b[tb][0][il * 32], (lds_u16*)&t_b[tb][G1 ? 1 : 0][il * 32],
+                                          it >> 1, (prow0 >> 5) + rgl, lane);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -661,11 +679,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
           const int nt = x * NT + wc * CW + j;
           if (nt < a.ntl) {
             // v[c]: column 16h + c of the tile after the exchange
-            float v[16];
+            // the tile's 16 values are read first (each read is a scheduling boundary), then exchanged
+            float v[16], ra[16];
+#pragma unroll
+            for (int i = 0; i < 16; i++) ra[i] = acc_read(acc[r][j][i]);
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-              float x0 = acc_read(acc[r][j][i]), x2 = acc_read(acc[r][j][8 + i]);
-              float x1 = acc_read(acc[r][j][4 + i]), x3 = acc_read(acc[r][j][12 + i]);
+              float x0 = ra[i], x2 = ra[8 + i];
+              float x1 = ra[4 + i], x3 = ra[12 + i];
               swap_halves(x0, x2);  // half 0: cols i | 4 + i;  half 1: cols 16 + i | 20 + i
               swap_halves(x1, x3);  // half 0: cols 8 + i | 12 + i;  half 1: cols 24 + i | 28 + i
               v[i] = x0;
