@@ -33,6 +33,7 @@ def test_route_configs(name):
 
 
 @pytest.mark.parametrize("T,E,k,ren", [(1, 1, 1, True), (5, 3, 3, False), (33, 64, 8, False), (100, 1024, 32, True),
+                                       (64, 1024, 32, True), (64, 300, 8, False), (65, 128, 8, True),
                                        (70, 200, 7, True), (513, 130, 5, True)])
 def test_route_shapes(T, E, k, ren):
     g = np.random.default_rng(T * 1000 + E)
