@@ -20,8 +20,8 @@ int launch_unpack_gfx950(const MoeGeom& g, const BlobOffsets& o, bool bias, cons
 int launch_repack_standard(const MoeGeom& g, bool bias, const void* w13_q, const void* w13_s, const void* w2_q,
                            const void* w2_s, const void* b13, const void* b2, int bias_is_fp32, bool swap, bool tiled,
                            const size_t off[6], void* out, hipStream_t stream);
-int launch_xprep(const void* x, int64_t T, int64_t ldx, const MoeGeom& g, void* xq, void* xs, int32_t* zero,
-                 int64_t nzero, hipStream_t stream);
+int launch_xprep(const void* x, int64_t T, int64_t ldx, const MoeGeom& g, void* xq, int32_t* zero, int64_t nzero,
+                 hipStream_t stream);
 int launch_zero_i32(int32_t* p, int64_t n, hipStream_t stream);
 int launch_route(const float* logits, int64_t T, int E, int k, int renormalize, int32_t* ids, float* w,
                  int32_t* blkcnt, hipStream_t stream);
@@ -288,6 +288,10 @@ static int forward_impl(const mxfp4_moe_dims* d, const void* packed_gfx950, cons
     return MXFP4_ERR_ALIGN;
   const MoeGeom g = moe_geom(d->E, d->H, d->I);
   const FwdWs w = fwd_ws(g, T, top_k);
+  // the GEMMs' copy sources are 32-bit byte offsets into the activation buffers
+  if ((uint64_t)T * g.nkt1 * kXRec >= (1ULL << 32) ||
+      (uint64_t)(w.nrows_alloc / 32) * g.nkt2 * 64 * kSlot >= (1ULL << 32))
+    return MXFP4_ERR_SHAPE;
   if (workspace_bytes < w.total) return MXFP4_ERR_WORKSPACE;
   const BlobOffsets o = blob_offsets(g, d->has_bias);
   uint8_t* ws = (uint8_t*)workspace;
@@ -302,8 +306,7 @@ static int forward_impl(const mxfp4_moe_dims* d, const void* packed_gfx950, cons
     return MXFP4_OK;
   };
   if ((st = mark())) return st;
-  if ((st = launch_xprep(x_bf16, T, ldx, g, ws + w.xq, ws + w.xs, (int32_t*)(ws + w.blkcnt), cdiv(T, kRouteTokens) * g.E,
-                         s)) ||
+  if ((st = launch_xprep(x_bf16, T, ldx, g, ws + w.xq, (int32_t*)(ws + w.blkcnt), cdiv(T, kRouteTokens) * g.E, s)) ||
       (st = mark()))
     return st;
   if ((st = launch_route(router_logits, T, (int)g.E, top_k, renormalize, ids, wts, (int32_t*)(ws + w.blkcnt), s)) ||
@@ -317,10 +320,10 @@ static int forward_impl(const mxfp4_moe_dims* d, const void* packed_gfx950, cons
     return st;
   const uint8_t* blob = (const uint8_t*)packed_gfx950;
   GemmArgs a1 = {blob + o.w13q, blob + o.w13s, d->has_bias ? (const uint16_t*)(blob + o.b13) : nullptr,
-                 ws + w.xq, ws + w.xs, (const int32_t*)(ws + w.prow_tok), (const int32_t*)(ws + w.prow_pair),
+                 ws + w.xq, nullptr, (const int32_t*)(ws + w.prow_tok), (const int32_t*)(ws + w.prow_pair),
                  (const float*)(ws + w.prow_w), (const int4*)(ws + w.tiles), (const int32_t*)(ws + w.ntiles),
                  ws + w.actq, ws + w.acts, nullptr, nullptr, (int32_t)g.nkt1, (int32_t)g.ncb1, (int32_t)g.nit,
-                 (int32_t)g.nkt2, (int32_t)(2 * g.nkt1), (int32_t)g.I, (int32_t)g.H};
+                 (int32_t)g.nkt2, (int32_t)g.nkt1, (int32_t)g.I, (int32_t)g.H};
   if ((st = launch_gemm1(NRG1, a1, w.max_tiles, s)) || (st = mark())) return st;
   GemmArgs a2 = a1;
   a2.wq = blob + o.w2q;

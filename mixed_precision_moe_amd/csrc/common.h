@@ -126,15 +126,20 @@ __host__ __device__ inline int w2_perm(int p) { return 8 * ((p & 15) >> 2) + 4 *
 // slot; the two scale bytes of a slot sit in one dword (term 0 in the low byte, two zero bytes).
 constexpr int kTerms = 2;
 constexpr int kSlot = 48;
+// The first GEMM's activation record of one token and one 64-wide K step: the two blocks' slots, their
+// two scale dwords, 8 zero bytes -- 112 bytes, seven 16-byte copies, so the first GEMM copies a row's
+// terms and scales together.
+constexpr int kXRec = 2 * kSlot + 16;
+constexpr int kRecChunks = 32 * kXRec / 16;  // 16-byte chunks of the records of one row group (224)
 
 // ---------------------------------------------------------------------------------------------
 // Forward-pass workspace.  Rows of the expert-sorted order are padded per expert to a multiple of
 // 32 ("padded rows"); a padded row with no pair has pair index -1, token 0 and weight 0.
 //   blkcnt : [nblk_route][E]  pairs per (block of kRouteTokens tokens, expert); after the scan, the
 //            exclusive prefix over blocks
-//   xq  : [T][2*nkt1 blocks][kSlot]  per token and 32-element block of x: the two E2M3 terms
-//   xs  : [T][2*nkt1 blocks][4]      E8M0 bytes of the two terms, two zero bytes (one dword per slot:
-//         LDS DMA moves whole dwords per lane)
+//   xq  : [T][nkt1][kXRec]  per token and K step of x: for each of the two 32-element blocks the two
+//         E2M3 terms (kSlot bytes), then per block a dword with the E8M0 bytes of the two terms and
+//         two zero bytes, then 8 zero bytes
 //   actq: [row group of 32][nkt2][64 lanes][kSlot]  the second GEMM's A operand, lane (row l%32,
 //         K block l/32)
 //   acts: [row group][nkt2][64 lanes][4]
@@ -148,7 +153,7 @@ constexpr int kRouteTokens = 64;
 
 struct FwdWs {
   uint64_t blkcnt, offsets, poffsets, sorted_pairs, ids, w, prow_pair, prow_tok, prow_w, pair_prow, tiles, ntiles, tiles2,
-      ntiles2, xq, xs, actq, acts, o16, osc, total;
+      ntiles2, xq, actq, acts, o16, osc, total;
   int64_t nrows_alloc, max_tiles;
 };
 
@@ -173,8 +178,7 @@ static inline FwdWs fwd_ws(const MoeGeom& g, int64_t T, int64_t k) {
   w.ntiles = take(16);
   w.tiles2 = take(16 * w.max_tiles);
   w.ntiles2 = take(16);
-  w.xq = take((uint64_t)T * 2 * g.nkt1 * kSlot);
-  w.xs = take((uint64_t)T * 2 * g.nkt1 * 4);
+  w.xq = take((uint64_t)T * g.nkt1 * kXRec);
   w.actq = take((uint64_t)(w.nrows_alloc / 32) * g.nkt2 * 64 * kSlot);
   w.acts = take((uint64_t)(w.nrows_alloc / 32) * g.nkt2 * 64 * 4);
   w.o16 = take((uint64_t)w.nrows_alloc * g.H * 2);
@@ -189,8 +193,8 @@ struct GemmArgs {
   const uint8_t* wq;        // weight pieces of this GEMM
   const uint8_t* ws;        // weight scale records
   const uint16_t* bias;     // b13 or b2 (bf16) or NULL
-  const uint8_t* xq;        // first GEMM: per-token slots; second: activation slots by row group
-  const uint8_t* xs;        // matching scale dwords
+  const uint8_t* xq;        // first GEMM: per-token K-step records; second: activation slots by row group
+  const uint8_t* xs;        // second GEMM: matching scale dwords (the first GEMM's are in its records)
   const int32_t* prow_tok;  // padded row -> token
   const int32_t* prow_pair; // padded row -> pair (-1 = padding)
   const float* prow_w;      // padded row -> routing weight
@@ -203,6 +207,6 @@ struct GemmArgs {
   int32_t nkt, ncb;         // K steps and column blocks of this GEMM
   int32_t ntl;              // output column tiles of this GEMM (I/32 activation tiles, or H/32)
   int32_t nkt2;             // K steps of the second GEMM (layout of the activation)
-  int32_t nblk;             // 32-element blocks per token row of xq (2 * K steps of the first GEMM)
+  int32_t nrec;             // records per token row of xq (K steps of the first GEMM)
   int32_t I, H;
 };

@@ -105,20 +105,24 @@ MX_DEV float acc_read(float v) {
 
 // ------------------------------------------------------------------------------------------------
 // Kernel configuration.  LDS stage: [NT weight pieces of 1 KB][1 KB weight scale records of the
-// column block][NRG x 3 KB activation slots, lane-major][NRG x 256 B activation scale dwords].
-template <int WR, int WC, int RW, int CW, int D>
+// column block], then the activation: first GEMM [NRG row groups x 32 rows x kXRec-byte records]
+// (padded to whole 1 KB copies); second GEMM [NRG x 3 KB activation slots, lane-major][NRG x 256 B
+// activation scale dwords].
+template <bool G1, int WR, int WC, int RW, int CW, int D>
 struct Cfg {
   static constexpr int NRG = WR * RW, NT = WC * CW;
   static_assert(WR * WC == 4, "four waves");
   static_assert(NT == 8 || NT == 16, "a workgroup covers a column block or half of one");
   static_assert(CW % 4 == 0, "weight scales are read four tiles per dword");
   static_assert(D >= 3 && D <= 6, "ring depth");  // stages issued D - 1 steps ahead
-  static constexpr int oW = 0, oWS = NT * 1024, oX = oWS + 1024, oXS = oX + NRG * 3072;
-  static constexpr int kStage = oXS + NRG * 256;
-  static constexpr int nW = NT / 4;              // weight pieces copied per wave
-  static constexpr int nX = (3 * NRG + 3) / 4;   // 1 KB activation copies per wave (last one repeated)
-  static constexpr int nXS = (NRG + 3) / 4;      // activation scale copies per wave
-  static constexpr int kOps = nW + 1 + nX + nXS; // copies per wave per stage
+  static constexpr int kXBytes = G1 ? (NRG * kRecChunks * 16 + 1023) / 1024 * 1024 : NRG * 3072;
+  static constexpr int oW = 0, oWS = NT * 1024, oX = oWS + 1024, oXS = oX + kXBytes;
+  static constexpr int kStage = oXS + (G1 ? 0 : NRG * 256);
+  static constexpr int nW = NT / 4;                // weight pieces copied per wave
+  static constexpr int nXI = kXBytes / 1024;       // 1 KB activation copies per stage
+  static constexpr int nX = (nXI + 3) / 4;         // ... per wave (the last one repeated)
+  static constexpr int nXS = G1 ? 0 : (NRG + 3) / 4;  // activation scale copies per wave
+  static constexpr int kOps = nW + 1 + nX + nXS;   // copies per wave per stage
 };
 
 // Order of the work of one K step of a wave: its NM MFMAs in a fixed order (groups of two weight
@@ -323,12 +327,12 @@ struct ItemSrc {
   int64_t wb;       // byte offset of this wave's first weight piece of step 0 (uniform)
   int64_t wsb;      // byte offset of this wave's quarter of the step-0 scale records (uniform)
   uint32_t x[NX];   // byte offsets of this lane's activation copies of step 0
-  uint32_t xs[NXS]; // byte offsets of this lane's activation scale copies of step 0
+  uint32_t xs[NXS > 0 ? NXS : 1]; // byte offsets of this lane's activation scale copies of step 0
 };
 
 template <bool G1, bool BIAS, int WR, int WC, int RW, int CW, int D, int OCC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void grouped_gemm_kernel(GemmArgs a) {
-  using C = Cfg<WR, WC, RW, CW, D>;
+  using C = Cfg<G1, WR, WC, RW, CW, D>;
   constexpr int NRG = C::NRG, NT = C::NT;
   constexpr int kTab = NRG * 32 > 64 ? NRG * 32 : 64;  // row table entries (one dword copy covers 64)
   constexpr int kBias = G1 ? NT / 2 * 32 : NT * 32;   // bias entries of one half (first GEMM) or of the tile
@@ -344,7 +348,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_vptr_t)smem;
   const int nkt = a.nkt, ncb = a.ncb;
   const int nx = ncb * kCB / NT;
-  const int nblk = a.nblk;  // token slots per row of xq (first GEMM)
+  const int nrec = a.nrec;  // K-step records per token row of xq (first GEMM)
 
   const int total = *a.ntiles * nx;
   const int chunk = (total + kXcds - 1) / kXcds;
@@ -379,32 +383,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
 #pragma unroll
     for (int q = 0; q < C::nX; q++) {
       int o = wave + 4 * q;
-      o = o < 3 * NRG ? o : 3 * NRG - 1;
-      const int rg = o / 3, pp = o % 3;
+      o = o < C::nXI ? o : C::nXI - 1;
       if (G1) {
-        const int c = pp * 64 + lane, s = c / 3, part = c % 3;
-        const int row = rg * 32 + (s & 31);
+        // 16-byte chunk c of the stage's records: row c / 7 of the tile, part c % 7 of its record; the
+        // chunks past the last row (one row group) repeat the last chunk into the stage's padding
+        int c = o * 64 + lane;
+        c = c < NRG * kRecChunks ? c : NRG * kRecChunks - 1;
+        const int row = c / 7, part = c % 7;
         const int tok = tb >= 0 ? t_row[tb][row] : a.prow_tok[prow0 + row];
-        sr.x[q] = (uint32_t)((tok * nblk + (s >> 5)) * kSlot + part * 16);
+        sr.x[q] = (uint32_t)(tok * nrec * kXRec + part * 16);
       } else {
+        const int rg = o / 3, pp = o % 3;
         sr.x[q] = (uint32_t)(((prow0 >> 5) + rg) * nkt * (64 * kSlot) + (pp * 64 + lane) * 16);
       }
     }
 #pragma unroll
-    for (int q = 0; q < C::nXS; q++) {
+    for (int q = 0; q < C::nXS; q++) {  // second GEMM only
       int o = wave + 4 * q;
       o = o < NRG ? o : NRG - 1;
-      if (G1) {
-        const int row = o * 32 + (lane & 31);
-        const int tok = tb >= 0 ? t_row[tb][row] : a.prow_tok[prow0 + row];
-        sr.xs[q] = (uint32_t)((tok * nblk + (lane >> 5)) * 4);
-      } else {
-        sr.xs[q] = (uint32_t)(((prow0 >> 5) + o) * nkt * 256 + lane * 4);
-      }
+      sr.xs[q] = (uint32_t)(((prow0 >> 5) + o) * nkt * 256 + lane * 4);
     }
   };
-  constexpr int xstep = G1 ? 2 * kSlot : 64 * kSlot;  // bytes per K step of an activation copy
-  constexpr int xsstep = G1 ? 8 : 256;
+  constexpr int xstep = G1 ? kXRec : 64 * kSlot;  // bytes per K step of an activation copy
+  constexpr int xsstep = 256;                      // ... of an activation scale copy (second GEMM)
   // Copy i (of kOps per wave) of stage `kt` of the item with sources `sr` into ring slot `slot`.
   auto issue_op = [&](const Src& sr, int kt, int slot, auto ic) __attribute__((always_inline)) {
     constexpr int i = decltype(ic)::value;
@@ -416,7 +417,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
     } else if constexpr (i < C::nW + 1 + C::nX) {
       constexpr int q = i - C::nW - 1;
       int o = wave + 4 * q;
-      o = o < 3 * NRG ? o : 3 * NRG - 1;
+      o = o < C::nXI ? o : C::nXI - 1;
       dma16(a.xq + (sr.x[q] + (uint32_t)(kt * xstep)), base + C::oX + o * 1024);
     } else {
       constexpr int q = i - C::nW - 1 - C::nX;
@@ -480,7 +481,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
   int jj0 = 0;
   auto load_x = [&](const uint8_t* base, int r, auto pc) __attribute__((always_inline)) {
     constexpr int P = decltype(pc)::value;
-    lds_u8 xp = (lds_u8)(base + C::oX + (wr * RW + r) * 3072 + lane * kSlot);
+    // first GEMM: lane l takes block l / 32 of row l % 32's record; second: slot l of the row group
+    lds_u8 rec = (lds_u8)(base + C::oX + (wr * RW + r) * (32 * kXRec) + (lane & 31) * kXRec);
+    lds_u8 xp = G1 ? rec + (lane >> 5) * kSlot : (lds_u8)(base + C::oX + (wr * RW + r) * 3072 + lane * kSlot);
     asm("" : "+v"(xp));
     lds_u8 xp1 = xp + 24;
     asm("" : "+v"(xp1));
@@ -490,7 +493,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
     const u32x4_t b4 = *(lds16_p)(xp1 + 8);
     xop[P][r][0] = i32x8_t{(int)a4[0], (int)a4[1], (int)a4[2], (int)a4[3], (int)a2[0], (int)a2[1], 0, 0};
     xop[P][r][1] = i32x8_t{(int)b2[0], (int)b2[1], (int)b4[0], (int)b4[1], (int)b4[2], (int)b4[3], 0, 0};
-    xsc[P][r] = *(lds4_p)(lds_u8)(base + C::oXS + (wr * RW + r) * 256 + lane * 4);
+    if constexpr (G1)
+      xsc[P][r] = *(lds4_p)(rec + 2 * kSlot + (lane >> 5) * 4);
+    else
+      xsc[P][r] = *(lds4_p)(lds_u8)(base + C::oXS + (wr * RW + r) * 256 + lane * 4);
   };
   auto load_w = [&](const uint8_t* base, int j) __attribute__((always_inline)) {
     w[j] = *(lds16_p)(lds_u8)(base + C::oW + (wc * CW + j) * 1024 + lane * 16);
@@ -781,7 +787,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 template <bool G1, int WR, int WC, int RW, int CW, int D, int OCC>
 int launch_cfg(const GemmArgs& a, int64_t max_tiles, hipStream_t stream) {
   const int wg_per_cu = OCC;
-  using C = Cfg<WR, WC, RW, CW, D>;
+  using C = Cfg<G1, WR, WC, RW, CW, D>;
   const int64_t nx = (int64_t)a.ncb * kCB / C::NT;
   int64_t items = max_tiles * nx;
   int64_t grid = 256 * wg_per_cu;

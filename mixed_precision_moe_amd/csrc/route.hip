@@ -25,7 +25,7 @@ MX_DEV uint32_t amax_bits32(const uint32_t* w) {  // 16 words = 32 bf16 -> large
   return m;
 }
 
-// x [T, ldx] bf16 -> xq/xs: per 32-element block the two E2M3 terms x = t0 + t1.  Each term is the
+// x [T, ldx] bf16 -> xq: per 32-element block the two E2M3 terms x = t0 + t1.  Each term is the
 // current remainder quantized with its own E8M0 scale from the 0.75 round-up rule (block maximum /
 // scale < 7 <= 7.5, the E2M3 maximum, so no term saturates).  The remainder x - t0 is exact in bf16
 // (a bf16 value minus its own rounding to a coarser grid).  K is padded to a multiple of 64 with zero
@@ -34,15 +34,16 @@ MX_DEV uint32_t amax_bits32(const uint32_t* w) {  // 16 words = 32 bf16 -> large
 // A wave handles 64 consecutive blocks (block gi = token * nblk + b), lane l computing block l.  Its
 // global accesses are staged through LDS so that every load and store instruction covers 1 KB of
 // consecutive bytes: 16-byte chunk c = 64 j + l of the wave's 4 KB of x is loaded by lane l in load j and
-// written to LDS, lane l then reads its block's four chunks; the 48-byte slots go to LDS and leave as
-// three 1 KB stores (the slots of consecutive blocks are consecutive in xq).
+// written to LDS, lane l then reads its block's four chunks; lane l writes its 48-byte slot and scale
+// dword into record l / 2 (blocks 2r and 2r + 1 form the K-step record r), and the wave's 32 records
+// (3.5 KB, consecutive in xq) leave as 16-byte chunks.
 typedef float xf32x2_t __attribute__((ext_vector_type(2)));
 
 __global__ __launch_bounds__(256) void xprep_kernel(const uint16_t* __restrict__ x, int64_t ldx, int64_t H, int64_t nblk,
-                                                    uint8_t* __restrict__ xq, uint8_t* __restrict__ xs,
-                                                    int32_t* __restrict__ zero, int64_t nzero, int64_t n) {
+                                                    uint8_t* __restrict__ xq, int32_t* __restrict__ zero,
+                                                    int64_t nzero, int64_t n) {
   __shared__ __attribute__((aligned(16))) uint8_t stage_in[4][4096];
-  __shared__ __attribute__((aligned(16))) uint8_t stage_out[4][64 * kSlot];
+  __shared__ __attribute__((aligned(16))) uint8_t stage_out[4][32 * kXRec];
   GRID_STRIDE(i, nzero) zero[i] = 0;  // the routing histogram, cleared for the next launch
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t hb = H / 32;  // real blocks per token
@@ -92,19 +93,22 @@ __global__ __launch_bounds__(256) void xprep_kernel(const uint16_t* __restrict__
         }
       }
     }
-    u32x4_t* sl = reinterpret_cast<u32x4_t*>(&stage_out[wave][lane * kSlot]);
+    uint8_t* rec = &stage_out[wave][(lane >> 1) * kXRec];
+    u32x4_t* sl = reinterpret_cast<u32x4_t*>(rec + (lane & 1) * kSlot);
     sl[0] = u32x4_t{tq[0][0], tq[0][1], tq[0][2], tq[0][3]};
     sl[1] = u32x4_t{tq[0][4], tq[0][5], tq[1][0], tq[1][1]};
     sl[2] = u32x4_t{tq[1][2], tq[1][3], tq[1][4], tq[1][5]};
-    const int64_t gl = g0 + lane;
-    if (gl < n) reinterpret_cast<uint32_t*>(xs)[gl] = te[0] | (te[1] << 8);
+    reinterpret_cast<uint32_t*>(rec + 2 * kSlot)[lane & 1] = te[0] | (te[1] << 8);
+    if ((lane & 1) == 0) *reinterpret_cast<u32x2_t*>(rec + 2 * kSlot + 8) = u32x2_t{0u, 0u};
     __builtin_amdgcn_wave_barrier();
-    // coalesced stores: 16-byte chunk c = 64 j + lane of the wave's 3 KB of slots
+    // coalesced stores: 16-byte chunk c = 64 j + lane of the wave's 32 records (g0 is even, so the
+    // wave's first record is g0 / 2; a record exists when its first block does)
+    const int64_t r0 = g0 / 2;
 #pragma unroll
-    for (int j = 0; j < 3; j++) {
+    for (int j = 0; j < 4; j++) {
       const int c = 64 * j + lane;
-      if (g0 + (c * 16) / kSlot < n)
-        *reinterpret_cast<u32x4_t*>(xq + g0 * kSlot + c * 16) = *reinterpret_cast<const u32x4_t*>(&stage_out[wave][c * 16]);
+      if (c < kRecChunks && 2 * (r0 + (c * 16) / kXRec) < n)
+        *reinterpret_cast<u32x4_t*>(xq + r0 * kXRec + c * 16) = *reinterpret_cast<const u32x4_t*>(&stage_out[wave][c * 16]);
     }
     __builtin_amdgcn_wave_barrier();  // the next iteration's LDS writes after these reads
   }
@@ -383,13 +387,13 @@ inline unsigned grid_for(int64_t n, int threads = 256) {
 
 }  // namespace
 
-int launch_xprep(const void* x, int64_t T, int64_t ldx, const MoeGeom& g, void* xq, void* xs, int32_t* zero,
-                 int64_t nzero, hipStream_t stream) {
+int launch_xprep(const void* x, int64_t T, int64_t ldx, const MoeGeom& g, void* xq, int32_t* zero, int64_t nzero,
+                 hipStream_t stream) {
   const int64_t nblk = 2 * g.nkt1;
   const int64_t n = T * nblk;
   if (n > 0 || nzero > 0)
     hipLaunchKernelGGL(xprep_kernel, dim3(grid_for(n > nzero ? n : nzero)), dim3(256), 0, stream, (const uint16_t*)x,
-                       ldx, g.H, nblk, (uint8_t*)xq, (uint8_t*)xs, zero, nzero, n);
+                       ldx, g.H, nblk, (uint8_t*)xq, zero, nzero, n);
   return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
 }
 
