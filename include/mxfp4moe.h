@@ -154,7 +154,7 @@ int moe_mxfp4_route(const float* router_logits, int64_t T, int32_t E, int32_t to
  * x_bf16  device bf16 [T, ldx], ldx >= H, ldx % 8 == 0.   y_bf16 device bf16 [T, H].
  * router_logits device fp32 [T, E].  topk_ids / topk_w: optional device outputs [T, top_k].
  * workspace device, >= moe_mxfp4_workspace_bytes(d, T, top_k), 256-byte aligned.
- * Size limit: the split activations of the first GEMM (T * H * 1.75 bytes) and of the second (about
+ * Size limit: the split activations of the first GEMM (T * H * 2 bytes) and of the second (about
  * 1.5 bytes per padded pair row and I element) must each stay below 4 GiB, else MXFP4_ERR_SHAPE.
  * Arithmetic: activations enter the block-scaled MFMA as two E2M3 (FP6) terms with E8M0 scales
  * per 32 elements (x = t0 + t1, t1 the rounding of the remainder), weights as E2M1 with their E8M0

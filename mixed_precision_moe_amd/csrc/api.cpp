@@ -289,7 +289,7 @@ static int forward_impl(const mxfp4_moe_dims* d, const void* packed_gfx950, cons
   const MoeGeom g = moe_geom(d->E, d->H, d->I);
   const FwdWs w = fwd_ws(g, T, top_k);
   // the GEMMs' copy sources are 32-bit byte offsets into the activation buffers
-  if ((uint64_t)T * g.nkt1 * kXRec >= (1ULL << 32) ||
+  if ((uint64_t)T * g.nkt1 * kXRecG >= (1ULL << 32) ||
       (uint64_t)(w.nrows_alloc / 32) * g.nkt2 * 64 * kSlot >= (1ULL << 32))
     return MXFP4_ERR_SHAPE;
   if (workspace_bytes < w.total) return MXFP4_ERR_WORKSPACE;

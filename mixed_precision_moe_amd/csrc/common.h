@@ -131,15 +131,18 @@ constexpr int kSlot = 48;
 // terms and scales together.
 constexpr int kXRec = 2 * kSlot + 16;
 constexpr int kRecChunks = 32 * kXRec / 16;  // 16-byte chunks of the records of one row group (224)
+// In global memory each record starts a 128-byte line of its own (the copies take its first kXRec
+// bytes), so every record of a copy is one cache line.
+constexpr int kXRecG = 128;
 
 // ---------------------------------------------------------------------------------------------
 // Forward-pass workspace.  Rows of the expert-sorted order are padded per expert to a multiple of
 // 32 ("padded rows"); a padded row with no pair has pair index -1, token 0 and weight 0.
 //   blkcnt : [nblk_route][E]  pairs per (block of kRouteTokens tokens, expert); after the scan, the
 //            exclusive prefix over blocks
-//   xq  : [T][nkt1][kXRec]  per token and K step of x: for each of the two 32-element blocks the two
+//   xq  : [T][nkt1][kXRecG]  per token and K step of x: for each of the two 32-element blocks the two
 //         E2M3 terms (kSlot bytes), then per block a dword with the E8M0 bytes of the two terms and
-//         two zero bytes, then 8 zero bytes
+//         two zero bytes, then zero bytes up to kXRecG
 //   actq: [row group of 32][nkt2][64 lanes][kSlot]  the second GEMM's A operand, lane (row l%32,
 //         K block l/32)
 //   acts: [row group][nkt2][64 lanes][4]
@@ -178,7 +181,7 @@ static inline FwdWs fwd_ws(const MoeGeom& g, int64_t T, int64_t k) {
   w.ntiles = take(16);
   w.tiles2 = take(16 * w.max_tiles);
   w.ntiles2 = take(16);
-  w.xq = take((uint64_t)T * g.nkt1 * kXRec);
+  w.xq = take((uint64_t)T * g.nkt1 * kXRecG);
   w.actq = take((uint64_t)(w.nrows_alloc / 32) * g.nkt2 * 64 * kSlot);
   w.acts = take((uint64_t)(w.nrows_alloc / 32) * g.nkt2 * 64 * 4);
   w.o16 = take((uint64_t)w.nrows_alloc * g.H * 2);

@@ -391,7 +391,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
         c = c < NRG * kRecChunks ? c : NRG * kRecChunks - 1;
         const int row = c / 7, part = c % 7;
         const int tok = tb >= 0 ? t_row[tb][row] : a.prow_tok[prow0 + row];
-        sr.x[q] = (uint32_t)(tok * nrec * kXRec + part * 16);
+        sr.x[q] = (uint32_t)(tok * nrec * kXRecG + part * 16);
       } else {
         const int rg = o / 3, pp = o % 3;
         sr.x[q] = (uint32_t)(((prow0 >> 5) + rg) * nkt * (64 * kSlot) + (pp * 64 + lane) * 16);
@@ -404,7 +404,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
       sr.xs[q] = (uint32_t)(((prow0 >> 5) + o) * nkt * 256 + lane * 4);
     }
   };
-  constexpr int xstep = G1 ? kXRec : 64 * kSlot;  // bytes per K step of an activation copy
+  constexpr int xstep = G1 ? kXRecG : 64 * kSlot;  // bytes per K step of an activation copy
   constexpr int xsstep = 256;                      // ... of an activation scale copy (second GEMM)
   // Copy i (of kOps per wave) of stage `kt` of the item with sources `sr` into ring slot `slot`.
   auto issue_op = [&](const Src& sr, int kt, int slot, auto ic) __attribute__((always_inline)) {

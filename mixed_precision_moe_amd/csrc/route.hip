@@ -36,14 +36,14 @@ MX_DEV uint32_t amax_bits32(const uint32_t* w) {  // 16 words = 32 bf16 -> large
 // consecutive bytes: 16-byte chunk c = 64 j + l of the wave's 4 KB of x is loaded by lane l in load j and
 // written to LDS, lane l then reads its block's four chunks; lane l writes its 48-byte slot and scale
 // dword into record l / 2 (blocks 2r and 2r + 1 form the K-step record r), and the wave's 32 records
-// (3.5 KB, consecutive in xq) leave as 16-byte chunks.
+// (4 KB, consecutive in xq) leave as four 1 KB stores.
 typedef float xf32x2_t __attribute__((ext_vector_type(2)));
 
 __global__ __launch_bounds__(256) void xprep_kernel(const uint16_t* __restrict__ x, int64_t ldx, int64_t H, int64_t nblk,
                                                     uint8_t* __restrict__ xq, int32_t* __restrict__ zero,
                                                     int64_t nzero, int64_t n) {
   __shared__ __attribute__((aligned(16))) uint8_t stage_in[4][4096];
-  __shared__ __attribute__((aligned(16))) uint8_t stage_out[4][32 * kXRec];
+  __shared__ __attribute__((aligned(16))) uint8_t stage_out[4][32 * kXRecG];
   GRID_STRIDE(i, nzero) zero[i] = 0;  // the routing histogram, cleared for the next launch
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t hb = H / 32;  // real blocks per token
@@ -93,13 +93,15 @@ __global__ __launch_bounds__(256) void xprep_kernel(const uint16_t* __restrict__
         }
       }
     }
-    uint8_t* rec = &stage_out[wave][(lane >> 1) * kXRec];
+    uint8_t* rec = &stage_out[wave][(lane >> 1) * kXRecG];
     u32x4_t* sl = reinterpret_cast<u32x4_t*>(rec + (lane & 1) * kSlot);
     sl[0] = u32x4_t{tq[0][0], tq[0][1], tq[0][2], tq[0][3]};
     sl[1] = u32x4_t{tq[0][4], tq[0][5], tq[1][0], tq[1][1]};
     sl[2] = u32x4_t{tq[1][2], tq[1][3], tq[1][4], tq[1][5]};
     reinterpret_cast<uint32_t*>(rec + 2 * kSlot)[lane & 1] = te[0] | (te[1] << 8);
+    // the record's tail (8 bytes after the scale dwords, then up to kXRecG): zero, 16 bytes per lane
     if ((lane & 1) == 0) *reinterpret_cast<u32x2_t*>(rec + 2 * kSlot + 8) = u32x2_t{0u, 0u};
+    else *reinterpret_cast<u32x4_t*>(rec + kXRec) = u32x4_t{0u, 0u, 0u, 0u};
     __builtin_amdgcn_wave_barrier();
     // coalesced stores: 16-byte chunk c = 64 j + lane of the wave's 32 records (g0 is even, so the
     // wave's first record is g0 / 2; a record exists when its first block does)
@@ -107,8 +109,8 @@ __global__ __launch_bounds__(256) void xprep_kernel(const uint16_t* __restrict__
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       const int c = 64 * j + lane;
-      if (c < kRecChunks && 2 * (r0 + (c * 16) / kXRec) < n)
-        *reinterpret_cast<u32x4_t*>(xq + r0 * kXRec + c * 16) = *reinterpret_cast<const u32x4_t*>(&stage_out[wave][c * 16]);
+      if (2 * (r0 + (c * 16) / kXRecG) < n)
+        *reinterpret_cast<u32x4_t*>(xq + r0 * kXRecG + c * 16) = *reinterpret_cast<const u32x4_t*>(&stage_out[wave][c * 16]);
     }
     __builtin_amdgcn_wave_barrier();  // the next iteration's LDS writes after these reads
   }
