@@ -236,6 +236,10 @@ __global__ __launch_bounds__(1024) void place_kernel(const int32_t* __restrict__
   __shared__ int e_pre[1024], e_off[1024], e_poff[1024], e_tot[1024], e_toff[1024], e_toff2[1024];
   __shared__ uint32_t mlo[1024], mhi[1024];
   __shared__ int wsum[4][16];
+  // the block's pairs as the first wave read them ([slot][lane]; top_k <= 32 at every entry point), so
+  // the ranking pass reads LDS instead of global memory again
+  __shared__ int32_t s_ex[32][64];
+  __shared__ float s_wt[32][64];
   __shared__ int slack0;  // first slack row (workgroup 0)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int blk = blockIdx.x;
@@ -340,21 +344,6 @@ __global__ __launch_bounds__(1024) void place_kernel(const int32_t* __restrict__
     if (live)
       for (int j0 = 0; j0 < k; j0 += 4) {
         int exs[4];
-#pragma unroll
-        for (int u = 0; u < 4; u++) exs[u] = j0 + u < k ? ids[t * k + j0 + u] : -1;
-#pragma unroll
-        for (int u = 0; u < 4; u++) {
-          if (exs[u] < 0) continue;
-          if (lane < 32) atomicOr(&mlo[exs[u]], 1u << lane);
-          else atomicOr(&mhi[exs[u]], 1u << (lane - 32));
-        }
-      }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
-    if (live) {
-      const uint64_t lt = (1ull << lane) - 1ull;
-      for (int j0 = 0; j0 < k; j0 += 4) {
-        int exs[4];
         float ws[4];
 #pragma unroll
         for (int u = 0; u < 4; u++) {
@@ -363,18 +352,28 @@ __global__ __launch_bounds__(1024) void place_kernel(const int32_t* __restrict__
         }
 #pragma unroll
         for (int u = 0; u < 4; u++) {
-          const int ex = exs[u];
-          if (ex < 0) continue;
-          const uint64_t m = ((uint64_t)mhi[ex] << 32) | mlo[ex];
-          const int rank = e_pre[ex] + __popcll(m & lt);
-          const int32_t pair = (int32_t)(t * k + j0 + u);
-          if (sorted_pairs) sorted_pairs[e_off[ex] + rank] = pair;
-          const int r = e_poff[ex] + rank;
-          prow_pair[r] = pair;
-          prow_tok[r] = (int32_t)t;
-          prow_w[r] = ws[u];
-          if (pair_prow) pair_prow[pair] = r;
+          if (exs[u] < 0) continue;
+          s_ex[j0 + u][lane] = exs[u];
+          s_wt[j0 + u][lane] = ws[u];
+          if (lane < 32) atomicOr(&mlo[exs[u]], 1u << lane);
+          else atomicOr(&mhi[exs[u]], 1u << (lane - 32));
         }
+      }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+    if (live) {
+      const uint64_t lt = (1ull << lane) - 1ull;
+      for (int j = 0; j < k; j++) {
+        const int ex = s_ex[j][lane];
+        const uint64_t m = ((uint64_t)mhi[ex] << 32) | mlo[ex];
+        const int rank = e_pre[ex] + __popcll(m & lt);
+        const int32_t pair = (int32_t)(t * k + j);
+        if (sorted_pairs) sorted_pairs[e_off[ex] + rank] = pair;
+        const int r = e_poff[ex] + rank;
+        prow_pair[r] = pair;
+        prow_tok[r] = (int32_t)t;
+        prow_w[r] = s_wt[j][lane];
+        if (pair_prow) pair_prow[pair] = r;
       }
     }
   }
