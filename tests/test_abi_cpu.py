@@ -120,3 +120,19 @@ def test_route_and_forward_validation(L):
     assert fw(*bad) == ALIGN
     bad = list(args); bad[3] = 0
     assert fw(*bad) == OK  # no tokens: nothing to do
+
+
+def test_forward_rejects_activation_buffers_past_32_bit_offsets(L):
+    """The GEMMs address the split activations with 32-bit byte offsets: the first GEMM's records
+    take T * H / 64 * 128 bytes, the second GEMM's operand about 1.5 bytes per padded row and I
+    element.  Shapes whose buffers reach 4 GiB are rejected before any launch (and before the
+    workspace size is looked at)."""
+    fw = L.moe_mxfp4_forward
+    d = dims(8, 7168, 2048)
+    limit = (1 << 32) // (7168 // 64 * 128)  # tokens at which the first GEMM's records reach 4 GiB
+    assert fw(d, FAKE, FAKE, limit + 1, 7168, FAKE, 1, 1, FAKE, None, None, FAKE, 1 << 62, None) == SHAPE
+    # just below: the size check passes and the (too small) workspace is what fails
+    assert fw(d, FAKE, FAKE, limit - 1, 7168, FAKE, 1, 1, FAKE, None, None, FAKE, 256, None) == WS
+    # the second GEMM's operand: 100000 tokens x top-16 pairs, I = 2048 -> about 4.9e9 bytes
+    d2 = dims(64, 256, 2048)
+    assert fw(d2, FAKE, FAKE, 100000, 256, FAKE, 16, 1, FAKE, None, None, FAKE, 1 << 62, None) == SHAPE

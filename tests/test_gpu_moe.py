@@ -66,6 +66,7 @@ def test_tiny_config():
     (200, 16, 4, 256, 160, False, False),  # unnormalized weights, 2 row groups per tile
     (2048, 8, 2, 128, 64, True, True),   # 4 row groups per tile, long expert lists
     (70, 33, 7, 224, 288, True, True),   # ragged everything
+    (100, 1024, 32, 64, 64, True, True),  # the largest expert count and top-k the entry points accept
 ])
 def test_ragged_shapes(T, E, k, H, I, bias, ren):
     cfg = synth.custom_moe_config(f"r{T}_{E}_{k}_{H}_{I}", T, E, k, H, I, bias=bias, renormalize=ren, cid=110 + T)
