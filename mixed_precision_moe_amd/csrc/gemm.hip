@@ -811,7 +811,7 @@ int launch_gemm1(int NRG, const GemmArgs& a, int64_t max_tiles, hipStream_t stre
   switch (NRG) {
     case 1: return launch_cfg<true, 1, 4, 1, 4, 3, 2>(a, max_tiles, stream);
     case 2: return launch_cfg<true, 1, 4, 2, 4, 3, 2>(a, max_tiles, stream);
-    case 4: return launch_cfg<true, 2, 2, 2, 8, 5, 1>(a, max_tiles, stream);
+    case 4: return launch_cfg<true, 2, 2, 2, 8, 4, 1>(a, max_tiles, stream);
     default: return MXFP4_ERR_SHAPE;
   }
 }
