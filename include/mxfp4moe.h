@@ -63,7 +63,8 @@ uint32_t mxfp4_version(void);
  *               stride is explicit.
  * q_u8          device, uint8 [M, K/2], required.
  * scale_flat_u8 device, uint8 [M, K/32], may be NULL (1-byte alignment suffices).
- * scale_tiled_u8 device, uint8 [ceil(M/128), ceil(K/128), 32, 4, 4], may be NULL: the byte at
+ * scale_tiled_u8 device, uint8 [ceil(M/128), ceil(K/128), 32, 4, 4], 16-byte aligned (each
+ *               [mT][kT][oM] group of 16 bytes is written with one store), may be NULL: the byte at
  *               [mT][kT][oM][iM][iK] is the scale of row mT*128 + iM*32 + oM and scale column
  *               kT*4 + iK; padding bytes are written as 0.  [P3 Key source snippets, the untile
  *               helper's permute (0, 3, 2, 1, 4)]

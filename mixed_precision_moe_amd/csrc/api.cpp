@@ -154,7 +154,7 @@ MX_API int mxfp4_quantize(const void* x_bf16, int64_t M, int64_t K, int64_t ldx,
   if (M > (1LL << 40) / (ldx > 0 ? ldx : 1)) return MXFP4_ERR_SHAPE;
   if (M == 0) return MXFP4_OK;
   if (!x_bf16 || !q_u8) return MXFP4_ERR_NULL;
-  if (!aligned(x_bf16, 16) || !aligned(q_u8, 4) || (scale_tiled_u8 && !aligned(scale_tiled_u8, 4)))
+  if (!aligned(x_bf16, 16) || !aligned(q_u8, 4) || (scale_tiled_u8 && !aligned(scale_tiled_u8, 16)))
     return MXFP4_ERR_ALIGN;
   return launch_quantize(x_bf16, M, K, ldx, q_u8, scale_flat_u8, scale_tiled_u8, S(stream));
 }

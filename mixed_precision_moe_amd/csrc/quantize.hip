@@ -3,8 +3,11 @@
 // [P3 Implementation breakdown item 1; Key source snippets: the E8M0 reference helper, the UE8M0_SF
 //  branch of the FP16/BF16 -> FP4 converter and the tiled-scale untile helper; DEF element rule]
 //
-// Work split: a wave covers 512 consecutive columns (16 blocks) of four rows; lane l owns eight
-// bf16 (one 16-byte load) of each row, four lanes per 32-element block.  The block maximum is a
+// Work split: a wave covers 512 consecutive columns (16 blocks) of four rows 32 apart, rows
+// mT*128 + iM*32 + oM for iM = 0..3 (a workgroup's four waves take four consecutive oM); lane l owns
+// eight bf16 (one 16-byte load) of each row, four lanes per 32-element block.  The four rows are the
+// four iM of one 16-byte group of the tiled scale layout, so each group is written whole, by one lane
+// with one store.  The block maximum is a
 // max of bf16 magnitude bits (monotone for non-negative values), reduced over the four lanes.
 // Cross-lane steps are DPP moves (no LDS round trips).  Elements are encoded by v_cvt_scalef32_pk_fp4_bf16, which divides by the E8M0 scale and rounds
 // to nearest even with saturation and a kept sign -- the element rule exactly (checked against the
@@ -31,12 +34,15 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
   const bool flat_words = (K / 32) % 4 == 0;  // every row's flat scales start dword-aligned
   const int64_t nby = Mpad / kRowsPerBlock;
   for (int64_t by = blockIdx.y; by < nby; by += gridDim.y) {
-  const int64_t row0 = by * kRowsPerBlock + wave * kRowsPerWave;
+  // row r of this wave: mT * 128 + r * 32 + oM (128 / kRowsPerBlock = 8 workgroups per 128-row tile)
+  const int64_t mT = by >> 3, oM = ((by & 7) << 2) + wave;
+  const int64_t row0 = mT * 128 + oM;
+  uint32_t tw[kRowsPerWave];  // tiled scale words of the four rows (lanes 16j)
 
   u32x4_t v[kRowsPerWave];
 #pragma unroll
   for (int r = 0; r < kRowsPerWave; r++) {
-    const int64_t row = row0 + r;
+    const int64_t row = row0 + 32 * r;
     if (col_in && row < M)
       v[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(x + row * ldx + col));
     else
@@ -45,7 +51,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
 
 #pragma unroll
   for (int r = 0; r < kRowsPerWave; r++) {
-    const int64_t row = row0 + r;
+    const int64_t row = row0 + 32 * r;
     // largest magnitude among this lane's eight values
     uint32_t w[4] = {v[r][0], v[r][1], v[r][2], v[r][3]};
     uint32_t m = 0;
@@ -86,11 +92,12 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
         }
       }
     }
-    if (stiled && col_live && (lane & 15) == 0) {
-      const int64_t mT = row >> 7, iM = (row >> 5) & 3, oM = row & 31;
-      const int64_t kT = col >> 7;
-      *reinterpret_cast<uint32_t*>(stiled + ((mT * kTiles + kT) * 32 + oM) * 16 + iM * 4) = word;
-    }
+    tw[r] = word;
+  }
+  // the 16-byte tiled group (mT, kT, oM): the words of iM = 0..3
+  if (stiled && col_live && (lane & 15) == 0) {
+    const int64_t kT = col >> 7;
+    *reinterpret_cast<u32x4_t*>(stiled + ((mT * kTiles + kT) * 32 + oM) * 16) = u32x4_t{tw[0], tw[1], tw[2], tw[3]};
   }
   }
 }

@@ -61,6 +61,7 @@ def test_quantize_validation(L):
     assert L.mxfp4_quantize(FAKE, 4, 64, 64, None, None, None, None) == NULL
     assert L.mxfp4_quantize(FAKE + 8, 4, 64, 64, FAKE, None, None, None) == ALIGN
     assert L.mxfp4_quantize(FAKE, 4, 64, 64, FAKE + 2, None, None, None) == ALIGN
+    assert L.mxfp4_quantize(FAKE, 4, 64, 64, FAKE, None, FAKE + 4, None) == ALIGN  # tiled scales: 16 bytes
     assert L.mxfp4_quantize(None, 0, 64, 64, None, None, None, None) == OK  # empty: no-op
     assert L.mxfp4_tiled_scale_bytes(8192, 7168) == 64 * 56 * 512
     assert L.mxfp4_tiled_scale_bytes(129, 160) == 2 * 2 * 512
