@@ -140,7 +140,9 @@ struct StepTask {
 };
 // COPIES_FIRST puts the copies right after the step's first MFMAs (for a latency-bound GEMM with few
 // K steps per item); otherwise they are spread over the MFMAs after the first group.
-template <int RW, int CW, int KOPS, bool COPIES_FIRST>
+// LATE: the step's fragment loads are not interleaved (they follow the step's MFMAs, see the kernel);
+// only the copies are placed.
+template <int RW, int CW, int KOPS, bool COPIES_FIRST, bool LATE = false>
 struct StepPlan {
   static constexpr int G = CW / 2, NM = 4 * RW * G, kCap = 6, kPer = 2;
   int t[NM][kCap];
@@ -158,6 +160,10 @@ struct StepPlan {
   constexpr StepPlan() : t{} {
     for (int m = 0; m < NM; m++)
       for (int c = 0; c < kCap; c++) t[m][c] = StepTask::kNone;
+    if (LATE) {
+      for (int i = 0; i < KOPS; i++) place(StepTask::kDma + i, COPIES_FIRST ? 0 : i * NM / KOPS);
+      return;
+    }
     // the last group's fragments shortly before that group, so few loads are younger than them
     const int def_at = (G - 1) * 4 * RW - 4 > 0 ? (G - 1) * 4 * RW - 4 : 0;
     if (COPIES_FIRST) {
@@ -183,6 +189,7 @@ struct StepPlan {
           n++;
           if (t[m][c] < StepTask::kX) def_last = m;
         }
+    if (LATE) return n == KOPS && n_at(NM - 1) < kCap;
     return n == 2 + RW + 1 + (CW - 2) + KOPS && def_last < (G - 1) * 4 * RW && n_at(NM - 1) < kCap;
   }
 };
@@ -470,7 +477,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
   typedef const __attribute__((address_space(3))) u32x4_t* lds16_p;
   typedef const __attribute__((address_space(3))) u32x2_t* lds8_p;
   typedef const __attribute__((address_space(3))) uint32_t* lds4_p;
-  using Plan = StepPlan<RW, CW, C::kOps, !G1>;
+  // The second GEMM (12 K steps at I = 768, two workgroups per CU, a 3-stage ring) loads the next
+  // step's fragments after the step's MFMAs (LATE), so a stage is needed one step later than with
+  // loads interleaved into the MFMAs: its copies get about two steps instead of one to land.
+  constexpr bool LATE = !G1;
+  using Plan = StepPlan<RW, CW, C::kOps, !G1, LATE>;
   static constexpr Plan plan{};
   static_assert(plan.valid(), "step plan");
   i32x8_t xop[2][RW][kTerms];
@@ -565,7 +576,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
 #pragma unroll
       for (int r = 0; r < RW; r++) load_x(b0, r, std::integral_constant<int, 0>{});
 #pragma unroll
-      for (int j = 0; j < CW - 2; j++) load_w(b0, j);
+      for (int j = 0; j < (LATE ? CW : CW - 2); j++) load_w(b0, j);
       load_ws(b0, std::integral_constant<int, 0>{});
     }
 #pragma unroll
@@ -584,12 +595,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
       constexpr int P = decltype(pc)::value;
       constexpr bool MAIN = decltype(mc)::value;
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (MAIN)
-        wait_vmcnt<C::kOps * (D - 3)>();
-      else
-        wait_stages(nkt - kt - 2, std::integral_constant<int, D - 3>{});
-      block_sync();
-      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (!LATE) {
+        if constexpr (MAIN)
+          wait_vmcnt<C::kOps * (D - 3)>();
+        else
+          wait_stages(nkt - kt - 2, std::integral_constant<int, D - 3>{});
+        block_sync();
+        __builtin_amdgcn_sched_barrier(0);
+      }
       const int kn = kt + 1 < nkt ? kt + 1 : kt;
       const uint8_t* cb = smem + (kt % D) * C::kStage;
       const uint8_t* nb = smem + (kn % D) * C::kStage;
@@ -617,6 +630,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
         });
         __builtin_amdgcn_sched_barrier(0);
       });
+      if constexpr (LATE) {
+        // Stage kt+1 (my copies landed) becomes everyone's at the barrier; the stages after it
+        // (kt+2 .. min(kt+D-1, nkt-1), this step's copies among them) may stay in flight.  Every wave
+        // has by then finished reading stage kt (its fragments fed this step's MFMAs), so the next
+        // step may copy into that slot.
+        if (kt + 1 < nkt) {
+          __builtin_amdgcn_sched_barrier(0);
+          if constexpr (MAIN)
+            wait_vmcnt<C::kOps * (D - 2)>();
+          else
+            wait_stages(nkt - kt - 2, std::integral_constant<int, D - 2>{});
+          block_sync();
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int r = 0; r < RW; r++) load_x(nb, r, std::integral_constant<int, 1 - P>{});
+#pragma unroll
+          for (int j = 0; j < CW; j++) load_w(nb, j);
+          load_ws(nb, std::integral_constant<int, 1 - P>{});
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
     };
     // main steps in pairs (an even count, so the buffers are back in place), then the rest
     const int nmain = nkt > D - 1 ? ((nkt - (D - 1)) & ~1) : 0;
