@@ -477,10 +477,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
   typedef const __attribute__((address_space(3))) u32x4_t* lds16_p;
   typedef const __attribute__((address_space(3))) u32x2_t* lds8_p;
   typedef const __attribute__((address_space(3))) uint32_t* lds4_p;
-  // The second GEMM (12 K steps at I = 768, two workgroups per CU, a 3-stage ring) loads the next
-  // step's fragments after the step's MFMAs (LATE), so a stage is needed one step later than with
-  // loads interleaved into the MFMAs: its copies get about two steps instead of one to land.
-  constexpr bool LATE = !G1;
+  // The second GEMM (two workgroups per CU, a 3-stage ring) and the first GEMM's 64-row configuration
+  // (two per CU, 3 stages; long weight streams such as H = 7168) load the next step's fragments after
+  // the step's MFMAs (LATE), so a stage is needed one step later than with loads interleaved into the
+  // MFMAs: its copies get about two steps instead of one to land.  The first GEMM's 32-row (decode)
+  // and 128-row configurations measured faster with interleaved loads.
+  constexpr bool LATE = !G1 || (D == 3 && RW == 2);
   using Plan = StepPlan<RW, CW, C::kOps, !G1, LATE>;
   static constexpr Plan plan{};
   static_assert(plan.valid(), "step plan");
