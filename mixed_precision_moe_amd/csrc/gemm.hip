@@ -32,6 +32,9 @@
 // barrier per step publishes the stage.  Operand fragments of step kt+1 are read from LDS while the
 // MFMAs of step kt run: a fixed plan (StepPlan) orders each step's MFMAs and puts after each MFMA its
 // share of the fragment loads and copies, so their instructions issue while the matrix core works.
+// Configurations with a 3-stage ring at two workgroups per CU (the second GEMM, the first GEMM's
+// 64-row tiles) instead load step kt+1's fragments after step kt's MFMAs ("late"), which leaves the
+// copies about one more step to land.
 // Work items (M tile, column position) are dealt to XCDs in contiguous ranges
 // so the column positions of one M tile (same gathered tokens) and consecutive tiles of one expert
 // (same weights) share an XCD's L2.
