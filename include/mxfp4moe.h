@@ -62,7 +62,8 @@ uint32_t mxfp4_version(void);
  *               contiguous copy before quantizing [P3 Implementation breakdown item 2]; here the
  *               stride is explicit.
  * q_u8          device, uint8 [M, K/2], required.
- * scale_flat_u8 device, uint8 [M, K/32], may be NULL (1-byte alignment suffices).
+ * scale_flat_u8 device, uint8 [M, K/32], may be NULL; any alignment (byte stores are used unless the
+ *               pointer is 4-byte aligned and K/32 is a multiple of 4, then whole dwords).
  * scale_tiled_u8 device, uint8 [ceil(M/128), ceil(K/128), 32, 4, 4], 16-byte aligned (each
  *               [mT][kT][oM] group of 16 bytes is written with one store), may be NULL: the byte at
  *               [mT][kT][oM][iM][iK] is the scale of row mT*128 + iM*32 + oM and scale column
@@ -97,8 +98,10 @@ enum {
 size_t mxfp4_repack_bytes(const mxfp4_moe_dims* d, uint32_t layout);
 
 /* Byte offsets of the six tensors inside a checked-conversion output (layout != GFX950), in the
- * order w13_q, w13_s, w2_q, w2_s, b13, b2 (the order of the pages' conversion result
- * [P2 Key source snippets]); each offset is 256-byte aligned.  Returns a status. */
+ * order w13_q, w2_q, w13_s, w2_s, b13, b2: the order in which the pages' conversion returns
+ * (w13 weight, w2 weight, w13 scale, w2 scale, w13 bias, w2 bias) [P2 Key source snippets, the
+ * conversion branch's return tuple and the test's converted[0..5]]; each offset is 256-byte aligned.
+ * Returns a status. */
 int mxfp4_repack_offsets(const mxfp4_moe_dims* d, uint32_t layout, size_t offsets_out[6]);
 
 /* Weight conversion at load time.  [P2 Implementation breakdown items 1-3, Key source snippets]
@@ -106,8 +109,9 @@ int mxfp4_repack_offsets(const mxfp4_moe_dims* d, uint32_t layout, size_t offset
  * required); bias_is_fp32 selects fp32 (else bf16) input, 4-byte/2-byte aligned.
  * layout = MXFP4_LAYOUT_GFX950: writes the execution blob consumed by moe_mxfp4_forward.
  * layout = MXFP4_LAYOUT_STD_W31 [| MXFP4_LAYOUT_SCALE_TILED], or MXFP4_LAYOUT_SCALE_TILED alone:
- *   writes the six standard tensors at mxfp4_repack_offsets(): w13_q and w13_s with their row
- *   halves exchanged ([w1; w3] -> [w3; w1]) when STD_W31 is set, w2 unchanged, b13 halves exchanged
+ *   writes the six standard tensors at mxfp4_repack_offsets() (w13_q, w2_q, w13_s, w2_s, b13, b2 in
+ *   that order): w13_q and w13_s with their row halves exchanged ([w1; w3] -> [w3; w1]) when
+ *   STD_W31 is set, w2 unchanged, b13 halves exchanged
  *   likewise, both biases as bf16; with SCALE_TILED both scale tensors are written per expert in the
  *   tiled layout [E, ceil(rows/128), ceil(K/128), 32, 4, 4] instead of flat.  These conversions
  *   exist to check this library against the pages' layouts; the forward pass does not use them.

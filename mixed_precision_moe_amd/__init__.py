@@ -17,7 +17,8 @@ LAYOUT_STD_W31 = 1
 LAYOUT_SCALE_TILED = 2
 
 __all__ = ["quantize", "tiled_scale_shape", "repack_weights", "unpack_weights", "check_packed", "route",
-           "moe_forward", "MoE", "MoeDims", "Mxfp4Error", "LAYOUT_GFX950", "LAYOUT_STD_W31", "LAYOUT_SCALE_TILED"]
+           "moe_forward", "MoE", "MoeDims", "Mxfp4Error",
+           "LAYOUT_GFX950", "LAYOUT_STD_W31", "LAYOUT_SCALE_TILED"]
 
 
 def _stream():
@@ -62,7 +63,8 @@ def _dims(E, H, I, has_bias):
 
 def repack_weights(w13_q, w13_s, w2_q, w2_s, b13=None, b2=None, layout=LAYOUT_GFX950):
     """Standard checkpoint tensors (w13 rows [w1; w3]) -> execution blob (layout GFX950), or the six
-    standard tensors of a checked conversion (other layouts), returned as a tuple."""
+    standard tensors of a checked conversion (other layouts), returned as a tuple in the order
+    (w13_q, w2_q, w13_s, w2_s, b13, b2)."""
     for n, t in (("w13_q", w13_q), ("w13_s", w13_s), ("w2_q", w2_q), ("w2_s", w2_s)):
         _cuda(t, n)
         _need(t.dtype == torch.uint8 and t.is_contiguous() and t.dim() == 3, f"{n} must be contiguous uint8 3-D")
@@ -91,9 +93,10 @@ def repack_weights(w13_q, w13_s, w2_q, w2_s, b13=None, b2=None, layout=LAYOUT_GF
     offs = (ctypes.c_size_t * 6)()
     check("mxfp4_repack_offsets", L.mxfp4_repack_offsets(ctypes.byref(d), layout, offs))
     tiled = bool(layout & LAYOUT_SCALE_TILED)
+    # the order of the pages' conversion result: w13, w2, w13 scales, w2 scales, b13, b2
     shapes = [(E, 2 * I, H // 2),
-              (E,) + tiled_scale_shape(2 * I, H) if tiled else (E, 2 * I, H // 32),
               (E, H, I // 2),
+              (E,) + tiled_scale_shape(2 * I, H) if tiled else (E, 2 * I, H // 32),
               (E,) + tiled_scale_shape(H, I) if tiled else (E, H, I // 32),
               (E, 2 * I), (E, H)]
     res = []

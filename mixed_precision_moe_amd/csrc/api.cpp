@@ -1,42 +1,18 @@
 // C ABI of the library: argument validation (before any device work), workspace carving and the
 // stream-ordered launch sequence.  Declarations and the contract of every entry point are in
 // include/mxfp4moe.h.
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <cstring>
 
-#include "common.h"
+#include "internal.h"
 
 #define MX_API extern "C" __attribute__((visibility("default")))
-
-// launchers (defined next to their kernels)
-int launch_quantize(const void* x, int64_t M, int64_t K, int64_t ldx, void* q, void* sflat, void* stiled,
-                    hipStream_t stream);
-int launch_repack_gfx950(const MoeGeom& g, const BlobOffsets& o, bool bias, const void* w13_q, const void* w13_s,
-                         const void* w2_q, const void* w2_s, const void* b13, const void* b2, int bias_is_fp32,
-                         void* out, hipStream_t stream);
-int launch_unpack_gfx950(const MoeGeom& g, const BlobOffsets& o, bool bias, const void* packed, void* w13_q,
-                         void* w13_s, void* w2_q, void* w2_s, void* b13, void* b2, hipStream_t stream);
-int launch_repack_standard(const MoeGeom& g, bool bias, const void* w13_q, const void* w13_s, const void* w2_q,
-                           const void* w2_s, const void* b13, const void* b2, int bias_is_fp32, bool swap, bool tiled,
-                           const size_t off[6], void* out, hipStream_t stream);
-int launch_xprep(const void* x, int64_t T, int64_t ldx, const MoeGeom& g, void* xq, int32_t* zero, int64_t nzero,
-                 hipStream_t stream);
-int launch_zero_i32(int32_t* p, int64_t n, hipStream_t stream);
-int launch_route(const float* logits, int64_t T, int E, int k, int renormalize, int32_t* ids, float* w,
-                 int32_t* blkcnt, hipStream_t stream);
-int launch_place(const int32_t* ids, const float* w, int32_t* blkcnt, int64_t T, int k, int E, int BM, int BM2,
-                 int32_t* offsets, int32_t* poffsets, int32_t* sorted_pairs, int32_t* prow_pair, int32_t* prow_tok,
-                 float* prow_w, int32_t* pair_prow, void* tiles, int32_t* ntiles, void* tiles2, int32_t* ntiles2,
-                 hipStream_t stream);
-int launch_gemm1(int NRG, const GemmArgs& a, int64_t max_tiles, hipStream_t stream);
-int launch_gemm2(int NRG, const GemmArgs& a, int64_t max_tiles, hipStream_t stream);
-int launch_combine(const uint16_t* o16, const uint8_t* osc, const int32_t* pair_prow, void* y, int64_t T, int64_t H, int k,
-                   hipStream_t stream);
 
 namespace {
 
 constexpr int kMaxE = 1024;
+constexpr int64_t kMaxDim = int64_t(1) << 40;  // bound on any matrix dimension (keeps sizes in 64 bits)
 constexpr int kMaxTopK = 32;
 
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -58,13 +34,14 @@ bool valid_layout(uint32_t layout) {
 void standard_sizes(const mxfp4_moe_dims* d, uint32_t layout, size_t sz[6]) {
   const int64_t E = d->E, H = d->H, I = d->I;
   const bool tiled = layout & MXFP4_LAYOUT_SCALE_TILED;
+  // the order of the pages' conversion result: w13, w2, w13 scales, w2 scales, b13, b2
   sz[0] = (size_t)(E * 2 * I * (H / 2));
-  sz[2] = (size_t)(E * H * (I / 2));
+  sz[1] = (size_t)(E * H * (I / 2));
   if (tiled) {
-    sz[1] = (size_t)(E * cdiv(2 * I, 128) * cdiv(H / 32, 4) * 512);
+    sz[2] = (size_t)(E * cdiv(2 * I, 128) * cdiv(H / 32, 4) * 512);
     sz[3] = (size_t)(E * cdiv(H, 128) * cdiv(I / 32, 4) * 512);
   } else {
-    sz[1] = (size_t)(E * 2 * I * (H / 32));
+    sz[2] = (size_t)(E * 2 * I * (H / 32));
     sz[3] = (size_t)(E * H * (I / 32));
   }
   sz[4] = d->has_bias ? (size_t)(E * 2 * I * 2) : 0;
@@ -122,7 +99,7 @@ RouteWs route_ws(int64_t T, int64_t E, int64_t k) {
 
 int check_route_args(int64_t T, int32_t E, int32_t top_k) {
   if (T < 0 || E < 1 || E > kMaxE || top_k < 1 || top_k > E || top_k > kMaxTopK) return MXFP4_ERR_SHAPE;
-  if (T * top_k + 32LL * E + 256 > (1LL << 31) - 1) return MXFP4_ERR_SHAPE;
+  if (T > (1LL << 31) || T * top_k + 32LL * E + 256 > (1LL << 31) - 1) return MXFP4_ERR_SHAPE;
   return MXFP4_OK;
 }
 
@@ -144,14 +121,14 @@ MX_API const char* mxfp4_status_str(int status) {
 MX_API uint32_t mxfp4_version(void) { return (1u << 16) | 0u; }
 
 MX_API size_t mxfp4_tiled_scale_bytes(int64_t M, int64_t K) {
-  if (M < 0 || K < 32 || K % 32) return 0;
+  if (M < 0 || K < 32 || K % 32 || M > kMaxDim || K > kMaxDim) return 0;
   return (size_t)(cdiv(M, 128) * cdiv(K / 32, 4) * 512);
 }
 
 MX_API int mxfp4_quantize(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, void* q_u8, void* scale_flat_u8,
                           void* scale_tiled_u8, void* stream) {
-  if (M < 0 || K < 32 || K % 32 || ldx < K || ldx % 8) return MXFP4_ERR_SHAPE;
-  if (M > (1LL << 40) / (ldx > 0 ? ldx : 1)) return MXFP4_ERR_SHAPE;
+  if (M < 0 || K < 32 || K % 32 || ldx < K || ldx % 8 || ldx > kMaxDim) return MXFP4_ERR_SHAPE;
+  if (M > kMaxDim / ldx) return MXFP4_ERR_SHAPE;
   if (M == 0) return MXFP4_OK;
   if (!x_bf16 || !q_u8) return MXFP4_ERR_NULL;
   if (!aligned(x_bf16, 16) || !aligned(q_u8, 4) || (scale_tiled_u8 && !aligned(scale_tiled_u8, 16)))
@@ -272,7 +249,7 @@ MX_API size_t moe_mxfp4_workspace_bytes(const mxfp4_moe_dims* d, int64_t T, int3
   return (size_t)fwd_ws(moe_geom(d->E, d->H, d->I), T, top_k).total;
 }
 
-static int forward_impl(const mxfp4_moe_dims* d, const void* packed_gfx950, const void* x_bf16, int64_t T,
+int forward_impl(const mxfp4_moe_dims* d, const void* packed_gfx950, const void* x_bf16, int64_t T,
                         int64_t ldx, const float* router_logits, int32_t top_k, int32_t renormalize, void* y_bf16,
                         int32_t* topk_ids, float* topk_w, void* workspace, size_t workspace_bytes, hipStream_t s,
                         void* const* events, int32_t n_events) {
@@ -321,7 +298,7 @@ static int forward_impl(const mxfp4_moe_dims* d, const void* packed_gfx950, cons
   const uint8_t* blob = (const uint8_t*)packed_gfx950;
   GemmArgs a1 = {blob + o.w13q, blob + o.w13s, d->has_bias ? (const uint16_t*)(blob + o.b13) : nullptr,
                  ws + w.xq, nullptr, (const int32_t*)(ws + w.prow_tok), (const int32_t*)(ws + w.prow_pair),
-                 (const float*)(ws + w.prow_w), (const int4*)(ws + w.tiles), (const int32_t*)(ws + w.ntiles),
+                 (const float*)(ws + w.prow_w), (const TileDesc*)(ws + w.tiles), (const int32_t*)(ws + w.ntiles),
                  ws + w.actq, ws + w.acts, nullptr, nullptr, (int32_t)g.nkt1, (int32_t)g.ncb1, (int32_t)g.nit,
                  (int32_t)g.nkt2, (int32_t)g.nkt1, (int32_t)g.I, (int32_t)g.H};
   if ((st = launch_gemm1(NRG1, a1, w.max_tiles, s)) || (st = mark())) return st;
@@ -336,7 +313,7 @@ static int forward_impl(const mxfp4_moe_dims* d, const void* packed_gfx950, cons
   a2.nkt = (int32_t)g.nkt2;
   a2.ncb = (int32_t)g.ncb2;
   a2.ntl = (int32_t)g.nht;
-  a2.tiles = (const int4*)(ws + w.tiles2);
+  a2.tiles = (const TileDesc*)(ws + w.tiles2);
   a2.ntiles = (const int32_t*)(ws + w.ntiles2);
   if ((st = launch_gemm2(NRG2, a2, w.max_tiles, s)) || (st = mark())) return st;
   if ((st = launch_combine((const uint16_t*)(ws + w.o16), ws + w.osc, (const int32_t*)(ws + w.pair_prow), y_bf16, T, g.H,

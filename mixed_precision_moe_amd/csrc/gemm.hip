@@ -41,6 +41,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "internal.h"
 
 namespace {
 
@@ -384,8 +385,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
   using Src = ItemSrc<C::nX, C::nXS>;
   auto make_src = [&](int item, int tb, Src& sr) __attribute__((always_inline)) {
     const int tile = item / nx, x = item % nx;
-    const int4 td = a.tiles[tile];
-    const int e = td.x, prow0 = td.y;
+    const TileDesc td = a.tiles[tile];
+    const int e = td.e, prow0 = td.prow0;
     const int cb = x * NT / kCB, jj0 = (x * NT) % kCB;
     const int64_t wstep0 = (int64_t)(e * ncb + cb) * nkt;
     sr.wb = wstep0 * (kCB * 1024) + (jj0 + wave * C::nW) * 1024;
@@ -443,8 +444,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
   // the item's bias entries; 256-byte dword copies spread over the waves (repeats are harmless).
   auto issue_tab = [&](int item, int tb) __attribute__((always_inline)) {
     const int tile = item / nx, x = item % nx;
-    const int4 td = a.tiles[tile];
-    const int prow0 = td.y;
+    const TileDesc td = a.tiles[tile];
+    const int prow0 = td.prow0;
     constexpr int kRowOps = kTab / 64;
     const uint8_t* rsrc = G1 ? reinterpret_cast<const uint8_t*>(a.prow_tok) : reinterpret_cast<const uint8_t*>(a.prow_w);
     {
@@ -455,7 +456,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
       constexpr int kBOps = kBias * 2 / 256;  // copies per bias half
       // entries past the end of the bias row (columns beyond I or H, never used) re-read its last pair
       const int len = G1 ? a.I : a.H;
-      const uint16_t* brow = a.bias + (int64_t)td.x * (G1 ? 2 * a.I : a.H);
+      const uint16_t* brow = a.bias + (int64_t)td.e * (G1 ? 2 * a.I : a.H);
 #pragma unroll
       for (int i = 0; i < (G1 ? 2 : 1) * kBOps; i += 4) {
         int o = wave + i;
@@ -564,8 +565,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
 
   while (true) {
     const int tile = item / nx, x = item % nx;
-    const int4 td = a.tiles[tile];
-    const int prow0 = td.y, nrows = td.z;
+    const TileDesc td = a.tiles[tile];
+    const int prow0 = td.prow0, nrows = td.nrows;
     jj0 = (x * NT) % kCB;
     const bool has_next = q + 1 < nq;
     const int tb = q & 1;
@@ -671,9 +672,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
     if (kt < nkt) step(kt, std::integral_constant<int, 0>{}, std::false_type{});
 
     // ---- next item's first D - 1 stages go out before this item's epilogue, so their latency hides
-    // under it.  The last step waited for every copy (the next item's tables included); the barrier
-    // makes sure every wave is done reading the ring.
+    // under it.  make_src reads the next item's token table, whose copy went out at this item's start:
+    // every copy of this wave is waited for here (the interleaved plan's last step has already waited
+    // for all of them, and so has a late-load item of two or more K steps; a late-load item of one K
+    // step has not), and the barrier then makes every wave's table copies visible and every wave done
+    // reading the ring.
     if (has_next) {
+      wait_vmcnt<0>();
       block_sync();
       make_src(item_of(q + 1), tb ^ 1, cur);
 #pragma unroll

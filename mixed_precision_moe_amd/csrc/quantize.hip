@@ -15,6 +15,7 @@
 // layout (rows up to a multiple of 128, columns up to a multiple of 128), whose lanes read nothing and
 // write zero scale bytes there.
 #include "common.h"
+#include "internal.h"
 
 namespace {
 
@@ -25,13 +26,13 @@ constexpr int kRowsPerBlock = kRowsPerWave * kWaves;  // 16
 __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                                        int64_t ldx, uint8_t* __restrict__ q,
                                                        uint8_t* __restrict__ sflat, uint8_t* __restrict__ stiled,
-                                                       int64_t Mpad, int64_t Kpad, int64_t kTiles) {
+                                                       int64_t Mpad, int64_t Kpad, int64_t kTiles,
+                                                       bool flat_words) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t col = (int64_t)blockIdx.x * 512 + lane * 8;
   const bool col_live = col < Kpad;   // uniform over each 16-lane (128-column) group
   const bool col_in = col < K;        // uniform over each 4-lane block (K % 32 == 0)
-  const bool flat_words = (K / 32) % 4 == 0;  // every row's flat scales start dword-aligned
   const int64_t nby = Mpad / kRowsPerBlock;
   for (int64_t by = blockIdx.y; by < nby; by += gridDim.y) {
   // row r of this wave: mT * 128 + r * 32 + oM (128 / kRowsPerBlock = 8 workgroups per 128-row tile)
@@ -112,7 +113,10 @@ int launch_quantize(const void* x, int64_t M, int64_t K, int64_t ldx, void* q, v
   const int64_t Kpad = kTiles * 128;
   const int64_t nby = Mpad / kRowsPerBlock;
   dim3 grid((unsigned)((Kpad + 511) / 512), (unsigned)(nby < 65535 ? nby : 65535));
+  // flat scales as whole dwords only where every row's scales start on a dword boundary (the flat
+  // output itself needs only byte alignment)
+  const bool flat_words = (K / 32) % 4 == 0 && ((uintptr_t)sflat & 3u) == 0;
   hipLaunchKernelGGL(quantize_kernel, grid, dim3(256), 0, stream, (const uint16_t*)x, M, K, ldx, (uint8_t*)q,
-                     (uint8_t*)sflat, (uint8_t*)stiled, Mpad, Kpad, kTiles);
+                     (uint8_t*)sflat, (uint8_t*)stiled, Mpad, Kpad, kTiles, flat_words);
   return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
 }

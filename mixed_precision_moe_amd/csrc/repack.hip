@@ -10,6 +10,7 @@
 // up tile i, so one wave sees both halves of SwiGLU for the same columns; the swap and the tiled
 // scales exist only as checked conversions.  All kernels are grid-stride loops over output units.
 #include "common.h"
+#include "internal.h"
 
 namespace {
 
@@ -292,14 +293,14 @@ int launch_repack_standard(const MoeGeom& g, bool bias, const void* w13_q, const
   const int sw = swap ? 1 : 0;
   LAUNCH1D(rows_copy16_kernel, g.E * 2 * g.I * (g.H / 32), (const u32x4_t*)w13_q, (u32x4_t*)(base + off[0]), 2 * g.I,
            g.H / 32, sw);
-  LAUNCH1D(rows_copy16_kernel, g.E * g.H * (g.I / 32), (const u32x4_t*)w2_q, (u32x4_t*)(base + off[2]), g.H, g.I / 32, 0);
+  LAUNCH1D(rows_copy16_kernel, g.E * g.H * (g.I / 32), (const u32x4_t*)w2_q, (u32x4_t*)(base + off[1]), g.H, g.I / 32, 0);
   if (tiled) {
     const int64_t n13 = g.E * cdiv(2 * g.I, 128) * cdiv(g.H / 32, 4) * 512;
     const int64_t n2 = g.E * cdiv(g.H, 128) * cdiv(g.I / 32, 4) * 512;
-    LAUNCH1D(tile_scales_kernel, n13, (const uint8_t*)w13_s, base + off[1], 2 * g.I, g.H / 32, sw);
+    LAUNCH1D(tile_scales_kernel, n13, (const uint8_t*)w13_s, base + off[2], 2 * g.I, g.H / 32, sw);
     LAUNCH1D(tile_scales_kernel, n2, (const uint8_t*)w2_s, base + off[3], g.H, g.I / 32, 0);
   } else {
-    LAUNCH1D(rows_copy8_kernel, g.E * 2 * g.I * (g.H / 32), (const uint8_t*)w13_s, base + off[1], 2 * g.I, g.H / 32, sw);
+    LAUNCH1D(rows_copy8_kernel, g.E * 2 * g.I * (g.H / 32), (const uint8_t*)w13_s, base + off[2], 2 * g.I, g.H / 32, sw);
     LAUNCH1D(rows_copy8_kernel, g.E * g.H * (g.I / 32), (const uint8_t*)w2_s, base + off[3], g.H, g.I / 32, 0);
   }
   if (bias) {

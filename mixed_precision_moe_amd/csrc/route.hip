@@ -11,6 +11,7 @@
 // the padding rows).  The resulting order is stable: pairs of one expert appear in increasing token
 // order.
 #include "common.h"
+#include "internal.h"
 
 namespace {
 
@@ -227,8 +228,8 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
 __global__ __launch_bounds__(1024) void place_kernel(const int32_t* __restrict__ ids, const float* __restrict__ wts,
                                                      const int32_t* __restrict__ blkcnt, int64_t T, int nb, int k,
                                                      int E, int BM, int BM2, int32_t* __restrict__ offsets,
-                                                     int32_t* __restrict__ poffsets, int4* __restrict__ tiles,
-                                                     int32_t* __restrict__ ntiles, int4* __restrict__ tiles2,
+                                                     int32_t* __restrict__ poffsets, TileDesc* __restrict__ tiles,
+                                                     int32_t* __restrict__ ntiles, TileDesc* __restrict__ tiles2,
                                                      int32_t* __restrict__ ntiles2, int32_t* __restrict__ sorted_pairs,
                                                      int32_t* __restrict__ prow_pair, int32_t* __restrict__ prow_tok,
                                                      float* __restrict__ prow_w, int32_t* __restrict__ pair_prow) {
@@ -317,11 +318,11 @@ __global__ __launch_bounds__(1024) void place_kernel(const int32_t* __restrict__
     for (int ee = wave; ee < E; ee += 16) {
       const int poff = e_poff[ee], total = e_tot[ee], toff = e_toff[ee];
       const int ntl = (total + BM - 1) / BM, pad = ((total + 31) & ~31) - total;
-      for (int i = lane; i < ntl; i += 64) tiles[toff + i] = make_int4(ee, poff + i * BM, min(BM, total - i * BM), 0);
+      for (int i = lane; i < ntl; i += 64) tiles[toff + i] = TileDesc{ee, poff + i * BM, min(BM, total - i * BM), 0};
       if (tiles2) {
         const int toff2 = e_toff2[ee], ntl2 = (total + BM2 - 1) / BM2;
         for (int i = lane; i < ntl2; i += 64)
-          tiles2[toff2 + i] = make_int4(ee, poff + i * BM2, min(BM2, total - i * BM2), 0);
+          tiles2[toff2 + i] = TileDesc{ee, poff + i * BM2, min(BM2, total - i * BM2), 0};
       }
       if (lane < pad) {
         const int r = poff + total + lane;
@@ -430,7 +431,7 @@ int launch_place(const int32_t* ids, const float* w, int32_t* blkcnt, int64_t T,
   const int nb = (int)cdiv(T, kRouteTokens);
   // at least one workgroup, which writes the tables even when there are no tokens
   hipLaunchKernelGGL(place_kernel, dim3((unsigned)(nb > 0 ? nb : 1)), dim3(1024), 0, stream, ids, w, blkcnt, T, nb, k, E,
-                     BM, BM2, offsets, poffsets, (int4*)tiles, ntiles, (int4*)tiles2, ntiles2, sorted_pairs, prow_pair,
+                     BM, BM2, offsets, poffsets, (TileDesc*)tiles, ntiles, (TileDesc*)tiles2, ntiles2, sorted_pairs, prow_pair,
                      prow_tok, prow_w, pair_prow);
   return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
 }

@@ -25,13 +25,15 @@ def silu(g):
 
 
 def moe_ref(x_bits, logits, k, w13_q, w13_s, w2_q, w2_s, b13_bits=None, b2_bits=None,
-            renormalize=True, tokens=None):
+            renormalize=True, tokens=None, experts=None):
     """Vectorized float64 MoE layer, one expert at a time (bounded memory for large E*I*H).
 
     x_bits uint16 [T, H] bf16; logits float32 [T, E]; w13_q uint8 [E, 2I, H/2]; w13_s uint8
     [E, 2I, H/32]; w2_q uint8 [E, H, I/2]; w2_s uint8 [E, H, I/32]; biases bf16 bit patterns
     [E, 2I] / [E, H] or None.  ``tokens``: optional index array; only those rows of y are computed
     (the others stay 0), which lets large configurations be checked on a sample of tokens.
+    ``experts``: optional expert ids; only their terms w_j * o_j are summed into y, so the layer is
+    the sum of the results over any partition of the experts (the sum over j has no prescribed order).
     Returns (y float64 [T, H], ids int32 [T, k], w float64 [T, k]).
     """
     ids, w = route_ref(logits, k, renormalize)
@@ -42,7 +44,7 @@ def moe_ref(x_bits, logits, k, w13_q, w13_s, w2_q, w2_s, b13_bits=None, b2_bits=
     rows = np.arange(T) if tokens is None else np.unique(np.asarray(tokens))
     y = np.zeros((T, H))
     sub_ids = ids[rows]
-    for e in range(E):
+    for e in (range(E) if experts is None else experts):
         r_idx, j_idx = np.nonzero(sub_ids == e)
         if r_idx.size == 0:
             continue

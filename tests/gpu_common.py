@@ -80,6 +80,67 @@ def gpu_standard_weights(cfg):
     return w13_q, w13_s, w2_q, w2_s, b13, b2
 
 
+class OracleExperts:
+    """Oracle-side expert weights held in memory: q and s index like stacked [E, ...] arrays."""
+
+    def __init__(self, E, rows, K):
+        self.qs = [None] * E
+        self.ss = [None] * E
+        self.q = _View(self, 0, (E, rows, K // 2))
+        self.s = _View(self, 1, (E, rows, K // 32))
+
+    def get(self, e):
+        return self.qs[e], self.ss[e]
+
+
+def prepared_weights(cfg):
+    """Both sides' weights from one generation of the bf16 masters: the library quantizes them on the
+    GPU (device tensors in the standard layout, as gpu_standard_weights), the oracle quantizes the same
+    masters itself on worker threads.  Returns (device tensors, oracle w13, oracle w2)."""
+    from oracle import quant as Q
+    dev = device()
+    E, H, I = cfg.E, cfg.H, cfg.I
+    w13_q = torch.empty((E, 2 * I, H // 2), dtype=torch.uint8, device=dev)
+    w13_s = torch.empty((E, 2 * I, H // 32), dtype=torch.uint8, device=dev)
+    w2_q = torch.empty((E, H, I // 2), dtype=torch.uint8, device=dev)
+    w2_s = torch.empty((E, H, I // 32), dtype=torch.uint8, device=dev)
+    o13, o2 = OracleExperts(E, 2 * I, H), OracleExperts(E, H, I)
+
+    def prep(e):
+        m13, m2 = synth.moe_master_expert(cfg, e)
+        return m13, m2, Q.quantize_ref(m13), Q.quantize_ref(m2)
+
+    for e, (m13, m2, r13, r2) in enumerate(ordered_prefetch(prep, range(E))):
+        q, s, _ = mx.quantize(bf16_dev(m13), flat=True, tiled=False)
+        w13_q[e].copy_(q)
+        w13_s[e].copy_(s)
+        q, s, _ = mx.quantize(bf16_dev(m2), flat=True, tiled=False)
+        w2_q[e].copy_(q)
+        w2_s[e].copy_(s)
+        o13.qs[e], o13.ss[e] = r13
+        o2.qs[e], o2.ss[e] = r2
+    b13, b2 = synth.moe_biases(cfg)
+    if b13 is not None:
+        b13, b2 = bf16_dev(b13), bf16_dev(b2)
+    torch.cuda.synchronize()
+    return (w13_q, w13_s, w2_q, w2_s, b13, b2), o13, o2
+
+
+def oracle_moe_threaded(x_bits, logits, k, w13, w2, b13, b2, renormalize=True, tokens=None):
+    """The oracle's MoE layer with its experts spread over worker threads (one BLAS thread each): y is
+    the sum of the results over a partition of the experts."""
+    from oracle import moe as M
+    E = w13.q.shape[0]
+    n = workers()
+    parts = [list(range(i, E, n)) for i in range(n)]
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1), ThreadPoolExecutor(max_workers=n) as ex:
+        ys = list(ex.map(lambda ex_ids: M.moe_ref(x_bits, logits, k, w13.q, w13.s, w2.q, w2.s, b13, b2,
+                                                  renormalize=renormalize, tokens=tokens, experts=ex_ids)[0],
+                         parts))
+    return sum(ys[1:], ys[0])
+
+
 class LazyExperts:
     """Oracle-side expert weights: the same bf16 masters quantized by the oracle, one expert at a time
     on first use.  Indexing yields (q, s) arrays of one expert, like slicing a stacked [E, ...] array."""

@@ -55,23 +55,46 @@ def test_ragged_and_strided_shapes(M, K, ldx):
     check_full(synth.quant_matrix(M, K, cid=200 + M), ldx)
 
 
-def test_full_size_quantize_config_sampled_rows():
+def test_full_size_quantize_config_every_row():
+    """The 8192 x 7168 workload, every nibble and both scale layouts compared with the oracle."""
     cfg = synth.QUANT_CONFIG
     M, K = cfg["M"], cfg["K"]
     bits = synth.quant_matrix(M, K, cid=cfg["cid"])
     print(f"quantize {M}x{K}", flush=True)
     q, sf, st = run_gpu(bits)
-    g = np.random.default_rng(5)
-    rows = np.sort(g.choice(M, size=512, replace=False))
-    qr, sr = Q.quantize_ref(bits[rows])
-    np.testing.assert_array_equal(q[rows], qr)
-    np.testing.assert_array_equal(sf[rows], sr)
-    # tiled output is the flat output permuted, for every row
-    np.testing.assert_array_equal(Q.untile_scales(st, M, K), sf)
-    # zero blocks of the input give scale 0 and zero nibbles
+    qr, sr = Q.quantize_ref(bits)
+    np.testing.assert_array_equal(sf, sr)
+    np.testing.assert_array_equal(q, qr)
+    np.testing.assert_array_equal(st, Q.tile_scales(sr))
+    # zero blocks of the input give scale 0
     zb = np.all(bits.reshape(M, K // 32, 32) == 0, axis=2)
     assert np.count_nonzero(zb) >= 18350
     assert np.all(sf[zb] == 0)
+    # saturated fraction: blocks whose largest scaled magnitude exceeds 6 (significand in (1.5, 1.75))
+    sig = Q.bf16_to_f64(bits.reshape(M, K // 32, 32) & np.uint16(0x7FFF)).max(axis=2)
+    m, _ = np.frexp(sig[sig > 0])
+    frac = float(np.mean((2 * m > 1.5) & (2 * m < 1.75)))
+    print(f"  saturating blocks: {frac:.4f}", flush=True)
+
+
+@pytest.mark.parametrize("offset", [1, 2, 3])
+def test_flat_scales_at_any_byte_offset(offset):
+    """The flat scale output may start at any byte: K/32 = 8 would take dword stores from an aligned
+    pointer, an offset pointer takes byte stores; nothing outside [M, K/32] is written."""
+    M, K = 130, 256
+    bits = synth.quant_matrix(M, K, cid=400 + offset)
+    xd = bf16_dev(bits)
+    q = torch.empty((M, K // 2), dtype=torch.uint8, device="cuda")
+    buf = torch.full((M * (K // 32) + 64,), 0xA5, dtype=torch.uint8, device="cuda")
+    L = mx._lib.lib()
+    st = L.mxfp4_quantize(xd.data_ptr(), M, K, K, q.data_ptr(), buf.data_ptr() + offset, None, None)
+    assert st == 0
+    torch.cuda.synchronize()
+    qr, sr = Q.quantize_ref(bits)
+    got = buf.cpu().numpy()
+    np.testing.assert_array_equal(got[offset: offset + M * (K // 32)].reshape(M, K // 32), sr)
+    assert np.all(got[:offset] == 0xA5) and np.all(got[offset + M * (K // 32):] == 0xA5)
+    np.testing.assert_array_equal(q.cpu().numpy(), qr)
 
 
 def test_empty_matrix_is_noop_and_bad_shapes_rejected():

@@ -70,10 +70,10 @@ def test_checked_conversions_match_oracle(layout, E, H, I):
         e2s = w2_s
     eb13 = C.f32_to_bf16_bits(C.swap_b13_b31(b13) if swap else b13)
     eb2 = C.f32_to_bf16_bits(b2)
-    got = [t.cpu() for t in out]
+    got = [t.cpu() for t in out]  # the page's order: w13, w2, w13 scale, w2 scale, b13, b2
     np.testing.assert_array_equal(got[0].numpy(), e13q)
-    np.testing.assert_array_equal(got[1].numpy(), e13s)
-    np.testing.assert_array_equal(got[2].numpy(), w2_q)
+    np.testing.assert_array_equal(got[1].numpy(), w2_q)
+    np.testing.assert_array_equal(got[2].numpy(), e13s)
     np.testing.assert_array_equal(got[3].numpy(), e2s)
     np.testing.assert_array_equal(got[4].view(torch.int16).numpy().view(np.uint16), eb13)
     np.testing.assert_array_equal(got[5].view(torch.int16).numpy().view(np.uint16), eb2)
@@ -89,11 +89,14 @@ def test_page_swap_probe_through_the_library():
     w2_s = np.arange(E * H, dtype=np.uint8).reshape(E, H, 1)
     b13 = np.arange(2 * I, dtype=np.float32).reshape(E, 2 * I)
     b2 = np.arange(H, dtype=np.float32).reshape(E, H)
-    out = mx.repack_weights(*[dev(a) for a in (w13_q, w13_s, w2_q, w2_s, b13, b2)], layout=mx.LAYOUT_STD_W31)
+    converted = mx.repack_weights(*[dev(a) for a in (w13_q, w13_s, w2_q, w2_s, b13, b2)], layout=mx.LAYOUT_STD_W31)
     torch.cuda.synchronize()
+    # indexed as the page's test indexes the conversion result: 0 w13, 1 w2, 2 w13 scale, 3 w2 scale,
+    # 4 w13 bias, 5 w2 bias
+    out = converted
     np.testing.assert_array_equal(out[0].cpu().numpy(), np.concatenate([w13_q[:, I:], w13_q[:, :I]], axis=1))
-    np.testing.assert_array_equal(out[1].cpu().numpy(), np.concatenate([w13_s[:, I:], w13_s[:, :I]], axis=1))
-    np.testing.assert_array_equal(out[2].cpu().numpy(), w2_q)
+    np.testing.assert_array_equal(out[1].cpu().numpy(), w2_q)
+    np.testing.assert_array_equal(out[2].cpu().numpy(), np.concatenate([w13_s[:, I:], w13_s[:, :I]], axis=1))
     np.testing.assert_array_equal(out[3].cpu().numpy(), w2_s)
     np.testing.assert_array_equal(out[4].float().cpu().numpy(), np.concatenate([b13[:, I:], b13[:, :I]], axis=1))
     np.testing.assert_array_equal(out[5].float().cpu().numpy(), b2)

@@ -82,3 +82,14 @@ def test_token_subset_equals_full_rows():
     ys, _, _ = M.moe_ref(*args[:2], cfg.k, *args[2:], tokens=sub)
     np.testing.assert_allclose(ys[sub], y[sub], rtol=1e-12, atol=1e-15)
     assert np.all(ys[np.setdiff1d(np.arange(12), sub)] == 0)
+
+
+def test_expert_partition_sums_to_the_whole_layer():
+    """y is a sum of per-expert terms: the results over a partition of the experts add up to the
+    result over all of them (how the full-size GPU parity tests spread the oracle over threads)."""
+    cfg = synth.custom_moe_config("p", T=20, E=6, k=3, H=64, I=32, bias=True)
+    args = build(cfg)
+    y, _, _ = M.moe_ref(*args[:2], cfg.k, *args[2:])
+    parts = [M.moe_ref(*args[:2], cfg.k, *args[2:], experts=ex)[0] for ex in ([0, 3], [1, 5], [2, 4])]
+    np.testing.assert_allclose(parts[0] + parts[1] + parts[2], y, rtol=1e-12, atol=1e-15)
+    assert not np.allclose(parts[0], y)  # each part alone is not the layer
