@@ -183,6 +183,25 @@ int moe_mxfp4_forward_profiled(const mxfp4_moe_dims* d, const void* packed_gfx95
                                void* y_bf16, int32_t* topk_ids, float* topk_w, void* workspace, size_t workspace_bytes,
                                void* stream, void* const* events, int32_t n_events);
 
+/* ------------------------------------------------------------------------------------------------
+ * The MoE layer without a workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same arguments,
+ * arithmetic and result as moe_mxfp4_forward, whose kernels it shares; the workspace is a device
+ * array of MXFP4_NOALLOC_SCRATCH_BYTES inside the library (one per device, held until the process
+ * ends), so the call allocates nothing.
+ * Limit: moe_mxfp4_workspace_bytes(d, T, top_k) must not exceed MXFP4_NOALLOC_SCRATCH_BYTES, else
+ *   MXFP4_ERR_WORKSPACE (nothing is launched).  It covers e.g. E = 128, H = 2048, I = 768, top-8 up
+ *   to about 200 tokens.
+ * The array of the current device is used (make the stream's device current).  Every call on a
+ * device shares that device's array: calls that may overlap on one device (streams without ordering
+ * between them) race and must not be issued.  Its address is looked up on the first call on each
+ * device (MXFP4_ERR_DEVICE if that fails).
+ */
+#define MXFP4_NOALLOC_SCRATCH_BYTES (32u << 20)
+int moe_mxfp4_forward_noalloc(const mxfp4_moe_dims* d, const void* packed_gfx950, const void* x_bf16, int64_t T,
+                              int64_t ldx, const float* router_logits, int32_t top_k, int32_t renormalize,
+                              void* y_bf16, int32_t* topk_ids, float* topk_w, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -17,7 +17,7 @@ LAYOUT_STD_W31 = 1
 LAYOUT_SCALE_TILED = 2
 
 __all__ = ["quantize", "tiled_scale_shape", "repack_weights", "unpack_weights", "check_packed", "route",
-           "moe_forward", "MoE", "MoeDims", "Mxfp4Error",
+           "moe_forward", "moe_forward_noalloc", "NOALLOC_SCRATCH_BYTES", "MoE", "MoeDims", "Mxfp4Error",
            "LAYOUT_GFX950", "LAYOUT_STD_W31", "LAYOUT_SCALE_TILED"]
 
 
@@ -184,6 +184,28 @@ def moe_forward(packed, E, H, I, has_bias, x, logits, top_k, renormalize=True, w
           L.moe_mxfp4_forward(ctypes.byref(d), _ptr(packed), _ptr(x), T, x.stride(0), _ptr(logits), top_k,
                               1 if renormalize else 0, _ptr(y), _ptr(topk_ids), _ptr(topk_w), _ptr(workspace),
                               workspace.numel(), _stream()))
+    return y
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # MXFP4_NOALLOC_SCRATCH_BYTES
+
+
+def moe_forward_noalloc(packed, E, H, I, has_bias, x, logits, top_k, y, renormalize=True, topk_ids=None,
+                        topk_w=None):
+    """moe_forward on the library's own device scratch array (no workspace, nothing allocated by the
+    library; y is the caller's).  Fails with status 4 when the shape needs more workspace than the
+    array holds (NOALLOC_SCRATCH_BYTES)."""
+    _cuda(x, "x")
+    _cuda(logits, "logits")
+    _need(x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1 and x.shape[1] == H, "x: bf16 [T, H]")
+    T = x.shape[0]
+    _need(logits.dtype == torch.float32 and logits.shape == (T, E) and logits.is_contiguous(), "logits: fp32 [T, E]")
+    _need(y.dtype == torch.bfloat16 and y.shape == (T, H) and y.is_contiguous(), "y: bf16 [T, H]")
+    d = _dims(E, H, I, has_bias)
+    check("moe_mxfp4_forward_noalloc",
+          _lib.lib().moe_mxfp4_forward_noalloc(ctypes.byref(d), _ptr(packed), _ptr(x), T, x.stride(0), _ptr(logits),
+                                               top_k, 1 if renormalize else 0, _ptr(y), _ptr(topk_ids),
+                                               _ptr(topk_w), _stream()))
     return y
 
 

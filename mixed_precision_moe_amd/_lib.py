@@ -32,6 +32,8 @@ _SIGS = {
     "moe_mxfp4_workspace_bytes": (c_sz, [ctypes.POINTER(MoeDims), c_i64, c_i32]),
     "moe_mxfp4_forward": (ctypes.c_int, [ctypes.POINTER(MoeDims), c_p, c_p, c_i64, c_i64, c_p, c_i32, c_i32, c_p, c_p,
                                          c_p, c_p, c_sz, c_p]),
+    "moe_mxfp4_forward_noalloc": (ctypes.c_int, [ctypes.POINTER(MoeDims), c_p, c_p, c_i64, c_i64, c_p, c_i32, c_i32,
+                                                 c_p, c_p, c_p, c_p]),
     "moe_mxfp4_forward_profiled": (ctypes.c_int, [ctypes.POINTER(MoeDims), c_p, c_p, c_i64, c_i64, c_p, c_i32, c_i32,
                                                   c_p, c_p, c_p, c_p, c_sz, c_p, ctypes.POINTER(c_p), c_i32]),
 }
