@@ -20,6 +20,11 @@ passage it follows.  Page tags used throughout:
 
 Readings of points the pages leave open are stated where they are used.
 
+Quantized-activation variants (``moe.moe_ref(act="mxfp8" | "mxfp4")``): the layer input and the
+SwiGLU output are quantized per 32-element block before the two products (MXFP8 with E4M3 elements,
+or MXFP4 with the weights' rule).  The E8M0 rule for E4M3 elements is a reading: the pages' round-up of
+the block maximum at a significand of 1.75, minus E4M3's largest exponent (8) instead of E2M1's (2).
+
 Parity status:  every function here is pinned by a ``-m "not gpu"`` test against something other than
 itself (hand values, closed forms, brute force, textbook cases or an independent library routine),
 except the two layout conventions the pages never state -- the nibble order inside a byte and the

@@ -25,19 +25,18 @@ def bf16_to_f64(bits):
 def e8m0_from_amax(amax):
     """E8M0 scale byte for blocks whose largest magnitude is ``amax`` (binary32 values).
 
-    [P3 Implementation breakdown, item 1; Key source snippets: compute_reference_e8m0_scale in
-    test_mxfp4_moe.py and the UE8M0_SF branch of cvt_warp_fp16_to_fp4 in nvfp4_utils.cuh, which state
-    the same rule twice]:
+    [P3 Implementation breakdown, item 1; Key source snippets: the reference helper in the MoE test
+    and the UE8M0_SF branch of the FP16/BF16 -> FP4 converter state the same rule]:
       * a block maximum that is not positive gives 0;
-      * otherwise take the binary32 bit pattern of the maximum, add 2**21 so that a significand of
-        1.75 or more carries into the next binade, keep only sign and exponent (mask 0xFF800000) and
-        read the biased exponent B from bits 23..30;
+      * otherwise add 2**21 to the binary32 bit pattern of the maximum (a significand of 1.75 or more
+        then carries into the next binade) and read the biased exponent B of the sum;
       * the scale exponent is B - 2, floored at 0 and capped at 254.
+    For a positive finite maximum the pattern is below 0x7F800000, so the sum stays below 2**31 and
+    B is simply the sum shifted right by 23.
     """
     a = np.asarray(amax, dtype=np.float32)
-    bits = a.view(np.uint32).astype(np.uint64)
-    rounded = (bits + np.uint64(1 << 21)) & np.uint64(0xFF800000)
-    biased = ((rounded >> np.uint64(23)) & np.uint64(0xFF)).astype(np.int64)
+    bits = a.view(np.uint32).astype(np.int64)
+    biased = (bits + (1 << 21)) >> 23
     e = np.minimum(np.maximum(biased - 2, 0), 254)
     return np.where(a > 0, e, 0).astype(np.uint8)
 
@@ -146,12 +145,105 @@ def tile_scales(flat):
     return out
 
 
+def tiled_offset(r, c, K):
+    """Byte offset of flat scale [r, c] in the tiled layout of a matrix with K columns:
+    ((mT * kTiles + kT) * 32 + oM) * 16 + iM * 4 + iK with mT = r // 128, iM = (r % 128) // 32,
+    oM = r % 32, kT = c // 4, iK = c % 4.  [P3 Key source snippets, untile_cutlass_scale: the tiles are
+    [numMTiles, numKTiles, 32 (outer M), 4 (inner M), 4 (inner K)]; reading 9 of the labels]"""
+    kt = (K // BLOCK + 3) // 4
+    r, c = np.asarray(r), np.asarray(c)
+    return (((r // 128) * kt + c // 4) * 32 + r % 32) * 16 + ((r % 128) // 32) * 4 + c % 4
+
+
 def untile_scales(tiled, rows, K):
-    """Tiled scale bytes -> flat [rows, K/32], following the pages' inverse: view the first
-    padded_M*padded_SK bytes as [mTiles, kTiles, 32, 4, 4], permute axes (0, 3, 2, 1, 4), reshape to
-    (padded_M, padded_SK) and crop.  [P3 Key source snippets, untile_cutlass_scale]"""
-    sk = K // BLOCK
-    mt, kt = (rows + 127) // 128, (sk + 3) // 4
-    b = np.asarray(tiled, dtype=np.uint8).reshape(-1)[: mt * 128 * kt * 4]
-    t = b.reshape(mt, kt, 32, 4, 4).transpose(0, 3, 2, 1, 4)
-    return np.ascontiguousarray(t).reshape(mt * 128, kt * 4)[:rows, :sk]
+    """Tiled scale bytes -> flat [rows, K/32]: element [r, c] is the byte at tiled_offset(r, c, K);
+    padding bytes are ignored.  The inverse of tile_scales.  [P3 Key source snippets,
+    untile_cutlass_scale]"""
+    b = np.asarray(tiled, dtype=np.uint8).reshape(-1)
+    r, c = np.indices((rows, K // BLOCK))
+    return b[tiled_offset(r, c, K)]
+
+
+# ------------------------------------------------------------------------------------------------
+# Activation quantizers of the MoE layer's quantized-activation variants.
+
+def quantize_values_ref(values):
+    """MXFP4 quantization of binary32 values [M, K] (K a multiple of 32), the element rule and the
+    E8M0 rule of quantize_ref applied to binary32 inputs: amax is the largest binary32 magnitude of
+    the block (exact), e = e8m0_from_amax(amax), v = |x| * 2**(127 - e) exact in float64, code by
+    e2m1_magnitude_code, sign bit 0x8 from the value's sign bit.  Returns (codes uint8 [M, K] unpacked,
+    scales uint8 [M, K/32]).  [P3 Implementation breakdown item 3: the experts-quant kernel quantizes
+    MoE activations with the same E8M0 rule]"""
+    x = np.asarray(values, dtype=np.float32)
+    M, K = x.shape
+    blocks = x.reshape(M, K // BLOCK, BLOCK)
+    mag = np.abs(blocks).astype(np.float64)
+    e = e8m0_from_amax(np.abs(blocks).max(axis=-1))
+    v = mag * np.ldexp(1.0, 127 - e.astype(np.int64))[..., None]
+    code = e2m1_magnitude_code(v) | (np.signbit(blocks).astype(np.uint8) << np.uint8(3))
+    return code.reshape(M, K), e
+
+
+def dequant_codes_ref(codes, scales):
+    """Unpacked E2M1 codes [..., K] and E8M0 scales [..., K/32] -> float64 values (as dequant_ref)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    mag = E2M1_MAGNITUDES[codes & 7]
+    sign = np.where(codes & 8, -1.0, 1.0)
+    s = np.repeat(np.ldexp(1.0, np.asarray(scales, dtype=np.int64) - 127), BLOCK, axis=-1)
+    return sign * mag * s
+
+
+E4M3_MAGNITUDES = np.array([m / 8 * 2.0 ** -6 for m in range(8)] +
+                           [(1 + m / 8) * 2.0 ** (E - 7) for E in range(1, 16) for m in range(8)])[:127]
+"""Magnitude of each 7-bit OCP FP8 E4M3 code (4 exponent bits, bias 7, 3 mantissa bits; exponent 0 is
+subnormal; no infinities, code 0x7F is NaN and left out): codes 0..126, largest 448 = 1.75 * 2**8."""
+
+_E4M3_MID = (E4M3_MAGNITUDES[1:] + E4M3_MAGNITUDES[:-1]) / 2
+
+
+def e4m3_magnitude_code(v):
+    """E4M3 magnitude code of v >= 0 (float64): the nearest magnitude, the even code on an exact
+    midpoint, 448 (code 126) for anything beyond.  [DEF: OCP FP8 E4M3 elements of MXFP8, rounded to
+    nearest even]"""
+    v = np.asarray(v, dtype=np.float64)
+    c = np.searchsorted(_E4M3_MID, v, side="left")  # midpoints strictly below v
+    on_mid = (c < _E4M3_MID.size) & (_E4M3_MID[np.minimum(c, _E4M3_MID.size - 1)] == v)
+    c = np.where(on_mid & (c % 2 == 1), c + 1, c)
+    return c.astype(np.uint8)
+
+
+def e8m0_for_e4m3(amax):
+    """E8M0 scale byte of an MXFP8 (E4M3) block, the pages' rule carried over to E4M3 elements
+    (reading; the pages give the rule for E2M1 only): the same round-up of the block maximum at a
+    significand of 1.75, minus the largest element exponent, 8 for E4M3 (448 = 1.75 * 2**8) where E2M1
+    subtracts 2 (6 = 1.5 * 2**2).  So e = B - 8 with B as in e8m0_from_amax, floored at 0, capped at
+    254, and 0 for a maximum that is not positive.  The maximum then maps into [224, 448): E4M3's
+    largest magnitude is 1.75 * 2**8, exactly the round-up threshold, so no element saturates."""
+    a = np.asarray(amax, dtype=np.float32)
+    bits = a.view(np.uint32).astype(np.int64)
+    biased = (bits + (1 << 21)) >> 23
+    e = np.minimum(np.maximum(biased - 8, 0), 254)
+    return np.where(a > 0, e, 0).astype(np.uint8)
+
+
+def mxfp8_quantize_values_ref(values):
+    """MXFP8 quantization of binary32 values [M, K]: per 32-element block e = e8m0_for_e4m3(amax),
+    v = |x| * 2**(127 - e) exact in float64, code = e4m3_magnitude_code(v) | sign bit 0x80.
+    Returns (codes uint8 [M, K], scales uint8 [M, K/32]).  [P2 Implementation breakdown item 3: the
+    MXFP8-activation variant of the FlashInfer CUTLASS MXFP4 MoE backend]"""
+    x = np.asarray(values, dtype=np.float32)
+    M, K = x.shape
+    blocks = x.reshape(M, K // BLOCK, BLOCK)
+    e = e8m0_for_e4m3(np.abs(blocks).max(axis=-1))
+    v = np.abs(blocks).astype(np.float64) * np.ldexp(1.0, 127 - e.astype(np.int64))[..., None]
+    code = e4m3_magnitude_code(v) | (np.signbit(blocks).astype(np.uint8) << np.uint8(7))
+    return code.reshape(M, K), e
+
+
+def mxfp8_dequant_ref(codes, scales):
+    """E4M3 codes [..., K] and E8M0 scales [..., K/32] -> float64 values."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    mag = E4M3_MAGNITUDES[codes & 0x7F]
+    sign = np.where(codes & 0x80, -1.0, 1.0)
+    s = np.repeat(np.ldexp(1.0, np.asarray(scales, dtype=np.int64) - 127), BLOCK, axis=-1)
+    return sign * mag * s
