@@ -65,8 +65,9 @@ def log(*a):
 
 
 class MoeBench:
-    def __init__(self, cfg, rotations, weight_copies=None):
+    def __init__(self, cfg, rotations, weight_copies=None, act=0):
         self.cfg = cfg
+        self.act = act
         w = gpu_standard_weights(cfg)
         self.packed = [mx.repack_weights(*w)]
         # extra weight copies so consecutive steps cannot hit in the 256 MB cache (not needed once the
@@ -90,12 +91,13 @@ class MoeBench:
         c = self.ctypes
         r = self.i % len(self.x)
         self.i += 1
-        args = [c.byref(self.d), c.c_void_p(self.packed[r % len(self.packed)].data_ptr()), c.c_void_p(self.x[r].data_ptr()),
+        args = [c.byref(self.d), self.act, c.c_void_p(self.packed[r % len(self.packed)].data_ptr()),
+                c.c_void_p(self.x[r].data_ptr()),
                 self.cfg.T, self.cfg.H, c.c_void_p(self.logits[r].data_ptr()), self.cfg.k,
                 1 if self.cfg.renormalize else 0, c.c_void_p(self.y.data_ptr()), None, None,
                 c.c_void_p(self.ws.data_ptr()), self.ws.numel(), c.c_void_p(self.stream.cuda_stream)]
         if events is None:
-            check("moe_mxfp4_forward", lib().moe_mxfp4_forward(*args))
+            check("moe_mxfp4_forward_act", lib().moe_mxfp4_forward_act(*args))
         else:
             arr = (c.c_void_p * len(events))(*events)
             check("moe_mxfp4_forward_profiled", lib().moe_mxfp4_forward_profiled(*args, arr, len(events)))

@@ -159,29 +159,54 @@ int moe_mxfp4_route(const float* router_logits, int64_t T, int32_t E, int32_t to
  * x_bf16  device bf16 [T, ldx], ldx >= H, ldx % 8 == 0.   y_bf16 device bf16 [T, H].
  * router_logits device fp32 [T, E].  topk_ids / topk_w: optional device outputs [T, top_k].
  * workspace device, >= moe_mxfp4_workspace_bytes(d, T, top_k), 256-byte aligned.
- * Size limit: the split activations of the first GEMM (T * H * 2 bytes) and of the second (about
- * 1.5 bytes per padded pair row and I element) must each stay below 4 GiB, else MXFP4_ERR_SHAPE.
- * Arithmetic: activations enter the block-scaled MFMA as two E2M3 (FP6) terms with E8M0 scales
- * per 32 elements (x = t0 + t1, t1 the rounding of the remainder), weights as E2M1 with their E8M0
- * scales, fp32 accumulation; the SwiGLU output stays fp32 and is split into two terms the same way;
- * each pair's weighted expert output is kept as fp16 with a power-of-two scale per 16 columns, and the
- * combine sums a token's k rows in fp32 in slot order, then rounds to bf16.  The result is
+ * Size limit: the split activations of the first GEMM (T * H * 2.25 bytes) and of the second (about
+ * 2 bytes per padded pair row and I element) must each stay below 4 GiB, else MXFP4_ERR_SHAPE.
+ * Arithmetic: activations enter the block-scaled MFMA as three terms with E8M0 scales per 32
+ * elements, x = t0 + t1 + t2 (E2M3, E2M3 of the remainder, E2M1 of what is left; each scale from the
+ * rule above), weights as E2M1 with their E8M0 scales, fp32 accumulation; the SwiGLU output stays
+ * fp32 and is split into three terms the same way; each pair's weighted expert output is kept as
+ * integers with a power-of-two scale per 16 columns (at most 2^-14 of the block maximum off), and
+ * the combine sums a token's k rows in fp32 in slot order, then rounds to bf16.  The result is
  * deterministic: repeated calls give the same bits.
  */
 size_t moe_mxfp4_workspace_bytes(const mxfp4_moe_dims* d, int64_t T, int32_t top_k);
+
+/* Activation formats of moe_mxfp4_forward_act. */
+enum {
+  MXFP4_ACT_BF16 = 0,  /* bf16 activations, as moe_mxfp4_forward */
+  MXFP4_ACT_MXFP8 = 1, /* both GEMM inputs quantized to MXFP8 */
+  MXFP4_ACT_MXFP4 = 2  /* both GEMM inputs quantized to MXFP4 */
+};
 int moe_mxfp4_forward(const mxfp4_moe_dims* d, const void* packed_gfx950, const void* x_bf16, int64_t T, int64_t ldx,
                       const float* router_logits, int32_t top_k, int32_t renormalize, void* y_bf16, int32_t* topk_ids,
                       float* topk_w, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Same as moe_mxfp4_forward, and records events[i] (hipEvent_t passed as void*, created by the caller)
+/* The MoE layer with quantized activations, or bf16 ones (act_format = MXFP4_ACT_BF16 is exactly
+ * moe_mxfp4_forward).  [P2 Implementation breakdown item 3: the MXFP8-activation variant of the MXFP4
+ * MoE backend; P3 Implementation breakdown item 3: the experts-quant step, MoE activations quantized to
+ * MXFP4 with the same E8M0 rule]
+ * With MXFP4_ACT_MXFP8 / MXFP4_ACT_MXFP4 the layer input x (each token row, per 32-element block) and
+ * the SwiGLU output (fp32, per 32-element block of I) are quantized before the two products and enter
+ * the MFMA as one term:
+ *   MXFP8: E4M3 elements (round to nearest even) with e = B - 8, B the rounded biased exponent of the
+ *          block maximum as in mxfp4_quantize (the pages' rule with E4M3's largest exponent 8 in place
+ *          of E2M1's 2), so the maximum maps into [224, 448) and nothing saturates;
+ *   MXFP4: exactly the element and scale rule of mxfp4_quantize.
+ * Arguments, workspace and errors as moe_mxfp4_forward; an unknown act_format -> MXFP4_ERR_LAYOUT. */
+int moe_mxfp4_forward_act(const mxfp4_moe_dims* d, int32_t act_format, const void* packed_gfx950, const void* x_bf16,
+                          int64_t T, int64_t ldx, const float* router_logits, int32_t top_k, int32_t renormalize,
+                          void* y_bf16, int32_t* topk_ids, float* topk_w, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* Same as moe_mxfp4_forward_act, and records events[i] (hipEvent_t passed as void*, created by the caller)
  * on `stream` at stage boundaries: events[0] before the first launch, then after each stage in the
  * order activation split, routing, pair placement/tile schedule, first GEMM (+SwiGLU), second GEMM
  * (weighted rows), combine (bf16 output) -- 7 events in all.  Only the first n_events are recorded.
  * For per-stage timing (measurement); the computation is identical. */
-int moe_mxfp4_forward_profiled(const mxfp4_moe_dims* d, const void* packed_gfx950, const void* x_bf16, int64_t T,
-                               int64_t ldx, const float* router_logits, int32_t top_k, int32_t renormalize,
-                               void* y_bf16, int32_t* topk_ids, float* topk_w, void* workspace, size_t workspace_bytes,
-                               void* stream, void* const* events, int32_t n_events);
+int moe_mxfp4_forward_profiled(const mxfp4_moe_dims* d, int32_t act_format, const void* packed_gfx950,
+                               const void* x_bf16, int64_t T, int64_t ldx, const float* router_logits, int32_t top_k,
+                               int32_t renormalize, void* y_bf16, int32_t* topk_ids, float* topk_w, void* workspace,
+                               size_t workspace_bytes, void* stream, void* const* events, int32_t n_events);
 
 /* ------------------------------------------------------------------------------------------------
  * The MoE layer without a workspace argument, for callers that cannot allocate device memory (code

@@ -16,9 +16,13 @@ LAYOUT_GFX950 = 0
 LAYOUT_STD_W31 = 1
 LAYOUT_SCALE_TILED = 2
 
+ACT_BF16 = 0   # bf16 activations (three-term split inside the kernels)
+ACT_MXFP8 = 1  # both GEMM inputs quantized to MXFP8 (E4M3 + E8M0 per 32)
+ACT_MXFP4 = 2  # both GEMM inputs quantized to MXFP4 (E2M1 + E8M0 per 32)
+
 __all__ = ["quantize", "tiled_scale_shape", "repack_weights", "unpack_weights", "check_packed", "route",
            "moe_forward", "moe_forward_noalloc", "NOALLOC_SCRATCH_BYTES", "MoE", "MoeDims", "Mxfp4Error",
-           "LAYOUT_GFX950", "LAYOUT_STD_W31", "LAYOUT_SCALE_TILED"]
+           "LAYOUT_GFX950", "LAYOUT_STD_W31", "LAYOUT_SCALE_TILED", "ACT_BF16", "ACT_MXFP8", "ACT_MXFP4"]
 
 
 def _stream():
@@ -165,8 +169,9 @@ def workspace_bytes(E, H, I, has_bias, T, top_k):
 
 
 def moe_forward(packed, E, H, I, has_bias, x, logits, top_k, renormalize=True, workspace=None, y=None,
-                topk_ids=None, topk_w=None):
-    """One MoE layer.  x bf16 [T, H] (rows may be strided), logits fp32 [T, E]; returns y bf16 [T, H]."""
+                topk_ids=None, topk_w=None, act_format=ACT_BF16):
+    """One MoE layer.  x bf16 [T, H] (rows may be strided), logits fp32 [T, E]; returns y bf16 [T, H].
+    act_format: ACT_BF16, or ACT_MXFP8 / ACT_MXFP4 for the quantized-activation variants."""
     _cuda(x, "x")
     _cuda(logits, "logits")
     _need(x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1 and x.shape[1] == H, "x: bf16 [T, H]")
@@ -180,10 +185,10 @@ def moe_forward(packed, E, H, I, has_bias, x, logits, top_k, renormalize=True, w
     _need(nws > 0, "invalid MoE arguments")
     if workspace is None:
         workspace = torch.empty(nws, dtype=torch.uint8, device=x.device)
-    check("moe_mxfp4_forward",
-          L.moe_mxfp4_forward(ctypes.byref(d), _ptr(packed), _ptr(x), T, x.stride(0), _ptr(logits), top_k,
-                              1 if renormalize else 0, _ptr(y), _ptr(topk_ids), _ptr(topk_w), _ptr(workspace),
-                              workspace.numel(), _stream()))
+    check("moe_mxfp4_forward_act",
+          L.moe_mxfp4_forward_act(ctypes.byref(d), act_format, _ptr(packed), _ptr(x), T, x.stride(0), _ptr(logits),
+                                  top_k, 1 if renormalize else 0, _ptr(y), _ptr(topk_ids), _ptr(topk_w),
+                                  _ptr(workspace), workspace.numel(), _stream()))
     return y
 
 
@@ -212,11 +217,11 @@ def moe_forward_noalloc(packed, E, H, I, has_bias, x, logits, top_k, y, renormal
 class MoE:
     """An MXFP4 MoE layer: packed weights and a reusable workspace."""
 
-    def __init__(self, w13_q, w13_s, w2_q, w2_s, b13=None, b2=None, top_k=8, renormalize=True):
+    def __init__(self, w13_q, w13_s, w2_q, w2_s, b13=None, b2=None, top_k=8, renormalize=True, act_format=ACT_BF16):
         self.E, I2, Hh = w13_q.shape
         self.H, self.I = Hh * 2, I2 // 2
         self.has_bias = b13 is not None
-        self.top_k, self.renormalize = top_k, renormalize
+        self.top_k, self.renormalize, self.act_format = top_k, renormalize, act_format
         self.packed = repack_weights(w13_q, w13_s, w2_q, w2_s, b13, b2, LAYOUT_GFX950)
         self._ws = None
 
@@ -228,4 +233,4 @@ class MoE:
 
     def __call__(self, x, logits, y=None, topk_ids=None, topk_w=None):
         return moe_forward(self.packed, self.E, self.H, self.I, self.has_bias, x, logits, self.top_k, self.renormalize,
-                           self.workspace(x.shape[0]), y, topk_ids, topk_w)
+                           self.workspace(x.shape[0]), y, topk_ids, topk_w, self.act_format)

@@ -34,8 +34,10 @@ _SIGS = {
                                          c_p, c_p, c_sz, c_p]),
     "moe_mxfp4_forward_noalloc": (ctypes.c_int, [ctypes.POINTER(MoeDims), c_p, c_p, c_i64, c_i64, c_p, c_i32, c_i32,
                                                  c_p, c_p, c_p, c_p]),
-    "moe_mxfp4_forward_profiled": (ctypes.c_int, [ctypes.POINTER(MoeDims), c_p, c_p, c_i64, c_i64, c_p, c_i32, c_i32,
-                                                  c_p, c_p, c_p, c_p, c_sz, c_p, ctypes.POINTER(c_p), c_i32]),
+    "moe_mxfp4_forward_act": (ctypes.c_int, [ctypes.POINTER(MoeDims), c_i32, c_p, c_p, c_i64, c_i64, c_p, c_i32,
+                                             c_i32, c_p, c_p, c_p, c_p, c_sz, c_p]),
+    "moe_mxfp4_forward_profiled": (ctypes.c_int, [ctypes.POINTER(MoeDims), c_i32, c_p, c_p, c_i64, c_i64, c_p, c_i32,
+                                                  c_i32, c_p, c_p, c_p, c_p, c_sz, c_p, ctypes.POINTER(c_p), c_i32]),
 }
 
 EXPORTED = tuple(_SIGS)

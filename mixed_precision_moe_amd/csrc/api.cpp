@@ -68,9 +68,12 @@ int choose_nrg1(int64_t P, int64_t E) {
 }
 
 // The same for the second GEMM, whose 64-row tiles measured faster than 128-row ones at every load
-// tried (its items are short, 12 K steps at I = 768, and bound by copy latency).
-int choose_nrg2(int64_t P, int64_t E) {
+// tried (its items are short, 12 K steps at I = 768, and bound by copy latency).  With the bf16 path's
+// three-term operand a 64-row tile needs more registers than two workgroups per CU leave (it spilled in
+// the K loop), and 32-row tiles measured fastest.
+int choose_nrg2(int64_t P, int64_t E, int32_t act) {
   const int64_t avg = P / (E > 0 ? E : 1);
+  if (act == MXFP4_ACT_BF16) return 1;
   return avg < 48 ? 1 : 2;
 }
 
@@ -249,12 +252,14 @@ MX_API size_t moe_mxfp4_workspace_bytes(const mxfp4_moe_dims* d, int64_t T, int3
   return (size_t)fwd_ws(moe_geom(d->E, d->H, d->I), T, top_k).total;
 }
 
-int forward_impl(const mxfp4_moe_dims* d, const void* packed_gfx950, const void* x_bf16, int64_t T,
-                        int64_t ldx, const float* router_logits, int32_t top_k, int32_t renormalize, void* y_bf16,
-                        int32_t* topk_ids, float* topk_w, void* workspace, size_t workspace_bytes, hipStream_t s,
-                        void* const* events, int32_t n_events) {
+int forward_impl(const mxfp4_moe_dims* d, int32_t act_format, const void* packed_gfx950, const void* x_bf16,
+                 int64_t T, int64_t ldx, const float* router_logits, int32_t top_k, int32_t renormalize, void* y_bf16,
+                 int32_t* topk_ids, float* topk_w, void* workspace, size_t workspace_bytes, hipStream_t s,
+                 void* const* events, int32_t n_events) {
   int st = check_dims(d);
   if (st) return st;
+  if (act_format != MXFP4_ACT_BF16 && act_format != MXFP4_ACT_MXFP8 && act_format != MXFP4_ACT_MXFP4)
+    return MXFP4_ERR_LAYOUT;
   if ((st = check_route_args(T, d->E, top_k))) return st;
   if (ldx < d->H || ldx % 8) return MXFP4_ERR_SHAPE;
   if (n_events < 0 || (n_events > 0 && !events)) return MXFP4_ERR_NULL;
@@ -266,8 +271,8 @@ int forward_impl(const mxfp4_moe_dims* d, const void* packed_gfx950, const void*
   const MoeGeom g = moe_geom(d->E, d->H, d->I);
   const FwdWs w = fwd_ws(g, T, top_k);
   // the GEMMs' copy sources are 32-bit byte offsets into the activation buffers
-  if ((uint64_t)T * g.nkt1 * kXRecG >= (1ULL << 32) ||
-      (uint64_t)(w.nrows_alloc / 32) * g.nkt2 * 64 * kSlot >= (1ULL << 32))
+  if ((uint64_t)T * g.nkt1 * kMaxRec >= (1ULL << 32) ||
+      (uint64_t)(w.nrows_alloc / 32) * g.nkt2 * 64 * kMaxSlot >= (1ULL << 32))
     return MXFP4_ERR_SHAPE;
   if (workspace_bytes < w.total) return MXFP4_ERR_WORKSPACE;
   const BlobOffsets o = blob_offsets(g, d->has_bias);
@@ -275,7 +280,7 @@ int forward_impl(const mxfp4_moe_dims* d, const void* packed_gfx950, const void*
   const int64_t P = T * top_k;
   int32_t* ids = topk_ids ? topk_ids : (int32_t*)(ws + w.ids);
   float* wts = topk_w ? topk_w : (float*)(ws + w.w);
-  const int NRG1 = choose_nrg1(P, g.E), NRG2 = choose_nrg2(P, g.E);
+  const int NRG1 = choose_nrg1(P, g.E), NRG2 = choose_nrg2(P, g.E, act_format);
   int ev = 0;
   auto mark = [&]() -> int {
     if (ev < n_events && hipEventRecord((hipEvent_t)events[ev], s) != hipSuccess) return MXFP4_ERR_DEVICE;
@@ -283,7 +288,7 @@ int forward_impl(const mxfp4_moe_dims* d, const void* packed_gfx950, const void*
     return MXFP4_OK;
   };
   if ((st = mark())) return st;
-  if ((st = launch_xprep(x_bf16, T, ldx, g, ws + w.xq, (int32_t*)(ws + w.blkcnt), cdiv(T, kRouteTokens) * g.E, s)) ||
+  if ((st = launch_xprep(act_format, x_bf16, T, ldx, g, ws + w.xq, (int32_t*)(ws + w.blkcnt), cdiv(T, kRouteTokens) * g.E, s)) ||
       (st = mark()))
     return st;
   if ((st = launch_route(router_logits, T, (int)g.E, top_k, renormalize, ids, wts, (int32_t*)(ws + w.blkcnt), s)) ||
@@ -301,7 +306,7 @@ int forward_impl(const mxfp4_moe_dims* d, const void* packed_gfx950, const void*
                  (const float*)(ws + w.prow_w), (const TileDesc*)(ws + w.tiles), (const int32_t*)(ws + w.ntiles),
                  ws + w.actq, ws + w.acts, nullptr, nullptr, (int32_t)g.nkt1, (int32_t)g.ncb1, (int32_t)g.nit,
                  (int32_t)g.nkt2, (int32_t)g.nkt1, (int32_t)g.I, (int32_t)g.H};
-  if ((st = launch_gemm1(NRG1, a1, w.max_tiles, s)) || (st = mark())) return st;
+  if ((st = launch_gemm1(act_format, NRG1, a1, w.max_tiles, s)) || (st = mark())) return st;
   GemmArgs a2 = a1;
   a2.wq = blob + o.w2q;
   a2.ws = blob + o.w2s;
@@ -315,7 +320,7 @@ int forward_impl(const mxfp4_moe_dims* d, const void* packed_gfx950, const void*
   a2.ntl = (int32_t)g.nht;
   a2.tiles = (const TileDesc*)(ws + w.tiles2);
   a2.ntiles = (const int32_t*)(ws + w.ntiles2);
-  if ((st = launch_gemm2(NRG2, a2, w.max_tiles, s)) || (st = mark())) return st;
+  if ((st = launch_gemm2(act_format, NRG2, a2, w.max_tiles, s)) || (st = mark())) return st;
   if ((st = launch_combine((const uint16_t*)(ws + w.o16), ws + w.osc, (const int32_t*)(ws + w.pair_prow), y_bf16, T, g.H,
                            top_k, s)) ||
       (st = mark()))
@@ -326,15 +331,23 @@ int forward_impl(const mxfp4_moe_dims* d, const void* packed_gfx950, const void*
 MX_API int moe_mxfp4_forward(const mxfp4_moe_dims* d, const void* packed_gfx950, const void* x_bf16, int64_t T,
                              int64_t ldx, const float* router_logits, int32_t top_k, int32_t renormalize, void* y_bf16,
                              int32_t* topk_ids, float* topk_w, void* workspace, size_t workspace_bytes, void* stream) {
-  return forward_impl(d, packed_gfx950, x_bf16, T, ldx, router_logits, top_k, renormalize, y_bf16, topk_ids, topk_w,
-                      workspace, workspace_bytes, S(stream), nullptr, 0);
+  return forward_impl(d, MXFP4_ACT_BF16, packed_gfx950, x_bf16, T, ldx, router_logits, top_k, renormalize, y_bf16,
+                      topk_ids, topk_w, workspace, workspace_bytes, S(stream), nullptr, 0);
 }
 
-MX_API int moe_mxfp4_forward_profiled(const mxfp4_moe_dims* d, const void* packed_gfx950, const void* x_bf16,
-                                      int64_t T, int64_t ldx, const float* router_logits, int32_t top_k,
-                                      int32_t renormalize, void* y_bf16, int32_t* topk_ids, float* topk_w,
-                                      void* workspace, size_t workspace_bytes, void* stream, void* const* events,
-                                      int32_t n_events) {
-  return forward_impl(d, packed_gfx950, x_bf16, T, ldx, router_logits, top_k, renormalize, y_bf16, topk_ids, topk_w,
-                      workspace, workspace_bytes, S(stream), events, n_events);
+MX_API int moe_mxfp4_forward_act(const mxfp4_moe_dims* d, int32_t act_format, const void* packed_gfx950,
+                                 const void* x_bf16, int64_t T, int64_t ldx, const float* router_logits, int32_t top_k,
+                                 int32_t renormalize, void* y_bf16, int32_t* topk_ids, float* topk_w, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  return forward_impl(d, act_format, packed_gfx950, x_bf16, T, ldx, router_logits, top_k, renormalize, y_bf16, topk_ids,
+                      topk_w, workspace, workspace_bytes, S(stream), nullptr, 0);
+}
+
+MX_API int moe_mxfp4_forward_profiled(const mxfp4_moe_dims* d, int32_t act_format, const void* packed_gfx950,
+                                      const void* x_bf16, int64_t T, int64_t ldx, const float* router_logits,
+                                      int32_t top_k, int32_t renormalize, void* y_bf16, int32_t* topk_ids,
+                                      float* topk_w, void* workspace, size_t workspace_bytes, void* stream,
+                                      void* const* events, int32_t n_events) {
+  return forward_impl(d, act_format, packed_gfx950, x_bf16, T, ldx, router_logits, top_k, renormalize, y_bf16, topk_ids,
+                      topk_w, workspace, workspace_bytes, S(stream), events, n_events);
 }

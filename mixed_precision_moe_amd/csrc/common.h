@@ -29,6 +29,16 @@ MX_DEV uint32_t e8m0_from_amax_bits(uint32_t amax_bits) {
   return amax_bits == 0u ? 0u : e;
 }
 
+// E8M0 scale of an MXFP8 block (E4M3 elements): the same round-up of the block maximum at a
+// significand of 1.75, minus E4M3's largest element exponent 8 instead of E2M1's 2, so the maximum maps
+// into [224, 448) and no element saturates (448 = 1.75 * 2^8 is E4M3's largest magnitude).
+MX_DEV uint32_t e8m0_e4m3_from_amax_bits(uint32_t amax_bits) {
+  uint32_t b = ((amax_bits + (1u << 21)) >> 23) & 0xFFu;
+  uint32_t e = b > 8u ? b - 8u : 0u;
+  e = e < 254u ? e : 254u;
+  return amax_bits == 0u ? 0u : e;
+}
+
 // The scale operand of the gfx950 scaled conversions: only its exponent field is used, as an E8M0
 // exponent (field 0 means 2^-127), so the byte shifted into place is the scale.
 MX_DEV float e8m0_as_scale_operand(uint32_t e) { return __uint_as_float(e << 23); }

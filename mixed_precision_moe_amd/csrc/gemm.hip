@@ -1,798 +1,18 @@
-// Grouped expert GEMMs of the MoE layer on gfx950 block-scaled MFMA
-// (v_mfma_scale_f32_32x32x64_f8f6f4), with the SwiGLU and the routing-weighted output fused into
-// their epilogues, and the final combine over the top-k experts of each token.
-//
-// [DEF: grouped w13 GEMM, SwiGLU = silu(w1 half) * (w3 half), grouped w2 GEMM, weighted top-k combine;
-//  MXFP4 weights with E8M0 scales per 32 elements; P1 Implementation breakdown: the mixed-input fused
-//  MoE multiplies packed 4-bit weights with per-32 group scales by 16-bit activations]
-//
-// The MFMA has no bf16 operand, so a bf16 activation enters as two E2M3 (FP6) terms x = t0 + t1, each
-// with its own E8M0 scale per 32 elements, and every product is issued once per term against the same
-// FP4 weight registers; FP6 x FP4 runs at the FP4 rate on gfx950.  The first GEMM's output (the SwiGLU
-// activation) stays fp32 until it is split into the second GEMM's two terms, and the second GEMM's rows
-// are block-scaled fp16 that the combine sums in fp32, so the only bf16 rounding after the input is the
-// output's.
-//
-// Both GEMMs are computed transposed, D[n][m] = sum_k W[n][k] act[m][k]: the weights are the A operand
-// (rows n = 32 output columns of one tile), the tokens the B operand (columns m = 32 rows of the padded
-// row order).  Lane l of a 32x32 result holds token l%32 and tile rows 8*jj + 4*(l/32) + i.
-//  - First GEMM: gate and up of a token sit in the same lane (SwiGLU in registers); the 32-element
-//    blocks of two adjacent activation tiles are spread over both lane halves, and one exchange of
-//    halves leaves each lane one whole block, which it splits into the second GEMM's two E2M3 terms.
-//  - Second GEMM: one exchange of halves leaves each lane 16 consecutive output columns of its token,
-//    stored as fp16 with one power-of-two exponent per 16 columns (about eleven significant bits of
-//    every value that matters for the sum) in the padded row order; the combine gathers each token's
-//    k rows.
-//
-// Both GEMMs run one kernel template.  A workgroup of four waves (WR x WC) computes an M tile of
-// NRG = WR*RW row groups of 32 rows against NT = WC*CW weight tiles of 32 columns; wave (wr, wc) holds
-// RW x CW accumulators.  Per 64-wide K step the workgroup copies the step's operands global -> LDS
-// with LDS DMA (global_load_lds: no registers, no address math beyond the source) into a ring of D
-// stages: every wave issues the same number of copies per stage, waits for its own with vmcnt and one
-// barrier per step publishes the stage.  Operand fragments of step kt+1 are read from LDS while the
-// MFMAs of step kt run: a fixed plan (StepPlan) orders each step's MFMAs and puts after each MFMA its
-// share of the fragment loads and copies, so their instructions issue while the matrix core works.
-// Configurations with a 3-stage ring at two workgroups per CU (the second GEMM, the first GEMM's
-// 64-row tiles) instead load step kt+1's fragments after step kt's MFMAs ("late"), which leaves the
-// copies about one more step to land.
-// Work items (M tile, column position) are dealt to XCDs in contiguous ranges
-// so the column positions of one M tile (same gathered tokens) and consecutive tiles of one expert
-// (same weights) share an XCD's L2.
-#include <type_traits>
-
-#include "common.h"
-#include "internal.h"
+// The bf16-activation instantiations of the grouped GEMM kernels (gemm_kernel.h), the launch
+// dispatch over activation formats, and the final combine over the top-k experts of each token.
+#include "gemm_kernel.h"
 
 namespace {
 
-typedef decltype(__builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(bf16x32_t{}, 1.0f)) fp6x32_t;
-typedef __attribute__((address_space(3))) void* lds_vptr_t;
-
-constexpr int kFp4 = 4, kFp6 = 2;  // MFMA operand format codes (E2M1, E2M3)
-constexpr int kXcds = 8;           // workgroup b runs on XCD b % 8
-
-
-// LDS DMA: lane i copies 16 (or 4) bytes from its global address to lds_wave_base + i * 16 (or 4).
-// (Sub-dword copies still occupy a dword per lane in LDS, so every copied record here is a dword or
-// a multiple of 16 bytes.)  The copies are issued as inline assembly with M0 set explicitly: the
-// compiler's wait-count tracking treats its own global_load_lds as a FLAT access to both memories and
-// would then wait for every LDS load (lgkmcnt(0)) before any use of one.  Every wait for these copies
-// is therefore explicit (vmcnt, counted per stage) and each LDS consumer follows such a wait and a
-// barrier.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"  // M0 is listed as clobbered; nothing else here uses it
-// lds_wave_base is an LDS byte address, uniform over the wave (it goes to M0).
-MX_DEV void dma16(const void* g, uint32_t lds_wave_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_wave_base);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(m0) : "memory", "m0");
-}
-MX_DEV void dma4(const void* g, uint32_t lds_wave_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_wave_base);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(g), "s"(m0) : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// f(integral_constant<int, i>) for i = 0 .. N-1 (operand selectors of the MFMA must be literals).
-template <int I, int N, typename F>
-MX_DEV void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<I + 1, N>(f);
-  }
-}
-
-template <int N>
-MX_DEV void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x70 | 0xF00);
-}
-MX_DEV void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-
-// Barrier without the implied full vmcnt wait of __syncthreads: the LDS DMA copies are waited for
-// explicitly, so only LDS and compiler ordering are needed here.
-MX_DEV void block_sync() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-
-// Reads an accumulator element where the epilogue needs it: the operand stays in its AGPR until this
-// point, so the accumulator tiles are not all copied to VGPRs when the K loop ends.
-MX_DEV float acc_read(float v) {
-  float r;
-  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(v));
-  return r;
-}
-
-// ------------------------------------------------------------------------------------------------
-// Kernel configuration.  LDS stage: [NT weight pieces of 1 KB][1 KB weight scale records of the
-// column block], then the activation: first GEMM [NRG row groups x 32 rows x kXRec-byte records]
-// (padded to whole 1 KB copies); second GEMM [NRG x 3 KB activation slots, lane-major][NRG x 256 B
-// activation scale dwords].
-template <bool G1, int WR, int WC, int RW, int CW, int D>
-struct Cfg {
-  static constexpr int NRG = WR * RW, NT = WC * CW;
-  static_assert(WR * WC == 4, "four waves");
-  static_assert(NT == 8 || NT == 16, "a workgroup covers a column block or half of one");
-  static_assert(CW % 4 == 0, "weight scales are read four tiles per dword");
-  static_assert(D >= 3 && D <= 6, "ring depth");  // stages issued D - 1 steps ahead
-  static constexpr int kXBytes = G1 ? (NRG * kRecChunks * 16 + 1023) / 1024 * 1024 : NRG * 3072;
-  static constexpr int oW = 0, oWS = NT * 1024, oX = oWS + 1024, oXS = oX + kXBytes;
-  static constexpr int kStage = oXS + (G1 ? 0 : NRG * 256);
-  static constexpr int nW = NT / 4;                // weight pieces copied per wave
-  static constexpr int nXI = kXBytes / 1024;       // 1 KB activation copies per stage
-  static constexpr int nX = (nXI + 3) / 4;         // ... per wave (the last one repeated)
-  static constexpr int nXS = G1 ? 0 : (NRG + 3) / 4;  // activation scale copies per wave
-  static constexpr int kOps = nW + 1 + nX + nXS;   // copies per wave per stage
-};
-
-// Order of the work of one K step of a wave: its NM MFMAs in a fixed order (groups of two weight
-// tiles; within a group term-major, then row group, then tile, so an accumulator is reused 2 * RW
-// MFMAs later), and after MFMA m up to kCap of the other tasks of the step, so that their instructions
-// issue while the matrix core works:
-//   kDef + i : weight fragment CW - 2 + i of this step, from the current stage (the last group's
-//              fragments are reloaded at the start of the step that uses them)
-//   kX + r   : activation fragments and scale of row group r for the next step, from the next stage
-//   kWs      : weight scale dwords for the next step
-//   kRel + j : weight fragment j (< CW - 2) for the next step, after the last MFMA that uses it
-//   kDma + i : copy i of the stage D - 1 steps ahead
-struct StepTask {
-  static constexpr int kNone = -1, kDef = 0, kX = 10, kWs = 20, kRel = 30, kDma = 100;
-};
-// COPIES_FIRST puts the copies right after the step's first MFMAs (for a latency-bound GEMM with few
-// K steps per item); otherwise they are spread over the MFMAs after the first group.
-// LATE: the step's fragment loads are not interleaved (they follow the step's MFMAs, see the kernel);
-// only the copies are placed.
-template <int RW, int CW, int KOPS, bool COPIES_FIRST, bool LATE = false>
-struct StepPlan {
-  static constexpr int G = CW / 2, NM = 4 * RW * G, kCap = 6, kPer = 2;
-  int t[NM][kCap];
-  constexpr void place(int task, int earliest) {
-    int m = earliest < NM ? earliest : NM - 1;
-    while (m < NM - 1 && n_at(m) >= kPer) m++;
-    int c = n_at(m);
-    t[m][c < kCap ? c : kCap - 1] = task;
-  }
-  constexpr int n_at(int m) const {
-    int c = 0;
-    while (c < kCap && t[m][c] != StepTask::kNone) c++;
-    return c;
-  }
-  constexpr StepPlan() : t{} {
-    for (int m = 0; m < NM; m++)
-      for (int c = 0; c < kCap; c++) t[m][c] = StepTask::kNone;
-    if (LATE) {
-      for (int i = 0; i < KOPS; i++) place(StepTask::kDma + i, COPIES_FIRST ? 0 : i * NM / KOPS);
-      return;
-    }
-    // the last group's fragments shortly before that group, so few loads are younger than them
-    const int def_at = (G - 1) * 4 * RW - 4 > 0 ? (G - 1) * 4 * RW - 4 : 0;
-    if (COPIES_FIRST) {
-      place(StepTask::kDef + 0, def_at);
-      place(StepTask::kDef + 1, def_at);
-      for (int i = 0; i < KOPS; i++) place(StepTask::kDma + i, 0);
-    }
-    for (int r = 0; r < RW; r++) place(StepTask::kX + r, 0);
-    place(StepTask::kWs, 0);
-    for (int j = 0; j < CW - 2; j++) place(StepTask::kRel + j, (j / 2 + 1) * 4 * RW - 1);
-    if (!COPIES_FIRST) {
-      for (int i = 0; i < KOPS; i++) place(StepTask::kDma + i, 4 * RW + i * (NM - 4 * RW) / KOPS);
-      place(StepTask::kDef + 0, def_at);
-      place(StepTask::kDef + 1, def_at);
-    }
-  }
-  // every task placed exactly once, the last group's fragments before that group
-  constexpr bool valid() const {
-    int n = 0, def_last = 0;
-    for (int m = 0; m < NM; m++)
-      for (int c = 0; c < kCap; c++)
-        if (t[m][c] != StepTask::kNone) {
-          n++;
-          if (t[m][c] < StepTask::kX) def_last = m;
-        }
-    if (LATE) return n == KOPS && n_at(NM - 1) < kCap;
-    return n == 2 + RW + 1 + (CW - 2) + KOPS && def_last < (G - 1) * 4 * RW && n_at(NM - 1) < kCap;
-  }
-};
-
-
-typedef const __attribute__((address_space(3))) uint16_t lds_u16;
-typedef const __attribute__((address_space(3))) uint8_t* lds_u8;
-
-// Exchanges lane halves: returns {lanes 0-31 of x, then lanes 0-31 of y} and {lanes 32-63 of x, then
-// lanes 32-63 of y} (one v_permlane32_swap).
-MX_DEV void swap_halves(float& x, float& y) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, y), false,
-                                                  false);
-  x = __builtin_bit_cast(float, (unsigned)r[0]);
-  y = __builtin_bit_cast(float, (unsigned)r[1]);
-}
-
-// Four consecutive bf16 entries of an LDS bias table (8-byte aligned) as fp32.
-MX_DEV void bias4(lds_u16* p, float* out) {
-  const u32x2_t v = *reinterpret_cast<const __attribute__((address_space(3))) u32x2_t*>(p);
-  out[0] = __uint_as_float(v[0] << 16);
-  out[1] = __uint_as_float(v[0] & 0xFFFF0000u);
-  out[2] = __uint_as_float(v[1] << 16);
-  out[3] = __uint_as_float(v[1] & 0xFFFF0000u);
-}
-
-// First GEMM epilogue for the activation tiles `it` (even) and it + 1 of one row group, which together
-// are one K step (kt2 = it / 2) of the second GEMM: bias, SwiGLU in fp32, then one exchange of lane
-// halves after which lane l holds the whole 32-element block of token l % 32 in tile it + l / 32, split
-// into two E2M3 terms and written as one 48-byte operand slot of the second GEMM (lane l of the step) and
-// its scale dword.  When tile it + 1 is past I / 32 its half is a zero block.
-// g0/u0, g1/u1: gate and up accumulators of the two tiles; bg/bu: the 64 gate / up biases of the pair
-// (bf16, LDS), read when BIAS.  SECOND is false only for the last pair of an odd tile count.
-template <bool BIAS, bool SECOND>
-MX_DEV void g1_epilogue_pair(const f32x16_t& g0, const f32x16_t& u0, const f32x16_t& g1, const f32x16_t& u1,
-                             const GemmArgs& a, lds_u16* bg, lds_u16* bu, int kt2, int rg, int lane) {
-  const int h = lane >> 5;
-  // All 64 accumulator values are read first: each read is a volatile asm statement, which the
-  // scheduler treats as a region boundary, so reading them up front leaves the SwiGLU arithmetic of the
-  // whole pair as one region whose 32 independent exp / reciprocal chains can interleave.
-  float ra[4][16];
-#pragma unroll
-  for (int q = 0; q < 16; q++) {
-    ra[0][q] = acc_read(g0[q]);
-    ra[1][q] = acc_read(u0[q]);
-    ra[2][q] = acc_read(g1[q]);
-    ra[3][q] = acc_read(u1[q]);
-  }
-  // lo[q], hi[q]: block positions q and 16 + q after the exchange (position p of a block holds the
-  // tile's row 8 * ((p & 15) >> 2) + 4 * (p >> 4) + (p & 3), the order the second GEMM's weights use)
-  float lo[16], hi[16];
-#pragma unroll
-  for (int jj = 0; jj < 4; jj++) {
-    // accumulator 4*jj + i holds row 8*jj + 4*h + i of its tile: four consecutive bias entries
-    float b1a[4] = {0.f, 0.f, 0.f, 0.f}, b3a[4] = {0.f, 0.f, 0.f, 0.f};
-    float b1b[4] = {0.f, 0.f, 0.f, 0.f}, b3b[4] = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (BIAS) {
-      const int o = 8 * jj + 4 * h;
-      bias4(bg + o, b1a);
-      bias4(bu + o, b3a);
-      bias4(bg + 32 + o, b1b);
-      bias4(bu + 32 + o, b3b);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int q = 4 * jj + i;
-      // silu(g) = g / (1 + exp(-g)) with the hardware exponential and reciprocal (exp overflow gives 0);
-      // without biases nothing is added (x + 0 is not foldable: it turns -0 into +0)
-      float ga = ra[0][q], ua = ra[1][q], gb = ra[2][q], ub = ra[3][q];
-      if constexpr (BIAS) {
-        ga += b1a[i];
-        ua += b3a[i];
-        gb += b1b[i];
-        ub += b3b[i];
-      }
-      float va = ga * __builtin_amdgcn_rcpf(1.0f + __expf(-ga)) * ua;
-      float vb = gb * __builtin_amdgcn_rcpf(1.0f + __expf(-gb)) * ub;
-      if constexpr (!SECOND) vb = 0.f;
-      swap_halves(va, vb);
-      lo[q] = va;
-      hi[q] = vb;
-    }
-  }
-  const int slot = (rg * a.nkt2 + kt2) * 64 + lane;
-  u32x4_t* dst = reinterpret_cast<u32x4_t*>(a.actq + (int64_t)slot * kSlot);
-  uint32_t out[12];
-  uint32_t scales = 0;
-  // Each term is the fp32 remainder rounded to E2M3 (nearest even) under its block's scale.  The
-  // fp32-input conversion takes the block's even positions from its first source and the odd ones
-  // from its second (code 2j <- ev[j], code 2j + 1 <- od[j]).
-#pragma unroll
-  for (int term = 0; term < kTerms; term++) {
-    // block maximum of magnitudes: four independent chains of three-operand maxima
-    float m4[4] = {0.f, 0.f, 0.f, 0.f};
-    f32x16_t ev, od;
-#pragma unroll
-    for (int q = 0; q < 16; q += 2) {
-      m4[(q / 2) & 1] = fmaxf(fmaxf(m4[(q / 2) & 1], fabsf(lo[q])), fabsf(lo[q + 1]));
-      m4[2 + ((q / 2) & 1)] = fmaxf(fmaxf(m4[2 + ((q / 2) & 1)], fabsf(hi[q])), fabsf(hi[q + 1]));
-      ev[q / 2] = lo[q];
-      od[q / 2] = lo[q + 1];
-      ev[8 + q / 2] = hi[q];
-      od[8 + q / 2] = hi[q + 1];
-    }
-    const float amax = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-    const uint32_t ex = e8m0_from_amax_bits(__float_as_uint(amax));
-    const float sv = e8m0_as_scale_operand(ex);
-    // The conversion reads its sources over several passes while it writes its six result registers,
-    // so the result must not share a register with any source; the builtin carries no such
-    // constraint (the compiler gave the result the scale operand's register, which corrupted the
-    // codes), so the instruction is issued with an early-clobber output.
-    fp6x32_t codes;
-    asm("v_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, %3" : "=&v"(codes) : "v"(ev), "v"(od), "v"(sv));
-#pragma unroll
-    for (int d = 0; d < 6; d++) out[term * 6 + d] = codes[d];
-    scales |= ex << (8 * term);
-    if (term + 1 < kTerms) {
-      const auto deq = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(codes, sv);
-#pragma unroll
-      for (int q = 0; q < 16; q++) {
-        lo[q] = lo[q] - deq[q];
-        hi[q] = hi[q] - deq[16 + q];
-      }
-    }
-  }
-  dst[0] = u32x4_t{out[0], out[1], out[2], out[3]};
-  dst[1] = u32x4_t{out[4], out[5], out[6], out[7]};
-  dst[2] = u32x4_t{out[8], out[9], out[10], out[11]};
-  reinterpret_cast<uint32_t*>(a.acts)[slot] = scales;
-}
-
-// ------------------------------------------------------------------------------------------------
-// The grouped GEMM.  G1: first GEMM (A = weights, B = gathered token terms, SwiGLU epilogue);
-// otherwise the second GEMM (A = activation terms, B = weights, weighted fp16 rows to o16).
-//
-// A workgroup processes the items (M tile, column position) dealt to it in turn; the first D - 1
-// stages of the next item are copied before the current item's epilogue runs, so the ring refills
-// while the epilogue computes and stores.  The first GEMM gathers the next item's token rows through a
-// table of its token indices, which one copy per wave brings into LDS at the start of the current item.
-template <int NX, int NXS>
-struct ItemSrc {
-  int64_t wb;       // byte offset of this wave's first weight piece of step 0 (uniform)
-  int64_t wsb;      // byte offset of this wave's quarter of the step-0 scale records (uniform)
-  uint32_t x[NX];   // byte offsets of this lane's activation copies of step 0
-  uint32_t xs[NXS > 0 ? NXS : 1]; // byte offsets of this lane's activation scale copies of step 0
-};
-
-template <bool G1, bool BIAS, int WR, int WC, int RW, int CW, int D, int OCC>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void grouped_gemm_kernel(GemmArgs a) {
-  using C = Cfg<G1, WR, WC, RW, CW, D>;
-  constexpr int NRG = C::NRG, NT = C::NT;
-  constexpr int kTab = NRG * 32 > 64 ? NRG * 32 : 64;  // row table entries (one dword copy covers 64)
-  constexpr int kBias = G1 ? NT / 2 * 32 : NT * 32;   // bias entries of one half (first GEMM) or of the tile
-  // The ring, then the per-item tables (double-buffered by item parity, copied with LDS DMA one item
-  // ahead): the first GEMM's row tokens and gate / up biases, the second GEMM's row weights and biases.
-  // One LDS object holds both, so the compiler's tracking of LDS DMA writes sees a single buffer.
-  constexpr int kTabRow = 2 * kTab * 4, kTabB = 2 * (G1 ? 2 : 1) * kBias * 2;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[D * C::kStage + kTabRow + kTabB];
-  int32_t(*t_row)[kTab] = reinterpret_cast<int32_t(*)[kTab]>(smem + D * C::kStage);
-  uint16_t(*t_b)[G1 ? 2 : 1][kBias] = reinterpret_cast<uint16_t(*)[G1 ? 2 : 1][kBias]>(smem + D * C::kStage + kTabRow);
-  const int tid = threadIdx.x;
-  // LDS byte address of smem (address-space arithmetic from here on, no generic-pointer conversions)
-  const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_vptr_t)smem;
-  const int nkt = a.nkt, ncb = a.ncb;
-  const int nx = ncb * kCB / NT;
-  const int nrec = a.nrec;  // K-step records per token row of xq (first GEMM)
-
-  const int total = *a.ntiles * nx;
-  const int chunk = (total + kXcds - 1) / kXcds;
-  const int xcd = blockIdx.x % kXcds, per_xcd = gridDim.x / kXcds;
-  const int p0 = blockIdx.x / kXcds;
-  // items of this workgroup: q = 0 .. nq - 1 -> item xcd * chunk + p0 + q * per_xcd
-  int nq = 0;
-  if (p0 < chunk) {
-    const int last = min(chunk, total - xcd * chunk);  // local positions of this XCD's items
-    if (last > p0) nq = (last - p0 + per_xcd - 1) / per_xcd;
-  }
-  if (nq == 0) return;
-
-  int lane, wave;
-  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
-  asm volatile("s_lshr_b32 %0, %1, 6" : "=s"(wave) : "s"(__builtin_amdgcn_readfirstlane(tid)));
-  const int wr = wave / WC, wc = wave % WC;
-
-  auto item_of = [&](int q) __attribute__((always_inline)) { return xcd * chunk + p0 + q * per_xcd; };
-
-  // Copy sources of an item.  G1 takes the tokens of the item's rows from `tab` (LDS) when given, else
-  // from global memory.
-  using Src = ItemSrc<C::nX, C::nXS>;
-  auto make_src = [&](int item, int tb, Src& sr) __attribute__((always_inline)) {
-    const int tile = item / nx, x = item % nx;
-    const TileDesc td = a.tiles[tile];
-    const int e = td.e, prow0 = td.prow0;
-    const int cb = x * NT / kCB, jj0 = (x * NT) % kCB;
-    const int64_t wstep0 = (int64_t)(e * ncb + cb) * nkt;
-    sr.wb = wstep0 * (kCB * 1024) + (jj0 + wave * C::nW) * 1024;
-    sr.wsb = wstep0 * 1024 + wave * 256;
-#pragma unroll
-    for (int q = 0; q < C::nX; q++) {
-      int o = wave + 4 * q;
-      o = o < C::nXI ? o : C::nXI - 1;
-      if (G1) {
-        // 16-byte chunk c of the stage's records: row c / 7 of the tile, part c % 7 of its record; the
-        // chunks past the last row (one row group) repeat the last chunk into the stage's padding
-        int c = o * 64 + lane;
-        c = c < NRG * kRecChunks ? c : NRG * kRecChunks - 1;
-        const int row = c / 7, part = c % 7;
-        const int tok = tb >= 0 ? t_row[tb][row] : a.prow_tok[prow0 + row];
-        sr.x[q] = (uint32_t)(tok * nrec * kXRecG + part * 16);
-      } else {
-        const int rg = o / 3, pp = o % 3;
-        sr.x[q] = (uint32_t)(((prow0 >> 5) + rg) * nkt * (64 * kSlot) + (pp * 64 + lane) * 16);
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < C::nXS; q++) {  // second GEMM only
-      int o = wave + 4 * q;
-      o = o < NRG ? o : NRG - 1;
-      sr.xs[q] = (uint32_t)(((prow0 >> 5) + o) * nkt * 256 + lane * 4);
-    }
-  };
-  constexpr int xstep = G1 ? kXRecG : 64 * kSlot;  // bytes per K step of an activation copy
-  constexpr int xsstep = 256;                      // ... of an activation scale copy (second GEMM)
-  // Copy i (of kOps per wave) of stage `kt` of the item with sources `sr` into ring slot `slot`.
-  auto issue_op = [&](const Src& sr, int kt, int slot, auto ic) __attribute__((always_inline)) {
-    constexpr int i = decltype(ic)::value;
-    const uint32_t base = smem_lds + slot * C::kStage;
-    if constexpr (i < C::nW) {
-      dma16(a.wq + (sr.wb + kt * (kCB * 1024) + i * 1024) + lane * 16, base + C::oW + (wave * C::nW + i) * 1024);
-    } else if constexpr (i == C::nW) {
-      dma4(a.ws + (sr.wsb + kt * 1024) + lane * 4, base + C::oWS + wave * 256);
-    } else if constexpr (i < C::nW + 1 + C::nX) {
-      constexpr int q = i - C::nW - 1;
-      int o = wave + 4 * q;
-      o = o < C::nXI ? o : C::nXI - 1;
-      dma16(a.xq + (sr.x[q] + (uint32_t)(kt * xstep)), base + C::oX + o * 1024);
-    } else {
-      constexpr int q = i - C::nW - 1 - C::nX;
-      int o = wave + 4 * q;
-      o = o < NRG ? o : NRG - 1;
-      dma4(a.xs + (sr.xs[q] + (uint32_t)(kt * xsstep)), base + C::oXS + o * 256);
-    }
-  };
-  auto issue = [&](const Src& sr, int kt, int slot) __attribute__((always_inline)) {
-    static_for<0, C::kOps>([&](auto ic) __attribute__((always_inline)) { issue_op(sr, kt, slot, ic); });
-  };
-  // The tables of item `item` into buffer `tb`: rows (tokens or weights, kTab dwords) and, with biases,
-  // the item's bias entries; 256-byte dword copies spread over the waves (repeats are harmless).
-  auto issue_tab = [&](int item, int tb) __attribute__((always_inline)) {
-    const int tile = item / nx, x = item % nx;
-    const TileDesc td = a.tiles[tile];
-    const int prow0 = td.prow0;
-    constexpr int kRowOps = kTab / 64;
-    const uint8_t* rsrc = G1 ? reinterpret_cast<const uint8_t*>(a.prow_tok) : reinterpret_cast<const uint8_t*>(a.prow_w);
-    {
-      const int o = wave < kRowOps ? wave : 0;
-      dma4(rsrc + (int64_t)(prow0 + o * 64) * 4 + lane * 4, smem_lds + D * C::kStage + (tb * kTab + o * 64) * 4);
-    }
-    if constexpr (BIAS) {
-      constexpr int kBOps = kBias * 2 / 256;  // copies per bias half
-      // entries past the end of the bias row (columns beyond I or H, never used) re-read its last pair
-      const int len = G1 ? a.I : a.H;
-      const uint16_t* brow = a.bias + (int64_t)td.e * (G1 ? 2 * a.I : a.H);
-#pragma unroll
-      for (int i = 0; i < (G1 ? 2 : 1) * kBOps; i += 4) {
-        int o = wave + i;
-        o = o < (G1 ? 2 : 1) * kBOps ? o : (G1 ? 2 : 1) * kBOps - 1;
-        const int half = o / kBOps, part = o % kBOps;
-        int el = x * kBias + part * 128 + lane * 2;  // first of this lane's two entries
-        el = el < len - 2 ? el : len - 2;
-        dma4(brow + half * len + el,
-             smem_lds + D * C::kStage + kTabRow + ((tb * (G1 ? 2 : 1) + half) * kBias) * 2 + part * 256);
-      }
-    }
-  };
-
-  // Each E2M3 term operand (6 dwords) is read by its own two LDS loads (16 + 8 bytes for term 0 at
-  // slot offset 0, 8 + 16 bytes for term 1 at offset 24), so every MFMA operand tuple is written in
-  // place by its loads.  Each row group's and each term's loads take their base address through an
-  // opaque copy: that keeps the compiler from merging adjacent 8-byte loads (of the two terms, or of
-  // two row groups) into wider loads whose parts would then have to be copied (and waited for) to
-  // form the tuples.  Activation fragments and
-  // weight scales are double-buffered across steps ([P], P a compile-time parity); a weight fragment
-  // is reloaded for the next step after the last MFMA that uses it.
-  typedef const __attribute__((address_space(3))) u32x4_t* lds16_p;
-  typedef const __attribute__((address_space(3))) u32x2_t* lds8_p;
-  typedef const __attribute__((address_space(3))) uint32_t* lds4_p;
-  // The second GEMM (two workgroups per CU, a 3-stage ring) and the first GEMM's 64-row configuration
-  // (two per CU, 3 stages; long weight streams such as H = 7168) load the next step's fragments after
-  // the step's MFMAs (LATE), so a stage is needed one step later than with loads interleaved into the
-  // MFMAs: its copies get about two steps instead of one to land.  The first GEMM's 32-row (decode)
-  // and 128-row configurations measured faster with interleaved loads.
-  constexpr bool LATE = !G1 || (D == 3 && RW == 2);
-  using Plan = StepPlan<RW, CW, C::kOps, !G1, LATE>;
-  static constexpr Plan plan{};
-  static_assert(plan.valid(), "step plan");
-  i32x8_t xop[2][RW][kTerms];
-  uint32_t xsc[2][RW];
-  u32x4_t w[CW];
-  uint32_t wsc[2][CW / 4];
-  f32x16_t acc[RW][CW];
-  int jj0 = 0;
-  auto load_x = [&](const uint8_t* base, int r, auto pc) __attribute__((always_inline)) {
-    constexpr int P = decltype(pc)::value;
-    // first GEMM: lane l takes block l / 32 of row l % 32's record; second: slot l of the row group
-    lds_u8 rec = (lds_u8)(base + C::oX + (wr * RW + r) * (32 * kXRec) + (lane & 31) * kXRec);
-    lds_u8 xp = G1 ? rec + (lane >> 5) * kSlot : (lds_u8)(base + C::oX + (wr * RW + r) * 3072 + lane * kSlot);
-    asm("" : "+v"(xp));
-    lds_u8 xp1 = xp + 24;
-    asm("" : "+v"(xp1));
-    const u32x4_t a4 = *(lds16_p)xp;
-    const u32x2_t a2 = *(lds8_p)(xp + 16);
-    const u32x2_t b2 = *(lds8_p)xp1;
-    const u32x4_t b4 = *(lds16_p)(xp1 + 8);
-    xop[P][r][0] = i32x8_t{(int)a4[0], (int)a4[1], (int)a4[2], (int)a4[3], (int)a2[0], (int)a2[1], 0, 0};
-    xop[P][r][1] = i32x8_t{(int)b2[0], (int)b2[1], (int)b4[0], (int)b4[1], (int)b4[2], (int)b4[3], 0, 0};
-    if constexpr (G1)
-      xsc[P][r] = *(lds4_p)(rec + 2 * kSlot + (lane >> 5) * 4);
-    else
-      xsc[P][r] = *(lds4_p)(lds_u8)(base + C::oXS + (wr * RW + r) * 256 + lane * 4);
-  };
-  auto load_w = [&](const uint8_t* base, int j) __attribute__((always_inline)) {
-    w[j] = *(lds16_p)(lds_u8)(base + C::oW + (wc * CW + j) * 1024 + lane * 16);
-  };
-  auto load_ws = [&](const uint8_t* base, auto pc) __attribute__((always_inline)) {
-    constexpr int P = decltype(pc)::value;
-#pragma unroll
-    for (int j4 = 0; j4 < CW / 4; j4++)
-      wsc[P][j4] = *(lds4_p)(lds_u8)(base + C::oWS + lane * 16 + jj0 + wc * CW + j4 * 4);
-  };
-
-  // MFMA m of a step (the order of StepPlan).  Each is pinned by an ordered use of its accumulator:
-  // the MFMAs are pure, and the compiler would otherwise sink them past later waits and barriers
-  // (across basic blocks, where scheduling barriers do not reach).
-  auto mfma_one = [&](auto mc, auto pc) __attribute__((always_inline)) {
-    constexpr int m = decltype(mc)::value, P = decltype(pc)::value;
-    constexpr int g = m / (4 * RW), u = m % (4 * RW);
-    constexpr int t = u / (2 * RW), r = (u % (2 * RW)) / 2, j = 2 * g + (u % 2);
-    const i32x8_t wo = i32x8_t{(int)w[j][0], (int)w[j][1], (int)w[j][2], (int)w[j][3], 0, 0, 0, 0};
-    acc[r][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wo, xop[P][r][t], acc[r][j], kFp4, kFp6, j & 3,
-                                                                wsc[P][j >> 2], t, xsc[P][r]);
-    asm volatile("" : "+a"(acc[r][j]));
-  };
-
-  // Waits until at most n (0 <= n <= N) of this wave's most recent stages may still be in flight
-  // (younger copies and stores count too, which only makes the wait longer).
-  auto wait_stages = [&](int n, auto nc) __attribute__((always_inline)) {
-    constexpr int N = decltype(nc)::value;
-    if (n < 0) n = 0;
-    if (n >= N) {
-      wait_vmcnt<C::kOps * N>();
-    } else {
-      static_for<0, N>([&](auto ic) __attribute__((always_inline)) {
-        if (n == decltype(ic)::value) wait_vmcnt<C::kOps * decltype(ic)::value>();
-      });
-    }
-  };
-
-  Src cur;
-  int q = 0;
-  int item = item_of(0);
-  make_src(item, -1, cur);
-  issue_tab(item, 0);
-  wait_vmcnt<0>();
-  block_sync();
-#pragma unroll
-  for (int s = 0; s < D - 1; s++)
-    if (s < nkt) issue(cur, s, s);
-
-  while (true) {
-    const int tile = item / nx, x = item % nx;
-    const TileDesc td = a.tiles[tile];
-    const int prow0 = td.prow0, nrows = td.nrows;
-    jj0 = (x * NT) % kCB;
-    const bool has_next = q + 1 < nq;
-    const int tb = q & 1;
-
-    // stage 0 visible: the later stages of the prologue (and younger stores) may be in flight; after
-    // the barrier every wave is done with the previous item's tables, so the next item's tables can
-    // go to the other buffer.
-    wait_stages(nkt - 1, std::integral_constant<int, D - 2>{});
-    block_sync();
-    if (has_next) issue_tab(item_of(q + 1), tb ^ 1);
-    {
-      const uint8_t* b0 = smem;
-#pragma unroll
-      for (int r = 0; r < RW; r++) load_x(b0, r, std::integral_constant<int, 0>{});
-#pragma unroll
-      for (int j = 0; j < (LATE ? CW : CW - 2); j++) load_w(b0, j);
-      load_ws(b0, std::integral_constant<int, 0>{});
-    }
-#pragma unroll
-    for (int r = 0; r < RW; r++)
-#pragma unroll
-      for (int j = 0; j < CW; j++)
-#pragma unroll
-        for (int i = 0; i < 16; i++) acc[r][j][i] = 0.f;
-
-    // One K step.  Stage kt+1 (my copies landed) becomes everyone's at the barrier; every wave has by
-    // then finished all reads of stage kt-1 (they fed the MFMAs of step kt-1), so that slot takes the
-    // stage D - 1 steps ahead, if there is one.  Stages kt+2 .. min(kt+D-2, nkt-1) may stay in flight.
-    // MAIN steps (kt + D - 1 < nkt) interleave their copies with the MFMAs; the last steps of an item
-    // issue any copy up front and wait by a runtime count.
-    auto step = [&](int kt, auto pc, auto mc) __attribute__((always_inline)) {
-      constexpr int P = decltype(pc)::value;
-      constexpr bool MAIN = decltype(mc)::value;
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (!LATE) {
-        if constexpr (MAIN)
-          wait_vmcnt<C::kOps * (D - 3)>();
-        else
-          wait_stages(nkt - kt - 2, std::integral_constant<int, D - 3>{});
-        block_sync();
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      const int kn = kt + 1 < nkt ? kt + 1 : kt;
-      const uint8_t* cb = smem + (kt % D) * C::kStage;
-      const uint8_t* nb = smem + (kn % D) * C::kStage;
-      const int s = kt + D - 1;
-      if constexpr (!MAIN) {
-        if (s < nkt) issue(cur, s, s % D);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      static_for<0, Plan::NM>([&](auto mi) __attribute__((always_inline)) {
-        constexpr int m = decltype(mi)::value;
-        mfma_one(mi, pc);
-        static_for<0, Plan::kCap>([&](auto ci) __attribute__((always_inline)) {
-          constexpr int task = plan.t[m][decltype(ci)::value];
-          if constexpr (task >= StepTask::kDma) {
-            if constexpr (MAIN) issue_op(cur, s, s % D, std::integral_constant<int, task - StepTask::kDma>{});
-          } else if constexpr (task >= StepTask::kRel) {
-            load_w(nb, task - StepTask::kRel);
-          } else if constexpr (task == StepTask::kWs) {
-            load_ws(nb, std::integral_constant<int, 1 - P>{});
-          } else if constexpr (task >= StepTask::kX) {
-            load_x(nb, task - StepTask::kX, std::integral_constant<int, 1 - P>{});
-          } else if constexpr (task >= StepTask::kDef) {
-            load_w(cb, CW - 2 + task - StepTask::kDef);
-          }
-        });
-        __builtin_amdgcn_sched_barrier(0);
-      });
-      if constexpr (LATE) {
-        // Stage kt+1 (my copies landed) becomes everyone's at the barrier; the stages after it
-        // (kt+2 .. min(kt+D-1, nkt-1), this step's copies among them) may stay in flight.  Every wave
-        // has by then finished reading stage kt (its fragments fed this step's MFMAs), so the next
-        // step may copy into that slot.
-        if (kt + 1 < nkt) {
-          __builtin_amdgcn_sched_barrier(0);
-          if constexpr (MAIN)
-            wait_vmcnt<C::kOps * (D - 2)>();
-          else
-            wait_stages(nkt - kt - 2, std::integral_constant<int, D - 2>{});
-          block_sync();
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int r = 0; r < RW; r++) load_x(nb, r, std::integral_constant<int, 1 - P>{});
-#pragma unroll
-          for (int j = 0; j < CW; j++) load_w(nb, j);
-          load_ws(nb, std::integral_constant<int, 1 - P>{});
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-    };
-    // main steps in pairs (an even count, so the buffers are back in place), then the rest
-    const int nmain = nkt > D - 1 ? ((nkt - (D - 1)) & ~1) : 0;
-    int kt = 0;
-    for (; kt < nmain; kt += 2) {
-      step(kt, std::integral_constant<int, 0>{}, std::true_type{});
-      step(kt + 1, std::integral_constant<int, 1>{}, std::true_type{});
-    }
-    for (; kt + 2 <= nkt; kt += 2) {
-      step(kt, std::integral_constant<int, 0>{}, std::false_type{});
-      step(kt + 1, std::integral_constant<int, 1>{}, std::false_type{});
-    }
-    if (kt < nkt) step(kt, std::integral_constant<int, 0>{}, std::false_type{});
-
-    // ---- next item's first D - 1 stages go out before this item's epilogue, so their latency hides
-    // under it.  make_src reads the next item's token table, whose copy went out at this item's start:
-    // every copy of this wave is waited for here (the interleaved plan's last step has already waited
-    // for all of them, and so has a late-load item of two or more K steps; a late-load item of one K
-    // step has not), and the barrier then makes every wave's table copies visible and every wave done
-    // reading the ring.
-    if (has_next) {
-      wait_vmcnt<0>();
-      block_sync();
-      make_src(item_of(q + 1), tb ^ 1, cur);
-#pragma unroll
-      for (int s = 0; s < D - 1; s++)
-        if (s < nkt) issue(cur, s, s);
-    }
-
-    // ---- epilogue (one tile or tile pair at a time: the scheduling barriers keep each one's values
-    // short-lived)
-    if constexpr (G1) {
-#pragma unroll
-      for (int r = 0; r < RW; r++) {
-        const int rgl = wr * RW + r;
-        if (rgl * 32 >= nrows) continue;
-#pragma unroll
-        for (int p = 0; p < CW / 4; p++) {
-          const int it = (x * NT + wc * CW) / 2 + 2 * p;  // even: a K step of the second GEMM
-          const int il = (wc * CW) / 2 + 2 * p;           // activation tile within the item
-          if (it + 1 < a.ntl)
-            g1_epilogue_pair<BIAS, true>(acc[r][4 * p], acc[r][4 * p + 1], acc[r][4 * p + 2], acc[r][4 * p + 3], a,
-                                         (lds_u16*)&t_b[tb][0][il * 32], (lds_u16*)&t_b[tb][G1 ? 1 : 0][il * 32],
-                                         it >> 1, (prow0 >> 5) + rgl, lane);
-          else if (it < a.ntl)
-            g1_epilogue_pair<BIAS, false>(acc[r][4 * p], acc[r][4 * p + 1], acc[r][4 * p + 2], acc[r][4 * p + 3], a,
-                                          (lds_u16*)&t_b[tb][0][il * 32], (lds_u16*)&t_b[tb][G1 ? 1 : 0][il * 32],
-                                          it >> 1, (prow0 >> 5) + rgl, lane);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-    } else {
-      // Lane l holds token row l % 32 of its row group and output columns 8*jj + 4*(l/32) + i of each
-      // tile; after one exchange of lane halves, half h holds the 16 consecutive columns 16h .. 16h+15
-      // of the row: one block with a power-of-two scale (largest magnitude in [2^14, 2^15) after
-      // scaling), stored as 32 bytes of fp16 plus the exponent byte.  Rows of a row group past the
-      // expert's pairs are padding rows of that expert, which nothing reads: their lanes store nothing.
-      const int m = lane & 31, h = lane >> 5;
-#pragma unroll
-      for (int r = 0; r < RW; r++) {
-        const int rgl = wr * RW + r;
-        if (rgl * 32 >= nrows) continue;
-        const float wt = __builtin_bit_cast(float, t_row[tb][rgl * 32 + m]);
-        const bool real = rgl * 32 + m < nrows;
-        const int64_t prow = prow0 + rgl * 32 + m;
-        uint16_t* orow = a.o16 + prow * a.H;
-        uint8_t* srow = a.osc + prow * (a.H / 16);
-#pragma unroll
-        for (int j = 0; j < CW; j++) {
-          const int nt = x * NT + wc * CW + j;
-          if (nt < a.ntl) {
-            // v[c]: column 16h + c of the tile after the exchange
-            // the tile's 16 values are read first (each read is a scheduling boundary), then exchanged
-            float v[16], ra[16];
-#pragma unroll
-            for (int i = 0; i < 16; i++) ra[i] = acc_read(acc[r][j][i]);
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-              float x0 = ra[i], x2 = ra[8 + i];
-              float x1 = ra[4 + i], x3 = ra[12 + i];
-              swap_halves(x0, x2);  // half 0: cols i | 4 + i;  half 1: cols 16 + i | 20 + i
-              swap_halves(x1, x3);  // half 0: cols 8 + i | 12 + i;  half 1: cols 24 + i | 28 + i
-              v[i] = x0;
-              v[4 + i] = x2;
-              v[8 + i] = x1;
-              v[12 + i] = x3;
-            }
-            if constexpr (BIAS) {
-              lds_u16* bp = (lds_u16*)&t_b[tb][0][(wc * CW + j) * 32 + 16 * h];
-              float b[16];
-#pragma unroll
-              for (int c = 0; c < 4; c++) bias4(bp + 4 * c, b + 4 * c);
-#pragma unroll
-              for (int c = 0; c < 16; c++) v[c] += b[c];
-            }
-            // The block maximum of w * v is |w| times that of v (rounding is monotonic), and scaling by a
-            // power of two commutes with rounding, so w * 2^-ex is applied as one factor.
-            float amax = 0.f;
-#pragma unroll
-            for (int c = 0; c < 16; c++) amax = fmaxf(amax, fabsf(v[c]));
-            amax *= fabsf(wt);
-            int ex = amax > 0.f ? __builtin_amdgcn_frexp_expf(amax) - 15 : 0;
-            ex = ex < -127 ? -127 : (ex > 127 ? 127 : ex);
-            const float f = __builtin_ldexpf(wt, -ex);
-            uint32_t hv[8];
-#pragma unroll
-            for (int c = 0; c < 8; c++) {
-              const f16x2_t e = __builtin_convertvector((f32x2_t){v[2 * c] * f, v[2 * c + 1] * f}, f16x2_t);
-              hv[c] = __builtin_bit_cast(uint32_t, e);
-            }
-            if (real) {
-              u32x4_t* op = reinterpret_cast<u32x4_t*>(orow + nt * 32 + 16 * h);
-              op[0] = u32x4_t{hv[0], hv[1], hv[2], hv[3]};
-              op[1] = u32x4_t{hv[4], hv[5], hv[6], hv[7]};
-              srow[nt * 2 + h] = (uint8_t)(ex + 127);
-            }
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-    }
-
-    if (++q >= nq) break;
-    item = item_of(q);
-  }
-}
-
-// y[t] = sum over the token's k pairs of the fp16 rows (times their block powers of two), fp32 sum in
+// y[t] = sum over the token's k pairs of the int16 rows (times their block powers of two), fp32 sum in
 // slot order, bf16 output.  One thread per 8 output columns of a token; the rows of four pairs are
 // loaded before any is added, so four gathers per thread are in flight.
 MX_DEV void combine_add(float* s, const u32x4_t& v, int ex) {
   const float f = __builtin_ldexpf(1.0f, ex);  // exact power of two (ex in [-127, 127])
 #pragma unroll
   for (int q = 0; q < 8; q++) {
-    const uint16_t hb = (uint16_t)(v[q >> 1] >> (16 * (q & 1)));
-    s[q] += (float)__builtin_bit_cast(_Float16, hb) * f;
+    const int16_t hb = (int16_t)(uint16_t)(v[q >> 1] >> (16 * (q & 1)));
+    s[q] += (float)hb * f;  // |hb| < 2^14: exact in fp32, as is the product by a power of two
   }
 }
 
@@ -828,44 +48,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   }
 }
 
-template <bool G1, int WR, int WC, int RW, int CW, int D, int OCC>
-int launch_cfg(const GemmArgs& a, int64_t max_tiles, hipStream_t stream) {
-  const int wg_per_cu = OCC;
-  using C = Cfg<G1, WR, WC, RW, CW, D>;
-  const int64_t nx = (int64_t)a.ncb * kCB / C::NT;
-  int64_t items = max_tiles * nx;
-  int64_t grid = 256 * wg_per_cu;
-  if (items < grid) grid = items;
-  grid = kXcds * cdiv(grid, kXcds);
-  if (grid < kXcds) grid = kXcds;
-  if (a.bias)
-    hipLaunchKernelGGL((grouped_gemm_kernel<G1, true, WR, WC, RW, CW, D, OCC>), dim3((unsigned)grid), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((grouped_gemm_kernel<G1, false, WR, WC, RW, CW, D, OCC>), dim3((unsigned)grid), dim3(256), 0, stream, a);
-  return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
-}
-
 }  // namespace
 
-// Tile configurations by rows per M tile (32 * NRG): 1 row group for decode-like loads, 2 or 4 (first
-// GEMM only) for larger ones.  The 128-row first GEMM covers a whole column block per workgroup, one
-// workgroup per CU; the others run two workgroups per CU so that one's stores and waits overlap the
-// other's MFMAs.
-int launch_gemm1(int NRG, const GemmArgs& a, int64_t max_tiles, hipStream_t stream) {
-  switch (NRG) {
-    case 1: return launch_cfg<true, 1, 4, 1, 4, 3, 2>(a, max_tiles, stream);
-    case 2: return launch_cfg<true, 1, 4, 2, 4, 3, 2>(a, max_tiles, stream);
-    case 4: return launch_cfg<true, 2, 2, 2, 8, 4, 1>(a, max_tiles, stream);
-    default: return MXFP4_ERR_SHAPE;
-  }
+int launch_gemm1(int af, int NRG, const GemmArgs& a, int64_t max_tiles, hipStream_t stream) {
+  return af == kActBf16 ? gemm1_launch<kActBf16>(NRG, a, max_tiles, stream) : launch_gemm1_mx(af, NRG, a, max_tiles, stream);
 }
 
-int launch_gemm2(int NRG, const GemmArgs& a, int64_t max_tiles, hipStream_t stream) {
-  switch (NRG) {
-    case 1: return launch_cfg<false, 1, 4, 1, 4, 3, 2>(a, max_tiles, stream);
-    case 2: return launch_cfg<false, 1, 4, 2, 4, 3, 2>(a, max_tiles, stream);
-    default: return MXFP4_ERR_SHAPE;
-  }
+int launch_gemm2(int af, int NRG, const GemmArgs& a, int64_t max_tiles, hipStream_t stream) {
+  return af == kActBf16 ? gemm2_launch<kActBf16>(NRG, a, max_tiles, stream) : launch_gemm2_mx(af, NRG, a, max_tiles, stream);
 }
 
 int launch_combine(const uint16_t* o16, const uint8_t* osc, const int32_t* pair_prow, void* y, int64_t T, int64_t H, int k,

@@ -17,8 +17,8 @@ int launch_unpack_gfx950(const MoeGeom& g, const BlobOffsets& o, bool bias, cons
 int launch_repack_standard(const MoeGeom& g, bool bias, const void* w13_q, const void* w13_s, const void* w2_q,
                            const void* w2_s, const void* b13, const void* b2, int bias_is_fp32, bool swap, bool tiled,
                            const size_t off[6], void* out, hipStream_t stream);
-int launch_xprep(const void* x, int64_t T, int64_t ldx, const MoeGeom& g, void* xq, int32_t* zero, int64_t nzero,
-                 hipStream_t stream);
+int launch_xprep(int af, const void* x, int64_t T, int64_t ldx, const MoeGeom& g, void* xq, int32_t* zero,
+                 int64_t nzero, hipStream_t stream);
 int launch_zero_i32(int32_t* p, int64_t n, hipStream_t stream);
 int launch_route(const float* logits, int64_t T, int E, int k, int renormalize, int32_t* ids, float* w,
                  int32_t* blkcnt, hipStream_t stream);
@@ -26,14 +26,16 @@ int launch_place(const int32_t* ids, const float* w, int32_t* blkcnt, int64_t T,
                  int32_t* offsets, int32_t* poffsets, int32_t* sorted_pairs, int32_t* prow_pair, int32_t* prow_tok,
                  float* prow_w, int32_t* pair_prow, void* tiles, int32_t* ntiles, void* tiles2, int32_t* ntiles2,
                  hipStream_t stream);
-int launch_gemm1(int NRG, const GemmArgs& a, int64_t max_tiles, hipStream_t stream);
-int launch_gemm2(int NRG, const GemmArgs& a, int64_t max_tiles, hipStream_t stream);
+int launch_gemm1(int af, int NRG, const GemmArgs& a, int64_t max_tiles, hipStream_t stream);
+int launch_gemm2(int af, int NRG, const GemmArgs& a, int64_t max_tiles, hipStream_t stream);
+int launch_gemm1_mx(int af, int NRG, const GemmArgs& a, int64_t max_tiles, hipStream_t stream);
+int launch_gemm2_mx(int af, int NRG, const GemmArgs& a, int64_t max_tiles, hipStream_t stream);
 int launch_combine(const uint16_t* o16, const uint8_t* osc, const int32_t* pair_prow, void* y, int64_t T, int64_t H, int k,
                    hipStream_t stream);
 
 // The MoE forward pass on a caller-given workspace: argument validation, then the launches in stream
 // order; events (may be NULL) are recorded at the stage boundaries.  Returns a status.
-int forward_impl(const mxfp4_moe_dims* d, const void* packed_gfx950, const void* x_bf16, int64_t T, int64_t ldx,
-                 const float* router_logits, int32_t top_k, int32_t renormalize, void* y_bf16, int32_t* topk_ids,
-                 float* topk_w, void* workspace, size_t workspace_bytes, hipStream_t s, void* const* events,
-                 int32_t n_events);
+int forward_impl(const mxfp4_moe_dims* d, int32_t act_format, const void* packed_gfx950, const void* x_bf16,
+                 int64_t T, int64_t ldx, const float* router_logits, int32_t top_k, int32_t renormalize, void* y_bf16,
+                 int32_t* topk_ids, float* topk_w, void* workspace, size_t workspace_bytes, hipStream_t s,
+                 void* const* events, int32_t n_events);

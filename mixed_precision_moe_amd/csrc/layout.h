@@ -82,36 +82,52 @@ static inline BlobOffsets blob_offsets(const MoeGeom& g, bool bias) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Activations enter the block-scaled MFMA as kTerms E2M3 terms x = t0 + t1, each with its own E8M0
-// scale per 32 elements: 24 bytes per term per lane, the two terms back to back in a kSlot = 48 byte
-// slot; the two scale bytes of a slot sit in one dword (term 0 in the low byte, two zero bytes).
-constexpr int kTerms = 2;
-constexpr int kSlot = 48;
+// Activation formats of the layer (MXFP4_ACT_* in the public header): the format in which both GEMMs
+// take their token operand (the layer input, then the SwiGLU output).  The MFMA's B operand is one or
+// more terms per 32-element block, each with its own E8M0 scale byte:
+//   kActBf16:  bf16-accurate activations as three terms v = t0 + t1 + t2 -- E2M3 (FP6), E2M3 of the
+//              remainder, E2M1 (FP4) of what is left -- each scale from the 0.75 round-up rule;
+//              24 + 24 + 16 bytes per lane
+//   kActMxfp8: one E4M3 (FP8) term, scale rule for E4M3 elements (block maximum to [224, 448)); 32 bytes
+//   kActMxfp4: one E2M1 term, the weights' rule; 16 bytes
+// A lane's terms sit back to back in one slot; the scale bytes of a slot in one dword (term t in byte
+// t, the other bytes zero).
+enum : int { kActBf16 = 0, kActMxfp8 = 1, kActMxfp4 = 2 };
+constexpr int kFmtFp8 = 0, kFmtFp6 = 2, kFmtFp4 = 4;  // MFMA operand format codes (E4M3, E2M3, E2M1)
+
+constexpr int act_terms(int af) { return af == kActBf16 ? 3 : 1; }
+constexpr int act_term_fmt(int af, int t) {
+  return af == kActMxfp8 ? kFmtFp8 : af == kActMxfp4 ? kFmtFp4 : (t < 2 ? kFmtFp6 : kFmtFp4);
+}
+constexpr int fmt_bytes(int fmt) { return fmt == kFmtFp8 ? 32 : fmt == kFmtFp6 ? 24 : 16; }
+constexpr int act_term_offset(int af, int t) {
+  return t == 0 ? 0 : act_term_offset(af, t - 1) + fmt_bytes(act_term_fmt(af, t - 1));
+}
+constexpr int act_slot(int af) { return act_term_offset(af, act_terms(af)); }
 // The first GEMM's activation record of one token and one 64-wide K step: the two blocks' slots, their
-// two scale dwords, 8 zero bytes -- 112 bytes, seven 16-byte copies, so the first GEMM copies a row's
-// terms and scales together.
-constexpr int kXRec = 2 * kSlot + 16;
-constexpr int kRecChunks = 32 * kXRec / 16;  // 16-byte chunks of the records of one row group (224)
-// In global memory each record starts a 128-byte line of its own (the copies take its first kXRec
-// bytes), so every record of a copy is one cache line.
-constexpr int kXRecG = 128;
+// two scale dwords, 8 zero bytes (144, 80 or 48 bytes); records of a token row are consecutive, so the
+// first GEMM copies a row's terms and scales together in 16-byte chunks.
+constexpr int act_rec(int af) { return 2 * act_slot(af) + 16; }
+constexpr int kMaxSlot = 64, kMaxRec = 144;  // the largest format (kActBf16), for workspace sizes
+static_assert(act_slot(kActBf16) == kMaxSlot && act_rec(kActBf16) == kMaxRec, "largest format");
+static_assert(act_slot(kActMxfp8) == 32 && act_slot(kActMxfp4) == 16, "slot sizes");
 
 // ---------------------------------------------------------------------------------------------
 // Forward-pass workspace.  Rows of the expert-sorted order are padded per expert to a multiple of
 // 32 ("padded rows"); a padded row with no pair has pair index -1, token 0 and weight 0.
 //   blkcnt : [nblk_route][E]  pairs per (block of kRouteTokens tokens, expert); after the scan, the
 //            exclusive prefix over blocks
-//   xq  : [T][nkt1][kXRecG]  per token and K step of x: for each of the two 32-element blocks the two
-//         E2M3 terms (kSlot bytes), then per block a dword with the E8M0 bytes of the two terms and
-//         two zero bytes, then zero bytes up to kXRecG
-//   actq: [row group of 32][nkt2][64 lanes][kSlot]  the second GEMM's A operand, lane (row l%32,
-//         K block l/32)
-//   acts: [row group][nkt2][64 lanes][4]
+//   xq  : [T][nkt1][act_rec]  per token and K step of x: the two 32-element blocks' slots (terms of the
+//         activation format), then per block the dword of its scale bytes, then 8 zero bytes
+//   actq: [row group of 32][nkt2][64 lanes][act_slot]  the second GEMM's activation operand, lane
+//         (row l%32, K block l/32)
+//   acts: [row group][nkt2][64 lanes][4]  the matching scale dwords
+//   (sized for the largest format; the other formats use the front of each buffer)
 //   tiles, tiles2: TileDesc (expert, first padded row, valid rows, 0) per M tile of the first and of the
 //         second GEMM (their tile heights may differ)
 //   pair_prow: [T*k] padded row of each (token, slot) pair
-//   o16 : fp16 [padded rows][H], row r = w * (expert output + b2) of the pair at row r, divided by the
-//         power of two 2^(osc - 127) of its block
+//   o16 : int16 [padded rows][H], row r = w * (expert output + b2) of the pair at row r, divided by
+//         the power of two 2^(osc - 127) of its block and rounded to an integer (|value| < 2^14)
 //   osc : [padded rows][H / 16] bytes, the block exponents: one per 16 consecutive columns of a row
 constexpr int kRouteTokens = 64;
 
@@ -142,8 +158,8 @@ static inline FwdWs fwd_ws(const MoeGeom& g, int64_t T, int64_t k) {
   w.ntiles = take(16);
   w.tiles2 = take(16 * w.max_tiles);
   w.ntiles2 = take(16);
-  w.xq = take((uint64_t)T * g.nkt1 * kXRecG);
-  w.actq = take((uint64_t)(w.nrows_alloc / 32) * g.nkt2 * 64 * kSlot);
+  w.xq = take((uint64_t)T * g.nkt1 * kMaxRec);
+  w.actq = take((uint64_t)(w.nrows_alloc / 32) * g.nkt2 * 64 * kMaxSlot);
   w.acts = take((uint64_t)(w.nrows_alloc / 32) * g.nkt2 * 64 * 4);
   w.o16 = take((uint64_t)w.nrows_alloc * g.H * 2);
   w.osc = take((uint64_t)w.nrows_alloc * (g.H / 16));
@@ -171,7 +187,7 @@ struct GemmArgs {
   const int32_t* ntiles;
   uint8_t* actq;            // first GEMM output
   uint8_t* acts;
-  uint16_t* o16;            // second GEMM output (fp16, padded-row order) and its block exponents
+  uint16_t* o16;            // second GEMM output (int16 blocks, padded-row order) and their exponents
   uint8_t* osc;
   int32_t nkt, ncb;         // K steps and column blocks of this GEMM
   int32_t ntl;              // output column tiles of this GEMM (I/32 activation tiles, or H/32)

@@ -45,13 +45,13 @@ MX_API int moe_mxfp4_forward_noalloc(const mxfp4_moe_dims* d, const void* packed
   // argument errors, or no tokens: the status of the same call on a caller workspace, and no device
   // contact
   if (need == 0 || T == 0)
-    return forward_impl(d, packed_gfx950, x_bf16, T, ldx, router_logits, top_k, renormalize, y_bf16, topk_ids, topk_w,
-                        nullptr, 0, (hipStream_t)stream, nullptr, 0);
+    return forward_impl(d, MXFP4_ACT_BF16, packed_gfx950, x_bf16, T, ldx, router_logits, top_k, renormalize, y_bf16,
+                        topk_ids, topk_w, nullptr, 0, (hipStream_t)stream, nullptr, 0);
   if (need > (size_t)MXFP4_NOALLOC_SCRATCH_BYTES) return MXFP4_ERR_WORKSPACE;
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MXFP4_ERR_DEVICE;
   void* ws = scratch_address(dev);
   if (!ws) return MXFP4_ERR_DEVICE;
-  return forward_impl(d, packed_gfx950, x_bf16, T, ldx, router_logits, top_k, renormalize, y_bf16, topk_ids, topk_w, ws,
-                      (size_t)MXFP4_NOALLOC_SCRATCH_BYTES, (hipStream_t)stream, nullptr, 0);
+  return forward_impl(d, MXFP4_ACT_BF16, packed_gfx950, x_bf16, T, ldx, router_logits, top_k, renormalize, y_bf16,
+                      topk_ids, topk_w, ws, (size_t)MXFP4_NOALLOC_SCRATCH_BYTES, (hipStream_t)stream, nullptr, 0);
 }

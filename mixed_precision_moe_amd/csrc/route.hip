@@ -26,25 +26,78 @@ MX_DEV uint32_t amax_bits32(const uint32_t* w) {  // 16 words = 32 bf16 -> large
   return m;
 }
 
-// x [T, ldx] bf16 -> xq: per 32-element block the two E2M3 terms x = t0 + t1.  Each term is the
-// current remainder quantized with its own E8M0 scale from the 0.75 round-up rule (block maximum /
-// scale < 7 <= 7.5, the E2M3 maximum, so no term saturates).  The remainder x - t0 is exact in bf16
-// (a bf16 value minus its own rounding to a coarser grid).  K is padded to a multiple of 64 with zero
-// blocks.  Also clears `zero` (nzero ints).
+// x [T, ldx] bf16 -> xq: per 32-element block the terms of activation format AF (layout.h), each the
+// current remainder quantized with its own E8M0 scale:
+//   kActBf16: t0 = E2M3 of x, t1 = E2M3 of x - t0, t2 = E2M1 of x - t0 - t1, scales from the 0.75
+//             round-up rule (an E2M3 term's maximum / scale < 7 <= 7.5, the E2M3 maximum, so it does
+//             not saturate; the last term may, by at most 1/7 of its own maximum).  Each remainder of a
+//             bf16 value after its rounding to a coarser grid is again exact in bf16.
+//   kActMxfp8: one E4M3 term, scale rule for E4M3 (no saturation)
+//   kActMxfp4: one E2M1 term, the weights' rule
+// K is padded to a multiple of 64 with zero blocks.  Also clears `zero` (nzero ints).
 //
 // A wave handles 64 consecutive blocks (block gi = token * nblk + b), lane l computing block l.  Its
 // global accesses are staged through LDS so that every load and store instruction covers 1 KB of
 // consecutive bytes: 16-byte chunk c = 64 j + l of the wave's 4 KB of x is loaded by lane l in load j and
-// written to LDS, lane l then reads its block's four chunks; lane l writes its 48-byte slot and scale
-// dword into record l / 2 (blocks 2r and 2r + 1 form the K-step record r), and the wave's 32 records
-// (4 KB, consecutive in xq) leave as four 1 KB stores.
+// written to LDS, lane l then reads its block's four chunks; lane l writes its slot and scale dword into
+// record l / 2 (blocks 2r and 2r + 1 form the K-step record r), and the wave's 32 records (consecutive
+// in xq) leave as 1 KB stores.
 typedef float xf32x2_t __attribute__((ext_vector_type(2)));
+typedef short xs16x2_t __attribute__((ext_vector_type(2)));
 
+MX_DEV bf16x32_t as_bf16x32(const uint32_t* w) {
+  bf16x32_t v;
+#pragma unroll
+  for (int j = 0; j < 16; j++) {
+    const bf16x2_t two = __builtin_bit_cast(bf16x2_t, w[j]);
+    v[2 * j] = two[0];
+    v[2 * j + 1] = two[1];
+  }
+  return v;
+}
+
+// w[j] (elements 2j, 2j + 1) -= the dequantized E2M3 codes, exactly, in bf16
+MX_DEV void sub_fp6(uint32_t* w, const fp6x32_t& codes, float sc) {
+  const auto deq = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(codes, sc);
+#pragma unroll
+  for (int j = 0; j < 16; j++) {
+    const float a = bf16_bits_to_f32(w[j] & 0xFFFFu) - deq[2 * j];
+    const float c = bf16_bits_to_f32(w[j] >> 16) - deq[2 * j + 1];
+    w[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector((xf32x2_t){a, c}, bf16x2_t));
+  }
+}
+
+// 32 bf16 (w[j]: elements 2j, 2j + 1) -> E2M1 codes, element i in nibble i of the 16 bytes
+MX_DEV void fp4_from_bf16(const uint32_t* w, float sc, uint32_t* out) {
+#pragma unroll
+  for (int d = 0; d < 4; d++) {
+    uint32_t p = 0;
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(p, __builtin_bit_cast(bf16x2_t, w[4 * d]), sc, 0);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(p, __builtin_bit_cast(bf16x2_t, w[4 * d + 1]), sc, 1);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(p, __builtin_bit_cast(bf16x2_t, w[4 * d + 2]), sc, 2);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(p, __builtin_bit_cast(bf16x2_t, w[4 * d + 3]), sc, 3);
+    out[d] = p;
+  }
+}
+
+// 32 bf16 -> E4M3 codes, element i in byte i of the 32 bytes
+MX_DEV void fp8_from_bf16(const uint32_t* w, float sc, uint32_t* out) {
+#pragma unroll
+  for (int d = 0; d < 8; d++) {
+    xs16x2_t p = xs16x2_t{0, 0};
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(p, __builtin_bit_cast(bf16x2_t, w[2 * d]), sc, false);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(p, __builtin_bit_cast(bf16x2_t, w[2 * d + 1]), sc, true);
+    out[d] = __builtin_bit_cast(uint32_t, p);
+  }
+}
+
+template <int AF>
 __global__ __launch_bounds__(256) void xprep_kernel(const uint16_t* __restrict__ x, int64_t ldx, int64_t H, int64_t nblk,
                                                     uint8_t* __restrict__ xq, int32_t* __restrict__ zero,
                                                     int64_t nzero, int64_t n) {
+  constexpr int SLOT = act_slot(AF), REC = act_rec(AF);
   __shared__ __attribute__((aligned(16))) uint8_t stage_in[4][4096];
-  __shared__ __attribute__((aligned(16))) uint8_t stage_out[4][32 * kXRecG];
+  __shared__ __attribute__((aligned(16))) uint8_t stage_out[4][32 * REC];
   GRID_STRIDE(i, nzero) zero[i] = 0;  // the routing histogram, cleared for the next launch
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t hb = H / 32;  // real blocks per token
@@ -69,49 +122,50 @@ __global__ __launch_bounds__(256) void xprep_kernel(const uint16_t* __restrict__
       const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&stage_in[wave][lane * 64 + p * 16]);
       w[4 * p] = v[0]; w[4 * p + 1] = v[1]; w[4 * p + 2] = v[2]; w[4 * p + 3] = v[3];
     }
-    fp6x32_t tq[kTerms];
-    uint32_t te[kTerms];
+    uint32_t slot[SLOT / 4];
+    uint32_t scales;
+    if constexpr (AF == kActBf16) {
+      const uint32_t e0 = e8m0_from_amax_bits(amax_bits32(w) << 16);
+      const fp6x32_t t0 = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(as_bf16x32(w), e8m0_as_scale_operand(e0));
+      sub_fp6(w, t0, e8m0_as_scale_operand(e0));
+      const uint32_t e1 = e8m0_from_amax_bits(amax_bits32(w) << 16);
+      const fp6x32_t t1 = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(as_bf16x32(w), e8m0_as_scale_operand(e1));
+      sub_fp6(w, t1, e8m0_as_scale_operand(e1));
+      const uint32_t e2 = e8m0_from_amax_bits(amax_bits32(w) << 16);
 #pragma unroll
-    for (int term = 0; term < kTerms; term++) {
-      bf16x32_t v;
-#pragma unroll
-      for (int j = 0; j < 16; j++) {
-        const bf16x2_t two = __builtin_bit_cast(bf16x2_t, w[j]);
-        v[2 * j] = two[0];
-        v[2 * j + 1] = two[1];
+      for (int d = 0; d < 6; d++) {
+        slot[d] = t0[d];
+        slot[6 + d] = t1[d];
       }
-      te[term] = e8m0_from_amax_bits(amax_bits32(w) << 16);
-      const float sc = e8m0_as_scale_operand(te[term]);
-      tq[term] = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(v, sc);
-      if (term + 1 < kTerms) {
-        const auto deq = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(tq[term], sc);
-#pragma unroll
-        for (int j = 0; j < 16; j++) {
-          // the remainder of a bf16 value is exact in fp32 (and in bf16); hardware conversion
-          const float a = bf16_bits_to_f32(w[j] & 0xFFFFu) - deq[2 * j];
-          const float c = bf16_bits_to_f32(w[j] >> 16) - deq[2 * j + 1];
-          w[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector((xf32x2_t){a, c}, bf16x2_t));
-        }
-      }
+      fp4_from_bf16(w, e8m0_as_scale_operand(e2), slot + 12);
+      scales = e0 | (e1 << 8) | (e2 << 16);
+    } else if constexpr (AF == kActMxfp8) {
+      const uint32_t e = e8m0_e4m3_from_amax_bits(amax_bits32(w) << 16);
+      fp8_from_bf16(w, e8m0_as_scale_operand(e), slot);
+      scales = e;
+    } else {
+      const uint32_t e = e8m0_from_amax_bits(amax_bits32(w) << 16);
+      fp4_from_bf16(w, e8m0_as_scale_operand(e), slot);
+      scales = e;
     }
-    uint8_t* rec = &stage_out[wave][(lane >> 1) * kXRecG];
-    u32x4_t* sl = reinterpret_cast<u32x4_t*>(rec + (lane & 1) * kSlot);
-    sl[0] = u32x4_t{tq[0][0], tq[0][1], tq[0][2], tq[0][3]};
-    sl[1] = u32x4_t{tq[0][4], tq[0][5], tq[1][0], tq[1][1]};
-    sl[2] = u32x4_t{tq[1][2], tq[1][3], tq[1][4], tq[1][5]};
-    reinterpret_cast<uint32_t*>(rec + 2 * kSlot)[lane & 1] = te[0] | (te[1] << 8);
-    // the record's tail (8 bytes after the scale dwords, then up to kXRecG): zero, 16 bytes per lane
-    if ((lane & 1) == 0) *reinterpret_cast<u32x2_t*>(rec + 2 * kSlot + 8) = u32x2_t{0u, 0u};
-    else *reinterpret_cast<u32x4_t*>(rec + kXRec) = u32x4_t{0u, 0u, 0u, 0u};
+    uint8_t* rec = &stage_out[wave][(lane >> 1) * REC];
+    u32x4_t* sl = reinterpret_cast<u32x4_t*>(rec + (lane & 1) * SLOT);
+    static_assert(SLOT % 16 == 0, "whole 16-byte stores");
+#pragma unroll
+    for (int d = 0; d < SLOT / 16; d++)
+      sl[d] = u32x4_t{slot[4 * d], slot[4 * d + 1], slot[4 * d + 2], slot[4 * d + 3]};
+    reinterpret_cast<uint32_t*>(rec + 2 * SLOT)[lane & 1] = scales;
+    // the record's last 8 bytes: zero
+    if (lane & 1) *reinterpret_cast<u32x2_t*>(rec + 2 * SLOT + 8) = u32x2_t{0u, 0u};
     __builtin_amdgcn_wave_barrier();
     // coalesced stores: 16-byte chunk c = 64 j + lane of the wave's 32 records (g0 is even, so the
     // wave's first record is g0 / 2; a record exists when its first block does)
     const int64_t r0 = g0 / 2;
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
+    for (int j = 0; j < (2 * REC + 63) / 64; j++) {
       const int c = 64 * j + lane;
-      if (2 * (r0 + (c * 16) / kXRecG) < n)
-        *reinterpret_cast<u32x4_t*>(xq + r0 * kXRecG + c * 16) = *reinterpret_cast<const u32x4_t*>(&stage_out[wave][c * 16]);
+      if (c < 2 * REC && 2 * (r0 + (c * 16) / REC) < n)
+        *reinterpret_cast<u32x4_t*>(xq + r0 * REC + c * 16) = *reinterpret_cast<const u32x4_t*>(&stage_out[wave][c * 16]);
     }
     __builtin_amdgcn_wave_barrier();  // the next iteration's LDS writes after these reads
   }
@@ -389,13 +443,22 @@ inline unsigned grid_for(int64_t n, int threads = 256) {
 
 }  // namespace
 
-int launch_xprep(const void* x, int64_t T, int64_t ldx, const MoeGeom& g, void* xq, int32_t* zero, int64_t nzero,
-                 hipStream_t stream) {
+int launch_xprep(int af, const void* x, int64_t T, int64_t ldx, const MoeGeom& g, void* xq, int32_t* zero,
+                 int64_t nzero, hipStream_t stream) {
   const int64_t nblk = 2 * g.nkt1;
   const int64_t n = T * nblk;
-  if (n > 0 || nzero > 0)
-    hipLaunchKernelGGL(xprep_kernel, dim3(grid_for(n > nzero ? n : nzero)), dim3(256), 0, stream, (const uint16_t*)x,
-                       ldx, g.H, nblk, (uint8_t*)xq, zero, nzero, n);
+  if (n > 0 || nzero > 0) {
+    const dim3 grid(grid_for(n > nzero ? n : nzero)), block(256);
+    if (af == kActMxfp8)
+      hipLaunchKernelGGL(xprep_kernel<kActMxfp8>, grid, block, 0, stream, (const uint16_t*)x, ldx, g.H, nblk,
+                         (uint8_t*)xq, zero, nzero, n);
+    else if (af == kActMxfp4)
+      hipLaunchKernelGGL(xprep_kernel<kActMxfp4>, grid, block, 0, stream, (const uint16_t*)x, ldx, g.H, nblk,
+                         (uint8_t*)xq, zero, nzero, n);
+    else
+      hipLaunchKernelGGL(xprep_kernel<kActBf16>, grid, block, 0, stream, (const uint16_t*)x, ldx, g.H, nblk,
+                         (uint8_t*)xq, zero, nzero, n);
+  }
   return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
 }
 

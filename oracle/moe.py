@@ -29,9 +29,11 @@ rule as the weights; the experts-quant step [P3 Implementation breakdown item 3]
 input x and the SwiGLU output are the activations quantized (the pages name the variants, not the
 points); the SwiGLU output is rounded to binary32 first, the precision in which the kernel decides."""
 
-AMBIGUITY_REL = 2.0 ** -13
+AMBIGUITY_REL = 2.0 ** -16
 """Relative window around a rounding decision of the quantized SwiGLU output within which the
-kernel's binary32 arithmetic (other summation order, hardware exp) may decide the other way."""
+kernel's binary32 arithmetic (other summation order, hardware exp) may decide the other way: about
+ten times the relative difference between a binary32 SwiGLU computed that way and the float64 one
+rounded to binary32."""
 
 
 def silu(g):
@@ -49,15 +51,15 @@ def quantize_activation(vals32, act):
 
 def activation_ambiguity(vals32, act, rel=AMBIGUITY_REL):
     """Per element, the largest change of its dequantized value when the block's values move by up to
-    rel of themselves plus rel**2 of the block maximum, all up or all down (a rounding midpoint or the
-    scale's round-up threshold crossed).  0 where every decision is clear of the window."""
+    rel of themselves plus rel / 64 of the block maximum, all up or all down (a rounding midpoint or
+    the scale's round-up threshold crossed).  0 where every decision is clear of the window."""
     v = np.asarray(vals32, dtype=np.float64)
     base = quantize_activation(vals32, act)
     n, K = v.shape
     bmax = np.repeat(np.abs(v.reshape(n, K // 32, 32)).max(axis=-1), 32, axis=-1)
     d = np.zeros_like(v)
     for sgn in (-1.0, 1.0):
-        p = v + sgn * (rel * np.abs(v) + rel * rel * bmax) * np.sign(v)
+        p = v + sgn * (rel * np.abs(v) + rel / 64 * bmax) * np.sign(v)
         d = np.maximum(d, np.abs(quantize_activation(p.astype(np.float32), act) - base))
     return d
 

@@ -173,7 +173,7 @@ static void check_forward_layout(const mxfp4_moe_dims& d, int64_t T, int k, size
   CHECK((names() == std::vector<std::string>{"xprep", "route", "place", "gemm1", "gemm2", "combine"}));
   if (g_calls.size() != 6) return;
   const Call& xp = g_calls[0];
-  CHECK(inside(xp.p[1], (size_t)T * g.nkt1 * kXRecG, ws, nws));
+  CHECK(inside(xp.p[1], (size_t)T * g.nkt1 * kMaxRec, ws, nws));
   CHECK(inside(xp.p[2], 4 * xp.i[2], ws, nws));
   const GemmArgs& a1 = g_calls[3].gemm;
   const GemmArgs& a2 = g_calls[4].gemm;
@@ -186,8 +186,8 @@ static void check_forward_layout(const mxfp4_moe_dims& d, int64_t T, int k, size
     CHECK(inside(a1.bias, (size_t)g.E * 2 * g.I * 2, blob, o.total));
     CHECK(inside(a2.bias, (size_t)g.E * g.H * 2, blob, o.total));
   }
-  CHECK(inside(a1.xq, (size_t)T * g.nkt1 * kXRecG, ws, nws));
-  CHECK(inside(a1.actq, (size_t)(w.nrows_alloc / 32) * g.nkt2 * 64 * kSlot, ws, nws));
+  CHECK(inside(a1.xq, (size_t)T * g.nkt1 * kMaxRec, ws, nws));
+  CHECK(inside(a1.actq, (size_t)(w.nrows_alloc / 32) * g.nkt2 * 64 * kMaxSlot, ws, nws));
   CHECK(inside(a1.acts, (size_t)(w.nrows_alloc / 32) * g.nkt2 * 64 * 4, ws, nws));
   CHECK(a2.xq == a1.actq && a2.xs == a1.acts);
   for (const GemmArgs* a : {&a1, &a2}) {
@@ -237,15 +237,30 @@ static void test_forward() {
     // profiled: one event per stage boundary (7), fewer when fewer are given
     g_events = 0;
     void* evs[7] = {fake(), fake(), fake(), fake(), fake(), fake(), fake()};
-    CHECK(moe_mxfp4_forward_profiled(&c.d, blob, x, c.T, c.d.H, lg, c.k, 1, y, nullptr, nullptr, ws, nws, nullptr,
+    CHECK(moe_mxfp4_forward_profiled(&c.d, 0, blob, x, c.T, c.d.H, lg, c.k, 1, y, nullptr, nullptr, ws, nws, nullptr,
                                      evs, 7) == MXFP4_OK);
     CHECK(g_events == 7);
     g_events = 0;
-    CHECK(moe_mxfp4_forward_profiled(&c.d, blob, x, c.T, c.d.H, lg, c.k, 1, y, nullptr, nullptr, ws, nws, nullptr,
+    CHECK(moe_mxfp4_forward_profiled(&c.d, 0, blob, x, c.T, c.d.H, lg, c.k, 1, y, nullptr, nullptr, ws, nws, nullptr,
                                      evs, 3) == MXFP4_OK);
     CHECK(g_events == 3);
-    CHECK(moe_mxfp4_forward_profiled(&c.d, blob, x, c.T, c.d.H, lg, c.k, 1, y, nullptr, nullptr, ws, nws, nullptr,
+    CHECK(moe_mxfp4_forward_profiled(&c.d, 0, blob, x, c.T, c.d.H, lg, c.k, 1, y, nullptr, nullptr, ws, nws, nullptr,
                                      nullptr, 3) == MXFP4_ERR_NULL);
+    // every activation format: the same launches on the same workspace, the format passed to the
+    // producers and the GEMMs; an unknown format is rejected before any launch
+    for (int af = 0; af < 3; af++) {
+      g_calls.clear();
+      CHECK(moe_mxfp4_forward_act(&c.d, af, blob, x, c.T, c.d.H, lg, c.k, 1, y, nullptr, nullptr, ws, nws, nullptr) ==
+            MXFP4_OK);
+      check_forward_layout(c.d, c.T, c.k, nws, ws, blob);
+      if (g_calls.size() == 6) CHECK(g_calls[0].i[3] == af && g_calls[3].i[2] == af && g_calls[4].i[2] == af);
+    }
+    g_calls.clear();
+    CHECK(moe_mxfp4_forward_act(&c.d, 3, blob, x, c.T, c.d.H, lg, c.k, 1, y, nullptr, nullptr, ws, nws, nullptr) ==
+          MXFP4_ERR_LAYOUT);
+    CHECK(moe_mxfp4_forward_act(&c.d, -1, blob, x, c.T, c.d.H, lg, c.k, 1, y, nullptr, nullptr, ws, nws, nullptr) ==
+          MXFP4_ERR_LAYOUT);
+    CHECK(g_calls.empty());
   }
   // no tokens: nothing to do
   mxfp4_moe_dims d = {8, 256, 128, 0};
@@ -253,9 +268,9 @@ static void test_forward() {
   CHECK(moe_mxfp4_forward(&d, nullptr, nullptr, 0, 256, nullptr, 2, 1, nullptr, nullptr, nullptr, nullptr, 0,
                           nullptr) == MXFP4_OK);
   CHECK(g_calls.empty());
-  // 32-bit copy offsets: T * H / 64 * 128 bytes of first-GEMM records must stay below 4 GiB
+  // 32-bit copy offsets: T * H / 64 * 144 bytes of first-GEMM records must stay below 4 GiB
   mxfp4_moe_dims dl = {8, 7168, 2048, 0};
-  const int64_t limit = (int64_t(1) << 32) / (7168 / 64 * 128);
+  const int64_t limit = (int64_t(1) << 32) / (7168 / 64 * 144);
   CHECK(moe_mxfp4_forward(&dl, fake(), fake(), limit + 1, 7168, (float*)fake(), 1, 1, fake(), nullptr, nullptr,
                           fake(), SIZE_MAX, nullptr) == MXFP4_ERR_SHAPE);
   CHECK(moe_mxfp4_workspace_bytes(&dl, INT64_MAX / 4, 8) == 0);

@@ -43,10 +43,10 @@ int launch_repack_standard(const MoeGeom& g, bool bias, const void*, const void*
   for (int k = 0; k < 6; k++) c.off[k] = off[k];
   return rec("repack_standard", c);
 }
-int launch_xprep(const void* x, int64_t T, int64_t ldx, const MoeGeom&, void* xq, int32_t* zero, int64_t nzero,
-                 hipStream_t) {
+int launch_xprep(int af, const void* x, int64_t T, int64_t ldx, const MoeGeom&, void* xq, int32_t* zero,
+                 int64_t nzero, hipStream_t) {
   Call c;
-  c.p[0] = x; c.p[1] = xq; c.p[2] = zero; c.i[0] = T; c.i[1] = ldx; c.i[2] = nzero;
+  c.p[0] = x; c.p[1] = xq; c.p[2] = zero; c.i[0] = T; c.i[1] = ldx; c.i[2] = nzero; c.i[3] = af;
   return rec("xprep", c);
 }
 int launch_zero_i32(int32_t* p, int64_t n, hipStream_t) {
@@ -70,14 +70,14 @@ int launch_place(const int32_t*, const float*, int32_t* blkcnt, int64_t T, int k
   c.i[0] = T; c.i[1] = k; c.i[2] = E; c.i[3] = BM; c.i[4] = BM2;
   return rec("place", c);
 }
-int launch_gemm1(int NRG, const GemmArgs& a, int64_t max_tiles, hipStream_t) {
+int launch_gemm1(int af, int NRG, const GemmArgs& a, int64_t max_tiles, hipStream_t) {
   Call c;
-  c.gemm = a; c.i[0] = NRG; c.i[1] = max_tiles;
+  c.gemm = a; c.i[0] = NRG; c.i[1] = max_tiles; c.i[2] = af;
   return rec("gemm1", c);
 }
-int launch_gemm2(int NRG, const GemmArgs& a, int64_t max_tiles, hipStream_t) {
+int launch_gemm2(int af, int NRG, const GemmArgs& a, int64_t max_tiles, hipStream_t) {
   Call c;
-  c.gemm = a; c.i[0] = NRG; c.i[1] = max_tiles;
+  c.gemm = a; c.i[0] = NRG; c.i[1] = max_tiles; c.i[2] = af;
   return rec("gemm2", c);
 }
 int launch_combine(const uint16_t* o16, const uint8_t* osc, const int32_t* pair_prow, void* y, int64_t T, int64_t H, int k,

@@ -125,12 +125,12 @@ def test_route_and_forward_validation(L):
 
 def test_forward_rejects_activation_buffers_past_32_bit_offsets(L):
     """The GEMMs address the split activations with 32-bit byte offsets: the first GEMM's records
-    take T * H / 64 * 128 bytes, the second GEMM's operand about 1.5 bytes per padded row and I
+    take T * H / 64 * 144 bytes, the second GEMM's operand about 2 bytes per padded row and I
     element.  Shapes whose buffers reach 4 GiB are rejected before any launch (and before the
     workspace size is looked at)."""
     fw = L.moe_mxfp4_forward
     d = dims(8, 7168, 2048)
-    limit = (1 << 32) // (7168 // 64 * 128)  # tokens at which the first GEMM's records reach 4 GiB
+    limit = (1 << 32) // (7168 // 64 * 144)  # tokens at which the first GEMM's records reach 4 GiB
     assert fw(d, FAKE, FAKE, limit + 1, 7168, FAKE, 1, 1, FAKE, None, None, FAKE, 1 << 62, None) == SHAPE
     # just below: the size check passes and the (too small) workspace is what fails
     assert fw(d, FAKE, FAKE, limit - 1, 7168, FAKE, 1, 1, FAKE, None, None, FAKE, 256, None) == WS
