@@ -25,6 +25,11 @@ SwiGLU output are quantized per 32-element block before the two products (MXFP8 
 or MXFP4 with the weights' rule).  The E8M0 rule for E4M3 elements is a reading: the pages' round-up of
 the block maximum at a significand of 1.75, minus E4M3's largest exponent (8) instead of E2M1's (2).
 
+NVFP4 (``quant.nvfp4_quantize_ref``): the converter's non-E8M0 branch -- 16-element blocks, an E4M3
+scale of global_scale * max / 6 computed in binary32, elements scaled by the dequantized stored scale
+(the fix the pages record).  The element step and the block size are readings (the pages show the scale
+step only).
+
 Parity status:  every function here is pinned by a ``-m "not gpu"`` test against something other than
 itself (hand values, closed forms, brute force, textbook cases or an independent library routine),
 except the two layout conventions the pages never state -- the nibble order inside a byte and the

@@ -247,3 +247,68 @@ def mxfp8_dequant_ref(codes, scales):
     sign = np.where(codes & 0x80, -1.0, 1.0)
     s = np.repeat(np.ldexp(1.0, np.asarray(scales, dtype=np.int64) - 127), BLOCK, axis=-1)
     return sign * mag * s
+
+
+# ------------------------------------------------------------------------------------------------
+# NVFP4: the sibling format the same converter handles when the scale is not E8M0.
+
+NV_BLOCK = 16
+"""Elements per NVFP4 scale block (reading: the pages show the NVFP4 branch of the converter but not
+its block size; NVFP4 blocks hold 16 elements)."""
+
+RCP6_F32 = np.float32(1.0) / np.float32(6.0)
+"""The binary32 reciprocal of 6 the NVFP4 scale multiplies by (reading: the page's reciprocal of 6.0f,
+taken as the correctly rounded binary32 value 0x3E2AAAAB)."""
+
+
+def nvfp4_quantize_ref(x_bits, global_scale):
+    """NVFP4 quantization of a bf16 matrix [M, K] (K a multiple of 16) with a binary32 global scale.
+
+    [P3 Implementation breakdown item 1 and Key source snippets, the non-UE8M0 branch of the converter;
+    Review highlights item 2, the fix that makes the element scale the dequantized stored scale]
+    Per 16-element block, every step in binary32 as the converter computes it:
+      1. vecMax = max |x| (exact);
+      2. SF = global_scale * (vecMax * RCP6_F32), two binary32 roundings;
+      3. the stored scale byte is SF as E4M3, nearest even, saturating at 448 (e4m3_magnitude_code);
+      4. SF_deq = that byte's value (the fix: elements use the dequantized scale);
+      5. r = global_scale / SF_deq in binary32 (0 when SF_deq is 0; reading, the page does not show the
+         element step: elements are divided by SF_deq / global_scale, the scale they dequantize with);
+      6. code = E2M1 of |x| * r (binary32 product, then nearest even, saturating at 6), sign bit 0x8 from
+         x (also for magnitude 0, reading 3 of the MXFP4 quantizer), two codes per byte as quantize_ref.
+    Returns (q uint8 [M, K/2], scale codes uint8 [M, K/16]).
+    """
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    M, K = x_bits.shape
+    if K % NV_BLOCK:
+        raise ValueError("K must be a multiple of 16")
+    gs = np.float32(global_scale)
+    blocks = x_bits.reshape(M, K // NV_BLOCK, NV_BLOCK)
+    mag = bf16_to_f64(blocks & np.uint16(0x7FFF)).astype(np.float32)  # exact
+    vmax = mag.max(axis=-1)
+    sf = (gs * (vmax * RCP6_F32).astype(np.float32)).astype(np.float32)
+    sf_code = e4m3_magnitude_code(sf.astype(np.float64))
+    sf_deq = E4M3_MAGNITUDES[sf_code].astype(np.float32)
+    with np.errstate(divide="ignore"):
+        r = np.where(sf_deq > 0, gs / np.where(sf_deq > 0, sf_deq, np.float32(1)), np.float32(0)).astype(np.float32)
+    v = (mag * r[..., None]).astype(np.float32)
+    code = e2m1_magnitude_code(v.astype(np.float64))
+    code |= ((blocks >> np.uint16(15)).astype(np.uint8) << np.uint8(3))
+    code = code.reshape(M, K)
+    q = (code[:, 0::2] | (code[:, 1::2] << np.uint8(4))).astype(np.uint8)
+    return q, sf_code.astype(np.uint8)
+
+
+def nvfp4_dequant_ref(q, scale_codes, global_scale):
+    """x_hat = (-1)**s * E2M1 value * SF_deq / global_scale, float64 (SF_deq the E4M3 scale's value)."""
+    codes = unpack_codes(q)
+    mag = E2M1_MAGNITUDES[codes & 7]
+    sign = np.where(codes & 8, -1.0, 1.0)
+    s = np.repeat(E4M3_MAGNITUDES[np.asarray(scale_codes, dtype=np.uint8)], NV_BLOCK, axis=-1)
+    return sign * mag * s / float(np.float32(global_scale))
+
+
+def nv_tile_scales(flat):
+    """NVFP4 scale bytes [M, K/16] in the same tiled layout as tile_scales (128 rows by 4 scale
+    columns per 512-byte tile; reading: the pages' tiling is written for scale columns, whatever the
+    block size)."""
+    return tile_scales(flat)
