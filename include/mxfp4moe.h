@@ -78,6 +78,30 @@ int mxfp4_quantize(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, void* 
 size_t mxfp4_tiled_scale_bytes(int64_t M, int64_t K);
 
 /* ------------------------------------------------------------------------------------------------
+ * NVFP4 block quantization, the converter's other scale format.  [P3 Implementation breakdown item 1
+ * and Key source snippets: the branch taken without UE8M0 scales (max / 6 stored as E4M3, times a
+ * global scale); Review highlights item 2: elements are scaled by the dequantized stored scale]
+ * For each row of x and each 16-element block along K, in binary32:
+ *   SF   = global_scale * (amax * r6), r6 the binary32 nearest to 1/6, amax = max |x| (exact);
+ *   s    = SF as E4M3 (round to nearest even; above 448 -> 448), the stored scale byte;
+ *   code = E2M1 of |x| * (global_scale / value(s)) (quotient and product rounded to binary32, then
+ *          nearest even, saturating at 6; 0 when value(s) is 0), sign bit 0x8 copied from x;
+ *   q[row][j] = code[2j] | code[2j+1] << 4.
+ * A value decodes as E2M1(code) * value(s) / global_scale.
+ * x_bf16 device bf16 [M, ldx]; K % 16 == 0, K >= 16, ldx >= K, ldx % 8 == 0.
+ * global_scale: host binary32, positive and finite (else MXFP4_ERR_SHAPE).
+ * q_u8 device uint8 [M, K/2], required.  scale_flat_u8 device uint8 [M, K/16], may be NULL, any
+ * alignment.  scale_tiled_u8 device, 16-byte aligned, may be NULL: [ceil(M/128), ceil(K/64), 32, 4, 4],
+ * the byte at [mT][kT][oM][iM][iK] the scale of row mT*128 + iM*32 + oM and scale column kT*4 + iK
+ * (the tiling of mxfp4_quantize over 16-element scale columns), padding bytes 0.
+ * M >= 0 (M == 0 is a no-op). */
+int nvfp4_quantize(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, float global_scale, void* q_u8,
+                   void* scale_flat_u8, void* scale_tiled_u8, void* stream);
+
+/* Bytes of nvfp4_quantize's tiled scale output: ceil(M/128) * ceil(K/64) * 512; 0 for invalid sizes. */
+size_t nvfp4_tiled_scale_bytes(int64_t M, int64_t K);
+
+/* ------------------------------------------------------------------------------------------------
  * MoE weight set.  The standard checkpoint layout [P2 Implementation breakdown item 2]:
  *   w13_q uint8 [E, 2I, H/2]  rows [w1 (gate); w3 (up)]     w13_s uint8 [E, 2I, H/32]  E8M0
  *   w2_q  uint8 [E, H, I/2]                                 w2_s  uint8 [E, H, I/32]   E8M0

@@ -20,7 +20,7 @@ ACT_BF16 = 0   # bf16 activations (three-term split inside the kernels)
 ACT_MXFP8 = 1  # both GEMM inputs quantized to MXFP8 (E4M3 + E8M0 per 32)
 ACT_MXFP4 = 2  # both GEMM inputs quantized to MXFP4 (E2M1 + E8M0 per 32)
 
-__all__ = ["quantize", "tiled_scale_shape", "repack_weights", "unpack_weights", "check_packed", "route",
+__all__ = ["quantize", "tiled_scale_shape", "nvfp4_quantize", "nvfp4_tiled_scale_shape", "repack_weights", "unpack_weights", "check_packed", "route",
            "moe_forward", "moe_forward_noalloc", "NOALLOC_SCRATCH_BYTES", "MoE", "MoeDims", "Mxfp4Error",
            "LAYOUT_GFX950", "LAYOUT_STD_W31", "LAYOUT_SCALE_TILED", "ACT_BF16", "ACT_MXFP8", "ACT_MXFP4"]
 
@@ -58,6 +58,26 @@ def quantize(x, flat=True, tiled=True):
     sf = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device) if flat else None
     st = torch.empty(tiled_scale_shape(M, K), dtype=torch.uint8, device=x.device) if tiled else None
     check("mxfp4_quantize", _lib.lib().mxfp4_quantize(_ptr(x), M, K, x.stride(0), _ptr(q), _ptr(sf), _ptr(st), _stream()))
+    return q, sf, st
+
+
+def nvfp4_tiled_scale_shape(M, K):
+    return ((M + 127) // 128, (K // 16 + 3) // 4, 32, 4, 4)
+
+
+def nvfp4_quantize(x, global_scale, flat=True, tiled=True):
+    """NVFP4: x bf16 [M, K] on the GPU (K % 16 == 0; rows may be strided), global_scale a positive float.
+    Returns (q uint8 [M, K/2], E4M3 scales uint8 [M, K/16] or None, tiled scales uint8
+    [ceil(M/128), ceil(K/64), 32, 4, 4] or None)."""
+    _cuda(x, "x")
+    _need(x.dtype == torch.bfloat16 and x.dim() == 2, "x must be a 2-D bfloat16 tensor")
+    _need(x.stride(1) == 1, "x's last dimension must be contiguous")
+    M, K = x.shape
+    q = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+    sf = torch.empty((M, K // 16), dtype=torch.uint8, device=x.device) if flat else None
+    st = torch.empty(nvfp4_tiled_scale_shape(M, K), dtype=torch.uint8, device=x.device) if tiled else None
+    check("nvfp4_quantize", _lib.lib().nvfp4_quantize(_ptr(x), M, K, x.stride(0), float(global_scale), _ptr(q), _ptr(sf),
+                                                      _ptr(st), _stream()))
     return q, sf, st
 
 

@@ -21,6 +21,8 @@ _SIGS = {
     "mxfp4_version": (c_u32, []),
     "mxfp4_quantize": (ctypes.c_int, [c_p, c_i64, c_i64, c_i64, c_p, c_p, c_p, c_p]),
     "mxfp4_tiled_scale_bytes": (c_sz, [c_i64, c_i64]),
+    "nvfp4_quantize": (ctypes.c_int, [c_p, c_i64, c_i64, c_i64, ctypes.c_float, c_p, c_p, c_p, c_p]),
+    "nvfp4_tiled_scale_bytes": (c_sz, [c_i64, c_i64]),
     "mxfp4_repack_bytes": (c_sz, [ctypes.POINTER(MoeDims), c_u32]),
     "mxfp4_repack_offsets": (ctypes.c_int, [ctypes.POINTER(MoeDims), c_u32, ctypes.POINTER(c_sz)]),
     "mxfp4_repack_weights": (ctypes.c_int, [ctypes.POINTER(MoeDims), c_p, c_p, c_p, c_p, c_p, c_p, c_i32, c_u32, c_p,

@@ -139,6 +139,24 @@ MX_API int mxfp4_quantize(const void* x_bf16, int64_t M, int64_t K, int64_t ldx,
   return launch_quantize(x_bf16, M, K, ldx, q_u8, scale_flat_u8, scale_tiled_u8, S(stream));
 }
 
+MX_API size_t nvfp4_tiled_scale_bytes(int64_t M, int64_t K) {
+  if (M < 0 || K < 16 || K % 16 || M > kMaxDim || K > kMaxDim) return 0;
+  return (size_t)(cdiv(M, 128) * cdiv(K / 16, 4) * 512);
+}
+
+MX_API int nvfp4_quantize(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, float global_scale, void* q_u8,
+                          void* scale_flat_u8, void* scale_tiled_u8, void* stream) {
+  if (M < 0 || K < 16 || K % 16 || ldx < K || ldx % 8 || ldx > kMaxDim) return MXFP4_ERR_SHAPE;
+  if (M > kMaxDim / ldx) return MXFP4_ERR_SHAPE;
+  // a positive, finite binary32 global scale (the comparison also rejects NaN)
+  if (!(global_scale > 0.0f && global_scale <= 3.40282347e38f)) return MXFP4_ERR_SHAPE;
+  if (M == 0) return MXFP4_OK;
+  if (!x_bf16 || !q_u8) return MXFP4_ERR_NULL;
+  if (!aligned(x_bf16, 16) || !aligned(q_u8, 4) || (scale_tiled_u8 && !aligned(scale_tiled_u8, 16)))
+    return MXFP4_ERR_ALIGN;
+  return launch_nvfp4_quantize(x_bf16, M, K, ldx, global_scale, q_u8, scale_flat_u8, scale_tiled_u8, S(stream));
+}
+
 MX_API size_t mxfp4_repack_bytes(const mxfp4_moe_dims* d, uint32_t layout) {
   if (check_dims(d) != MXFP4_OK || !valid_layout(layout)) return 0;
   if (layout == MXFP4_LAYOUT_GFX950) return (size_t)blob_offsets(moe_geom(d->E, d->H, d->I), d->has_bias).total;

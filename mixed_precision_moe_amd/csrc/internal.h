@@ -9,6 +9,8 @@
 
 int launch_quantize(const void* x, int64_t M, int64_t K, int64_t ldx, void* q, void* sflat, void* stiled,
                     hipStream_t stream);
+int launch_nvfp4_quantize(const void* x, int64_t M, int64_t K, int64_t ldx, float gs, void* q, void* sflat,
+                          void* stiled, hipStream_t stream);
 int launch_repack_gfx950(const MoeGeom& g, const BlobOffsets& o, bool bias, const void* w13_q, const void* w13_s,
                          const void* w2_q, const void* w2_s, const void* b13, const void* b2, int bias_is_fp32,
                          void* out, hipStream_t stream);

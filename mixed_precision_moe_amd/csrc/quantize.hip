@@ -103,7 +103,107 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
   }
 }
 
+// ------------------------------------------------------------------------------------------------
+// NVFP4: the converter's non-E8M0 branch.  [P3 Key source snippets, the NVFP4 branch of the
+// FP16/BF16 -> FP4 converter; Review highlights item 2, elements scaled by the dequantized scale]
+// Per 16-element block, in binary32: SF = gs * (max|x| * fl(1/6)); the stored byte is SF as E4M3
+// (nearest even; SF above 448 saturates); SF_deq = its value; r = gs / SF_deq (0 when SF_deq is 0);
+// element code = E2M1 of x * r (nearest even, saturating at 6, sign kept).  Same work split as the MXFP4
+// kernel: a wave covers 512 columns of four rows 32 apart, lane l owns eight bf16 (half a block, two
+// lanes per block); the four scale bytes of one 64-column group of the tiled layout sit in lanes 8j,
+// 8j + 2, 8j + 4, 8j + 6 and DPP row shifts bring them to lane 8j, which writes the group.
+typedef short q_s16x2_t __attribute__((ext_vector_type(2)));
+constexpr float kRcp6 = 0x1.555556p-3f;  // the binary32 nearest to 1/6
+
+__global__ __launch_bounds__(256) void nvfp4_quantize_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                                             int64_t ldx, float gs, uint8_t* __restrict__ q,
+                                                             uint8_t* __restrict__ sflat, uint8_t* __restrict__ stiled,
+                                                             int64_t Mpad, int64_t Kpad, int64_t kTiles,
+                                                             bool flat_words) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t col = (int64_t)blockIdx.x * 512 + lane * 8;
+  const bool col_live = col < Kpad;  // uniform over each 8-lane (64-column) group
+  const bool col_in = col < K;       // uniform over each 2-lane block (K % 16 == 0)
+  const int64_t nby = Mpad / kRowsPerBlock;
+  for (int64_t by = blockIdx.y; by < nby; by += gridDim.y) {
+    const int64_t mT = by >> 3, oM = ((by & 7) << 2) + wave;
+    const int64_t row0 = mT * 128 + oM;
+    uint32_t tw[kRowsPerWave];
+    u32x4_t v[kRowsPerWave];
+#pragma unroll
+    for (int r = 0; r < kRowsPerWave; r++) {
+      const int64_t row = row0 + 32 * r;
+      if (col_in && row < M)
+        v[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(x + row * ldx + col));
+      else
+        v[r] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int r = 0; r < kRowsPerWave; r++) {
+      const int64_t row = row0 + 32 * r;
+      const uint32_t w[4] = {v[r][0], v[r][1], v[r][2], v[r][3]};
+      uint32_t m = 0;
+#pragma unroll
+      for (int i = 0; i < 4; i++) m = max(m, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+      m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false));  // lane ^ 1
+      const float vmax = bf16_bits_to_f32(m);
+      const float sf = gs * (vmax * kRcp6);
+      q_s16x2_t sb = q_s16x2_t{0, 0};
+      sb = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(sb, fminf(sf, 448.0f), 0.0f, 1.0f, false);
+      const uint32_t e = (uint32_t)__builtin_bit_cast(uint32_t, sb) & 0xFFu;
+      const float sf_deq = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(e, 1.0f, false)[0];
+      const float rs = sf_deq > 0.0f ? gs / sf_deq : 0.0f;
+      float sv[8];
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        sv[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu) * rs;
+        sv[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16) * rs;
+      }
+      uint32_t packed = 0;
+      packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, sv[0], sv[1], 1.0f, 0);
+      packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, sv[2], sv[3], 1.0f, 1);
+      packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, sv[4], sv[5], 1.0f, 2);
+      packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, sv[6], sv[7], 1.0f, 3);
+      // the scale bytes of the group's four blocks: lanes 8j, 8j + 2, 8j + 4, 8j + 6 (row_shl 2, 4, 6)
+      const uint32_t e1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)e, 0x102, 0xF, 0xF, false);
+      const uint32_t e2 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)e, 0x104, 0xF, 0xF, false);
+      const uint32_t e3 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)e, 0x106, 0xF, 0xF, false);
+      const uint32_t word = e | (e1 << 8) | (e2 << 16) | (e3 << 24);
+      if (col_in && row < M) {
+        __builtin_nontemporal_store(packed, reinterpret_cast<uint32_t*>(q + row * (K / 2) + col / 2));
+        if (sflat) {
+          if (flat_words && col + 64 <= K) {
+            if ((lane & 7) == 0) *reinterpret_cast<uint32_t*>(sflat + row * (K / 16) + col / 16) = word;
+          } else if ((lane & 1) == 0) {
+            sflat[row * (K / 16) + col / 16] = (uint8_t)e;
+          }
+        }
+      }
+      tw[r] = word;
+    }
+    if (stiled && col_live && (lane & 7) == 0) {
+      const int64_t kT = col >> 6;
+      *reinterpret_cast<u32x4_t*>(stiled + ((mT * kTiles + kT) * 32 + oM) * 16) = u32x4_t{tw[0], tw[1], tw[2], tw[3]};
+    }
+  }
+}
+
 }  // namespace
+
+int launch_nvfp4_quantize(const void* x, int64_t M, int64_t K, int64_t ldx, float gs, void* q, void* sflat,
+                          void* stiled, hipStream_t stream) {
+  const int64_t mTiles = (M + 127) / 128;
+  const int64_t kTiles = (K / 16 + 3) / 4;
+  const int64_t Mpad = mTiles * 128;
+  const int64_t Kpad = kTiles * 64;
+  const int64_t nby = Mpad / kRowsPerBlock;
+  dim3 grid((unsigned)((Kpad + 511) / 512), (unsigned)(nby < 65535 ? nby : 65535));
+  const bool flat_words = (K / 16) % 4 == 0 && ((uintptr_t)sflat & 3u) == 0;
+  hipLaunchKernelGGL(nvfp4_quantize_kernel, grid, dim3(256), 0, stream, (const uint16_t*)x, M, K, ldx, gs, (uint8_t*)q,
+                     (uint8_t*)sflat, (uint8_t*)stiled, Mpad, Kpad, kTiles, flat_words);
+  return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
+}
 
 int launch_quantize(const void* x, int64_t M, int64_t K, int64_t ldx, void* q, void* sflat, void* stiled,
                     hipStream_t stream) {

@@ -103,17 +103,17 @@ def moe_biases(cfg: MoEConfig):
     return to_bf16_bits(b13), to_bf16_bits(b2)
 
 
-def quant_matrix(M: int, K: int, cid: int = 1, zero_frac: float = 0.01):
+def quant_matrix(M: int, K: int, cid: int = 1, zero_frac: float = 0.01, block: int = 32):
     """bf16 bits [M, K]: Student-t(3) values times a per-row 2**U(-8, 8) factor (U continuous), with
-    round(zero_frac * blocks) of the 32-element blocks set to zero, chosen without replacement."""
+    round(zero_frac * blocks) of the `block`-element blocks set to zero, chosen without replacement."""
     g = rng(cid, _QMAT)
     v = g.standard_t(3, size=(M, K))
     v *= np.exp2(g.uniform(-8.0, 8.0, size=(M, 1)))
-    nblk = M * (K // 32)
+    nblk = M * (K // block)
     nz = int(round(zero_frac * nblk))
     if nz:
         zb = rng(cid, _ZERO).choice(nblk, size=nz, replace=False)
-        v.reshape(nblk, 32)[zb] = 0.0
+        v.reshape(nblk, block)[zb] = 0.0
     return to_bf16_bits(v)
 
 

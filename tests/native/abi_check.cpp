@@ -53,6 +53,27 @@ static void test_quantize() {
   CHECK(mxfp4_tiled_scale_bytes(-1, 64) == 0);
 }
 
+static void test_nvfp4() {
+  CHECK(nvfp4_quantize(fake(), 4, 40, 48, 1.0f, fake(), nullptr, nullptr, nullptr) == MXFP4_ERR_SHAPE);  // K % 16
+  CHECK(nvfp4_quantize(fake(), 4, 64, 64, 0.0f, fake(), nullptr, nullptr, nullptr) == MXFP4_ERR_SHAPE);
+  CHECK(nvfp4_quantize(fake(), 4, 64, 64, -2.0f, fake(), nullptr, nullptr, nullptr) == MXFP4_ERR_SHAPE);
+  CHECK(nvfp4_quantize(fake(), 4, 64, 64, __builtin_nanf(""), fake(), nullptr, nullptr, nullptr) == MXFP4_ERR_SHAPE);
+  CHECK(nvfp4_quantize(fake(), 4, 64, 64, __builtin_inff(), fake(), nullptr, nullptr, nullptr) == MXFP4_ERR_SHAPE);
+  CHECK(nvfp4_quantize(fake(), INT64_MAX, 64, 64, 1.0f, fake(), nullptr, nullptr, nullptr) == MXFP4_ERR_SHAPE);
+  CHECK(nvfp4_quantize(nullptr, 4, 64, 64, 1.0f, fake(), nullptr, nullptr, nullptr) == MXFP4_ERR_NULL);
+  CHECK(nvfp4_quantize(fake(8), 4, 64, 64, 1.0f, fake(), nullptr, nullptr, nullptr) == MXFP4_ERR_ALIGN);
+  CHECK(nvfp4_quantize(fake(), 4, 64, 64, 1.0f, fake(), nullptr, fake(8), nullptr) == MXFP4_ERR_ALIGN);
+  g_calls.clear();
+  CHECK(nvfp4_quantize(nullptr, 0, 64, 64, 1.0f, nullptr, nullptr, nullptr, nullptr) == MXFP4_OK);
+  CHECK(g_calls.empty());
+  CHECK(nvfp4_quantize(fake(), 130, 80, 88, 2.5f, fake(), fake(1), fake(16), nullptr) == MXFP4_OK);
+  CHECK(g_calls.size() == 1 && g_calls[0].name == "nvfp4_quantize" && g_calls[0].i[3] == 2560 &&
+        g_calls[0].p[2] == fake(1));
+  CHECK(nvfp4_tiled_scale_bytes(8192, 7168) == 64u * 112 * 512);
+  CHECK(nvfp4_tiled_scale_bytes(129, 80) == 2u * 2 * 512);
+  CHECK(nvfp4_tiled_scale_bytes(1, 40) == 0 && nvfp4_tiled_scale_bytes(INT64_MAX, 64) == 0);
+}
+
 static void test_repack() {
   mxfp4_moe_dims d = {4, 256, 128, 1};
   CHECK(mxfp4_repack_bytes(&d, 0) > 0);
@@ -278,6 +299,7 @@ static void test_forward() {
 
 int main() {
   test_quantize();
+  test_nvfp4();
   test_repack();
   test_header_checks();
   test_route();

@@ -23,6 +23,13 @@ int launch_quantize(const void* x, int64_t M, int64_t K, int64_t ldx, void* q, v
   c.i[0] = M; c.i[1] = K; c.i[2] = ldx;
   return rec("quantize", c);
 }
+int launch_nvfp4_quantize(const void* x, int64_t M, int64_t K, int64_t ldx, float gs, void* q, void* sflat,
+                          void* stiled, hipStream_t) {
+  Call c;
+  c.p[0] = x; c.p[1] = q; c.p[2] = sflat; c.p[3] = stiled;
+  c.i[0] = M; c.i[1] = K; c.i[2] = ldx; c.i[3] = (int64_t)(gs * 1024.0f);
+  return rec("nvfp4_quantize", c);
+}
 int launch_repack_gfx950(const MoeGeom& g, const BlobOffsets& o, bool bias, const void*, const void*, const void*,
                          const void*, const void*, const void*, int, void* out, hipStream_t) {
   Call c;
