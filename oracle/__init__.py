@@ -30,6 +30,9 @@ scale of global_scale * max / 6 computed in binary32, elements scaled by the deq
 (the fix the pages record).  The element step and the block size are readings (the pages show the scale
 step only).
 
+Dense linear (``linear.linear_ref``): y = x . dequant(W)^T + b, the MXFP4-weight linear layer of the
+pages' W4A16 models (a MoE layer of one expert without routing or activation function).
+
 Parity status:  every function here is pinned by a ``-m "not gpu"`` test against something other than
 itself (hand values, closed forms, brute force, textbook cases or an independent library routine),
 except the two layout conventions the pages never state -- the nibble order inside a byte and the
@@ -37,4 +40,4 @@ sign kept on codes that round to zero.  Those two are "parity unpinned" with res
 they are fixed by this library's ABI and tested only for internal consistency.
 """
 
-from . import quant, convert, route, moe  # noqa: F401
+from . import quant, convert, route, moe, linear  # noqa: F401
