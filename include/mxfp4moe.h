@@ -233,6 +233,35 @@ int moe_mxfp4_forward_profiled(const mxfp4_moe_dims* d, int32_t act_format, cons
                                size_t workspace_bytes, void* stream, void* const* events, int32_t n_events);
 
 /* ------------------------------------------------------------------------------------------------
+ * Dense MXFP4-weight linear layer (W4A16): y = x W^T + b, W dequantized MXFP4.  [P3 Implementation
+ * breakdown item 2: the MXFP4 linear path; DEF: a MoE layer of one expert without routing or
+ * activation function]
+ * Weights in the standard layout: w_q uint8 [N, K/2] (element 2j in the low nibble), w_s uint8 [N, K/32]
+ * E8M0; bias [N] fp32 or bf16 (converted to bf16, round to nearest even), optional.
+ * Requirements: N, K multiples of 32, 32 <= N, K <= 2^20.
+ * Arithmetic as the second product of moe_mxfp4_forward: x enters as three terms per 32 elements, fp32
+ * accumulation, bias added in fp32, one rounding to bf16.
+ */
+/* Output bytes of mxfp4_linear_pack; 0 for invalid sizes. */
+size_t mxfp4_linear_pack_bytes(int64_t N, int64_t K, int32_t has_bias);
+
+/* Weight conversion at load time into this library's layout (opaque, 256-byte header).  w_q, w_s,
+ * bias (may be NULL) device; out device, 256-byte aligned, >= mxfp4_linear_pack_bytes (else
+ * MXFP4_ERR_WORKSPACE). */
+int mxfp4_linear_pack(int64_t N, int64_t K, const void* w_q, const void* w_s, const void* bias, int32_t bias_is_fp32,
+                      void* out, size_t out_bytes, void* stream);
+
+/* Workspace bytes of mxfp4_linear_forward for M rows; 0 for invalid sizes. */
+size_t mxfp4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* y_bf16 device bf16 [M, N] (row-major, contiguous, 16-byte aligned) = x_bf16 (device bf16 [M, ldx],
+ * ldx >= K, ldx % 8 == 0) times the packed weights (has_bias as packed).  workspace device, 256-byte
+ * aligned, >= mxfp4_linear_workspace_bytes(M, N, K).  M == 0 is a no-op; M * K * 2 bytes of split
+ * activations must stay below 4 GiB (else MXFP4_ERR_SHAPE).  Deterministic. */
+int mxfp4_linear_forward(const void* packed, int64_t N, int64_t K, int32_t has_bias, const void* x_bf16, int64_t M,
+                         int64_t ldx, void* y_bf16, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------------
  * The MoE layer without a workspace argument, for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same arguments,
  * arithmetic and result as moe_mxfp4_forward, whose kernels it shares; the workspace is a device

@@ -21,7 +21,7 @@ ACT_MXFP8 = 1  # both GEMM inputs quantized to MXFP8 (E4M3 + E8M0 per 32)
 ACT_MXFP4 = 2  # both GEMM inputs quantized to MXFP4 (E2M1 + E8M0 per 32)
 
 __all__ = ["quantize", "tiled_scale_shape", "nvfp4_quantize", "nvfp4_tiled_scale_shape", "repack_weights", "unpack_weights", "check_packed", "route",
-           "moe_forward", "moe_forward_noalloc", "NOALLOC_SCRATCH_BYTES", "MoE", "MoeDims", "Mxfp4Error",
+           "moe_forward", "moe_forward_noalloc", "NOALLOC_SCRATCH_BYTES", "MoE", "Linear", "MoeDims", "Mxfp4Error",
            "LAYOUT_GFX950", "LAYOUT_STD_W31", "LAYOUT_SCALE_TILED", "ACT_BF16", "ACT_MXFP8", "ACT_MXFP4"]
 
 
@@ -232,6 +232,49 @@ def moe_forward_noalloc(packed, E, H, I, has_bias, x, logits, top_k, y, renormal
                                                top_k, 1 if renormalize else 0, _ptr(y), _ptr(topk_ids),
                                                _ptr(topk_w), _stream()))
     return y
+
+
+class Linear:
+    """A dense MXFP4-weight linear layer y = x W^T + b (W4A16): packed weights and a reusable workspace.
+    w_q uint8 [N, K/2], w_s uint8 [N, K/32] (device), bias fp32 / bf16 [N] or None."""
+
+    def __init__(self, w_q, w_s, bias=None):
+        for n, t in (("w_q", w_q), ("w_s", w_s)):
+            _cuda(t, n)
+            _need(t.dtype == torch.uint8 and t.is_contiguous() and t.dim() == 2, f"{n} must be contiguous uint8 2-D")
+        self.N, Kh = w_q.shape
+        self.K = 2 * Kh
+        _need(w_s.shape == (self.N, self.K // 32), "w_s shape")
+        self.has_bias = bias is not None
+        is_fp32 = 0
+        if bias is not None:
+            _need(bias.dtype in (torch.float32, torch.bfloat16) and bias.shape == (self.N,) and bias.is_contiguous(),
+                  "bias: contiguous fp32 or bf16 [N]")
+            is_fp32 = 1 if bias.dtype == torch.float32 else 0
+        L = _lib.lib()
+        n = L.mxfp4_linear_pack_bytes(self.N, self.K, 1 if self.has_bias else 0)
+        _need(n > 0, "invalid linear dimensions")
+        self.packed = torch.empty(n, dtype=torch.uint8, device=w_q.device)
+        check("mxfp4_linear_pack", L.mxfp4_linear_pack(self.N, self.K, _ptr(w_q), _ptr(w_s), _ptr(bias), is_fp32,
+                                                        _ptr(self.packed), n, _stream()))
+        self._ws = None
+
+    def __call__(self, x, y=None):
+        _cuda(x, "x")
+        _need(x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1 and x.shape[1] == self.K,
+              "x: bf16 [M, K]")
+        M = x.shape[0]
+        if y is None:
+            y = torch.empty((M, self.N), dtype=torch.bfloat16, device=x.device)
+        L = _lib.lib()
+        n = L.mxfp4_linear_workspace_bytes(M, self.N, self.K)
+        _need(n > 0, "invalid linear arguments")
+        if self._ws is None or self._ws.numel() < n:
+            self._ws = torch.empty(n, dtype=torch.uint8, device=x.device)
+        check("mxfp4_linear_forward",
+              L.mxfp4_linear_forward(_ptr(self.packed), self.N, self.K, 1 if self.has_bias else 0, _ptr(x), M,
+                                     x.stride(0), _ptr(y), _ptr(self._ws), self._ws.numel(), _stream()))
+        return y
 
 
 class MoE:

@@ -29,6 +29,10 @@ _SIGS = {
                                             c_sz, c_p]),
     "mxfp4_unpack_weights": (ctypes.c_int, [ctypes.POINTER(MoeDims), c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p]),
     "mxfp4_check_packed": (ctypes.c_int, [ctypes.POINTER(MoeDims), c_p, c_p]),
+    "mxfp4_linear_pack_bytes": (c_sz, [c_i64, c_i64, c_i32]),
+    "mxfp4_linear_pack": (ctypes.c_int, [c_i64, c_i64, c_p, c_p, c_p, c_i32, c_p, c_sz, c_p]),
+    "mxfp4_linear_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64]),
+    "mxfp4_linear_forward": (ctypes.c_int, [c_p, c_i64, c_i64, c_i32, c_p, c_i64, c_i64, c_p, c_p, c_sz, c_p]),
     "moe_mxfp4_route_workspace_bytes": (c_sz, [c_i64, c_i32, c_i32]),
     "moe_mxfp4_route": (ctypes.c_int, [c_p, c_i64, c_i32, c_i32, c_i32, c_p, c_p, c_p, c_p, c_p, c_sz, c_p]),
     "moe_mxfp4_workspace_bytes": (c_sz, [ctypes.POINTER(MoeDims), c_i64, c_i32]),

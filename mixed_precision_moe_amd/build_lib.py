@@ -10,7 +10,7 @@ CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libmxfp4moe.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["quantize.hip", "repack.hip", "route.hip", "gemm.hip", "gemm_mx.hip", "api.cpp", "noalloc.hip"]
+SOURCES = ["quantize.hip", "repack.hip", "route.hip", "gemm.hip", "gemm_mx.hip", "linear.hip", "api.cpp", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops keeps the compiler from emitting packed fp32 VALU forms on gfx950.

@@ -239,6 +239,74 @@ MX_API int mxfp4_unpack_weights(const mxfp4_moe_dims* d, const void* packed, voi
                               b2_bf16, S(stream));
 }
 
+// ------------------------------------------------------------------------------------------------
+// Dense linear layer.
+
+static int check_linear_dims(int64_t N, int64_t K) {
+  if (N < 32 || K < 32 || N % 32 || K % 32 || N > (1 << 20) || K > (1 << 20)) return MXFP4_ERR_SHAPE;
+  return MXFP4_OK;
+}
+
+MX_API size_t mxfp4_linear_pack_bytes(int64_t N, int64_t K, int32_t has_bias) {
+  if (check_linear_dims(N, K) != MXFP4_OK || (has_bias != 0 && has_bias != 1)) return 0;
+  return (size_t)linear_offsets(moe_geom(1, N, K), has_bias != 0).total;
+}
+
+MX_API int mxfp4_linear_pack(int64_t N, int64_t K, const void* w_q, const void* w_s, const void* bias,
+                             int32_t bias_is_fp32, void* out, size_t out_bytes, void* stream) {
+  int st = check_linear_dims(N, K);
+  if (st) return st;
+  if (!w_q || !w_s || !out) return MXFP4_ERR_NULL;
+  if (!aligned(w_q, 16) || !aligned(out, 256) || (bias && !aligned(bias, bias_is_fp32 ? 4 : 2))) return MXFP4_ERR_ALIGN;
+  const MoeGeom g = moe_geom(1, N, K);
+  const LinearOffsets o = linear_offsets(g, bias != nullptr);
+  if (out_bytes < o.total) return MXFP4_ERR_WORKSPACE;
+  return launch_pack_linear(g, o, bias != nullptr, w_q, w_s, bias, bias_is_fp32, out, S(stream));
+}
+
+MX_API size_t mxfp4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (check_linear_dims(N, K) != MXFP4_OK || M < 0 || M > (1LL << 31)) return 0;
+  return (size_t)linear_ws(M, moe_geom(1, N, K)).total;
+}
+
+MX_API int mxfp4_linear_forward(const void* packed, int64_t N, int64_t K, int32_t has_bias, const void* x_bf16,
+                                int64_t M, int64_t ldx, void* y_bf16, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  int st = check_linear_dims(N, K);
+  if (st) return st;
+  if (M < 0 || M > (1LL << 31) || ldx < K || ldx % 8 || (has_bias != 0 && has_bias != 1)) return MXFP4_ERR_SHAPE;
+  const MoeGeom g = moe_geom(1, N, K);
+  const LinearWs w = linear_ws(M, g);
+  // the GEMM's copy sources are 32-bit byte offsets into the activation operand
+  if ((uint64_t)w.nrg * g.nkt2 * 64 * kMaxSlot >= (1ULL << 32)) return MXFP4_ERR_SHAPE;
+  if (M == 0) return MXFP4_OK;
+  if (!packed || !x_bf16 || !y_bf16 || !workspace) return MXFP4_ERR_NULL;
+  if (!aligned(packed, 256) || !aligned(x_bf16, 16) || !aligned(y_bf16, 16) || !aligned(workspace, 256))
+    return MXFP4_ERR_ALIGN;
+  if (workspace_bytes < w.total) return MXFP4_ERR_WORKSPACE;
+  const LinearOffsets o = linear_offsets(g, has_bias != 0);
+  const uint8_t* blob = (const uint8_t*)packed;
+  uint8_t* ws = (uint8_t*)workspace;
+  if ((st = launch_linear_prep(x_bf16, M, ldx, g, w, ws, S(stream)))) return st;
+  GemmArgs a = {};
+  a.wq = blob + o.wq;
+  a.ws = blob + o.ws;
+  a.bias = has_bias ? (const uint16_t*)(blob + o.bias) : nullptr;
+  a.xq = ws + w.actq;
+  a.xs = ws + w.acts;
+  a.prow_w = (const float*)(ws + w.roww);
+  a.tiles = (const TileDesc*)(ws + w.tiles);
+  a.ntiles = (const int32_t*)(ws + w.ntiles);
+  a.ydense = (uint16_t*)y_bf16;
+  a.nkt = (int32_t)g.nkt2;
+  a.ncb = (int32_t)g.ncb2;
+  a.ntl = (int32_t)g.nht;
+  a.nkt2 = (int32_t)g.nkt2;
+  a.I = (int32_t)K;
+  a.H = (int32_t)N;
+  return launch_gemm2(MXFP4_ACT_BF16, 1, a, w.nrg, S(stream));
+}
+
 MX_API size_t moe_mxfp4_route_workspace_bytes(int64_t T, int32_t E, int32_t top_k) {
   if (check_route_args(T, E, top_k) != MXFP4_OK) return 0;
   return (size_t)route_ws(T, E, top_k).total;
@@ -322,7 +390,7 @@ int forward_impl(const mxfp4_moe_dims* d, int32_t act_format, const void* packed
   GemmArgs a1 = {blob + o.w13q, blob + o.w13s, d->has_bias ? (const uint16_t*)(blob + o.b13) : nullptr,
                  ws + w.xq, nullptr, (const int32_t*)(ws + w.prow_tok), (const int32_t*)(ws + w.prow_pair),
                  (const float*)(ws + w.prow_w), (const TileDesc*)(ws + w.tiles), (const int32_t*)(ws + w.ntiles),
-                 ws + w.actq, ws + w.acts, nullptr, nullptr, (int32_t)g.nkt1, (int32_t)g.ncb1, (int32_t)g.nit,
+                 ws + w.actq, ws + w.acts, nullptr, nullptr, nullptr, (int32_t)g.nkt1, (int32_t)g.ncb1, (int32_t)g.nit,
                  (int32_t)g.nkt2, (int32_t)g.nkt1, (int32_t)g.I, (int32_t)g.H};
   if ((st = launch_gemm1(act_format, NRG1, a1, w.max_tiles, s)) || (st = mark())) return st;
   GemmArgs a2 = a1;

@@ -47,7 +47,6 @@
 
 namespace {
 
-typedef decltype(__builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(bf16x32_t{}, 1.0f)) fp6x32_t;
 typedef __attribute__((address_space(3))) void* lds_vptr_t;
 
 constexpr int kXcds = 8;           // workgroup b runs on XCD b % 8
@@ -843,6 +842,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
               for (int c = 0; c < 4; c++) bias4(bp + 4 * c, b + 4 * c);
 #pragma unroll
               for (int c = 0; c < 16; c++) v[c] += b[c];
+            }
+            if (a.ydense) {
+              // dense linear layer (one expert, unit row weights): the row of y itself, bf16
+              if (real) {
+                uint32_t bv[8];
+#pragma unroll
+                for (int c = 0; c < 8; c++) bv[c] = f32_to_bf16_bits(v[2 * c]) | (f32_to_bf16_bits(v[2 * c + 1]) << 16);
+                u32x4_t* yp = reinterpret_cast<u32x4_t*>(a.ydense + prow * a.H + nt * 32 + 16 * h);
+                yp[0] = u32x4_t{bv[0], bv[1], bv[2], bv[3]};
+                yp[1] = u32x4_t{bv[4], bv[5], bv[6], bv[7]};
+              }
+              __builtin_amdgcn_sched_barrier(0);
+              continue;
             }
             // The block maximum of w * v is |w| times that of v (rounding is monotonic), and scaling by a
             // power of two commutes with rounding, so w * 2^-ex is applied as one factor.

@@ -32,6 +32,10 @@ int launch_gemm1(int af, int NRG, const GemmArgs& a, int64_t max_tiles, hipStrea
 int launch_gemm2(int af, int NRG, const GemmArgs& a, int64_t max_tiles, hipStream_t stream);
 int launch_gemm1_mx(int af, int NRG, const GemmArgs& a, int64_t max_tiles, hipStream_t stream);
 int launch_gemm2_mx(int af, int NRG, const GemmArgs& a, int64_t max_tiles, hipStream_t stream);
+int launch_pack_linear(const MoeGeom& g, const LinearOffsets& o, bool bias, const void* w_q, const void* w_s,
+                       const void* b, int bias_is_fp32, void* out, hipStream_t stream);
+int launch_linear_prep(const void* x, int64_t M, int64_t ldx, const MoeGeom& g, const LinearWs& w, uint8_t* ws,
+                       hipStream_t stream);
 int launch_combine(const uint16_t* o16, const uint8_t* osc, const int32_t* pair_prow, void* y, int64_t T, int64_t H, int k,
                    hipStream_t stream);
 

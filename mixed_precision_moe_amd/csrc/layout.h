@@ -172,6 +172,48 @@ struct alignas(16) TileDesc {
   int32_t e, prow0, nrows, pad;
 };
 
+// Execution layout of a dense MXFP4 linear layer y = x W^T + b (mxfp4_linear_pack): a 256-byte header,
+// then W [N, K] in the second GEMM's layout for one expert with H = N output rows and I = K (pieces
+// [ncb2][nkt2][16 tiles][64 lanes][16 B], block elements in w2_perm order; scale records
+// [ncb2][nkt2][64][16]), then the bias as bf16 [N] if present.
+#define MX_LINEAR_MAGIC "MX4LIN95"
+
+struct LinearOffsets {
+  uint64_t wq, ws, bias, total;
+};
+
+static inline LinearOffsets linear_offsets(const MoeGeom& g, bool bias) {
+  LinearOffsets o;
+  uint64_t p = 256;
+  o.wq = p;   p = align256(p + (uint64_t)g.ncb2 * g.nkt2 * kCB * 1024);
+  o.ws = p;   p = align256(p + (uint64_t)g.ncb2 * g.nkt2 * 1024);
+  o.bias = p; p = align256(p + (bias ? (uint64_t)g.H * 2 : 0));
+  o.total = p;
+  return o;
+}
+
+// Linear-layer workspace: the activation operand in the second GEMM's layout (row groups of 32 rows;
+// kActBf16 terms in w2_perm order) and its scale dwords, the M tiles of 32 rows, their count, and a
+// unit weight per row (plus 64 slack entries read by the row-table copies).
+struct LinearWs {
+  uint64_t actq, acts, tiles, ntiles, roww, total;
+  int64_t nrg;
+};
+
+static inline LinearWs linear_ws(int64_t M, const MoeGeom& g) {
+  LinearWs w;
+  w.nrg = cdiv(M, 32);
+  uint64_t p = 0;
+  auto take = [&](uint64_t bytes) { uint64_t o = p; p = align256(p + bytes); return o; };
+  w.actq = take((uint64_t)w.nrg * g.nkt2 * 64 * kMaxSlot);
+  w.acts = take((uint64_t)w.nrg * g.nkt2 * 64 * 4);
+  w.tiles = take(16 * (uint64_t)w.nrg);
+  w.ntiles = take(16);
+  w.roww = take(4 * ((uint64_t)w.nrg * 32 + 64));
+  w.total = p;
+  return w;
+}
+
 // Arguments of the grouped GEMM kernels (device pointers into the blob and the workspace, and the
 // 32-bit sizes the kernels index with).
 struct GemmArgs {
@@ -187,6 +229,7 @@ struct GemmArgs {
   const int32_t* ntiles;
   uint8_t* actq;            // first GEMM output
   uint8_t* acts;
+  uint16_t* ydense;         // second GEMM in a dense linear layer: bf16 rows [rows][H] (else NULL)
   uint16_t* o16;            // second GEMM output (int16 blocks, padded-row order) and their exponents
   uint8_t* osc;
   int32_t nkt, ncb;         // K steps and column blocks of this GEMM

@@ -309,3 +309,20 @@ int launch_repack_standard(const MoeGeom& g, bool bias, const void* w13_q, const
   }
   return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
 }
+
+// The dense linear layer's weights: header, then W as the second GEMM's weights of one expert with
+// H = N rows and I = K, then the bias in bf16.
+int launch_pack_linear(const MoeGeom& g, const LinearOffsets& o, bool bias, const void* w_q, const void* w_s,
+                       const void* b, int bias_is_fp32, void* out, hipStream_t stream) {
+  uint8_t* base = (uint8_t*)out;
+  BlobHeader h = {};
+  for (int i = 0; i < 8; i++) h.magic[i] = MX_LINEAR_MAGIC[i];
+  h.version = MX_BLOB_VERSION;
+  h.E = 1; h.H = (int32_t)g.H; h.I = (int32_t)g.I; h.has_bias = bias ? 1 : 0;
+  h.off_w2q = o.wq; h.off_w2s = o.ws; h.off_b2 = o.bias; h.total = o.total;
+  hipLaunchKernelGGL(write_header_kernel, dim3(1), dim3(64), 0, stream, base, h);
+  LAUNCH1D(pack_w2q_kernel, g.ncb2 * g.nkt2 * kCB * 64, (const uint8_t*)w_q, (u32x4_t*)(base + o.wq), g);
+  LAUNCH1D(pack_w2s_kernel, g.ncb2 * g.nkt2 * 64, (const uint8_t*)w_s, (u32x4_t*)(base + o.ws), g);
+  if (bias) LAUNCH1D(bias_kernel, g.H, b, (uint16_t*)(base + o.bias), bias_is_fp32, 1, g.H, 0);
+  return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
+}

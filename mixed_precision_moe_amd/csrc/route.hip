@@ -17,15 +17,6 @@ namespace {
 
 #define GRID_STRIDE(i, n) for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < (n); i += (int64_t)gridDim.x * blockDim.x)
 
-typedef decltype(__builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(bf16x32_t{}, 1.0f)) fp6x32_t;
-
-MX_DEV uint32_t amax_bits32(const uint32_t* w) {  // 16 words = 32 bf16 -> largest magnitude bits
-  uint32_t m = 0;
-#pragma unroll
-  for (int i = 0; i < 16; i++) m = max(m, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
-  return m;
-}
-
 // x [T, ldx] bf16 -> xq: per 32-element block the terms of activation format AF (layout.h), each the
 // current remainder quantized with its own E8M0 scale:
 //   kActBf16: t0 = E2M3 of x, t1 = E2M3 of x - t0, t2 = E2M1 of x - t0 - t1, scales from the 0.75
@@ -42,55 +33,6 @@ MX_DEV uint32_t amax_bits32(const uint32_t* w) {  // 16 words = 32 bf16 -> large
 // written to LDS, lane l then reads its block's four chunks; lane l writes its slot and scale dword into
 // record l / 2 (blocks 2r and 2r + 1 form the K-step record r), and the wave's 32 records (consecutive
 // in xq) leave as 1 KB stores.
-typedef float xf32x2_t __attribute__((ext_vector_type(2)));
-typedef short xs16x2_t __attribute__((ext_vector_type(2)));
-
-MX_DEV bf16x32_t as_bf16x32(const uint32_t* w) {
-  bf16x32_t v;
-#pragma unroll
-  for (int j = 0; j < 16; j++) {
-    const bf16x2_t two = __builtin_bit_cast(bf16x2_t, w[j]);
-    v[2 * j] = two[0];
-    v[2 * j + 1] = two[1];
-  }
-  return v;
-}
-
-// w[j] (elements 2j, 2j + 1) -= the dequantized E2M3 codes, exactly, in bf16
-MX_DEV void sub_fp6(uint32_t* w, const fp6x32_t& codes, float sc) {
-  const auto deq = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(codes, sc);
-#pragma unroll
-  for (int j = 0; j < 16; j++) {
-    const float a = bf16_bits_to_f32(w[j] & 0xFFFFu) - deq[2 * j];
-    const float c = bf16_bits_to_f32(w[j] >> 16) - deq[2 * j + 1];
-    w[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector((xf32x2_t){a, c}, bf16x2_t));
-  }
-}
-
-// 32 bf16 (w[j]: elements 2j, 2j + 1) -> E2M1 codes, element i in nibble i of the 16 bytes
-MX_DEV void fp4_from_bf16(const uint32_t* w, float sc, uint32_t* out) {
-#pragma unroll
-  for (int d = 0; d < 4; d++) {
-    uint32_t p = 0;
-    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(p, __builtin_bit_cast(bf16x2_t, w[4 * d]), sc, 0);
-    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(p, __builtin_bit_cast(bf16x2_t, w[4 * d + 1]), sc, 1);
-    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(p, __builtin_bit_cast(bf16x2_t, w[4 * d + 2]), sc, 2);
-    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(p, __builtin_bit_cast(bf16x2_t, w[4 * d + 3]), sc, 3);
-    out[d] = p;
-  }
-}
-
-// 32 bf16 -> E4M3 codes, element i in byte i of the 32 bytes
-MX_DEV void fp8_from_bf16(const uint32_t* w, float sc, uint32_t* out) {
-#pragma unroll
-  for (int d = 0; d < 8; d++) {
-    xs16x2_t p = xs16x2_t{0, 0};
-    p = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(p, __builtin_bit_cast(bf16x2_t, w[2 * d]), sc, false);
-    p = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(p, __builtin_bit_cast(bf16x2_t, w[2 * d + 1]), sc, true);
-    out[d] = __builtin_bit_cast(uint32_t, p);
-  }
-}
-
 template <int AF>
 __global__ __launch_bounds__(256) void xprep_kernel(const uint16_t* __restrict__ x, int64_t ldx, int64_t H, int64_t nblk,
                                                     uint8_t* __restrict__ xq, int32_t* __restrict__ zero,

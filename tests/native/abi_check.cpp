@@ -74,6 +74,51 @@ static void test_nvfp4() {
   CHECK(nvfp4_tiled_scale_bytes(1, 40) == 0 && nvfp4_tiled_scale_bytes(INT64_MAX, 64) == 0);
 }
 
+static void test_linear() {
+  CHECK(mxfp4_linear_pack_bytes(2048, 2048, 1) > 0);
+  CHECK(mxfp4_linear_pack_bytes(2040, 2048, 0) == 0 && mxfp4_linear_pack_bytes(2048, 16, 0) == 0);
+  CHECK(mxfp4_linear_pack_bytes(INT64_MAX, 64, 0) == 0 && mxfp4_linear_pack_bytes(64, 64, 3) == 0);
+  const int64_t N = 96, K = 160, M = 70;
+  const size_t nb = mxfp4_linear_pack_bytes(N, K, 1);
+  CHECK(mxfp4_linear_pack(N, K, fake(), fake(), fake(), 1, fake(), nb - 1, nullptr) == MXFP4_ERR_WORKSPACE);
+  CHECK(mxfp4_linear_pack(N, K, fake(8), fake(), nullptr, 0, fake(), nb, nullptr) == MXFP4_ERR_ALIGN);
+  CHECK(mxfp4_linear_pack(N, K, nullptr, fake(), nullptr, 0, fake(), nb, nullptr) == MXFP4_ERR_NULL);
+  g_calls.clear();
+  CHECK(mxfp4_linear_pack(N, K, fake(), fake(), fake(), 1, fake(), nb, nullptr) == MXFP4_OK);
+  CHECK(g_calls.size() == 1 && g_calls[0].name == "pack_linear" && (size_t)g_calls[0].i[0] == nb);
+  const size_t nw = mxfp4_linear_workspace_bytes(M, N, K);
+  CHECK(nw > 0 && mxfp4_linear_workspace_bytes(-1, N, K) == 0);
+  void* ws = fake(1ull << 40);
+  void* blob = fake(1ull << 36);
+  CHECK(mxfp4_linear_forward(blob, N, K, 1, fake(), M, K, fake(), ws, nw - 1, nullptr) == MXFP4_ERR_WORKSPACE);
+  CHECK(mxfp4_linear_forward(blob, N, K, 1, fake(), M, K - 8, fake(), ws, nw, nullptr) == MXFP4_ERR_SHAPE);
+  CHECK(mxfp4_linear_forward(blob, N, K, 1, fake(2), M, K, fake(), ws, nw, nullptr) == MXFP4_ERR_ALIGN);
+  CHECK(mxfp4_linear_forward(blob, N, K, 2, fake(), M, K, fake(), ws, nw, nullptr) == MXFP4_ERR_SHAPE);
+  g_calls.clear();
+  CHECK(mxfp4_linear_forward(nullptr, N, K, 1, nullptr, 0, K, nullptr, nullptr, 0, nullptr) == MXFP4_OK);
+  CHECK(g_calls.empty());
+  CHECK(mxfp4_linear_forward(blob, N, K, 1, fake(), M, K, fake(), ws, nw, nullptr) == MXFP4_OK);
+  CHECK((names() == std::vector<std::string>{"linear_prep", "gemm2"}));
+  if (g_calls.size() == 2) {
+    const GemmArgs& a = g_calls[1].gemm;
+    const MoeGeom g = moe_geom(1, N, K);
+    const LinearOffsets o = linear_offsets(g, true);
+    const LinearWs w = linear_ws(M, g);
+    CHECK(a.ydense == fake() && a.o16 == nullptr && g_calls[1].i[0] == 1 && g_calls[1].i[1] == w.nrg);
+    CHECK(inside(a.wq, (size_t)g.ncb2 * g.nkt2 * kCB * 1024, blob, o.total));
+    CHECK(inside(a.ws, (size_t)g.ncb2 * g.nkt2 * 1024, blob, o.total));
+    CHECK(inside(a.bias, (size_t)N * 2, blob, o.total));
+    CHECK(inside(a.xq, (size_t)w.nrg * g.nkt2 * 64 * kMaxSlot, ws, nw));
+    CHECK(inside(a.xs, (size_t)w.nrg * g.nkt2 * 64 * 4, ws, nw));
+    CHECK(inside(a.prow_w, 4 * ((size_t)w.nrg * 32 + 64), ws, nw));
+    CHECK(inside(a.tiles, 16 * (size_t)w.nrg, ws, nw) && inside(a.ntiles, 4, ws, nw));
+    CHECK(a.ntl == N / 32 && a.H == N && a.nkt == (K + 63) / 64);
+  }
+  // the split activations must stay addressable with 32-bit offsets
+  CHECK(mxfp4_linear_forward(blob, 64, 1 << 20, 0, fake(), 4096, 1 << 20, fake(), ws, SIZE_MAX, nullptr) ==
+        MXFP4_ERR_SHAPE);
+}
+
 static void test_repack() {
   mxfp4_moe_dims d = {4, 256, 128, 1};
   CHECK(mxfp4_repack_bytes(&d, 0) > 0);
@@ -300,6 +345,7 @@ static void test_forward() {
 int main() {
   test_quantize();
   test_nvfp4();
+  test_linear();
   test_repack();
   test_header_checks();
   test_route();

@@ -50,6 +50,18 @@ int launch_repack_standard(const MoeGeom& g, bool bias, const void*, const void*
   for (int k = 0; k < 6; k++) c.off[k] = off[k];
   return rec("repack_standard", c);
 }
+int launch_pack_linear(const MoeGeom& g, const LinearOffsets& o, bool bias, const void*, const void*, const void*, int,
+                       void* out, hipStream_t) {
+  Call c;
+  c.p[0] = out; c.i[0] = (int64_t)o.total; c.i[1] = bias; c.i[2] = g.H; c.i[3] = g.I;
+  return rec("pack_linear", c);
+}
+int launch_linear_prep(const void* x, int64_t M, int64_t ldx, const MoeGeom&, const LinearWs& w, uint8_t* ws,
+                       hipStream_t) {
+  Call c;
+  c.p[0] = x; c.p[1] = ws; c.i[0] = M; c.i[1] = ldx; c.i[2] = (int64_t)w.total;
+  return rec("linear_prep", c);
+}
 int launch_xprep(int af, const void* x, int64_t T, int64_t ldx, const MoeGeom&, void* xq, int32_t* zero,
                  int64_t nzero, hipStream_t) {
   Call c;
