@@ -67,13 +67,14 @@ int choose_nrg1(int64_t P, int64_t E) {
   return 4;
 }
 
-// The same for the second GEMM, whose 64-row tiles measured faster than 128-row ones at every load
-// tried (its items are short, 12 K steps at I = 768, and bound by copy latency).  With the bf16 path's
-// three-term operand a 64-row tile needs more registers than two workgroups per CU leave (it spilled in
-// the K loop), and 32-row tiles measured fastest.
+// The same for the second GEMM.  With one-term operands (the quantized-activation formats) its 64-row
+// tiles measured fastest once experts average 48 rows.  With the bf16 path's three-term operand a
+// 64-row tile needs more registers than two workgroups per CU leave, and 32-row tiles at two workgroups
+// per CU measured fastest up to a few hundred rows per expert; from an average of 160 rows the first
+// GEMM's 128-row shape (one workgroup per CU) is a little faster.
 int choose_nrg2(int64_t P, int64_t E, int32_t act) {
   const int64_t avg = P / (E > 0 ? E : 1);
-  if (act == MXFP4_ACT_BF16) return 1;
+  if (act == MXFP4_ACT_BF16) return avg < 160 ? 1 : 4;
   return avg < 48 ? 1 : 2;
 }
 

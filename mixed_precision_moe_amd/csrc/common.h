@@ -56,6 +56,23 @@ MX_DEV uint32_t f32_to_bf16_bits(float f) {
 // 8*jj + 4*h + i (accumulator index 4*jj + i), which it stores at positions 16*h + 4*jj + i.
 __host__ __device__ inline int w2_perm(int p) { return 8 * ((p & 15) >> 2) + 4 * (p >> 4) + (p & 3); }
 
+// Stores the SLOT / 4 words of lane L's operand slot into the region-ordered slots `blk` of its row
+// group and K step (slot_byte in layout.h): one 16- or 8-byte store per region, each coalesced over
+// the wave.
+template <int AF>
+MX_DEV void store_slot(uint8_t* blk, int L, const uint32_t* words) {
+  constexpr int SLOT = act_slot(AF);
+#pragma unroll
+  for (int o = 0; o < SLOT; o += 8) {
+    if (slot_region_start(AF, o) != o) continue;
+    if (slot_region_bytes(AF, o) == 16)
+      *reinterpret_cast<u32x4_t*>(blk + slot_byte(AF, L, o)) =
+          u32x4_t{words[o / 4], words[o / 4 + 1], words[o / 4 + 2], words[o / 4 + 3]};
+    else
+      *reinterpret_cast<u32x2_t*>(blk + slot_byte(AF, L, o)) = u32x2_t{words[o / 4], words[o / 4 + 1]};
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // Activation split helpers: 32 bf16 of one block held as 16 words (w[j]: elements 2j, 2j + 1).
 typedef decltype(__builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(bf16x32_t{}, 1.0f)) fp6x32_t;

@@ -6,23 +6,23 @@
 //  MXFP4 weights with E8M0 scales per 32 elements; P1 Implementation breakdown: the mixed-input fused
 //  MoE multiplies packed 4-bit weights with per-32 group scales by 16-bit activations]
 //
-// The MFMA has no bf16 operand, so a bf16 activation enters as two E2M3 (FP6) terms x = t0 + t1, each
-// with its own E8M0 scale per 32 elements, and every product is issued once per term against the same
-// FP4 weight registers; FP6 x FP4 runs at the FP4 rate on gfx950.  The first GEMM's output (the SwiGLU
-// activation) stays fp32 until it is split into the second GEMM's two terms, and the second GEMM's rows
-// are block-scaled fp16 that the combine sums in fp32, so the only bf16 rounding after the input is the
-// output's.
+// The MFMA has no bf16 operand, so a bf16 activation enters as three block-scaled terms x = t0 + t1 + t2
+// (E2M3, E2M3 of the remainder, E2M1 of what is left; each with its own E8M0 scale per 32 elements),
+// and every product is issued once per term against the same FP4 weight registers; FP6 x FP4 and
+// FP4 x FP4 run at the same rate on gfx950.  The first GEMM's output (the SwiGLU activation) stays fp32
+// until it is split into the second GEMM's three terms, and the second GEMM's rows are 16-bit integers
+// with a power-of-two scale per 16 columns that the combine sums in fp32, so the only bf16 rounding
+// after the input is the output's.  The quantized-activation formats (MXFP8, MXFP4) are one term.
 //
 // Both GEMMs are computed transposed, D[n][m] = sum_k W[n][k] act[m][k]: the weights are the A operand
 // (rows n = 32 output columns of one tile), the tokens the B operand (columns m = 32 rows of the padded
 // row order).  Lane l of a 32x32 result holds token l%32 and tile rows 8*jj + 4*(l/32) + i.
 //  - First GEMM: gate and up of a token sit in the same lane (SwiGLU in registers); the 32-element
 //    blocks of two adjacent activation tiles are spread over both lane halves, and one exchange of
-//    halves leaves each lane one whole block, which it splits into the second GEMM's two E2M3 terms.
+//    halves leaves each lane one whole block, which it splits into the second GEMM's operand terms.
 //  - Second GEMM: one exchange of halves leaves each lane 16 consecutive output columns of its token,
-//    stored as fp16 with one power-of-two exponent per 16 columns (about eleven significant bits of
-//    every value that matters for the sum) in the padded row order; the combine gathers each token's
-//    k rows.
+//    stored as 16-bit integers with one power-of-two exponent per 16 columns (an absolute error of at
+//    most 2^-14 of the block maximum) in the padded row order; the combine gathers each token's k rows.
 //
 // Both GEMMs run one kernel template.  A workgroup of four waves (WR x WC) computes an M tile of
 // NRG = WR*RW row groups of 32 rows against NT = WC*CW weight tiles of 32 columns; wave (wr, wc) holds
@@ -329,8 +329,7 @@ MX_DEV void g1_epilogue_pair(const f32x16_t& g0, const f32x16_t& u0, const f32x1
     }
   }
   constexpr int SLOT = act_slot(AF);
-  const int slot = (rg * a.nkt2 + kt2) * 64 + lane;
-  u32x4_t* dst = reinterpret_cast<u32x4_t*>(a.actq + (int64_t)slot * SLOT);
+  const int64_t blk = (int64_t)rg * a.nkt2 + kt2;
   uint32_t out[SLOT / 4];
   uint32_t scales = 0;
   if constexpr (AF == kActBf16) {
@@ -384,14 +383,13 @@ MX_DEV void g1_epilogue_pair(const f32x16_t& g0, const f32x16_t& u0, const f32x1
   } else {
     fp4_from_f32(lo, hi, e8m0_as_scale_operand(block_amax_e8m0(lo, hi, scales, 0)), out);
   }
-#pragma unroll
-  for (int d = 0; d < SLOT / 16; d++) dst[d] = u32x4_t{out[4 * d], out[4 * d + 1], out[4 * d + 2], out[4 * d + 3]};
-  reinterpret_cast<uint32_t*>(a.acts)[slot] = scales;
+  store_slot<AF>(a.actq + blk * 64 * SLOT, lane, out);
+  reinterpret_cast<uint32_t*>(a.acts)[blk * 64 + lane] = scales;
 }
 
 // ------------------------------------------------------------------------------------------------
 // The grouped GEMM.  G1: first GEMM (A = weights, B = gathered token terms, SwiGLU epilogue);
-// otherwise the second GEMM (A = activation terms, B = weights, weighted fp16 rows to o16).
+// otherwise the second GEMM (A = weights, B = activation terms, weighted 16-bit rows to o16).
 //
 // A workgroup processes the items (M tile, column position) dealt to it in turn; the first D - 1
 // stages of the next item are copied before the current item's epilogue runs, so the ring refills
@@ -537,7 +535,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
   // Each E2M3 term operand (6 dwords) is read by its own two LDS loads (16 + 8 bytes for term 0 at
   // slot offset 0, 8 + 16 bytes for term 1 at offset 24), so every MFMA operand tuple is written in
   // place by its loads.  Each row group's and each term's loads take their base address through an
-  // opaque copy: that keeps the compiler from merging adjacent 8-byte loads (of the two terms, or of
+  // opaque copy: that keeps the compiler from merging adjacent 8-byte loads (of two terms, or of
   // two row groups) into wider loads whose parts would then have to be copied (and waited for) to
   // form the tuples.  Activation fragments and
   // weight scales are double-buffered across steps ([P], P a compile-time parity); a weight fragment
@@ -545,12 +543,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
   typedef const __attribute__((address_space(3))) u32x4_t* lds16_p;
   typedef const __attribute__((address_space(3))) u32x2_t* lds8_p;
   typedef const __attribute__((address_space(3))) uint32_t* lds4_p;
-  // The second GEMM (two workgroups per CU, a 3-stage ring) and the first GEMM's 64-row configuration
-  // (two per CU, 3 stages; long weight streams such as H = 7168) load the next step's fragments after
-  // the step's MFMAs (LATE), so a stage is needed one step later than with loads interleaved into the
-  // MFMAs: its copies get about two steps instead of one to land.  The first GEMM's 32-row (decode)
-  // and 128-row configurations measured faster with interleaved loads.
-  constexpr bool LATE = !G1 || (D == 3 && RW == 2);
+  // The 3-stage configurations of the second GEMM (two workgroups per CU) and the first GEMM's 64-row
+  // one load the next step's fragments after the step's MFMAs (LATE), so a stage is needed one step
+  // later than with loads interleaved into the MFMAs: its copies get about two steps instead of one to
+  // land.  The first GEMM's 32-row (decode) configuration and the 128-row ones of both GEMMs measured
+  // faster with interleaved loads.
+  constexpr bool LATE = D == 3 && (!G1 || RW == 2);
   using Plan = StepPlan<RW, CW, C::kOps, !G1, LATE, NTERMS>;
   static constexpr Plan plan{};
   static_assert(plan.valid(), "step plan");
@@ -569,32 +567,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
     // first GEMM: lane l takes block l / 32 of row l % 32's record; second: slot l of the row group
     lds_u8 rec = (lds_u8)(base + C::oX + (wr * RW + r) * (32 * C::REC) + (lane & 31) * C::REC);
     lds_u8 rgb = (lds_u8)(base + C::oX + (wr * RW + r) * C::kXRG);  // second GEMM: the row group's slots
-    lds_u8 xp = G1 ? rec + (lane >> 5) * C::SLOT : rgb + lane * C::SLOT;
+    // Byte O of this lane's slot: in its record (first GEMM), or in the region order of the row group's
+    // slots (second GEMM: region [R, R + n) of slot L at 64 * R + n * L)
+    auto at = [&](auto oc) __attribute__((always_inline)) {
+      constexpr int O = decltype(oc)::value;
+      return G1 ? rec + (lane >> 5) * C::SLOT + O : rgb + slot_byte(AF, 0, O) + slot_region_bytes(AF, O) * lane;
+    };
     static_for<0, NTERMS>([&](auto tc) __attribute__((always_inline)) {
       constexpr int t = decltype(tc)::value;
       constexpr int off = act_term_offset(AF, t), nb = fmt_bytes(act_term_fmt(AF, t));
-      lds_u8 tp = xp + off;
-      asm("" : "+v"(tp));
-      if constexpr (nb == 24 && off % 16 == 0) {  // E2M3 at a 16-byte boundary: 16 + 8 bytes
-        const u32x4_t p4 = *(lds16_p)tp;
-        const u32x2_t p2 = *(lds8_p)(tp + 16);
-        xop[P][r][t] = i32x8_t{(int)p4[0], (int)p4[1], (int)p4[2], (int)p4[3], (int)p2[0], (int)p2[1], 0, 0};
-      } else if constexpr (nb == 24) {  // E2M3 at an 8-byte boundary: 8 + 16 bytes
-        const u32x2_t p2 = *(lds8_p)tp;
-        const u32x4_t p4 = *(lds16_p)(tp + 8);
-        xop[P][r][t] = i32x8_t{(int)p2[0], (int)p2[1], (int)p4[0], (int)p4[1], (int)p4[2], (int)p4[3], 0, 0};
+      if constexpr (nb == 24) {  // E2M3: 16 + 8 bytes at a 16-byte boundary, else 8 + 16
+        constexpr int first = off % 16 == 0 ? 16 : 8;
+        lds_u8 pa = at(std::integral_constant<int, off>{});
+        asm("" : "+v"(pa));
+        lds_u8 pb = at(std::integral_constant<int, off + first>{});
+        asm("" : "+v"(pb));
+        if constexpr (first == 16) {
+          const u32x4_t p4 = *(lds16_p)pa;
+          const u32x2_t p2 = *(lds8_p)pb;
+          xop[P][r][t] = i32x8_t{(int)p4[0], (int)p4[1], (int)p4[2], (int)p4[3], (int)p2[0], (int)p2[1], 0, 0};
+        } else {
+          const u32x2_t p2 = *(lds8_p)pa;
+          const u32x4_t p4 = *(lds16_p)pb;
+          xop[P][r][t] = i32x8_t{(int)p2[0], (int)p2[1], (int)p4[0], (int)p4[1], (int)p4[2], (int)p4[3], 0, 0};
+        }
       } else if constexpr (nb == 32) {
         // E4M3: the operand interleaves K by 16: lane half h holds elements 16h .. 16h + 15 of the step's
         // first block, then the same elements of its second block (the scale of block b still comes
         // from lane half b); the two blocks of row l % 32 are the two slots of its record (first GEMM)
         // or the slots of lanes l % 32 and l % 32 + 32 (second GEMM)
-        lds_u8 s0 = (G1 ? rec : rgb + (lane & 31) * C::SLOT) + off + (lane >> 5) * 16;
-        lds_u8 s1 = s0 + (G1 ? C::SLOT : 32 * C::SLOT);
+        // (second GEMM: the two 16-byte halves are regions at 64 * off and 64 * (off + 16))
+        lds_u8 s0 = G1 ? rec + off + (lane >> 5) * 16 : rgb + 64 * off + (lane >> 5) * (64 * 16) + (lane & 31) * 16;
+        lds_u8 s1 = s0 + (G1 ? C::SLOT : 32 * 16);
         asm("" : "+v"(s1));
         const u32x4_t p4 = *(lds16_p)s0;
         const u32x4_t q4 = *(lds16_p)s1;
         xop[P][r][t] = i32x8_t{(int)p4[0], (int)p4[1], (int)p4[2], (int)p4[3], (int)q4[0], (int)q4[1], (int)q4[2], (int)q4[3]};
       } else {  // E2M1
+        lds_u8 tp = at(std::integral_constant<int, off>{});
+        asm("" : "+v"(tp));
         const u32x4_t p4 = *(lds16_p)tp;
         xop[P][r][t] = i32x8_t{(int)p4[0], (int)p4[1], (int)p4[2], (int)p4[3], 0, 0, 0, 0};
       }
@@ -926,9 +937,13 @@ int gemm2_cfg(int NRG, const GemmArgs& a, int64_t max_tiles, hipStream_t stream)
   switch (NRG) {
     case 1: return launch_cfg<false, AF, BIAS, 1, 4, 1, 4, 3>(a, max_tiles, stream);
     case 2:
-      // the bf16 path's second GEMM runs 32-row tiles only (the placement's tile list follows it)
+      // the bf16 path's second GEMM runs 32- or 128-row tiles (the placement's tile list follows it)
       if constexpr (AF == kActBf16) return MXFP4_ERR_SHAPE;
       else return launch_cfg<false, AF, BIAS, 1, 4, 2, 4, 3>(a, max_tiles, stream);
+    case 4:
+      // the first GEMM's 128-row shape (one workgroup per CU, interleaved fragment loads)
+      if constexpr (AF == kActBf16) return launch_cfg<false, AF, BIAS, 2, 2, 2, 8, 4>(a, max_tiles, stream);
+      else return MXFP4_ERR_SHAPE;
     default: return MXFP4_ERR_SHAPE;
   }
 }

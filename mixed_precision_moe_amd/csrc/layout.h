@@ -104,6 +104,36 @@ constexpr int act_term_offset(int af, int t) {
   return t == 0 ? 0 : act_term_offset(af, t - 1) + fmt_bytes(act_term_fmt(af, t - 1));
 }
 constexpr int act_slot(int af) { return act_term_offset(af, act_terms(af)); }
+// The slots of one row group and K step (64 lanes) are stored region by region: a slot's bytes are cut
+// where the second GEMM's LDS loads cut them (an E2M3 term into 16 + 8 bytes at a 16-byte boundary or
+// 8 + 16 after one, E4M3 into two 16-byte halves, E2M1 whole), and region [o, o + n) of slot L sits at
+// 64 * o + n * L.  A wave's load of one region then reads consecutive bytes, free of LDS bank conflicts,
+// where lanes reading one slot each at the slot stride would collide.
+constexpr int slot_region_start(int af, int o) {
+  for (int t = 0; t < act_terms(af); t++) {
+    const int off = act_term_offset(af, t), nb = fmt_bytes(act_term_fmt(af, t));
+    if (o >= off && o < off + nb) {
+      const int first = nb == 24 ? (off % 16 == 0 ? 16 : 8) : 16;
+      return o < off + first ? off : off + first;
+    }
+  }
+  return -1;
+}
+constexpr int slot_region_bytes(int af, int o) {
+  const int st = slot_region_start(af, o);
+  int end = st + 1;
+  while (end < act_slot(af) && slot_region_start(af, end) == st) end++;
+  return end - st;
+}
+// Byte offset of slot byte o of lane L within its row group's and K step's 64 * act_slot(af) bytes.
+constexpr int slot_byte(int af, int L, int o) {
+  return 64 * slot_region_start(af, o) + slot_region_bytes(af, o) * L + (o - slot_region_start(af, o));
+}
+static_assert(slot_region_bytes(kActBf16, 0) == 16 && slot_region_bytes(kActBf16, 16) == 8 &&
+                  slot_region_bytes(kActBf16, 24) == 8 && slot_region_bytes(kActBf16, 32) == 16 &&
+                  slot_region_bytes(kActBf16, 48) == 16 && slot_region_bytes(kActMxfp8, 16) == 16 &&
+                  slot_region_bytes(kActMxfp4, 0) == 16,
+              "slot regions");
 // The first GEMM's activation record of one token and one 64-wide K step: the two blocks' slots, their
 // two scale dwords, 8 zero bytes (144, 80 or 48 bytes); records of a token row are consecutive, so the
 // first GEMM copies a row's terms and scales together in 16-byte chunks.

@@ -64,11 +64,10 @@ __global__ __launch_bounds__(256) void linear_prep_kernel(const uint16_t* __rest
       slot[6 + d] = t1[d];
     }
     fp4_from_bf16(w, e8m0_as_scale_operand(e2), slot + 12);
-    const int64_t si = (rg * nkt + b / 2) * 64 + (b & 1) * 32 + rlo;
-    u32x4_t* dst = reinterpret_cast<u32x4_t*>(actq + si * SLOT);
-#pragma unroll
-    for (int d = 0; d < SLOT / 16; d++) dst[d] = u32x4_t{slot[4 * d], slot[4 * d + 1], slot[4 * d + 2], slot[4 * d + 3]};
-    acts[si] = e0 | (e1 << 8) | (e2 << 16);
+    const int64_t blk = rg * nkt + b / 2;
+    const int L = (int)((b & 1) * 32 + rlo);
+    store_slot<kActBf16>(actq + blk * 64 * SLOT, L, slot);
+    acts[blk * 64 + L] = e0 | (e1 << 8) | (e2 << 16);
   }
 }
 
