@@ -285,12 +285,16 @@ def nvfp4_quantize_ref(x_bits, global_scale):
     blocks = x_bits.reshape(M, K // NV_BLOCK, NV_BLOCK)
     mag = bf16_to_f64(blocks & np.uint16(0x7FFF)).astype(np.float32)  # exact
     vmax = mag.max(axis=-1)
-    sf = (gs * (vmax * RCP6_F32).astype(np.float32)).astype(np.float32)
+    # a binary32 product may overflow to infinity for huge global scales: the E4M3 and E2M1 steps then
+    # saturate it, as the conversions do
+    with np.errstate(over="ignore"):
+        sf = (gs * (vmax * RCP6_F32).astype(np.float32)).astype(np.float32)
     sf_code = e4m3_magnitude_code(sf.astype(np.float64))
     sf_deq = E4M3_MAGNITUDES[sf_code].astype(np.float32)
     with np.errstate(divide="ignore"):
         r = np.where(sf_deq > 0, gs / np.where(sf_deq > 0, sf_deq, np.float32(1)), np.float32(0)).astype(np.float32)
-    v = (mag * r[..., None]).astype(np.float32)
+    with np.errstate(over="ignore"):
+        v = (mag * r[..., None]).astype(np.float32)
     code = e2m1_magnitude_code(v.astype(np.float64))
     code |= ((blocks >> np.uint16(15)).astype(np.uint8) << np.uint8(3))
     code = code.reshape(M, K)
