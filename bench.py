@@ -52,7 +52,7 @@ STAGE_KERNELS = ["xprep_kernel", "route_kernel", "place_kernel", "grouped_gemm_k
                  "grouped_gemm_kernel<G1=false>", "combine_kernel"]
 DTYPE = ("mxfp4 (e2m1 + e8m0) weights x bf16 activations split into three block-scaled terms "
          "(e2m3, e2m3, e2m1) on scaled MFMA, fp32 accumulate, bf16 out")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_prefill_gemm1_and_quantize.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_per_kernel.txt")
 CSRC = os.path.join(ROOT, "mixed_precision_moe_amd", "csrc")
 # the sources each measured kernel is compiled from: a counter figure stands only while they are unchanged
 KERNEL_SOURCES = {"gemm": ["gemm_kernel.h", "gemm.hip", "common.h", "layout.h"],
