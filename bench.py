@@ -2,7 +2,7 @@
 """Benchmark of the MXFP4 MoE layer and the MXFP4 quantizer on one MI355X.
 
 A step is one MoE layer forward on the prefill-shaped workload (8192 bf16 tokens, 128 experts, top-8,
-hidden 2048, intermediate 768, MXFP4 weights): activation split, routing, pair sort, first grouped
+hidden 2048, intermediate 768, MXFP4 weights): activation split and routing, pair sort, first grouped
 GEMM + SwiGLU, second grouped GEMM + weighted combine, bf16 output.  `value` is algorithmic TFLOP/s
 of that layer (2 * T * k * 3 * H * I flops per step).
 
@@ -47,9 +47,9 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 PEAK_FP4_TFLOPS = 10100.0  # MI355X dense MXFP4 / MXFP6 MFMA
 ACT_TERMS = 3              # bf16 activations enter the MFMA as three block-scaled terms
 # the forward's stages as the library's events bracket them, and the kernels each stage launches
-STAGES = ["act_split", "route", "pair_sort", "gemm1_swiglu", "gemm2_weighted", "combine"]
-STAGE_KERNELS = ["xprep_kernel", "route_kernel", "place_kernel", "grouped_gemm_kernel<G1=true>",
-                 "grouped_gemm_kernel<G1=false>", "combine_kernel"]
+STAGES = ["split_and_route", "pair_sort", "gemm1_swiglu", "gemm2_weighted", "combine"]
+STAGE_KERNELS = ["front_kernel", "place_kernel", "grouped_gemm_kernel<G1=true>", "grouped_gemm_kernel<G1=false>",
+                 "combine_kernel"]
 DTYPE = ("mxfp4 (e2m1 + e8m0) weights x bf16 activations split into three block-scaled terms "
          "(e2m3, e2m3, e2m1) on scaled MFMA, fp32 accumulate, bf16 out")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_per_kernel.txt")
@@ -535,7 +535,7 @@ def main():
     P = cfg.T * cfg.k
     g1_flops = 2.0 * P * cfg.H * 2 * cfg.I
     g2_flops = 2.0 * P * cfg.I * cfg.H
-    g1_ms, g2_ms = stages[3], stages[4]
+    g1_ms, g2_ms = stages[STAGES.index("gemm1_swiglu")], stages[STAGES.index("gemm2_weighted")]
     # the dominant kernel: algorithmic flops of the first GEMM per launch over its measured launch time
     # (HIP events the library records on its own stream around the launch).  The MFMA issues every
     # product once per activation term, so the matrix cores execute three times the algorithmic flops.

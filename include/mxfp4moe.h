@@ -224,8 +224,9 @@ int moe_mxfp4_forward_act(const mxfp4_moe_dims* d, int32_t act_format, const voi
 
 /* Same as moe_mxfp4_forward_act, and records events[i] (hipEvent_t passed as void*, created by the caller)
  * on `stream` at stage boundaries: events[0] before the first launch, then after each stage in the
- * order activation split, routing, pair placement/tile schedule, first GEMM (+SwiGLU), second GEMM
- * (weighted rows), combine (bf16 output) -- 7 events in all.  Only the first n_events are recorded.
+ * order activation split and routing (one launch), pair placement/tile schedule, first GEMM (+SwiGLU),
+ * second GEMM (weighted rows), combine (bf16 output) -- 6 events in all.  Only the first n_events are
+ * recorded.
  * For per-stage timing (measurement); the computation is identical. */
 int moe_mxfp4_forward_profiled(const mxfp4_moe_dims* d, int32_t act_format, const void* packed_gfx950,
                                const void* x_bf16, int64_t T, int64_t ldx, const float* router_logits, int32_t top_k,

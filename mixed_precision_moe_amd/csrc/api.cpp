@@ -327,7 +327,6 @@ MX_API int moe_mxfp4_route(const float* router_logits, int64_t T, int32_t E, int
   if (workspace_bytes < w.total) return MXFP4_ERR_WORKSPACE;
   uint8_t* ws = (uint8_t*)workspace;
   int32_t* blkcnt = (int32_t*)(ws + w.blkcnt);
-  if ((st = launch_zero_i32(blkcnt, cdiv(T, kRouteTokens) * E, S(stream)))) return st;
   if ((st = launch_route(router_logits, T, E, top_k, renormalize, topk_ids, topk_w, blkcnt, S(stream)))) return st;
   return launch_place(topk_ids, topk_w, blkcnt, T, top_k, E, 32, 32, expert_offsets, (int32_t*)(ws + w.poffsets),
                       sorted_pairs, (int32_t*)(ws + w.prow_pair), (int32_t*)(ws + w.prow_tok), (float*)(ws + w.prow_w),
@@ -375,10 +374,8 @@ int forward_impl(const mxfp4_moe_dims* d, int32_t act_format, const void* packed
     return MXFP4_OK;
   };
   if ((st = mark())) return st;
-  if ((st = launch_xprep(act_format, x_bf16, T, ldx, g, ws + w.xq, (int32_t*)(ws + w.blkcnt), cdiv(T, kRouteTokens) * g.E, s)) ||
-      (st = mark()))
-    return st;
-  if ((st = launch_route(router_logits, T, (int)g.E, top_k, renormalize, ids, wts, (int32_t*)(ws + w.blkcnt), s)) ||
+  if ((st = launch_front(act_format, x_bf16, T, ldx, g, ws + w.xq, router_logits, (int)g.E, top_k, renormalize, ids,
+                          wts, (int32_t*)(ws + w.blkcnt), s)) ||
       (st = mark()))
     return st;
   if ((st = launch_place(ids, wts, (int32_t*)(ws + w.blkcnt), T, top_k, (int)g.E, 32 * NRG1, 32 * NRG2,

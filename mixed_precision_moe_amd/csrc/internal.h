@@ -19,9 +19,10 @@ int launch_unpack_gfx950(const MoeGeom& g, const BlobOffsets& o, bool bias, cons
 int launch_repack_standard(const MoeGeom& g, bool bias, const void* w13_q, const void* w13_s, const void* w2_q,
                            const void* w2_s, const void* b13, const void* b2, int bias_is_fp32, bool swap, bool tiled,
                            const size_t off[6], void* out, hipStream_t stream);
-int launch_xprep(int af, const void* x, int64_t T, int64_t ldx, const MoeGeom& g, void* xq, int32_t* zero,
-                 int64_t nzero, hipStream_t stream);
-int launch_zero_i32(int32_t* p, int64_t n, hipStream_t stream);
+// The activation split of x into xq (format af) and the routing (ids, weights, per-block expert
+// histograms) in one launch.
+int launch_front(int af, const void* x, int64_t T, int64_t ldx, const MoeGeom& g, void* xq, const float* logits, int E,
+                 int k, int renormalize, int32_t* ids, float* w, int32_t* blkcnt, hipStream_t stream);
 int launch_route(const float* logits, int64_t T, int E, int k, int renormalize, int32_t* ids, float* w,
                  int32_t* blkcnt, hipStream_t stream);
 int launch_place(const int32_t* ids, const float* w, int32_t* blkcnt, int64_t T, int k, int E, int BM, int BM2,

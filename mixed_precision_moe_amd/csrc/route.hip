@@ -4,18 +4,18 @@
 // [DEF: top-k routing of softmax(router logits) renormalized over the selected experts; the router
 //  sort/permute/gather step]
 //
-// Routing runs in two launches: route_kernel (top-k per token, counted into a per-block expert
-// histogram of kRouteTokens tokens) and place_kernel (per block of tokens: prefix sums over blocks and
-// experts from the histogram, the block's pairs ranked per expert in token order and written to their
-// rows; the first workgroup also writes the expert offsets, the padded row offsets, the M-tile list and
-// the padding rows).  The resulting order is stable: pairs of one expert appear in increasing token
-// order.
+// The forward pass runs the front in two launches: front_kernel (the activation split and the routing
+// side by side: the first workgroups route one block of kRouteTokens tokens each -- top-k per token,
+// the block's expert histogram counted in LDS and written whole -- and the others split the
+// activations) and place_kernel (per block of tokens: prefix sums over blocks and experts from the
+// histograms, the block's pairs ranked per expert in token order and written to their rows; the first
+// workgroup also writes the expert offsets, the padded row offsets, the M-tile lists and the padding
+// rows).  The resulting order is stable: pairs of one expert appear in increasing token order.  The
+// routing-only entry point launches the routing workgroups alone (route_kernel).
 #include "common.h"
 #include "internal.h"
 
 namespace {
-
-#define GRID_STRIDE(i, n) for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < (n); i += (int64_t)gridDim.x * blockDim.x)
 
 // x [T, ldx] bf16 -> xq: per 32-element block the terms of activation format AF (layout.h), each the
 // current remainder quantized with its own E8M0 scale:
@@ -25,26 +25,23 @@ namespace {
 //             bf16 value after its rounding to a coarser grid is again exact in bf16.
 //   kActMxfp8: one E4M3 term, scale rule for E4M3 (no saturation)
 //   kActMxfp4: one E2M1 term, the weights' rule
-// K is padded to a multiple of 64 with zero blocks.  Also clears `zero` (nzero ints).
+// K is padded to a multiple of 64 with zero blocks.
 //
 // A wave handles 64 consecutive blocks (block gi = token * nblk + b), lane l computing block l.  Its
 // global accesses are staged through LDS so that every load and store instruction covers 1 KB of
 // consecutive bytes: 16-byte chunk c = 64 j + l of the wave's 4 KB of x is loaded by lane l in load j and
 // written to LDS, lane l then reads its block's four chunks; lane l writes its slot and scale dword into
 // record l / 2 (blocks 2r and 2r + 1 form the K-step record r), and the wave's 32 records (consecutive
-// in xq) leave as 1 KB stores.
+// in xq) leave as 1 KB stores.  Wave slot wv0 of nw (the wave's own LDS stage_in / stage_out) takes
+// the wave indices wv0, wv0 + nw, ...
 template <int AF>
-__global__ __launch_bounds__(256) void xprep_kernel(const uint16_t* __restrict__ x, int64_t ldx, int64_t H, int64_t nblk,
-                                                    uint8_t* __restrict__ xq, int32_t* __restrict__ zero,
-                                                    int64_t nzero, int64_t n) {
+MX_DEV void xprep_waves(const uint16_t* __restrict__ x, int64_t ldx, int64_t H, int64_t nblk, uint8_t* __restrict__ xq,
+                        int64_t n, int64_t wv0, int64_t nw, uint8_t* stage_in, uint8_t* stage_out) {
   constexpr int SLOT = act_slot(AF), REC = act_rec(AF);
-  __shared__ __attribute__((aligned(16))) uint8_t stage_in[4][4096];
-  __shared__ __attribute__((aligned(16))) uint8_t stage_out[4][32 * REC];
-  GRID_STRIDE(i, nzero) zero[i] = 0;  // the routing histogram, cleared for the next launch
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   const int64_t hb = H / 32;  // real blocks per token
   const int64_t nwaves = (n + 63) / 64;
-  for (int64_t wv = (int64_t)blockIdx.x * 4 + wave; wv < nwaves; wv += (int64_t)gridDim.x * 4) {
+  for (int64_t wv = wv0; wv < nwaves; wv += nw) {
     const int64_t g0 = wv * 64;
     // coalesced loads: chunk c = 64 j + lane is part c % 4 of block c / 4
 #pragma unroll
@@ -55,13 +52,13 @@ __global__ __launch_bounds__(256) void xprep_kernel(const uint16_t* __restrict__
       u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
       if (gi < n && b < hb)
         v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(x + t * ldx + b * 32 + (c % 4) * 8));
-      *reinterpret_cast<u32x4_t*>(&stage_in[wave][c * 16]) = v;
+      *reinterpret_cast<u32x4_t*>(&stage_in[c * 16]) = v;
     }
     __builtin_amdgcn_wave_barrier();  // the wave's LDS writes before its reads (single wave, in order)
     uint32_t w[16];
 #pragma unroll
     for (int p = 0; p < 4; p++) {
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&stage_in[wave][lane * 64 + p * 16]);
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&stage_in[lane * 64 + p * 16]);
       w[4 * p] = v[0]; w[4 * p + 1] = v[1]; w[4 * p + 2] = v[2]; w[4 * p + 3] = v[3];
     }
     uint32_t slot[SLOT / 4];
@@ -90,7 +87,7 @@ __global__ __launch_bounds__(256) void xprep_kernel(const uint16_t* __restrict__
       fp4_from_bf16(w, e8m0_as_scale_operand(e), slot);
       scales = e;
     }
-    uint8_t* rec = &stage_out[wave][(lane >> 1) * REC];
+    uint8_t* rec = &stage_out[(lane >> 1) * REC];
     u32x4_t* sl = reinterpret_cast<u32x4_t*>(rec + (lane & 1) * SLOT);
     static_assert(SLOT % 16 == 0, "whole 16-byte stores");
 #pragma unroll
@@ -107,7 +104,7 @@ __global__ __launch_bounds__(256) void xprep_kernel(const uint16_t* __restrict__
     for (int j = 0; j < (2 * REC + 63) / 64; j++) {
       const int c = 64 * j + lane;
       if (c < 2 * REC && 2 * (r0 + (c * 16) / REC) < n)
-        *reinterpret_cast<u32x4_t*>(xq + r0 * REC + c * 16) = *reinterpret_cast<const u32x4_t*>(&stage_out[wave][c * 16]);
+        *reinterpret_cast<u32x4_t*>(xq + r0 * REC + c * 16) = *reinterpret_cast<const u32x4_t*>(&stage_out[c * 16]);
     }
     __builtin_amdgcn_wave_barrier();  // the next iteration's LDS writes after these reads
   }
@@ -144,66 +141,234 @@ MX_DEV float wave_sum_f32(float v) {
   return r;
 }
 
-// One wave per token: k rounds of a wave-wide maximum of the logit keys, the winner being the lowest
-// expert index holding that key (a ballot per lane slot), so equal logits go to the lower expert
-// index; the winner's logit is read back from its key.
-// Softmax weights of the selected experts (renormalized over them, or over all experts).  Each pair
-// also counts into blkcnt[token / kRouteTokens][expert] (zeroed beforehand), the per-block histogram of
-// the counting sort.  NPL logits per lane (E <= 64 * NPL).
-template <int NPL>
-__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int64_t T, int E, int k,
-                                                    int renormalize, int32_t* __restrict__ ids, float* __restrict__ wts,
-                                                    int32_t* __restrict__ blkcnt) {
+// Routing of NT tokens by one wave, their selections interleaved (independent chains): k rounds of a
+// wave-wide maximum of the logit keys, the winner being the lowest expert index holding that key (a
+// ballot per lane slot), so equal logits go to the lower expert index; the winner's logit is read back
+// from its key.  Softmax weights of the selected experts (renormalized over them, or over all experts).
+// For token i, lane j < k returns pair j's expert and weight.  NPL logits per lane (E <= 64 * NPL).
+template <int NPL, int NT>
+MX_DEV void route_tokens(const float (&val)[NT][NPL], int E, int k, int renormalize, int (&my_id)[NT],
+                         float (&my_w)[NT]) {
   const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;  // uniform per wave
-  float val[NPL];
-  uint32_t key[NPL];  // 0 = absent or already selected (no logit maps to 0)
+  uint32_t key[NT][NPL];  // 0 = absent or already selected (no logit maps to 0)
+  float my_l[NT], lmax[NT];
 #pragma unroll
-  for (int j = 0; j < NPL; j++) {
-    const int idx = lane + 64 * j;
-    val[j] = idx < E ? logits[t * E + idx] : 0.f;
-    key[j] = idx < E ? logit_key(val[j]) : 0u;
+  for (int i = 0; i < NT; i++) {
+#pragma unroll
+    for (int j = 0; j < NPL; j++) key[i][j] = lane + 64 * j < E ? logit_key(val[i][j]) : 0u;
+    my_id[i] = 0;
+    my_l[i] = 0.f;
+    lmax[i] = 0.f;
   }
-  int my_id = 0;
+  for (int r = 0; r < k; r++) {
+    uint32_t best[NT];
+#pragma unroll
+    for (int i = 0; i < NT; i++) {
+      best[i] = 0;
+#pragma unroll
+      for (int j = 0; j < NPL; j++) best[i] = max(best[i], key[i][j]);
+    }
+#pragma unroll
+    for (int i = 0; i < NT; i++) best[i] = wave_max_u32(best[i]);
+#pragma unroll
+    for (int i = 0; i < NT; i++) {
+      int id = -1;
+#pragma unroll
+      for (int j = 0; j < NPL; j++) {
+        const uint64_t hit = __ballot(key[i][j] == best[i]);
+        if (id < 0 && hit != 0) id = 64 * j + __ffsll((unsigned long long)hit) - 1;
+      }
+      const float wl = key_logit(best[i]);
+#pragma unroll
+      for (int j = 0; j < NPL; j++)
+        if (lane + 64 * j == id) key[i][j] = 0;
+      if (r == 0) lmax[i] = wl;
+      if (lane == r) {
+        my_id[i] = id;
+        my_l[i] = wl;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NT; i++) {
+    const float ex = lane < k ? __expf(my_l[i] - lmax[i]) : 0.f;
+    float den;
+    if (renormalize) {
+      den = wave_sum_f32(ex);
+    } else {
+      float part = 0.f;
+#pragma unroll
+      for (int j = 0; j < NPL; j++)
+        if (lane + 64 * j < E) part += __expf(val[i][j] - lmax[i]);
+      den = wave_sum_f32(part);
+    }
+    my_w[i] = ex / den;
+  }
+}
+
+// Reductions over each row of 16 lanes (DPP: quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_ror:4,
+// row_ror:8); every lane of a row gets its row's result.
+MX_DEV uint32_t row_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));
+  return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));
+}
+MX_DEV float row_sum_f32(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+}
+
+// Routing of four tokens per wave, one per row of 16 lanes (E <= 16 * NPR, k <= 16): the same
+// selection as route_tokens with row-wide reductions -- lane q of a row holds experts q + 16 j, so the
+// first j whose row ballot hits gives the lowest expert index holding the maximum.  For the row's
+// token, lane q < k returns pair q's expert and weight.
+template <int NPR>
+MX_DEV void route_rows(const float* val, int E, int k, int renormalize, int& my_id, float& my_w) {
+  const int lane = threadIdx.x & 63, q = lane & 15, row = lane >> 4;
+  uint32_t key[NPR];
+#pragma unroll
+  for (int j = 0; j < NPR; j++) key[j] = q + 16 * j < E ? logit_key(val[j]) : 0u;
+  my_id = 0;
   float my_l = 0.f, lmax = 0.f;
   for (int r = 0; r < k; r++) {
     uint32_t best = 0;
 #pragma unroll
-    for (int j = 0; j < NPL; j++) best = max(best, key[j]);
-    best = wave_max_u32(best);
+    for (int j = 0; j < NPR; j++) best = max(best, key[j]);
+    best = row_max_u32(best);
     int id = -1;
 #pragma unroll
-    for (int j = 0; j < NPL; j++) {
-      const uint64_t hit = __ballot(key[j] == best);
-      if (id < 0 && hit != 0) id = 64 * j + __ffsll((unsigned long long)hit) - 1;
+    for (int j = 0; j < NPR; j++) {
+      const uint32_t hit = (uint32_t)(__ballot(key[j] == best) >> (16 * row)) & 0xFFFFu;
+      if (id < 0 && hit != 0) id = 16 * j + __ffs(hit) - 1;
     }
     const float wl = key_logit(best);
 #pragma unroll
-    for (int j = 0; j < NPL; j++)
-      if (lane + 64 * j == id) key[j] = 0;
+    for (int j = 0; j < NPR; j++)
+      if (q + 16 * j == id) key[j] = 0;
     if (r == 0) lmax = wl;
-    if (lane == r) {
+    if (q == r) {
       my_id = id;
       my_l = wl;
     }
   }
-  const float ex = lane < k ? __expf(my_l - lmax) : 0.f;
+  const float ex = q < k ? __expf(my_l - lmax) : 0.f;
   float den;
   if (renormalize) {
-    den = wave_sum_f32(ex);
+    den = row_sum_f32(ex);
   } else {
     float part = 0.f;
 #pragma unroll
-    for (int j = 0; j < NPL; j++)
-      if (lane + 64 * j < E) part += __expf(val[j] - lmax);
-    den = wave_sum_f32(part);
+    for (int j = 0; j < NPR; j++)
+      if (q + 16 * j < E) part += __expf(val[j] - lmax);
+    den = row_sum_f32(part);
   }
-  if (lane < k) {
-    ids[t * k + lane] = my_id;
-    wts[t * k + lane] = ex / den;
-    atomicAdd(&blkcnt[(t / kRouteTokens) * E + my_id], 1);
+  my_w = ex / den;
+}
+
+// Routing of token block blk (kRouteTokens tokens) by one workgroup of 1024 threads: wave w takes tokens
+// 4w .. 4w + 3 of the block -- one per row of 16 lanes up to 256 experts and top-16, else one after
+// another across the wave with their selections interleaved (two at a time past 512 experts, for
+// registers) -- counts each pair into the block's expert histogram in LDS (hist, >= E ints) and writes
+// ids and weights; the histogram is then written whole to blkcnt[blk][0 .. E), so nothing needs
+// clearing beforehand.
+constexpr int kRouteThreads = 1024;
+constexpr int kTokPerWave = kRouteTokens / (kRouteThreads / 64);  // 4
+static_assert(kTokPerWave == 4, "one token per row of 16 lanes");
+template <int NPL>
+MX_DEV void route_block(const float* __restrict__ logits, int64_t T, int E, int k, int renormalize,
+                        int32_t* __restrict__ ids, float* __restrict__ wts, int32_t* __restrict__ blkcnt, int64_t blk,
+                        int32_t* hist) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < E; e += kRouteThreads) hist[e] = 0;
+  __syncthreads();
+  const int64_t t0 = blk * kRouteTokens + wave * kTokPerWave;
+  if constexpr (NPL <= 4) {
+    if (k <= 16) {
+      constexpr int NPR = 4 * NPL;  // E <= 16 * NPR
+      const int q = lane & 15;
+      const int64_t t = t0 + (lane >> 4);
+      float val[NPR];
+#pragma unroll
+      for (int j = 0; j < NPR; j++) {
+        const int idx = q + 16 * j;
+        val[j] = t < T && idx < E ? logits[t * E + idx] : 0.f;
+      }
+      int my_id;
+      float my_w;
+      route_rows<NPR>(val, E, k, renormalize, my_id, my_w);
+      if (t < T && q < k) {
+        ids[t * k + q] = my_id;
+        wts[t * k + q] = my_w;
+        atomicAdd(&hist[my_id], 1);
+      }
+      __syncthreads();
+      for (int e = tid; e < E; e += kRouteThreads) blkcnt[blk * E + e] = hist[e];
+      return;
+    }
   }
+  constexpr int NT = NPL <= 8 ? kTokPerWave : 2;  // tokens routed together
+#pragma unroll
+  for (int i0 = 0; i0 < kTokPerWave; i0 += NT) {
+    if (t0 + i0 >= T) break;  // uniform per wave
+    float val[NT][NPL];
+#pragma unroll
+    for (int i = 0; i < NT; i++) {
+      const int64_t t = t0 + i0 + i;
+#pragma unroll
+      for (int j = 0; j < NPL; j++) {
+        const int idx = lane + 64 * j;
+        val[i][j] = t < T && idx < E ? logits[t * E + idx] : 0.f;
+      }
+    }
+    int my_id[NT];
+    float my_w[NT];
+    route_tokens<NPL, NT>(val, E, k, renormalize, my_id, my_w);
+#pragma unroll
+    for (int i = 0; i < NT; i++) {
+      const int64_t t = t0 + i0 + i;
+      if (t < T && lane < k) {
+        ids[t * k + lane] = my_id[i];
+        wts[t * k + lane] = my_w[i];
+        atomicAdd(&hist[my_id[i]], 1);
+      }
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kRouteThreads) blkcnt[blk * E + e] = hist[e];
+}
+
+template <int NPL>
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(const float* __restrict__ logits, int64_t T, int E, int k,
+                                                              int renormalize, int32_t* __restrict__ ids,
+                                                              float* __restrict__ wts, int32_t* __restrict__ blkcnt) {
+  __shared__ int32_t hist[1024];
+  route_block<NPL>(logits, T, E, k, renormalize, ids, wts, blkcnt, blockIdx.x, hist);
+}
+
+// The forward pass's front in one launch: workgroups 0 .. nroute - 1 route one token block each, the
+// others split the activations (16 waves each, with their own LDS staging; the routing histogram
+// reuses the same LDS).
+template <int AF, int NPL>
+__global__ __launch_bounds__(kRouteThreads) void front_kernel(const uint16_t* __restrict__ x, int64_t ldx, int64_t H,
+                                                              int64_t nblk, uint8_t* __restrict__ xq, int64_t n,
+                                                              const float* __restrict__ logits, int64_t T, int E, int k,
+                                                              int renormalize, int32_t* __restrict__ ids,
+                                                              float* __restrict__ wts, int32_t* __restrict__ blkcnt,
+                                                              int nroute) {
+  constexpr int REC = act_rec(AF), NW = kRouteThreads / 64;
+  constexpr int kIn = 4096, kOut = 32 * REC;
+  static_assert(NW * (kIn + kOut) >= 1024 * 4, "the histogram fits the staging LDS");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NW * (kIn + kOut)];
+  if ((int)blockIdx.x < nroute) {
+    route_block<NPL>(logits, T, E, k, renormalize, ids, wts, blkcnt, blockIdx.x, reinterpret_cast<int32_t*>(smem));
+    return;
+  }
+  const int wave = threadIdx.x >> 6;
+  xprep_waves<AF>(x, ldx, H, nblk, xq, n, (int64_t)(blockIdx.x - nroute) * NW + wave,
+                  (int64_t)(gridDim.x - nroute) * NW, smem + wave * kIn, smem + NW * kIn + wave * kOut);
 }
 
 // Pair placement, one workgroup of 1024 threads per block of kRouteTokens tokens.  blkcnt[b][e] holds
@@ -376,55 +541,57 @@ __global__ __launch_bounds__(1024) void place_kernel(const int32_t* __restrict__
   }
 }
 
-inline unsigned grid_for(int64_t n, int threads = 256) {
-  int64_t b = (n + threads - 1) / threads;
-  if (b > 65536) b = 65536;
-  if (b < 1) b = 1;
-  return (unsigned)b;
+// E <= 64 * NPL: the NPL of a routing instantiation, or 0 past 1024 experts
+inline int route_npl(int E) { return E <= 64 ? 1 : E <= 128 ? 2 : E <= 256 ? 4 : E <= 512 ? 8 : E <= 1024 ? 16 : 0; }
+
+template <int AF>
+void launch_front_af(const void* x, int64_t T, int64_t ldx, const MoeGeom& g, void* xq, const float* logits, int E,
+                     int k, int renormalize, int32_t* ids, float* w, int32_t* blkcnt, hipStream_t stream) {
+  const int64_t nblk = 2 * g.nkt1;
+  const int64_t n = T * nblk;
+  const int nroute = (int)cdiv(T, kRouteTokens);
+  int64_t nx = cdiv(cdiv(n, 64), kRouteThreads / 64);  // split workgroups: one wave per 64 blocks
+  if (nx > 65536) nx = 65536;
+  const dim3 grid((unsigned)(nroute + nx)), block(kRouteThreads);
+#define MX_FRONT(NPL)                                                                                                   \
+  hipLaunchKernelGGL((front_kernel<AF, NPL>), grid, block, 0, stream, (const uint16_t*)x, ldx, g.H, nblk, (uint8_t*)xq, n, \
+                     logits, T, E, k, renormalize, ids, w, blkcnt, nroute)
+  switch (route_npl(E)) {
+    case 1: MX_FRONT(1); break;
+    case 2: MX_FRONT(2); break;
+    case 4: MX_FRONT(4); break;
+    case 8: MX_FRONT(8); break;
+    default: MX_FRONT(16); break;
+  }
+#undef MX_FRONT
 }
 
 }  // namespace
 
-int launch_xprep(int af, const void* x, int64_t T, int64_t ldx, const MoeGeom& g, void* xq, int32_t* zero,
-                 int64_t nzero, hipStream_t stream) {
-  const int64_t nblk = 2 * g.nkt1;
-  const int64_t n = T * nblk;
-  if (n > 0 || nzero > 0) {
-    const dim3 grid(grid_for(n > nzero ? n : nzero)), block(256);
+int launch_front(int af, const void* x, int64_t T, int64_t ldx, const MoeGeom& g, void* xq, const float* logits, int E,
+                 int k, int renormalize, int32_t* ids, float* w, int32_t* blkcnt, hipStream_t stream) {
+  if (T > 0) {
     if (af == kActMxfp8)
-      hipLaunchKernelGGL(xprep_kernel<kActMxfp8>, grid, block, 0, stream, (const uint16_t*)x, ldx, g.H, nblk,
-                         (uint8_t*)xq, zero, nzero, n);
+      launch_front_af<kActMxfp8>(x, T, ldx, g, xq, logits, E, k, renormalize, ids, w, blkcnt, stream);
     else if (af == kActMxfp4)
-      hipLaunchKernelGGL(xprep_kernel<kActMxfp4>, grid, block, 0, stream, (const uint16_t*)x, ldx, g.H, nblk,
-                         (uint8_t*)xq, zero, nzero, n);
+      launch_front_af<kActMxfp4>(x, T, ldx, g, xq, logits, E, k, renormalize, ids, w, blkcnt, stream);
     else
-      hipLaunchKernelGGL(xprep_kernel<kActBf16>, grid, block, 0, stream, (const uint16_t*)x, ldx, g.H, nblk,
-                         (uint8_t*)xq, zero, nzero, n);
+      launch_front_af<kActBf16>(x, T, ldx, g, xq, logits, E, k, renormalize, ids, w, blkcnt, stream);
   }
-  return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
-}
-
-__global__ void zero_i32_kernel(int32_t* p, int64_t n) { GRID_STRIDE(i, n) p[i] = 0; }
-
-int launch_zero_i32(int32_t* p, int64_t n, hipStream_t stream) {
-  if (n > 0) hipLaunchKernelGGL(zero_i32_kernel, dim3(grid_for(n)), dim3(256), 0, stream, p, n);
   return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
 }
 
 int launch_route(const float* logits, int64_t T, int E, int k, int renormalize, int32_t* ids, float* w,
                  int32_t* blkcnt, hipStream_t stream) {
-  const dim3 grid((unsigned)cdiv(T, 4)), block(256);
+  const dim3 grid((unsigned)cdiv(T, kRouteTokens)), block(kRouteThreads);
   if (T > 0) {
-    if (E <= 64)
-      hipLaunchKernelGGL(route_kernel<1>, grid, block, 0, stream, logits, T, E, k, renormalize, ids, w, blkcnt);
-    else if (E <= 128)
-      hipLaunchKernelGGL(route_kernel<2>, grid, block, 0, stream, logits, T, E, k, renormalize, ids, w, blkcnt);
-    else if (E <= 256)
-      hipLaunchKernelGGL(route_kernel<4>, grid, block, 0, stream, logits, T, E, k, renormalize, ids, w, blkcnt);
-    else if (E <= 512)
-      hipLaunchKernelGGL(route_kernel<8>, grid, block, 0, stream, logits, T, E, k, renormalize, ids, w, blkcnt);
-    else
-      hipLaunchKernelGGL(route_kernel<16>, grid, block, 0, stream, logits, T, E, k, renormalize, ids, w, blkcnt);
+    switch (route_npl(E)) {
+      case 1: hipLaunchKernelGGL(route_kernel<1>, grid, block, 0, stream, logits, T, E, k, renormalize, ids, w, blkcnt); break;
+      case 2: hipLaunchKernelGGL(route_kernel<2>, grid, block, 0, stream, logits, T, E, k, renormalize, ids, w, blkcnt); break;
+      case 4: hipLaunchKernelGGL(route_kernel<4>, grid, block, 0, stream, logits, T, E, k, renormalize, ids, w, blkcnt); break;
+      case 8: hipLaunchKernelGGL(route_kernel<8>, grid, block, 0, stream, logits, T, E, k, renormalize, ids, w, blkcnt); break;
+      default: hipLaunchKernelGGL(route_kernel<16>, grid, block, 0, stream, logits, T, E, k, renormalize, ids, w, blkcnt); break;
+    }
   }
   return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
 }

@@ -217,11 +217,12 @@ static void test_route() {
   CHECK(moe_mxfp4_route(lg, T, E, k, 1, ids, w, offs, nullptr, ws, n, nullptr) == MXFP4_ERR_NULL);
   g_calls.clear();
   CHECK(moe_mxfp4_route(lg, T, E, k, 1, ids, w, offs, sp, ws, n, nullptr) == MXFP4_OK);
-  CHECK((names() == std::vector<std::string>{"zero", "route", "place"}));
-  // every table the launches use lies inside the workspace
-  const Call& z = g_calls[0];
-  CHECK(inside(z.p[0], 4 * z.i[0], ws, n));
-  const Call& pl = g_calls[2];
+  CHECK((names() == std::vector<std::string>{"route", "place"}));
+  // every table the launches use lies inside the workspace; the routing writes the histograms the
+  // placement reads
+  const Call& rt = g_calls[0];
+  const Call& pl = g_calls[1];
+  CHECK(rt.p[3] == pl.p[0] && rt.i[0] == T && rt.i[1] == E && rt.i[2] == k);
   const int64_t nrows = ((T * k + 31 * E + 31) / 32) * 32 + 128;
   CHECK(inside(pl.p[0], 4 * cdiv(T, kRouteTokens) * E, ws, n));
   CHECK(inside(pl.p[2], 4 * (E + 1), ws, n));
@@ -236,13 +237,15 @@ static void check_forward_layout(const mxfp4_moe_dims& d, int64_t T, int k, size
   const FwdWs w = fwd_ws(g, T, k);
   const BlobOffsets o = blob_offsets(g, d.has_bias);
   CHECK(w.total <= nws);
-  CHECK((names() == std::vector<std::string>{"xprep", "route", "place", "gemm1", "gemm2", "combine"}));
-  if (g_calls.size() != 6) return;
-  const Call& xp = g_calls[0];
-  CHECK(inside(xp.p[1], (size_t)T * g.nkt1 * kMaxRec, ws, nws));
-  CHECK(inside(xp.p[2], 4 * xp.i[2], ws, nws));
-  const GemmArgs& a1 = g_calls[3].gemm;
-  const GemmArgs& a2 = g_calls[4].gemm;
+  CHECK((names() == std::vector<std::string>{"front", "place", "gemm1", "gemm2", "combine"}));
+  if (g_calls.size() != 5) return;
+  const Call& fr = g_calls[0];
+  CHECK(inside(fr.p[1], (size_t)T * g.nkt1 * kMaxRec, ws, nws));
+  CHECK(inside(fr.p[2], 4 * (size_t)((T + kRouteTokens - 1) / kRouteTokens) * fr.i[2], ws, nws));
+  CHECK(fr.i[2] == d.E && fr.i[4] == k && fr.p[2] == g_calls[1].p[0]);
+  CHECK(inside(fr.p[4], 4 * (size_t)T * k, ws, nws) && inside(fr.p[5], 4 * (size_t)T * k, ws, nws));
+  const GemmArgs& a1 = g_calls[2].gemm;
+  const GemmArgs& a2 = g_calls[3].gemm;
   CHECK(inside(a1.wq, (size_t)g.E * g.ncb1 * g.nkt1 * kCB * 1024, blob, o.total));
   CHECK(inside(a1.ws, (size_t)g.E * g.ncb1 * g.nkt1 * 1024, blob, o.total));
   CHECK(inside(a2.wq, (size_t)g.E * g.ncb2 * g.nkt2 * kCB * 1024, blob, o.total));
@@ -266,7 +269,7 @@ static void check_forward_layout(const mxfp4_moe_dims& d, int64_t T, int k, size
   CHECK(inside(a2.o16, (size_t)w.nrows_alloc * g.H * 2, ws, nws));
   CHECK(inside(a2.osc, (size_t)w.nrows_alloc * (g.H / 16), ws, nws));
   CHECK(a1.nkt == g.nkt1 && a2.nkt == g.nkt2 && a1.ncb == g.ncb1 && a2.ncb == g.ncb2);
-  const Call& cb = g_calls[5];
+  const Call& cb = g_calls[4];
   CHECK(cb.p[0] == a2.o16 && cb.p[1] == a2.osc && cb.i[0] == T && cb.i[2] == k);
   CHECK(inside(cb.p[2], 4 * T * k, ws, nws));
 }
@@ -300,12 +303,12 @@ static void test_forward() {
     CHECK(moe_mxfp4_forward(&c.d, blob, x, c.T, c.d.H, lg, c.k + 33, 1, y, nullptr, nullptr, ws, nws, nullptr) ==
           MXFP4_ERR_SHAPE);
     CHECK(g_calls.empty());
-    // profiled: one event per stage boundary (7), fewer when fewer are given
+    // profiled: one event per stage boundary (6), fewer when fewer are given
     g_events = 0;
-    void* evs[7] = {fake(), fake(), fake(), fake(), fake(), fake(), fake()};
+    void* evs[6] = {fake(), fake(), fake(), fake(), fake(), fake()};
     CHECK(moe_mxfp4_forward_profiled(&c.d, 0, blob, x, c.T, c.d.H, lg, c.k, 1, y, nullptr, nullptr, ws, nws, nullptr,
-                                     evs, 7) == MXFP4_OK);
-    CHECK(g_events == 7);
+                                     evs, 6) == MXFP4_OK);
+    CHECK(g_events == 6);
     g_events = 0;
     CHECK(moe_mxfp4_forward_profiled(&c.d, 0, blob, x, c.T, c.d.H, lg, c.k, 1, y, nullptr, nullptr, ws, nws, nullptr,
                                      evs, 3) == MXFP4_OK);
@@ -319,7 +322,7 @@ static void test_forward() {
       CHECK(moe_mxfp4_forward_act(&c.d, af, blob, x, c.T, c.d.H, lg, c.k, 1, y, nullptr, nullptr, ws, nws, nullptr) ==
             MXFP4_OK);
       check_forward_layout(c.d, c.T, c.k, nws, ws, blob);
-      if (g_calls.size() == 6) CHECK(g_calls[0].i[3] == af && g_calls[3].i[2] == af && g_calls[4].i[2] == af);
+      if (g_calls.size() == 5) CHECK(g_calls[0].i[3] == af && g_calls[2].i[2] == af && g_calls[3].i[2] == af);
     }
     g_calls.clear();
     CHECK(moe_mxfp4_forward_act(&c.d, 3, blob, x, c.T, c.d.H, lg, c.k, 1, y, nullptr, nullptr, ws, nws, nullptr) ==

@@ -62,16 +62,12 @@ int launch_linear_prep(const void* x, int64_t M, int64_t ldx, const MoeGeom&, co
   c.p[0] = x; c.p[1] = ws; c.i[0] = M; c.i[1] = ldx; c.i[2] = (int64_t)w.total;
   return rec("linear_prep", c);
 }
-int launch_xprep(int af, const void* x, int64_t T, int64_t ldx, const MoeGeom&, void* xq, int32_t* zero,
-                 int64_t nzero, hipStream_t) {
+int launch_front(int af, const void* x, int64_t T, int64_t ldx, const MoeGeom&, void* xq, const float* logits, int E,
+                 int k, int, int32_t* ids, float* w, int32_t* blkcnt, hipStream_t) {
   Call c;
-  c.p[0] = x; c.p[1] = xq; c.p[2] = zero; c.i[0] = T; c.i[1] = ldx; c.i[2] = nzero; c.i[3] = af;
-  return rec("xprep", c);
-}
-int launch_zero_i32(int32_t* p, int64_t n, hipStream_t) {
-  Call c;
-  c.p[0] = p; c.i[0] = n;
-  return rec("zero", c);
+  c.p[0] = x; c.p[1] = xq; c.p[2] = blkcnt; c.p[3] = logits; c.p[4] = ids; c.p[5] = w;
+  c.i[0] = T; c.i[1] = ldx; c.i[2] = E; c.i[3] = af; c.i[4] = k;
+  return rec("front", c);
 }
 int launch_route(const float* logits, int64_t T, int E, int k, int, int32_t* ids, float* w, int32_t* blkcnt,
                  hipStream_t) {
