@@ -79,7 +79,7 @@ int choose_nrg2(int64_t P, int64_t E, int32_t act) {
 }
 
 struct RouteWs {
-  uint64_t blkcnt, poffsets, prow_pair, prow_tok, prow_w, tiles, ntiles, total;
+  uint64_t blkcnt, rank, poffsets, prow_pair, prow_tok, prow_w, tiles, ntiles, total;
   int64_t max_tiles;
 };
 
@@ -91,6 +91,7 @@ RouteWs route_ws(int64_t T, int64_t E, int64_t k) {
   uint64_t p = 0;
   auto take = [&](uint64_t bytes) { uint64_t o = p; p = align256((int64_t)(p + bytes)); return o; };
   w.blkcnt = take(4 * cdiv(T, kRouteTokens) * E + 4);
+  w.rank = take(4 * P + 4);
   w.poffsets = take(4 * (E + 1));
   w.prow_pair = take(4 * nrows);
   w.prow_tok = take(4 * nrows);
@@ -327,8 +328,9 @@ MX_API int moe_mxfp4_route(const float* router_logits, int64_t T, int32_t E, int
   if (workspace_bytes < w.total) return MXFP4_ERR_WORKSPACE;
   uint8_t* ws = (uint8_t*)workspace;
   int32_t* blkcnt = (int32_t*)(ws + w.blkcnt);
-  if ((st = launch_route(router_logits, T, E, top_k, renormalize, topk_ids, topk_w, blkcnt, S(stream)))) return st;
-  return launch_place(topk_ids, topk_w, blkcnt, T, top_k, E, 32, 32, expert_offsets, (int32_t*)(ws + w.poffsets),
+  int32_t* rank = (int32_t*)(ws + w.rank);
+  if ((st = launch_route(router_logits, T, E, top_k, renormalize, topk_ids, topk_w, blkcnt, rank, S(stream)))) return st;
+  return launch_place(topk_ids, topk_w, blkcnt, rank, T, top_k, E, 32, 32, expert_offsets, (int32_t*)(ws + w.poffsets),
                       sorted_pairs, (int32_t*)(ws + w.prow_pair), (int32_t*)(ws + w.prow_tok), (float*)(ws + w.prow_w),
                       nullptr, ws + w.tiles, (int32_t*)(ws + w.ntiles), nullptr, nullptr, S(stream));
 }
@@ -374,13 +376,15 @@ int forward_impl(const mxfp4_moe_dims* d, int32_t act_format, const void* packed
     return MXFP4_OK;
   };
   if ((st = mark())) return st;
+  // the pairs' in-block ranks go to pair_prow, which the placement overwrites with their rows
+  int32_t* pair_prow = (int32_t*)(ws + w.pair_prow);
   if ((st = launch_front(act_format, x_bf16, T, ldx, g, ws + w.xq, router_logits, (int)g.E, top_k, renormalize, ids,
-                          wts, (int32_t*)(ws + w.blkcnt), s)) ||
+                          wts, (int32_t*)(ws + w.blkcnt), pair_prow, s)) ||
       (st = mark()))
     return st;
-  if ((st = launch_place(ids, wts, (int32_t*)(ws + w.blkcnt), T, top_k, (int)g.E, 32 * NRG1, 32 * NRG2,
+  if ((st = launch_place(ids, wts, (int32_t*)(ws + w.blkcnt), pair_prow, T, top_k, (int)g.E, 32 * NRG1, 32 * NRG2,
                          (int32_t*)(ws + w.offsets), (int32_t*)(ws + w.poffsets), nullptr, (int32_t*)(ws + w.prow_pair),
-                         (int32_t*)(ws + w.prow_tok), (float*)(ws + w.prow_w), (int32_t*)(ws + w.pair_prow),
+                         (int32_t*)(ws + w.prow_tok), (float*)(ws + w.prow_w), pair_prow,
                          ws + w.tiles, (int32_t*)(ws + w.ntiles), ws + w.tiles2, (int32_t*)(ws + w.ntiles2), s)) ||
       (st = mark()))
     return st;

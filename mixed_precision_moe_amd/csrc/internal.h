@@ -20,15 +20,16 @@ int launch_repack_standard(const MoeGeom& g, bool bias, const void* w13_q, const
                            const void* w2_s, const void* b13, const void* b2, int bias_is_fp32, bool swap, bool tiled,
                            const size_t off[6], void* out, hipStream_t stream);
 // The activation split of x into xq (format af) and the routing (ids, weights, per-block expert
-// histograms) in one launch.
+// histograms, each pair's rank within its block and expert) in one launch.
 int launch_front(int af, const void* x, int64_t T, int64_t ldx, const MoeGeom& g, void* xq, const float* logits, int E,
-                 int k, int renormalize, int32_t* ids, float* w, int32_t* blkcnt, hipStream_t stream);
+                 int k, int renormalize, int32_t* ids, float* w, int32_t* blkcnt, int32_t* rank, hipStream_t stream);
 int launch_route(const float* logits, int64_t T, int E, int k, int renormalize, int32_t* ids, float* w,
-                 int32_t* blkcnt, hipStream_t stream);
-int launch_place(const int32_t* ids, const float* w, int32_t* blkcnt, int64_t T, int k, int E, int BM, int BM2,
-                 int32_t* offsets, int32_t* poffsets, int32_t* sorted_pairs, int32_t* prow_pair, int32_t* prow_tok,
-                 float* prow_w, int32_t* pair_prow, void* tiles, int32_t* ntiles, void* tiles2, int32_t* ntiles2,
-                 hipStream_t stream);
+                 int32_t* blkcnt, int32_t* rank, hipStream_t stream);
+// pair_prow may be the rank array itself.
+int launch_place(const int32_t* ids, const float* w, int32_t* blkcnt, const int32_t* rank, int64_t T, int k, int E,
+                 int BM, int BM2, int32_t* offsets, int32_t* poffsets, int32_t* sorted_pairs, int32_t* prow_pair,
+                 int32_t* prow_tok, float* prow_w, int32_t* pair_prow, void* tiles, int32_t* ntiles, void* tiles2,
+                 int32_t* ntiles2, hipStream_t stream);
 int launch_gemm1(int af, int NRG, const GemmArgs& a, int64_t max_tiles, hipStream_t stream);
 int launch_gemm2(int af, int NRG, const GemmArgs& a, int64_t max_tiles, hipStream_t stream);
 int launch_gemm1_mx(int af, int NRG, const GemmArgs& a, int64_t max_tiles, hipStream_t stream);

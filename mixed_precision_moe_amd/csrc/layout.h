@@ -155,7 +155,8 @@ static_assert(act_slot(kActMxfp8) == 32 && act_slot(kActMxfp4) == 16, "slot size
 //   (sized for the largest format; the other formats use the front of each buffer)
 //   tiles, tiles2: TileDesc (expert, first padded row, valid rows, 0) per M tile of the first and of the
 //         second GEMM (their tile heights may differ)
-//   pair_prow: [T*k] padded row of each (token, slot) pair
+//   pair_prow: [T*k] padded row of each (token, slot) pair (until the placement writes it: the pair's rank
+//            among its expert's pairs within its token block, from the routing)
 //   o16 : int16 [padded rows][H], row r = w * (expert output + b2) of the pair at row r, divided by
 //         the power of two 2^(osc - 127) of its block and rounded to an integer (|value| < 2^14)
 //   osc : [padded rows][H / 16] bytes, the block exponents: one per 16 consecutive columns of a row

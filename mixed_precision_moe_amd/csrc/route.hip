@@ -271,22 +271,44 @@ MX_DEV void route_rows(const float* val, int E, int k, int renormalize, int& my_
 // Routing of token block blk (kRouteTokens tokens) by one workgroup of 1024 threads: wave w takes tokens
 // 4w .. 4w + 3 of the block -- one per row of 16 lanes up to 256 experts and top-16, else one after
 // another across the wave with their selections interleaved (two at a time past 512 experts, for
-// registers) -- counts each pair into the block's expert histogram in LDS (hist, >= E ints) and writes
-// ids and weights; the histogram is then written whole to blkcnt[blk][0 .. E), so nothing needs
-// clearing beforehand.
+// registers) -- and writes ids and weights.  Each pair is counted into the block's expert histogram
+// in LDS and marks its token in the expert's 64-bit token mask; after a barrier each pair's rank among
+// the block's pairs of its expert (the earlier tokens in the mask: the sort is stable) goes to
+// rank[pair], and the histogram is written whole to blkcnt[blk][0 .. E), so nothing needs clearing
+// beforehand.  lds: 3 * E ints (histogram, mask low and high words).
 constexpr int kRouteThreads = 1024;
 constexpr int kTokPerWave = kRouteTokens / (kRouteThreads / 64);  // 4
-static_assert(kTokPerWave == 4, "one token per row of 16 lanes");
+static_assert(kTokPerWave == 4 && kRouteTokens == 64, "one token per row of 16 lanes; 64-bit token masks");
+constexpr int kRouteLdsInts = 3 * 1024;
 template <int NPL>
 MX_DEV void route_block(const float* __restrict__ logits, int64_t T, int E, int k, int renormalize,
-                        int32_t* __restrict__ ids, float* __restrict__ wts, int32_t* __restrict__ blkcnt, int64_t blk,
-                        int32_t* hist) {
+                        int32_t* __restrict__ ids, float* __restrict__ wts, int32_t* __restrict__ blkcnt,
+                        int32_t* __restrict__ rank, int64_t blk, int32_t* lds) {
+  int32_t* hist = lds;
+  uint32_t* mlo = reinterpret_cast<uint32_t*>(lds + E);
+  uint32_t* mhi = reinterpret_cast<uint32_t*>(lds + 2 * E);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int e = tid; e < E; e += kRouteThreads) hist[e] = 0;
+  for (int e = tid; e < E; e += kRouteThreads) {
+    hist[e] = 0;
+    mlo[e] = 0;
+    mhi[e] = 0;
+  }
   __syncthreads();
   const int64_t t0 = blk * kRouteTokens + wave * kTokPerWave;
-  if constexpr (NPL <= 4) {
+  // this lane's pairs: token (local index within the block) and expert, -1 where the lane holds none
+  constexpr bool ROWS = NPL <= 4;
+  int pl[kTokPerWave], pe[kTokPerWave], pj[kTokPerWave];
+#pragma unroll
+  for (int i = 0; i < kTokPerWave; i++) pl[i] = -1;
+  auto count = [&](int tl, int e) __attribute__((always_inline)) {
+    atomicAdd(&hist[e], 1);
+    if (tl < 32) atomicOr(&mlo[e], 1u << tl);
+    else atomicOr(&mhi[e], 1u << (tl - 32));
+  };
+  bool rows = false;
+  if constexpr (ROWS) {
     if (k <= 16) {
+      rows = true;
       constexpr int NPR = 4 * NPL;  // E <= 16 * NPR
       const int q = lane & 15;
       const int64_t t = t0 + (lane >> 4);
@@ -302,50 +324,62 @@ MX_DEV void route_block(const float* __restrict__ logits, int64_t T, int E, int 
       if (t < T && q < k) {
         ids[t * k + q] = my_id;
         wts[t * k + q] = my_w;
-        atomicAdd(&hist[my_id], 1);
+        pl[0] = (int)(t - blk * kRouteTokens);
+        pe[0] = my_id;
+        pj[0] = q;
+        count(pl[0], my_id);
       }
-      __syncthreads();
-      for (int e = tid; e < E; e += kRouteThreads) blkcnt[blk * E + e] = hist[e];
-      return;
     }
   }
-  constexpr int NT = NPL <= 8 ? kTokPerWave : 2;  // tokens routed together
+  if (!rows) {
+    constexpr int NT = NPL <= 8 ? kTokPerWave : 2;  // tokens routed together
 #pragma unroll
-  for (int i0 = 0; i0 < kTokPerWave; i0 += NT) {
-    if (t0 + i0 >= T) break;  // uniform per wave
-    float val[NT][NPL];
+    for (int i0 = 0; i0 < kTokPerWave; i0 += NT) {
+      if (t0 + i0 >= T) break;  // uniform per wave
+      float val[NT][NPL];
 #pragma unroll
-    for (int i = 0; i < NT; i++) {
-      const int64_t t = t0 + i0 + i;
+      for (int i = 0; i < NT; i++) {
+        const int64_t t = t0 + i0 + i;
 #pragma unroll
-      for (int j = 0; j < NPL; j++) {
-        const int idx = lane + 64 * j;
-        val[i][j] = t < T && idx < E ? logits[t * E + idx] : 0.f;
+        for (int j = 0; j < NPL; j++) {
+          const int idx = lane + 64 * j;
+          val[i][j] = t < T && idx < E ? logits[t * E + idx] : 0.f;
+        }
       }
-    }
-    int my_id[NT];
-    float my_w[NT];
-    route_tokens<NPL, NT>(val, E, k, renormalize, my_id, my_w);
+      int my_id[NT];
+      float my_w[NT];
+      route_tokens<NPL, NT>(val, E, k, renormalize, my_id, my_w);
 #pragma unroll
-    for (int i = 0; i < NT; i++) {
-      const int64_t t = t0 + i0 + i;
-      if (t < T && lane < k) {
-        ids[t * k + lane] = my_id[i];
-        wts[t * k + lane] = my_w[i];
-        atomicAdd(&hist[my_id[i]], 1);
+      for (int i = 0; i < NT; i++) {
+        const int64_t t = t0 + i0 + i;
+        if (t < T && lane < k) {
+          ids[t * k + lane] = my_id[i];
+          wts[t * k + lane] = my_w[i];
+          pl[i0 + i] = (int)(t - blk * kRouteTokens);
+          pe[i0 + i] = my_id[i];
+          pj[i0 + i] = lane;
+          count(pl[i0 + i], my_id[i]);
+        }
       }
     }
   }
   __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kTokPerWave; i++)
+    if (pl[i] >= 0) {
+      const uint64_t m = ((uint64_t)mhi[pe[i]] << 32) | mlo[pe[i]];
+      rank[(blk * kRouteTokens + pl[i]) * k + pj[i]] = __popcll(m & ((1ull << pl[i]) - 1ull));
+    }
   for (int e = tid; e < E; e += kRouteThreads) blkcnt[blk * E + e] = hist[e];
 }
 
 template <int NPL>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(const float* __restrict__ logits, int64_t T, int E, int k,
                                                               int renormalize, int32_t* __restrict__ ids,
-                                                              float* __restrict__ wts, int32_t* __restrict__ blkcnt) {
-  __shared__ int32_t hist[1024];
-  route_block<NPL>(logits, T, E, k, renormalize, ids, wts, blkcnt, blockIdx.x, hist);
+                                                              float* __restrict__ wts, int32_t* __restrict__ blkcnt,
+                                                              int32_t* __restrict__ rank) {
+  __shared__ int32_t lds[kRouteLdsInts];
+  route_block<NPL>(logits, T, E, k, renormalize, ids, wts, blkcnt, rank, blockIdx.x, lds);
 }
 
 // The forward pass's front in one launch: workgroups 0 .. nroute - 1 route one token block each, the
@@ -357,13 +391,13 @@ __global__ __launch_bounds__(kRouteThreads) void front_kernel(const uint16_t* __
                                                               const float* __restrict__ logits, int64_t T, int E, int k,
                                                               int renormalize, int32_t* __restrict__ ids,
                                                               float* __restrict__ wts, int32_t* __restrict__ blkcnt,
-                                                              int nroute) {
+                                                              int32_t* __restrict__ rank, int nroute) {
   constexpr int REC = act_rec(AF), NW = kRouteThreads / 64;
   constexpr int kIn = 4096, kOut = 32 * REC;
-  static_assert(NW * (kIn + kOut) >= 1024 * 4, "the histogram fits the staging LDS");
+  static_assert(NW * (kIn + kOut) >= kRouteLdsInts * 4, "the routing tables fit the staging LDS");
   __shared__ __attribute__((aligned(16))) uint8_t smem[NW * (kIn + kOut)];
   if ((int)blockIdx.x < nroute) {
-    route_block<NPL>(logits, T, E, k, renormalize, ids, wts, blkcnt, blockIdx.x, reinterpret_cast<int32_t*>(smem));
+    route_block<NPL>(logits, T, E, k, renormalize, ids, wts, blkcnt, rank, blockIdx.x, reinterpret_cast<int32_t*>(smem));
     return;
   }
   const int wave = threadIdx.x >> 6;
@@ -372,20 +406,22 @@ __global__ __launch_bounds__(kRouteThreads) void front_kernel(const uint16_t* __
 }
 
 // Pair placement, one workgroup of 1024 threads per block of kRouteTokens tokens.  blkcnt[b][e] holds
-// the pairs of expert e among the tokens of block b (the routing histogram, read only here).
+// the pairs of expert e among the tokens of block b (the routing histogram, read only here) and
+// rank[pair] the pair's rank among the pairs of its expert within its block (token order).
 //  (1) Every workgroup sums, per expert, the counts of the blocks before its own and of all blocks
 //      (threads split the blocks, partial sums meet in LDS), then scans over experts: the exclusive
 //      prefixes of the counts, of the counts padded to 32 and of the M tiles of BM and of BM2 rows.
-//  (2) Workgroup 0 also writes offsets, padded offsets, two tile lists (expert, first padded row,
+//  (2) Workgroup 0 writes offsets, padded offsets and the tile counts; the workgroups share the
+//      experts (expert e goes to workgroup e % nb) to write two tile lists (expert, first padded row,
 //      valid rows) for M tiles of BM rows (first GEMM) and of BM2 rows (second GEMM; the list is
-//      skipped when tiles2 is NULL), and the padding rows of every expert plus 128 slack rows after the
-//      last one (pair -1, token 0, weight 0), so a GEMM tile may read up to 128 rows past its expert's
-//      start.
-//  (3) The first wave (lane = token of the block) ranks each pair among the pairs of its expert in
-//      token order: (pairs of that expert in earlier blocks) + (earlier lanes of this block with that
-//      expert, from a 64-bit lane mask per expert), and writes the compact order (sorted_pairs, may be
-//      NULL), the padded rows (pair, token, routing weight) and each pair's padded row (pair_prow, may be
-//      NULL).  Padding rows and pair rows are disjoint, so the workgroups never write the same row.
+//      skipped when tiles2 is NULL) and the padding rows of each expert; workgroup 0 also writes 128
+//      slack rows after the last expert (pair -1, token 0, weight 0), so a GEMM tile may read up to
+//      128 rows past its expert's start.
+//  (3) Each thread takes pairs of the block: rank = (pairs of that expert in earlier blocks) +
+//      rank[pair]; it writes the compact order (sorted_pairs, may be NULL), the padded row (pair,
+//      token, routing weight) and the pair's padded row (pair_prow, may be NULL; it may also be the
+//      rank array itself, each entry read before its thread overwrites it).  Padding rows and pair rows
+//      are disjoint, so the workgroups never write the same row.
 __global__ __launch_bounds__(1024) void place_kernel(const int32_t* __restrict__ ids, const float* __restrict__ wts,
                                                      const int32_t* __restrict__ blkcnt, int64_t T, int nb, int k,
                                                      int E, int BM, int BM2, int32_t* __restrict__ offsets,
@@ -393,16 +429,11 @@ __global__ __launch_bounds__(1024) void place_kernel(const int32_t* __restrict__
                                                      int32_t* __restrict__ ntiles, TileDesc* __restrict__ tiles2,
                                                      int32_t* __restrict__ ntiles2, int32_t* __restrict__ sorted_pairs,
                                                      int32_t* __restrict__ prow_pair, int32_t* __restrict__ prow_tok,
-                                                     float* __restrict__ prow_w, int32_t* __restrict__ pair_prow) {
+                                                     float* __restrict__ prow_w, int32_t* pair_prow,
+                                                     const int32_t* rank) {
   __shared__ int part_pre[1024], part_tot[1024];
   __shared__ int e_pre[1024], e_off[1024], e_poff[1024], e_tot[1024], e_toff[1024], e_toff2[1024];
-  __shared__ uint32_t mlo[1024], mhi[1024];
   __shared__ int wsum[4][16];
-  // the block's pairs as the first wave read them ([slot][lane]; top_k <= 32 at every entry point), so
-  // the ranking pass reads LDS instead of global memory again
-  __shared__ int32_t s_ex[32][64];
-  __shared__ float s_wt[32][64];
-  __shared__ int slack0;  // first slack row (workgroup 0)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int blk = blockIdx.x;
   int es = 64;  // expert stride: power of two >= E, at least one wave
@@ -411,7 +442,20 @@ __global__ __launch_bounds__(1024) void place_kernel(const int32_t* __restrict__
   const int e = tid % es, grp = tid / es;
   const int per = (nb + G - 1) / G;
   const int b0 = min(nb, grp * per), b1 = min(nb, b0 + per);
-  for (int i = tid; i < E; i += 1024) { mlo[i] = 0; mhi[i] = 0; }
+  // this thread's pairs of the block (top_k <= 32: at most two per thread), loaded before phase (1)
+  const int64_t pb0 = (int64_t)blk * kRouteTokens * k, npb = min((int64_t)kRouteTokens * k, T * k - pb0);
+  int p_ex[2], p_rk[2];
+  float p_wt[2];
+#pragma unroll
+  for (int u = 0; u < 2; u++) {
+    const int64_t p = tid + 1024 * u;
+    p_ex[u] = -1;
+    if (p < npb) {
+      p_ex[u] = ids[pb0 + p];
+      p_wt[u] = wts[pb0 + p];
+      p_rk[u] = rank[pb0 + p];
+    }
+  }
   // (1) partial sums over this thread's blocks, 16 independent loads at a time
   constexpr int kBatch = 16;
   int s_pre = 0, s_tot = 0;
@@ -461,8 +505,8 @@ __global__ __launch_bounds__(1024) void place_kernel(const int32_t* __restrict__
     e_toff[e] = x2 - v2;
     e_toff2[e] = x3 - v3;
   }
-  // (2) the tables, once: offsets by expert thread, then each wave takes experts wave, wave + 16, ...
-  // and writes their tiles and padding rows with one lane per tile or row
+  // (2) offsets and counts by workgroup 0's expert threads; tiles and padding rows of expert ee by
+  // workgroup ee % nb, its waves taking those experts in turn with one lane per tile or row
   if (blk == 0 && grp == 0 && e < E) {
     offsets[e] = x0 - v0;
     poffsets[e] = x1 - v1;
@@ -471,73 +515,44 @@ __global__ __launch_bounds__(1024) void place_kernel(const int32_t* __restrict__
       poffsets[E] = x1;
       *ntiles = x2;
       if (tiles2) *ntiles2 = x3;
-      slack0 = x1;
     }
   }
   __syncthreads();
-  if (blk == 0) {
-    for (int ee = wave; ee < E; ee += 16) {
-      const int poff = e_poff[ee], total = e_tot[ee], toff = e_toff[ee];
-      const int ntl = (total + BM - 1) / BM, pad = ((total + 31) & ~31) - total;
-      for (int i = lane; i < ntl; i += 64) tiles[toff + i] = TileDesc{ee, poff + i * BM, min(BM, total - i * BM), 0};
-      if (tiles2) {
-        const int toff2 = e_toff2[ee], ntl2 = (total + BM2 - 1) / BM2;
-        for (int i = lane; i < ntl2; i += 64)
-          tiles2[toff2 + i] = TileDesc{ee, poff + i * BM2, min(BM2, total - i * BM2), 0};
-      }
-      if (lane < pad) {
-        const int r = poff + total + lane;
-        prow_pair[r] = -1;
-        prow_tok[r] = 0;
-        prow_w[r] = 0.f;
-      }
+  const int nwg = nb > 0 ? nb : 1;
+  for (int ee = blk + wave * nwg; ee < E; ee += 16 * nwg) {
+    const int poff = e_poff[ee], total = e_tot[ee], toff = e_toff[ee];
+    const int ntl = (total + BM - 1) / BM, pad = ((total + 31) & ~31) - total;
+    for (int i = lane; i < ntl; i += 64) tiles[toff + i] = TileDesc{ee, poff + i * BM, min(BM, total - i * BM), 0};
+    if (tiles2) {
+      const int toff2 = e_toff2[ee], ntl2 = (total + BM2 - 1) / BM2;
+      for (int i = lane; i < ntl2; i += 64) tiles2[toff2 + i] = TileDesc{ee, poff + i * BM2, min(BM2, total - i * BM2), 0};
     }
-    if (tid < 128) {  // slack rows after the last expert
-      const int r = slack0 + tid;
+    if (lane < pad) {
+      const int r = poff + total + lane;
       prow_pair[r] = -1;
       prow_tok[r] = 0;
       prow_w[r] = 0.f;
     }
   }
-  // (3) ranks within the block (the pair loads go out four at a time: k is a runtime count)
-  if (wave == 0) {
-    const int64_t t = (int64_t)blk * kRouteTokens + lane;
-    const bool live = t < T;
-    if (live)
-      for (int j0 = 0; j0 < k; j0 += 4) {
-        int exs[4];
-        float ws[4];
+  if (blk == 0 && tid < 128) {  // slack rows after the last expert
+    const int r = e_poff[E - 1] + ((e_tot[E - 1] + 31) & ~31) + tid;
+    prow_pair[r] = -1;
+    prow_tok[r] = 0;
+    prow_w[r] = 0.f;
+  }
+  // (3) the block's pairs, from the ranks the routing wrote
 #pragma unroll
-        for (int u = 0; u < 4; u++) {
-          exs[u] = j0 + u < k ? ids[t * k + j0 + u] : -1;
-          ws[u] = j0 + u < k ? wts[t * k + j0 + u] : 0.f;
-        }
-#pragma unroll
-        for (int u = 0; u < 4; u++) {
-          if (exs[u] < 0) continue;
-          s_ex[j0 + u][lane] = exs[u];
-          s_wt[j0 + u][lane] = ws[u];
-          if (lane < 32) atomicOr(&mlo[exs[u]], 1u << lane);
-          else atomicOr(&mhi[exs[u]], 1u << (lane - 32));
-        }
-      }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
-    if (live) {
-      const uint64_t lt = (1ull << lane) - 1ull;
-      for (int j = 0; j < k; j++) {
-        const int ex = s_ex[j][lane];
-        const uint64_t m = ((uint64_t)mhi[ex] << 32) | mlo[ex];
-        const int rank = e_pre[ex] + __popcll(m & lt);
-        const int32_t pair = (int32_t)(t * k + j);
-        if (sorted_pairs) sorted_pairs[e_off[ex] + rank] = pair;
-        const int r = e_poff[ex] + rank;
-        prow_pair[r] = pair;
-        prow_tok[r] = (int32_t)t;
-        prow_w[r] = s_wt[j][lane];
-        if (pair_prow) pair_prow[pair] = r;
-      }
-    }
+  for (int u = 0; u < 2; u++) {
+    const int ex = p_ex[u];
+    if (ex < 0) continue;
+    const int64_t pair = pb0 + tid + 1024 * u;
+    const int rk = e_pre[ex] + p_rk[u];
+    if (sorted_pairs) sorted_pairs[e_off[ex] + rk] = (int32_t)pair;
+    const int r = e_poff[ex] + rk;
+    prow_pair[r] = (int32_t)pair;
+    prow_tok[r] = (int32_t)(pair / k);
+    prow_w[r] = p_wt[u];
+    if (pair_prow) pair_prow[pair] = r;
   }
 }
 
@@ -546,7 +561,8 @@ inline int route_npl(int E) { return E <= 64 ? 1 : E <= 128 ? 2 : E <= 256 ? 4 :
 
 template <int AF>
 void launch_front_af(const void* x, int64_t T, int64_t ldx, const MoeGeom& g, void* xq, const float* logits, int E,
-                     int k, int renormalize, int32_t* ids, float* w, int32_t* blkcnt, hipStream_t stream) {
+                     int k, int renormalize, int32_t* ids, float* w, int32_t* blkcnt, int32_t* rank,
+                     hipStream_t stream) {
   const int64_t nblk = 2 * g.nkt1;
   const int64_t n = T * nblk;
   const int nroute = (int)cdiv(T, kRouteTokens);
@@ -555,7 +571,7 @@ void launch_front_af(const void* x, int64_t T, int64_t ldx, const MoeGeom& g, vo
   const dim3 grid((unsigned)(nroute + nx)), block(kRouteThreads);
 #define MX_FRONT(NPL)                                                                                                   \
   hipLaunchKernelGGL((front_kernel<AF, NPL>), grid, block, 0, stream, (const uint16_t*)x, ldx, g.H, nblk, (uint8_t*)xq, n, \
-                     logits, T, E, k, renormalize, ids, w, blkcnt, nroute)
+                     logits, T, E, k, renormalize, ids, w, blkcnt, rank, nroute)
   switch (route_npl(E)) {
     case 1: MX_FRONT(1); break;
     case 2: MX_FRONT(2); break;
@@ -569,41 +585,44 @@ void launch_front_af(const void* x, int64_t T, int64_t ldx, const MoeGeom& g, vo
 }  // namespace
 
 int launch_front(int af, const void* x, int64_t T, int64_t ldx, const MoeGeom& g, void* xq, const float* logits, int E,
-                 int k, int renormalize, int32_t* ids, float* w, int32_t* blkcnt, hipStream_t stream) {
+                 int k, int renormalize, int32_t* ids, float* w, int32_t* blkcnt, int32_t* rank, hipStream_t stream) {
   if (T > 0) {
     if (af == kActMxfp8)
-      launch_front_af<kActMxfp8>(x, T, ldx, g, xq, logits, E, k, renormalize, ids, w, blkcnt, stream);
+      launch_front_af<kActMxfp8>(x, T, ldx, g, xq, logits, E, k, renormalize, ids, w, blkcnt, rank, stream);
     else if (af == kActMxfp4)
-      launch_front_af<kActMxfp4>(x, T, ldx, g, xq, logits, E, k, renormalize, ids, w, blkcnt, stream);
+      launch_front_af<kActMxfp4>(x, T, ldx, g, xq, logits, E, k, renormalize, ids, w, blkcnt, rank, stream);
     else
-      launch_front_af<kActBf16>(x, T, ldx, g, xq, logits, E, k, renormalize, ids, w, blkcnt, stream);
+      launch_front_af<kActBf16>(x, T, ldx, g, xq, logits, E, k, renormalize, ids, w, blkcnt, rank, stream);
   }
   return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
 }
 
 int launch_route(const float* logits, int64_t T, int E, int k, int renormalize, int32_t* ids, float* w,
-                 int32_t* blkcnt, hipStream_t stream) {
+                 int32_t* blkcnt, int32_t* rank, hipStream_t stream) {
   const dim3 grid((unsigned)cdiv(T, kRouteTokens)), block(kRouteThreads);
+#define MX_ROUTE(NPL) \
+  hipLaunchKernelGGL(route_kernel<NPL>, grid, block, 0, stream, logits, T, E, k, renormalize, ids, w, blkcnt, rank)
   if (T > 0) {
     switch (route_npl(E)) {
-      case 1: hipLaunchKernelGGL(route_kernel<1>, grid, block, 0, stream, logits, T, E, k, renormalize, ids, w, blkcnt); break;
-      case 2: hipLaunchKernelGGL(route_kernel<2>, grid, block, 0, stream, logits, T, E, k, renormalize, ids, w, blkcnt); break;
-      case 4: hipLaunchKernelGGL(route_kernel<4>, grid, block, 0, stream, logits, T, E, k, renormalize, ids, w, blkcnt); break;
-      case 8: hipLaunchKernelGGL(route_kernel<8>, grid, block, 0, stream, logits, T, E, k, renormalize, ids, w, blkcnt); break;
-      default: hipLaunchKernelGGL(route_kernel<16>, grid, block, 0, stream, logits, T, E, k, renormalize, ids, w, blkcnt); break;
+      case 1: MX_ROUTE(1); break;
+      case 2: MX_ROUTE(2); break;
+      case 4: MX_ROUTE(4); break;
+      case 8: MX_ROUTE(8); break;
+      default: MX_ROUTE(16); break;
     }
   }
+#undef MX_ROUTE
   return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
 }
 
-int launch_place(const int32_t* ids, const float* w, int32_t* blkcnt, int64_t T, int k, int E, int BM, int BM2,
-                 int32_t* offsets, int32_t* poffsets, int32_t* sorted_pairs, int32_t* prow_pair, int32_t* prow_tok,
-                 float* prow_w, int32_t* pair_prow, void* tiles, int32_t* ntiles, void* tiles2, int32_t* ntiles2,
-                 hipStream_t stream) {
+int launch_place(const int32_t* ids, const float* w, int32_t* blkcnt, const int32_t* rank, int64_t T, int k, int E,
+                 int BM, int BM2, int32_t* offsets, int32_t* poffsets, int32_t* sorted_pairs, int32_t* prow_pair,
+                 int32_t* prow_tok, float* prow_w, int32_t* pair_prow, void* tiles, int32_t* ntiles, void* tiles2,
+                 int32_t* ntiles2, hipStream_t stream) {
   const int nb = (int)cdiv(T, kRouteTokens);
   // at least one workgroup, which writes the tables even when there are no tokens
   hipLaunchKernelGGL(place_kernel, dim3((unsigned)(nb > 0 ? nb : 1)), dim3(1024), 0, stream, ids, w, blkcnt, T, nb, k, E,
                      BM, BM2, offsets, poffsets, (TileDesc*)tiles, ntiles, (TileDesc*)tiles2, ntiles2, sorted_pairs, prow_pair,
-                     prow_tok, prow_w, pair_prow);
+                     prow_tok, prow_w, pair_prow, rank);
   return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
 }

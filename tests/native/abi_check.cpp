@@ -222,7 +222,8 @@ static void test_route() {
   // placement reads
   const Call& rt = g_calls[0];
   const Call& pl = g_calls[1];
-  CHECK(rt.p[3] == pl.p[0] && rt.i[0] == T && rt.i[1] == E && rt.i[2] == k);
+  CHECK(rt.p[3] == pl.p[0] && rt.p[4] == pl.p[12] && rt.i[0] == T && rt.i[1] == E && rt.i[2] == k);
+  CHECK(inside(rt.p[4], 4 * T * k, ws, n));
   const int64_t nrows = ((T * k + 31 * E + 31) / 32) * 32 + 128;
   CHECK(inside(pl.p[0], 4 * cdiv(T, kRouteTokens) * E, ws, n));
   CHECK(inside(pl.p[2], 4 * (E + 1), ws, n));
@@ -242,7 +243,8 @@ static void check_forward_layout(const mxfp4_moe_dims& d, int64_t T, int k, size
   const Call& fr = g_calls[0];
   CHECK(inside(fr.p[1], (size_t)T * g.nkt1 * kMaxRec, ws, nws));
   CHECK(inside(fr.p[2], 4 * (size_t)((T + kRouteTokens - 1) / kRouteTokens) * fr.i[2], ws, nws));
-  CHECK(fr.i[2] == d.E && fr.i[4] == k && fr.p[2] == g_calls[1].p[0]);
+  CHECK(fr.i[2] == d.E && fr.i[4] == k && fr.p[2] == g_calls[1].p[0] && fr.p[6] == g_calls[1].p[12]);
+  CHECK(fr.p[6] == g_calls[1].p[7]);  // the ranks live in pair_prow until the placement overwrites them
   CHECK(inside(fr.p[4], 4 * (size_t)T * k, ws, nws) && inside(fr.p[5], 4 * (size_t)T * k, ws, nws));
   const GemmArgs& a1 = g_calls[2].gemm;
   const GemmArgs& a2 = g_calls[3].gemm;

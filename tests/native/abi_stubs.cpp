@@ -63,25 +63,26 @@ int launch_linear_prep(const void* x, int64_t M, int64_t ldx, const MoeGeom&, co
   return rec("linear_prep", c);
 }
 int launch_front(int af, const void* x, int64_t T, int64_t ldx, const MoeGeom&, void* xq, const float* logits, int E,
-                 int k, int, int32_t* ids, float* w, int32_t* blkcnt, hipStream_t) {
+                 int k, int, int32_t* ids, float* w, int32_t* blkcnt, int32_t* rank, hipStream_t) {
   Call c;
-  c.p[0] = x; c.p[1] = xq; c.p[2] = blkcnt; c.p[3] = logits; c.p[4] = ids; c.p[5] = w;
+  c.p[0] = x; c.p[1] = xq; c.p[2] = blkcnt; c.p[3] = logits; c.p[4] = ids; c.p[5] = w; c.p[6] = rank;
   c.i[0] = T; c.i[1] = ldx; c.i[2] = E; c.i[3] = af; c.i[4] = k;
   return rec("front", c);
 }
 int launch_route(const float* logits, int64_t T, int E, int k, int, int32_t* ids, float* w, int32_t* blkcnt,
-                 hipStream_t) {
+                 int32_t* rank, hipStream_t) {
   Call c;
-  c.p[0] = logits; c.p[1] = ids; c.p[2] = w; c.p[3] = blkcnt; c.i[0] = T; c.i[1] = E; c.i[2] = k;
+  c.p[0] = logits; c.p[1] = ids; c.p[2] = w; c.p[3] = blkcnt; c.p[4] = rank; c.i[0] = T; c.i[1] = E; c.i[2] = k;
   return rec("route", c);
 }
-int launch_place(const int32_t*, const float*, int32_t* blkcnt, int64_t T, int k, int E, int BM, int BM2, int32_t* offsets,
-                 int32_t* poffsets, int32_t* sorted_pairs, int32_t* prow_pair, int32_t* prow_tok, float* prow_w,
-                 int32_t* pair_prow, void* tiles, int32_t* ntiles, void* tiles2, int32_t* ntiles2, hipStream_t) {
+int launch_place(const int32_t*, const float*, int32_t* blkcnt, const int32_t* rank, int64_t T, int k, int E, int BM,
+                 int BM2, int32_t* offsets, int32_t* poffsets, int32_t* sorted_pairs, int32_t* prow_pair,
+                 int32_t* prow_tok, float* prow_w, int32_t* pair_prow, void* tiles, int32_t* ntiles, void* tiles2,
+                 int32_t* ntiles2, hipStream_t) {
   Call c;
   c.p[0] = blkcnt; c.p[1] = offsets; c.p[2] = poffsets; c.p[3] = sorted_pairs; c.p[4] = prow_pair;
   c.p[5] = prow_tok; c.p[6] = prow_w; c.p[7] = pair_prow; c.p[8] = tiles; c.p[9] = ntiles; c.p[10] = tiles2;
-  c.p[11] = ntiles2;
+  c.p[11] = ntiles2; c.p[12] = rank;
   c.i[0] = T; c.i[1] = k; c.i[2] = E; c.i[3] = BM; c.i[4] = BM2;
   return rec("place", c);
 }

@@ -10,7 +10,7 @@
 
 struct Call {
   std::string name;
-  const void* p[12] = {};
+  const void* p[13] = {};
   int64_t i[6] = {};
   size_t off[6] = {};
   GemmArgs gemm = {};
