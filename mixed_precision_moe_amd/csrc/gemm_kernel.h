@@ -876,11 +876,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
             int ex = amax > 0.f ? __builtin_amdgcn_frexp_expf(amax) - 14 : 0;
             ex = ex < -127 ? -127 : (ex > 127 ? 127 : ex);
             const float f = __builtin_ldexpf(wt, -ex);
+            // v * f rounded once to the nearest integer (even on ties): fma(v, f, 1.5 * 2^23) is exact up to
+            // that rounding while |v * f| < 2^22 (here < 2^14 + 1), and the sum's low 16 bits are the integer
+            // in two's complement; one byte permute packs a pair.
+            constexpr float kRound = 12582912.0f;  // 1.5 * 2^23
             uint32_t hv[8];
 #pragma unroll
             for (int c = 0; c < 8; c++) {
-              const int i0 = (int)__builtin_rintf(v[2 * c] * f), i1 = (int)__builtin_rintf(v[2 * c + 1] * f);
-              hv[c] = ((uint32_t)i0 & 0xFFFFu) | ((uint32_t)i1 << 16);
+              const uint32_t u0 = __float_as_uint(__builtin_fmaf(v[2 * c], f, kRound));
+              const uint32_t u1 = __float_as_uint(__builtin_fmaf(v[2 * c + 1], f, kRound));
+              hv[c] = __builtin_amdgcn_perm(u1, u0, 0x05040100u);  // low half of u0, then low half of u1
             }
             if (real) {
               u32x4_t* op = reinterpret_cast<u32x4_t*>(orow + nt * 32 + 16 * h);
