@@ -32,11 +32,14 @@ namespace {
 // consecutive bytes: 16-byte chunk c = 64 j + l of the wave's 4 KB of x is loaded by lane l in load j and
 // written to LDS, lane l then reads its block's four chunks; lane l writes its slot and scale dword into
 // record l / 2 (blocks 2r and 2r + 1 form the K-step record r), and the wave's 32 records (consecutive
-// in xq) leave as 1 KB stores.  Wave slot wv0 of nw (the wave's own LDS stage_in / stage_out) takes
-// the wave indices wv0, wv0 + nw, ...
+// in xq) leave as 1 KB stores.  Wave slot wv0 of nw takes the wave indices wv0, wv0 + nw, ... with its
+// own LDS stage (max(4 KB, 32 records)): the records may overwrite the staged input, since every lane
+// has read its x chunks (an earlier LDS instruction of the same wave) before any lane writes a record.
 template <int AF>
 MX_DEV void xprep_waves(const uint16_t* __restrict__ x, int64_t ldx, int64_t H, int64_t nblk, uint8_t* __restrict__ xq,
-                        int64_t n, int64_t wv0, int64_t nw, uint8_t* stage_in, uint8_t* stage_out) {
+                        int64_t n, int64_t wv0, int64_t nw, uint8_t* stage) {
+  uint8_t* stage_in = stage;
+  uint8_t* stage_out = stage;
   constexpr int SLOT = act_slot(AF), REC = act_rec(AF);
   const int lane = threadIdx.x & 63;
   const int64_t hb = H / 32;  // real blocks per token
@@ -393,16 +396,16 @@ __global__ __launch_bounds__(kRouteThreads) void front_kernel(const uint16_t* __
                                                               float* __restrict__ wts, int32_t* __restrict__ blkcnt,
                                                               int32_t* __restrict__ rank, int nroute) {
   constexpr int REC = act_rec(AF), NW = kRouteThreads / 64;
-  constexpr int kIn = 4096, kOut = 32 * REC;
-  static_assert(NW * (kIn + kOut) >= kRouteLdsInts * 4, "the routing tables fit the staging LDS");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[NW * (kIn + kOut)];
+  constexpr int kStage = 4096 > 32 * REC ? 4096 : 32 * REC;  // a wave's staging bytes
+  static_assert(NW * kStage >= kRouteLdsInts * 4, "the routing tables fit the staging LDS");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NW * kStage];
   if ((int)blockIdx.x < nroute) {
     route_block<NPL>(logits, T, E, k, renormalize, ids, wts, blkcnt, rank, blockIdx.x, reinterpret_cast<int32_t*>(smem));
     return;
   }
   const int wave = threadIdx.x >> 6;
   xprep_waves<AF>(x, ldx, H, nblk, xq, n, (int64_t)(blockIdx.x - nroute) * NW + wave,
-                  (int64_t)(gridDim.x - nroute) * NW, smem + wave * kIn, smem + NW * kIn + wave * kOut);
+                  (int64_t)(gridDim.x - nroute) * NW, smem + wave * kStage);
 }
 
 // Pair placement, one workgroup of 1024 threads per block of kRouteTokens tokens.  blkcnt[b][e] holds
