@@ -415,7 +415,8 @@ __global__ __launch_bounds__(kRouteThreads) void front_kernel(const uint16_t* __
 //      (threads split the blocks, partial sums meet in LDS), then scans over experts: the exclusive
 //      prefixes of the counts, of the counts padded to 32 and of the M tiles of BM and of BM2 rows.
 //  (2) Workgroup 0 writes offsets, padded offsets and the tile counts; the workgroups share the
-//      experts (expert e goes to workgroup e % nb) to write two tile lists (expert, first padded row,
+//      experts (expert e goes to workgroup e % gridDim.x; with few token blocks the grid has extra
+//      workgroups, which hold no pairs) to write two tile lists (expert, first padded row,
 //      valid rows) for M tiles of BM rows (first GEMM) and of BM2 rows (second GEMM; the list is
 //      skipped when tiles2 is NULL) and the padding rows of each expert; workgroup 0 also writes 128
 //      slack rows after the last expert (pair -1, token 0, weight 0), so a GEMM tile may read up to
@@ -521,7 +522,7 @@ __global__ __launch_bounds__(1024) void place_kernel(const int32_t* __restrict__
     }
   }
   __syncthreads();
-  const int nwg = nb > 0 ? nb : 1;
+  const int nwg = gridDim.x;  // at least nb (workgroups past nb have no pairs and only write tables)
   for (int ee = blk + wave * nwg; ee < E; ee += 16 * nwg) {
     const int poff = e_poff[ee], total = e_tot[ee], toff = e_toff[ee];
     const int ntl = (total + BM - 1) / BM, pad = ((total + 31) & ~31) - total;
@@ -623,8 +624,12 @@ int launch_place(const int32_t* ids, const float* w, int32_t* blkcnt, const int3
                  int32_t* prow_tok, float* prow_w, int32_t* pair_prow, void* tiles, int32_t* ntiles, void* tiles2,
                  int32_t* ntiles2, hipStream_t stream) {
   const int nb = (int)cdiv(T, kRouteTokens);
-  // at least one workgroup, which writes the tables even when there are no tokens
-  hipLaunchKernelGGL(place_kernel, dim3((unsigned)(nb > 0 ? nb : 1)), dim3(1024), 0, stream, ids, w, blkcnt, T, nb, k, E,
+  // one workgroup per token block, and at least one (the tables are written even without tokens); with
+  // few blocks, more workgroups (up to one expert per wave) share the tile lists and padding rows
+  int nwg = nb > 0 ? nb : 1;
+  const int by_experts = (int)cdiv(E, 16) < 16 ? (int)cdiv(E, 16) : 16;
+  if (nwg < by_experts) nwg = by_experts;
+  hipLaunchKernelGGL(place_kernel, dim3((unsigned)nwg), dim3(1024), 0, stream, ids, w, blkcnt, T, nb, k, E,
                      BM, BM2, offsets, poffsets, (TileDesc*)tiles, ntiles, (TileDesc*)tiles2, ntiles2, sorted_pairs, prow_pair,
                      prow_tok, prow_w, pair_prow, rank);
   return hipGetLastError() == hipSuccess ? MXFP4_OK : MXFP4_ERR_DEVICE;
