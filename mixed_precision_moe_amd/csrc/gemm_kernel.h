@@ -50,6 +50,7 @@ namespace {
 typedef __attribute__((address_space(3))) void* lds_vptr_t;
 
 constexpr int kXcds = 8;           // workgroup b runs on XCD b % 8
+constexpr int kBufFlags = 0x00020000;  // buffer resource word 3: raw dword access (stride 0)
 
 
 // LDS DMA: lane i copies 16 (or 4) bytes from its global address to lds_wave_base + i * 16 (or 4).
@@ -228,6 +229,12 @@ MX_DEV void swap_halves(float& x, float& y) {
                                                   false);
   x = __builtin_bit_cast(float, (unsigned)r[0]);
   y = __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+MX_DEV void swap_halves_u32(uint32_t& x, uint32_t& y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+  x = (uint32_t)r[0];
+  y = (uint32_t)r[1];
 }
 
 // Four consecutive bf16 entries of an LDS bias table (8-byte aligned) as fp32.
@@ -813,89 +820,188 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
       // Lane l holds token row l % 32 of its row group and output columns 8*jj + 4*(l/32) + i of each
       // tile; after one exchange of lane halves, half h holds the 16 consecutive columns 16h .. 16h+15
       // of the row: one block with a power-of-two scale (largest magnitude in [2^13, 2^14) after
-      // scaling), stored as 16 integers (round to nearest even; 32 bytes) plus the exponent byte: an
-      // absolute error of at most 2^-14 of the block maximum.  Rows of a row group past the expert's
-      // pairs are padding rows of that expert, which nothing reads: their lanes store nothing.
+      // scaling), converted to 16 integers (round to nearest even) plus the exponent byte: an absolute
+      // error of at most 2^-14 of the block maximum.  A second exchange leaves each lane the 64 bytes of
+      // one tile of a tile pair, and the pair's 32 rows of 128 bytes go out through this wave's part of
+      // ring stage D - 1 (unused until the next item's first step): written one row per lane pair, read
+      // back eight lanes per row, so each store instruction writes eight whole 128-byte row segments
+      // rather than 32-byte pieces of 32 rows; a pair's read-back completes while the next pair is
+      // computed, and its stores follow that (a wave's LDS accesses complete in order, so the next
+      // pair's rows may go to the same place).  The exponent bytes of the wave's CW tiles are gathered
+      // the same way into CW consecutive bytes per lane.  Rows of a row group past the expert's pairs
+      // (padding rows, or the dense layer's rows past M) are not stored.
       const int m = lane & 31, h = lane >> 5;
+      const int srow = lane >> 3, sch = lane & 7;  // read-back: row within eight, 16-byte chunk
+      constexpr int kStRow = 144;                  // a staged row: 128 bytes + 16 (spreads the banks)
+      static_assert(4 * 32 * kStRow <= C::kStage, "the staging rows fit one ring stage");
+      typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+      __attribute__((address_space(3))) uint8_t* stg =
+          (__attribute__((address_space(3))) uint8_t*)(smem + (D - 1) * C::kStage + wave * (32 * kStRow));
+      // without a next item no barrier followed the K loop: another wave may still read stage D - 1
+      if (!has_next) block_sync();
+      const int ntw0 = x * NT + wc * CW;  // first tile of this wave
+      // FULL: every tile of the wave is inside the output (no per-pair checks, so no branches between
+      // the pairs and the read-back of one pair stays in flight across the next pair's arithmetic)
+      auto epi = [&](auto dc, auto fc) __attribute__((always_inline)) {
+        constexpr bool DENSE = decltype(dc)::value, FULL = decltype(fc)::value;
+        uint16_t* const obase = DENSE ? a.ydense : a.o16;
 #pragma unroll
-      for (int r = 0; r < RW; r++) {
-        const int rgl = wr * RW + r;
-        if (rgl * 32 >= nrows) continue;
-        const float wt = __builtin_bit_cast(float, t_row[tb][rgl * 32 + m]);
-        const bool real = rgl * 32 + m < nrows;
-        const int64_t prow = prow0 + rgl * 32 + m;
-        uint16_t* orow = a.o16 + prow * a.H;
-        uint8_t* srow = a.osc + prow * (a.H / 16);
+        for (int r = 0; r < RW; r++) {
+          const int rgl = wr * RW + r;
+          if (rgl * 32 >= nrows) continue;
+          const float wt = __builtin_bit_cast(float, t_row[tb][rgl * 32 + m]);
+          const int64_t prow_rg = prow0 + rgl * 32;
+          uint32_t eb[2] = {0u, 0u};  // exponent bytes of tiles 0 .. CW/2 - 1 and CW/2 .. CW - 1
+          const bool rg_full = rgl * 32 + 32 <= nrows;
+          const int glim = rg_full ? 32 : nrows - rgl * 32;  // rows of this group that are stored
+          // the staged pair whose stores are pending: its first tile (-1: none) and its read-back
+          int pnt = -1;
+          u32x4_t sv[4];
+          auto store_pending = [&]() __attribute__((always_inline)) {
+            if constexpr (FULL) {
+              // buffer stores over the group's stored rows: a row past them falls outside the buffer
+              // range and is dropped, so no lane mask (and no branch) is needed
+              const __amdgpu_buffer_rsrc_t rs =
+                  __builtin_amdgcn_make_buffer_rsrc(obase + prow_rg * a.H, (short)0, glim * a.H * 2, kBufFlags);
+              const int vo = srow * a.H * 2 + (pnt * 32 + sch * 8) * 2;
 #pragma unroll
-        for (int j = 0; j < CW; j++) {
-          const int nt = x * NT + wc * CW + j;
-          if (nt < a.ntl) {
-            // v[c]: column 16h + c of the tile after the exchange
-            // the tile's 16 values are read first (each read is a scheduling boundary), then exchanged
-            float v[16], ra[16];
-#pragma unroll
-            for (int i = 0; i < 16; i++) ra[i] = acc_read(acc[r][j][i]);
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-              float x0 = ra[i], x2 = ra[8 + i];
-              float x1 = ra[4 + i], x3 = ra[12 + i];
-              swap_halves(x0, x2);  // half 0: cols i | 4 + i;  half 1: cols 16 + i | 20 + i
-              swap_halves(x1, x3);  // half 0: cols 8 + i | 12 + i;  half 1: cols 24 + i | 28 + i
-              v[i] = x0;
-              v[4 + i] = x2;
-              v[8 + i] = x1;
-              v[12 + i] = x3;
+              for (int s = 0; s < 4; s++) __builtin_amdgcn_raw_buffer_store_b128(sv[s], rs, vo, s * 16 * a.H, 0);
+              return;
             }
-            if constexpr (BIAS) {
-              lds_u16* bp = (lds_u16*)&t_b[tb][0][(wc * CW + j) * 32 + 16 * h];
-              float b[16];
+            // chunks 4 .. 7 are tile pnt + 1, which is past the output when H / 32 is odd; row 8s + srow
+            // of the group is 8s rows (8s * H / 8 chunks) past the first
+            const bool second = pnt + 1 < a.ntl;
+            u32x4_t* op = reinterpret_cast<u32x4_t*>(obase + (prow_rg + srow) * a.H + pnt * 32 + sch * 8);
+            if (second && rg_full) {
 #pragma unroll
-              for (int c = 0; c < 4; c++) bias4(bp + 4 * c, b + 4 * c);
+              for (int s = 0; s < 4; s++) op[(int64_t)s * a.H] = sv[s];
+            } else {
+              const bool col = sch < 4 || second;
+              const int lim = nrows - rgl * 32;  // rows of this group that are stored
 #pragma unroll
-              for (int c = 0; c < 16; c++) v[c] += b[c];
+              for (int s = 0; s < 4; s++)
+                if (col && 8 * s + srow < lim) op[(int64_t)s * a.H] = sv[s];
             }
-            if (a.ydense) {
-              // dense linear layer (one expert, unit row weights): the row of y itself, bf16
-              if (real) {
-                uint32_t bv[8];
+          };
 #pragma unroll
-                for (int c = 0; c < 8; c++) bv[c] = f32_to_bf16_bits(v[2 * c]) | (f32_to_bf16_bits(v[2 * c + 1]) << 16);
-                u32x4_t* yp = reinterpret_cast<u32x4_t*>(a.ydense + prow * a.H + nt * 32 + 16 * h);
-                yp[0] = u32x4_t{bv[0], bv[1], bv[2], bv[3]};
-                yp[1] = u32x4_t{bv[4], bv[5], bv[6], bv[7]};
+          for (int jp = 0; jp < CW / 2; jp++) {
+            const int nt0 = ntw0 + 2 * jp;
+            if (!FULL && nt0 >= a.ntl) continue;
+            uint32_t hv[2][8];
+#pragma unroll
+            for (int t = 0; t < 2; t++) {
+              const int j = 2 * jp + t;
+              // v[c]: column 16h + c of the tile after the exchange; the tile's 16 values are read
+              // first (each read is a scheduling boundary), then exchanged
+              float v[16], ra[16];
+#pragma unroll
+              for (int i = 0; i < 16; i++) ra[i] = acc_read(acc[r][j][i]);
+#pragma unroll
+              for (int i = 0; i < 4; i++) {
+                float x0 = ra[i], x2 = ra[8 + i];
+                float x1 = ra[4 + i], x3 = ra[12 + i];
+                swap_halves(x0, x2);  // half 0: cols i | 4 + i;  half 1: cols 16 + i | 20 + i
+                swap_halves(x1, x3);  // half 0: cols 8 + i | 12 + i;  half 1: cols 24 + i | 28 + i
+                v[i] = x0;
+                v[4 + i] = x2;
+                v[8 + i] = x1;
+                v[12 + i] = x3;
               }
-              __builtin_amdgcn_sched_barrier(0);
-              continue;
-            }
-            // The block maximum of w * v is |w| times that of v (rounding is monotonic), and scaling by a
-            // power of two commutes with rounding, so w * 2^-ex is applied as one factor.
-            float amax = 0.f;
+              if constexpr (BIAS) {
+                lds_u16* bp = (lds_u16*)&t_b[tb][0][(wc * CW + j) * 32 + 16 * h];
+                float b[16];
 #pragma unroll
-            for (int c = 0; c < 16; c++) amax = fmaxf(amax, fabsf(v[c]));
-            amax *= fabsf(wt);
-            int ex = amax > 0.f ? __builtin_amdgcn_frexp_expf(amax) - 14 : 0;
-            ex = ex < -127 ? -127 : (ex > 127 ? 127 : ex);
-            const float f = __builtin_ldexpf(wt, -ex);
-            // v * f rounded once to the nearest integer (even on ties): fma(v, f, 1.5 * 2^23) is exact up to
-            // that rounding while |v * f| < 2^22 (here < 2^14 + 1), and the sum's low 16 bits are the integer
-            // in two's complement; one byte permute packs a pair.
-            constexpr float kRound = 12582912.0f;  // 1.5 * 2^23
-            uint32_t hv[8];
+                for (int c = 0; c < 4; c++) bias4(bp + 4 * c, b + 4 * c);
 #pragma unroll
-            for (int c = 0; c < 8; c++) {
-              const uint32_t u0 = __float_as_uint(__builtin_fmaf(v[2 * c], f, kRound));
-              const uint32_t u1 = __float_as_uint(__builtin_fmaf(v[2 * c + 1], f, kRound));
-              hv[c] = __builtin_amdgcn_perm(u1, u0, 0x05040100u);  // low half of u0, then low half of u1
+                for (int c = 0; c < 16; c++) v[c] += b[c];
+              }
+              if constexpr (DENSE) {
+                // dense linear layer (one expert, unit row weights): the row of y itself, bf16
+#pragma unroll
+                for (int c = 0; c < 8; c++)
+                  hv[t][c] = f32_to_bf16_bits(v[2 * c]) | (f32_to_bf16_bits(v[2 * c + 1]) << 16);
+              } else {
+                // The block maximum of w * v is |w| times that of v (rounding is monotonic), and scaling
+                // by a power of two commutes with rounding, so w * 2^-ex is applied as one factor.
+                float amax = 0.f;
+#pragma unroll
+                for (int c = 0; c < 16; c++) amax = fmaxf(amax, fabsf(v[c]));
+                amax *= fabsf(wt);
+                int ex = amax > 0.f ? __builtin_amdgcn_frexp_expf(amax) - 14 : 0;
+                ex = ex < -127 ? -127 : (ex > 127 ? 127 : ex);
+                const float f = __builtin_ldexpf(wt, -ex);
+                // v * f rounded once to the nearest integer (even on ties): fma(v, f, 1.5 * 2^23) is exact
+                // up to that rounding while |v * f| < 2^22 (here < 2^14 + 1), and the sum's low 16 bits are
+                // the integer in two's complement; one byte permute packs a pair.
+                constexpr float kRound = 12582912.0f;  // 1.5 * 2^23
+#pragma unroll
+                for (int c = 0; c < 8; c++) {
+                  const uint32_t u0 = __float_as_uint(__builtin_fmaf(v[2 * c], f, kRound));
+                  const uint32_t u1 = __float_as_uint(__builtin_fmaf(v[2 * c + 1], f, kRound));
+                  hv[t][c] = __builtin_amdgcn_perm(u1, u0, 0x05040100u);  // low half of u0, then of u1
+                }
+                eb[j / (CW / 2)] |= (uint32_t)(ex + 127) << (8 * (j % (CW / 2)));
+              }
             }
-            if (real) {
-              u32x4_t* op = reinterpret_cast<u32x4_t*>(orow + nt * 32 + 16 * h);
-              op[0] = u32x4_t{hv[0], hv[1], hv[2], hv[3]};
-              op[1] = u32x4_t{hv[4], hv[5], hv[6], hv[7]};
-              srow[nt * 2 + h] = (uint8_t)(ex + 127);
+            // the previous pair's read-back has landed while this pair was computed
+            __builtin_amdgcn_sched_barrier(0);
+            if (FULL ? jp > 0 : pnt >= 0) store_pending();
+            __builtin_amdgcn_sched_barrier(0);
+            // half h takes tile nt0 + h whole: hv[0] its columns 0 .. 15, hv[1] columns 16 .. 31
+#pragma unroll
+            for (int d = 0; d < 8; d++) swap_halves_u32(hv[0][d], hv[1][d]);
+            __attribute__((address_space(3))) uint8_t* wrow = stg + m * kStRow + h * 64;
+            *(lds_u32x4*)(wrow + 0) = u32x4_t{hv[0][0], hv[0][1], hv[0][2], hv[0][3]};
+            *(lds_u32x4*)(wrow + 16) = u32x4_t{hv[0][4], hv[0][5], hv[0][6], hv[0][7]};
+            *(lds_u32x4*)(wrow + 32) = u32x4_t{hv[1][0], hv[1][1], hv[1][2], hv[1][3]};
+            *(lds_u32x4*)(wrow + 48) = u32x4_t{hv[1][4], hv[1][5], hv[1][6], hv[1][7]};
+            // read back: lane chunk sch of row 8s + srow
+#pragma unroll
+            for (int s = 0; s < 4; s++) sv[s] = *(lds_u32x4*)(stg + (8 * s + srow) * kStRow + sch * 16);
+            pnt = nt0;
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          if (pnt >= 0) store_pending();
+          if constexpr (!DENSE) {
+            // lane (m, h) holds exponent byte j of tile ntw0 + j, columns 16h ..: after one exchange
+            // and a byte interleave, lane (m, h) has the CW bytes 2 * ntw0 + CW * h .. of row m
+            swap_halves_u32(eb[0], eb[1]);
+            const uint32_t lo = __builtin_amdgcn_perm(eb[1], eb[0], 0x05010400u);
+            const uint32_t hi = __builtin_amdgcn_perm(eb[1], eb[0], 0x07030602u);
+            const int pos = 2 * ntw0 + CW * h;
+            uint8_t* sp = a.osc + (prow_rg + m) * (a.H / 16) + pos;
+            if (FULL && (a.H / 16) % CW == 0) {
+              const __amdgpu_buffer_rsrc_t rs =
+                  __builtin_amdgcn_make_buffer_rsrc(a.osc + prow_rg * (a.H / 16), (short)0, glim * (a.H / 16), kBufFlags);
+              if constexpr (CW == 8)
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{lo, hi}, rs, m * (a.H / 16) + pos, 0, 0);
+              else
+                __builtin_amdgcn_raw_buffer_store_b32(lo, rs, m * (a.H / 16) + pos, 0, 0);
+            } else if (rgl * 32 + m >= nrows) {
+            } else if ((FULL || ntw0 + CW <= a.ntl) && (a.H / 16) % CW == 0) {
+              if constexpr (CW == 8)
+                *reinterpret_cast<u32x2_t*>(sp) = u32x2_t{lo, hi};
+              else
+                *reinterpret_cast<uint32_t*>(sp) = lo;
+            } else {
+#pragma unroll
+              for (int b = 0; b < CW; b++)
+                if (pos + b < 2 * a.ntl) sp[b] = (uint8_t)((b < 4 ? lo : hi) >> (8 * (b & 3)));
             }
           }
-          __builtin_amdgcn_sched_barrier(0);
         }
+      };
+      const bool full = ntw0 + CW <= a.ntl;
+      if (a.ydense) {
+        if (full)
+          epi(std::true_type{}, std::true_type{});
+        else
+          epi(std::true_type{}, std::false_type{});
+      } else {
+        if (full)
+          epi(std::false_type{}, std::true_type{});
+        else
+          epi(std::false_type{}, std::false_type{});
       }
     }
 
