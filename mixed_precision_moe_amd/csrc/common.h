@@ -14,6 +14,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned u32x16_t __attribute__((ext_vector_type(16)));
 
 #define MX_DEV __device__ __forceinline__
 
@@ -98,13 +99,14 @@ MX_DEV bf16x32_t as_bf16x32(const uint32_t* w) {
   return v;
 }
 
-// w[j] (elements 2j, 2j + 1) -= the dequantized E2M3 codes, exactly, in bf16
+// w[j] (elements 2j, 2j + 1) -= the dequantized E2M3 codes, exactly, in bf16 (a code times its power-of-two
+// scale has four significant bits, so the dequantized values are exact in bf16, and so is each difference)
 MX_DEV void sub_fp6(uint32_t* w, const fp6x32_t& codes, float sc) {
-  const auto deq = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(codes, sc);
+  const auto deq = __builtin_bit_cast(u32x16_t, __builtin_amdgcn_cvt_scalef32_pk32_bf16_fp6(codes, sc));
 #pragma unroll
   for (int j = 0; j < 16; j++) {
-    const float a = bf16_bits_to_f32(w[j] & 0xFFFFu) - deq[2 * j];
-    const float c = bf16_bits_to_f32(w[j] >> 16) - deq[2 * j + 1];
+    const float a = bf16_bits_to_f32(w[j] & 0xFFFFu) - bf16_bits_to_f32(deq[j] & 0xFFFFu);
+    const float c = bf16_bits_to_f32(w[j] >> 16) - bf16_bits_to_f32(deq[j] >> 16);
     w[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector((xf32x2_t){a, c}, bf16x2_t));
   }
 }

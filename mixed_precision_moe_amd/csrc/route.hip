@@ -32,31 +32,49 @@ namespace {
 // consecutive bytes: 16-byte chunk c = 64 j + l of the wave's 4 KB of x is loaded by lane l in load j and
 // written to LDS, lane l then reads its block's four chunks; lane l writes its slot and scale dword into
 // record l / 2 (blocks 2r and 2r + 1 form the K-step record r), and the wave's 32 records (consecutive
-// in xq) leave as 1 KB stores.  Wave slot wv0 of nw takes the wave indices wv0, wv0 + nw, ... with its
+// in xq) leave as 1 KB stores.  A wave takes the group indices wv0, wv0 + nw, ... below wv_end with its
 // own LDS stage (max(4 KB, 32 records)): the records may overwrite the staged input, since every lane
 // has read its x chunks (an earlier LDS instruction of the same wave) before any lane writes a record.
+// The loads of a wave's next group are issued before the current group is converted and stored.
 template <int AF>
 MX_DEV void xprep_waves(const uint16_t* __restrict__ x, int64_t ldx, int64_t H, int64_t nblk, uint8_t* __restrict__ xq,
-                        int64_t n, int64_t wv0, int64_t nw, uint8_t* stage) {
+                        int64_t n, int64_t wv0, int64_t wv_end, int64_t nw, uint8_t* stage) {
   uint8_t* stage_in = stage;
   uint8_t* stage_out = stage;
   constexpr int SLOT = act_slot(AF), REC = act_rec(AF);
   const int lane = threadIdx.x & 63;
   const int64_t hb = H / 32;  // real blocks per token
-  const int64_t nwaves = (n + 63) / 64;
-  for (int64_t wv = wv0; wv < nwaves; wv += nw) {
-    const int64_t g0 = wv * 64;
-    // coalesced loads: chunk c = 64 j + lane is part c % 4 of block c / 4
+  // coalesced loads of group wv: chunk c = 64 j + lane is part c % 4 of block c / 4.  The group's first
+  // token comes from one (wave-uniform) division; every lane loads (a chunk past the data reads x's
+  // first chunk, and its value is replaced by zero when it is staged), so each group is four loads.
+  auto load = [&](int64_t wv, u32x4_t (&v)[4], uint32_t& okm) __attribute__((always_inline)) {
+    const int64_t wu = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(wv >> 32)) << 32) |
+                                 (uint32_t)__builtin_amdgcn_readfirstlane((int)wv));  // wv, in scalar registers
+    const int64_t gb = wu * 64;  // the group's first block
+    const int64_t t0 = gb / nblk;
+    const int r0 = (int)(gb - t0 * nblk);
+    okm = 0;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       const int c = 64 * j + lane;
-      const int64_t gi = g0 + c / 4;
-      const int64_t t = gi / nblk, b = gi % nblk;
-      u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-      if (gi < n && b < hb)
-        v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(x + t * ldx + b * 32 + (c % 4) * 8));
-      *reinterpret_cast<u32x4_t*>(&stage_in[c * 16]) = v;
+      const int loc = r0 + c / 4;          // block index from token t0's first block (< nblk + 64)
+      const int dt = loc / (int)nblk;
+      const int b = loc - dt * (int)nblk;
+      const bool ok = gb + c / 4 < n && b < hb;
+      okm |= ok ? 1u << j : 0u;
+      const uint16_t* src = ok ? x + (t0 + dt) * ldx + b * 32 + (c % 4) * 8 : x;
+      v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src));
     }
+  };
+  u32x4_t cur[4], nxt[4] = {};
+  uint32_t okc = 0, okn = 0;
+  if (wv0 < wv_end) load(wv0, cur, okc);
+  for (int64_t wv = wv0; wv < wv_end; wv += nw) {
+    const int64_t g0 = wv * 64;
+    if (wv + nw < wv_end) load(wv + nw, nxt, okn);
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+      *reinterpret_cast<u32x4_t*>(&stage_in[(64 * j + lane) * 16]) = (okc >> j) & 1u ? cur[j] : u32x4_t{0u, 0u, 0u, 0u};
     __builtin_amdgcn_wave_barrier();  // the wave's LDS writes before its reads (single wave, in order)
     uint32_t w[16];
 #pragma unroll
@@ -110,6 +128,9 @@ MX_DEV void xprep_waves(const uint16_t* __restrict__ x, int64_t ldx, int64_t H, 
         *reinterpret_cast<u32x4_t*>(xq + r0 * REC + c * 16) = *reinterpret_cast<const u32x4_t*>(&stage_out[c * 16]);
     }
     __builtin_amdgcn_wave_barrier();  // the next iteration's LDS writes after these reads
+#pragma unroll
+    for (int j = 0; j < 4; j++) cur[j] = nxt[j];
+    okc = okn;
   }
 }
 
@@ -133,6 +154,16 @@ MX_DEV uint32_t wave_max_u32(uint32_t v) {
   for (int row = 0; row < 4; row++) r = max(r, (uint32_t)__builtin_amdgcn_readlane((int)v, 16 * row));
   return r;
 }
+MX_DEV uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));
+  uint32_t r = 0xFFFFFFFFu;
+#pragma unroll
+  for (int row = 0; row < 4; row++) r = min(r, (uint32_t)__builtin_amdgcn_readlane((int)v, 16 * row));
+  return r;
+}
 MX_DEV float wave_sum_f32(float v) {
   v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
   v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
@@ -146,8 +177,8 @@ MX_DEV float wave_sum_f32(float v) {
 
 // Routing of NT tokens by one wave, their selections interleaved (independent chains): k rounds of a
 // wave-wide maximum of the logit keys, the winner being the lowest expert index holding that key (a
-// ballot per lane slot), so equal logits go to the lower expert index; the winner's logit is read back
-// from its key.  Softmax weights of the selected experts (renormalized over them, or over all experts).
+// wave-wide minimum over the indices of the lanes' slots that hold it), so equal logits go to the lower
+// expert index; the winner's logit is read back from its key.  Softmax weights of the selected experts (renormalized over them, or over all experts).
 // For token i, lane j < k returns pair j's expert and weight.  NPL logits per lane (E <= 64 * NPL).
 template <int NPL, int NT>
 MX_DEV void route_tokens(const float (&val)[NT][NPL], int E, int k, int renormalize, int (&my_id)[NT],
@@ -173,14 +204,19 @@ MX_DEV void route_tokens(const float (&val)[NT][NPL], int E, int k, int renormal
     }
 #pragma unroll
     for (int i = 0; i < NT; i++) best[i] = wave_max_u32(best[i]);
+    uint32_t cand[NT];
 #pragma unroll
     for (int i = 0; i < NT; i++) {
-      int id = -1;
+      cand[i] = 0xFFFFFFFFu;
 #pragma unroll
-      for (int j = 0; j < NPL; j++) {
-        const uint64_t hit = __ballot(key[i][j] == best[i]);
-        if (id < 0 && hit != 0) id = 64 * j + __ffsll((unsigned long long)hit) - 1;
-      }
+      for (int j = NPL - 1; j >= 0; j--)
+        if (key[i][j] == best[i]) cand[i] = (uint32_t)(lane + 64 * j);
+    }
+#pragma unroll
+    for (int i = 0; i < NT; i++) cand[i] = wave_min_u32(cand[i]);
+#pragma unroll
+    for (int i = 0; i < NT; i++) {
+      const int id = (int)cand[i];
       const float wl = key_logit(best[i]);
 #pragma unroll
       for (int j = 0; j < NPL; j++)
@@ -217,6 +253,12 @@ MX_DEV uint32_t row_max_u32(uint32_t v) {
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));
   return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));
 }
+MX_DEV uint32_t row_min_u32(uint32_t v) {
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));
+  return min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));
+}
 MX_DEV float row_sum_f32(float v) {
   v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
   v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
@@ -225,12 +267,12 @@ MX_DEV float row_sum_f32(float v) {
 }
 
 // Routing of four tokens per wave, one per row of 16 lanes (E <= 16 * NPR, k <= 16): the same
-// selection as route_tokens with row-wide reductions -- lane q of a row holds experts q + 16 j, so the
-// first j whose row ballot hits gives the lowest expert index holding the maximum.  For the row's
+// selection as route_tokens with row-wide reductions -- lane q of a row holds experts q + 16 j, and the
+// row minimum of the indices that hold the maximum gives the lowest one.  For the row's
 // token, lane q < k returns pair q's expert and weight.
 template <int NPR>
 MX_DEV void route_rows(const float* val, int E, int k, int renormalize, int& my_id, float& my_w) {
-  const int lane = threadIdx.x & 63, q = lane & 15, row = lane >> 4;
+  const int lane = threadIdx.x & 63, q = lane & 15;
   uint32_t key[NPR];
 #pragma unroll
   for (int j = 0; j < NPR; j++) key[j] = q + 16 * j < E ? logit_key(val[j]) : 0u;
@@ -241,12 +283,11 @@ MX_DEV void route_rows(const float* val, int E, int k, int renormalize, int& my_
 #pragma unroll
     for (int j = 0; j < NPR; j++) best = max(best, key[j]);
     best = row_max_u32(best);
-    int id = -1;
+    uint32_t cand = 0xFFFFFFFFu;
 #pragma unroll
-    for (int j = 0; j < NPR; j++) {
-      const uint32_t hit = (uint32_t)(__ballot(key[j] == best) >> (16 * row)) & 0xFFFFu;
-      if (id < 0 && hit != 0) id = 16 * j + __ffs(hit) - 1;
-    }
+    for (int j = NPR - 1; j >= 0; j--)
+      if (key[j] == best) cand = (uint32_t)(q + 16 * j);
+    const int id = (int)row_min_u32(cand);
     const float wl = key_logit(best);
 #pragma unroll
     for (int j = 0; j < NPR; j++)
@@ -385,26 +426,45 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const float* __res
   route_block<NPL>(logits, T, E, k, renormalize, ids, wts, blkcnt, rank, blockIdx.x, lds);
 }
 
-// The forward pass's front in one launch: workgroups 0 .. nroute - 1 route one token block each, the
-// others split the activations (16 waves each, with their own LDS staging; the routing histogram
-// reuses the same LDS).
+// The forward pass's front in one launch.  When the routing and the split workgroups all fit on the
+// CUs at once (merged = 0), workgroups 0 .. nroute - 1 route one token block each and the others split
+// the activations (16 waves each, with their own LDS staging; the routing histogram reuses the same
+// LDS).  Otherwise (merged = 1) the grid has one workgroup per CU: the first min(nroute, grid) route
+// the blocks dealt to them and then split groups 0 .. gsplit - 1, the others split the rest from the
+// start, so that both kinds finish together.
 template <int AF, int NPL>
 __global__ __launch_bounds__(kRouteThreads) void front_kernel(const uint16_t* __restrict__ x, int64_t ldx, int64_t H,
                                                               int64_t nblk, uint8_t* __restrict__ xq, int64_t n,
                                                               const float* __restrict__ logits, int64_t T, int E, int k,
                                                               int renormalize, int32_t* __restrict__ ids,
                                                               float* __restrict__ wts, int32_t* __restrict__ blkcnt,
-                                                              int32_t* __restrict__ rank, int nroute) {
+                                                              int32_t* __restrict__ rank, int nroute, int merged,
+                                                              int64_t gsplit) {
   constexpr int REC = act_rec(AF), NW = kRouteThreads / 64;
   constexpr int kStage = 4096 > 32 * REC ? 4096 : 32 * REC;  // a wave's staging bytes
   static_assert(NW * kStage >= kRouteLdsInts * 4, "the routing tables fit the staging LDS");
   __shared__ __attribute__((aligned(16))) uint8_t smem[NW * kStage];
+  const int wave = threadIdx.x >> 6;
+  const int64_t ngroups = (n + 63) / 64;
+  if (merged) {
+    const int nr = nroute < (int)gridDim.x ? nroute : (int)gridDim.x;  // workgroups that route
+    for (int b = blockIdx.x; b < nroute; b += gridDim.x) {
+      route_block<NPL>(logits, T, E, k, renormalize, ids, wts, blkcnt, rank, b, reinterpret_cast<int32_t*>(smem));
+      __syncthreads();  // the routing tables' last reads before the LDS holds split stages
+    }
+    if ((int)blockIdx.x < nr)
+      xprep_waves<AF>(x, ldx, H, nblk, xq, n, (int64_t)blockIdx.x * NW + wave, gsplit, (int64_t)nr * NW,
+                      smem + wave * kStage);
+    else
+      xprep_waves<AF>(x, ldx, H, nblk, xq, n, gsplit + (int64_t)(blockIdx.x - nr) * NW + wave, ngroups,
+                      (int64_t)(gridDim.x - nr) * NW, smem + wave * kStage);
+    return;
+  }
   if ((int)blockIdx.x < nroute) {
     route_block<NPL>(logits, T, E, k, renormalize, ids, wts, blkcnt, rank, blockIdx.x, reinterpret_cast<int32_t*>(smem));
     return;
   }
-  const int wave = threadIdx.x >> 6;
-  xprep_waves<AF>(x, ldx, H, nblk, xq, n, (int64_t)(blockIdx.x - nroute) * NW + wave,
+  xprep_waves<AF>(x, ldx, H, nblk, xq, n, (int64_t)(blockIdx.x - nroute) * NW + wave, ngroups,
                   (int64_t)(gridDim.x - nroute) * NW, smem + wave * kStage);
 }
 
@@ -570,12 +630,23 @@ void launch_front_af(const void* x, int64_t T, int64_t ldx, const MoeGeom& g, vo
   const int64_t nblk = 2 * g.nkt1;
   const int64_t n = T * nblk;
   const int nroute = (int)cdiv(T, kRouteTokens);
-  int64_t nx = cdiv(cdiv(n, 64), kRouteThreads / 64);  // split workgroups: one wave per 64 blocks
-  if (nx > 65536) nx = 65536;
-  const dim3 grid((unsigned)(nroute + nx)), block(kRouteThreads);
+  // Split workgroups: one wave per group of 64 blocks when they fit beside the routing workgroups on
+  // the CUs at once (one 1024-thread workgroup per CU).  Otherwise one workgroup per CU; a routing
+  // workgroup's waves then take fewer groups, the routing of a block costing about NPL / 2 groups.
+  constexpr int kCus = 256, NW = kRouteThreads / 64;
+  const int64_t ngroups = cdiv(n, 64);
+  const int64_t nx = cdiv(ngroups, NW);
+  const int merged = nroute + nx > kCus ? 1 : 0;
+  int64_t gsplit = ngroups;
+  if (merged && nroute < kCus) {
+    const int64_t avg = ngroups / (kCus * NW);           // groups per wave, all waves alike
+    const int64_t per = avg - route_npl(E) / 2;          // per routing wave
+    gsplit = per > 0 ? (int64_t)nroute * NW * per : 0;
+  }
+  const dim3 grid((unsigned)(merged ? kCus : nroute + nx)), block(kRouteThreads);
 #define MX_FRONT(NPL)                                                                                                   \
   hipLaunchKernelGGL((front_kernel<AF, NPL>), grid, block, 0, stream, (const uint16_t*)x, ldx, g.H, nblk, (uint8_t*)xq, n, \
-                     logits, T, E, k, renormalize, ids, w, blkcnt, rank, nroute)
+                     logits, T, E, k, renormalize, ids, w, blkcnt, rank, nroute, merged, gsplit)
   switch (route_npl(E)) {
     case 1: MX_FRONT(1); break;
     case 2: MX_FRONT(2); break;
