@@ -404,6 +404,7 @@ MX_DEV void g1_epilogue_pair(const f32x16_t& g0, const f32x16_t& u0, const f32x1
 // table of its token indices, which one copy per wave brings into LDS at the start of the current item.
 template <int NX, int NXS>
 struct ItemSrc {
+  int prow0, nrows; // the item's tile: first padded row and rows of its expert (read with the sources)
   int64_t wb;       // byte offset of this wave's first weight piece of step 0 (uniform)
   int64_t wsb;      // byte offset of this wave's quarter of the step-0 scale records (uniform)
   uint32_t x[NX];   // byte offsets of this lane's activation copies of step 0
@@ -455,6 +456,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
     const int tile = item / nx, x = item % nx;
     const TileDesc td = a.tiles[tile];
     const int e = td.e, prow0 = td.prow0;
+    sr.prow0 = prow0;
+    sr.nrows = td.nrows;
     const int cb = x * NT / kCB, jj0 = (x * NT) % kCB;
     const int64_t wstep0 = (int64_t)(e * ncb + cb) * nkt;
     sr.wb = wstep0 * (kCB * 1024) + (jj0 + wave * C::nW) * 1024;
@@ -572,8 +575,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
   auto load_x = [&](const uint8_t* base, int r, auto pc) __attribute__((always_inline)) {
     constexpr int P = LATE ? 0 : decltype(pc)::value;
     // first GEMM: lane l takes block l / 32 of row l % 32's record; second: slot l of the row group
-    lds_u8 rec = (lds_u8)(base + C::oX + (wr * RW + r) * (32 * C::REC) + (lane & 31) * C::REC);
-    lds_u8 rgb = (lds_u8)(base + C::oX + (wr * RW + r) * C::kXRG);  // second GEMM: the row group's slots
+    lds_u8 rec = (lds_u8)(base + C::oX + (wr + WR * r) * (32 * C::REC) + (lane & 31) * C::REC);
+    lds_u8 rgb = (lds_u8)(base + C::oX + (wr + WR * r) * C::kXRG);  // second GEMM: the row group's slots
     // Byte O of this lane's slot: in its record (first GEMM), or in the region order of the row group's
     // slots (second GEMM: region [R, R + n) of slot L at 64 * R + n * L)
     auto at = [&](auto oc) __attribute__((always_inline)) {
@@ -620,7 +623,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
     if constexpr (G1)
       xsc[P][r] = *(lds4_p)(rec + 2 * C::SLOT + (lane >> 5) * 4);
     else
-      xsc[P][r] = *(lds4_p)(lds_u8)(base + C::oXS + (wr * RW + r) * 256 + lane * 4);
+      xsc[P][r] = *(lds4_p)(lds_u8)(base + C::oXS + (wr + WR * r) * 256 + lane * 4);
   };
   auto load_w = [&](const uint8_t* base, int j) __attribute__((always_inline)) {
     w[j] = *(lds16_p)(lds_u8)(base + C::oW + (wc * CW + j) * 1024 + lane * 16);
@@ -635,11 +638,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
   // MFMA m of a step (the order of StepPlan).  Each is pinned by an ordered use of its accumulator:
   // the MFMAs are pure, and the compiler would otherwise sink them past later waits and barriers
   // (across basic blocks, where scheduling barriers do not reach).
-  auto mfma_one = [&](auto mc, auto pc) __attribute__((always_inline)) {
+  auto mfma_one = [&](auto mc, auto pc, auto rac) __attribute__((always_inline)) {
     constexpr int m = decltype(mc)::value, P = LATE ? 0 : decltype(pc)::value;
     constexpr int g = m / Plan::PG, u = m % Plan::PG;
     constexpr int t = u / (2 * RW), r = (u % (2 * RW)) / 2, j = 2 * g + (u % 2);
     constexpr int BFMT = act_term_fmt(AF, t);
+    if constexpr (r >= decltype(rac)::value) return;  // a row group of padding rows only
     const i32x8_t wo = i32x8_t{(int)w[j][0], (int)w[j][1], (int)w[j][2], (int)w[j][3], 0, 0, 0, 0};
     acc[r][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wo, xop[P][r][t], acc[r][j], kFmtFp4, BFMT, j & 3,
                                                                 wsc[P][j >> 2], t, xsc[P][r]);
@@ -672,9 +676,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
     if (s < nkt) issue(cur, s, s);
 
   while (true) {
-    const int tile = item / nx, x = item % nx;
-    const TileDesc td = a.tiles[tile];
-    const int prow0 = td.prow0, nrows = td.nrows;
+    const int x = item % nx;
+    const int prow0 = cur.prow0, nrows = cur.nrows;  // cur is rebuilt for the next item before the epilogue
     jj0 = (x * NT) % kCB;
     const bool has_next = q + 1 < nq;
     const int tb = q & 1;
@@ -685,10 +688,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
     wait_stages(nkt - 1, std::integral_constant<int, D - 2>{});
     block_sync();
     if (has_next) issue_tab(item_of(q + 1), tb ^ 1);
+    // The K loop for this wave's RA row groups that hold pairs (row group wr + WR r, r < RA; the rest
+    // hold padding rows only and get no MFMAs and no fragment loads): every wave issues the same
+    // copies and barriers whatever its RA.
+    static_assert(RW == 1 || RW == 2, "one or two row groups per wave");
+    auto kloop = [&](auto rac) __attribute__((always_inline)) {
+    constexpr int RA = decltype(rac)::value;
     {
       const uint8_t* b0 = smem;
 #pragma unroll
-      for (int r = 0; r < RW; r++) load_x(b0, r, std::integral_constant<int, 0>{});
+      for (int r = 0; r < RA; r++) load_x(b0, r, std::integral_constant<int, 0>{});
 #pragma unroll
       for (int j = 0; j < (LATE ? CW : CW - 2); j++) load_w(b0, j);
       load_ws(b0, std::integral_constant<int, 0>{});
@@ -727,7 +736,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
       }
       static_for<0, Plan::NM>([&](auto mi) __attribute__((always_inline)) {
         constexpr int m = decltype(mi)::value;
-        mfma_one(mi, pc);
+        mfma_one(mi, pc, rac);
         static_for<0, Plan::kCap>([&](auto ci) __attribute__((always_inline)) {
           constexpr int task = plan.t[m][decltype(ci)::value];
           if constexpr (task >= StepTask::kDma) {
@@ -737,7 +746,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
           } else if constexpr (task == StepTask::kWs) {
             load_ws(nb, std::integral_constant<int, 1 - P>{});
           } else if constexpr (task >= StepTask::kX) {
-            load_x(nb, task - StepTask::kX, std::integral_constant<int, 1 - P>{});
+            if constexpr (task - StepTask::kX < RA) load_x(nb, task - StepTask::kX, std::integral_constant<int, 1 - P>{});
           } else if constexpr (task >= StepTask::kDef) {
             load_w(cb, CW - 2 + task - StepTask::kDef);
           }
@@ -758,7 +767,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
           block_sync();
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int r = 0; r < RW; r++) load_x(nb, r, std::integral_constant<int, 1 - P>{});
+          for (int r = 0; r < RA; r++) load_x(nb, r, std::integral_constant<int, 1 - P>{});
 #pragma unroll
           for (int j = 0; j < CW; j++) load_w(nb, j);
           load_ws(nb, std::integral_constant<int, 1 - P>{});
@@ -778,6 +787,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
       step(kt + 1, std::integral_constant<int, 1>{}, std::false_type{});
     }
     if (kt < nkt) step(kt, std::integral_constant<int, 0>{}, std::false_type{});
+    };
+    {
+      const int nreal = (nrows + 31) >> 5;  // row groups holding pairs
+      if constexpr (RW == 2) {
+        if (wr + WR < nreal)
+          kloop(std::integral_constant<int, 2>{});
+        else if (wr < nreal)
+          kloop(std::integral_constant<int, 1>{});
+        else
+          kloop(std::integral_constant<int, 0>{});
+      } else {
+        if (wr < nreal)
+          kloop(std::integral_constant<int, RW>{});
+        else
+          kloop(std::integral_constant<int, 0>{});
+      }
+    }
 
     // ---- next item's first D - 1 stages go out before this item's epilogue, so their latency hides
     // under it.  make_src reads the next item's token table, whose copy went out at this item's start:
@@ -799,7 +825,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
     if constexpr (G1) {
 #pragma unroll
       for (int r = 0; r < RW; r++) {
-        const int rgl = wr * RW + r;
+        const int rgl = wr + WR * r;
         if (rgl * 32 >= nrows) continue;
 #pragma unroll
         for (int p = 0; p < CW / 4; p++) {
@@ -847,7 +873,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC))) void
         uint16_t* const obase = DENSE ? a.ydense : a.o16;
 #pragma unroll
         for (int r = 0; r < RW; r++) {
-          const int rgl = wr * RW + r;
+          const int rgl = wr + WR * r;
           if (rgl * 32 >= nrows) continue;
           const float wt = __builtin_bit_cast(float, t_row[tb][rgl * 32 + m]);
           const int64_t prow_rg = prow0 + rgl * 32;
