@@ -5,8 +5,8 @@
 namespace {
 
 // y[t] = sum over the token's k pairs of the int16 rows (times their block powers of two), fp32 sum in
-// slot order, bf16 output.  One thread per 8 output columns of a token; the rows of four pairs are
-// loaded before any is added, so four gathers per thread are in flight.
+// slot order, bf16 output.  One thread per 8 output columns of a token; the rows of eight (then four)
+// pairs are loaded before any is added, so that many gathers per thread are in flight.
 MX_DEV void combine_add(float* s, const u32x4_t& v, int ex) {
   const float f = __builtin_ldexpf(1.0f, ex);  // exact power of two (ex in [-127, 127])
 #pragma unroll
@@ -24,6 +24,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
     const int64_t t = i / H8, c = (i - t * H8) * 8;
     float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     int j = 0;
+    for (; j + 8 <= k; j += 8) {
+      u32x4_t v[8];
+      int ex[8];
+#pragma unroll
+      for (int u = 0; u < 8; u++) {
+        const int64_t r = pair_prow[t * k + j + u];
+        v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(o16 + r * H + c));
+        ex[u] = (int)osc[r * (H / 16) + c / 16] - 127;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; u++) combine_add(s, v[u], ex[u]);
+    }
     for (; j + 4 <= k; j += 4) {
       u32x4_t v[4];
       int ex[4];
