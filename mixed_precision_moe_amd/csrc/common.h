@@ -85,30 +85,62 @@ MX_DEV uint32_t amax_bits32(const uint32_t* w) {  // 16 words = 32 bf16 -> large
   return m;
 }
 
-typedef float xf32x2_t __attribute__((ext_vector_type(2)));
 typedef short xs16x2_t __attribute__((ext_vector_type(2)));
 
-MX_DEV bf16x32_t as_bf16x32(const uint32_t* w) {
-  bf16x32_t v;
-#pragma unroll
-  for (int j = 0; j < 16; j++) {
-    const bf16x2_t two = __builtin_bit_cast(bf16x2_t, w[j]);
-    v[2 * j] = two[0];
-    v[2 * j + 1] = two[1];
-  }
-  return v;
-}
 
-// w[j] (elements 2j, 2j + 1) -= the dequantized E2M3 codes, exactly, in bf16 (a code times its power-of-two
-// scale has four significant bits, so the dequantized values are exact in bf16, and so is each difference)
-MX_DEV void sub_fp6(uint32_t* w, const fp6x32_t& codes, float sc) {
-  const auto deq = __builtin_bit_cast(u32x16_t, __builtin_amdgcn_cvt_scalef32_pk32_bf16_fp6(codes, sc));
+// The three terms of a bf16 block (w[j]: elements 2j, 2j + 1) into slot[0..15] (E2M3 codes of t0 and
+// t1, six dwords each, then the 16 bytes of E2M1 codes of t2, element i at code i), returning the
+// scale dword (e0 | e1 << 8 | e2 << 16).  The block is held as its even (ev) and odd (od) elements in
+// binary32, where every value involved is exact: a bf16 value, an E2M3 code times its power-of-two
+// scale (four significant bits) and each remainder, which is again exact in bf16.  So the split is the
+// one bf16 arithmetic gives, with no conversion back to bf16 between the terms.
+MX_DEV uint32_t split3_bf16(const uint32_t* w, uint32_t* slot) {
+  f32x16_t ev, od;
 #pragma unroll
   for (int j = 0; j < 16; j++) {
-    const float a = bf16_bits_to_f32(w[j] & 0xFFFFu) - bf16_bits_to_f32(deq[j] & 0xFFFFu);
-    const float c = bf16_bits_to_f32(w[j] >> 16) - bf16_bits_to_f32(deq[j] >> 16);
-    w[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector((xf32x2_t){a, c}, bf16x2_t));
+    ev[j] = __uint_as_float(w[j] << 16);
+    od[j] = __uint_as_float(w[j] & 0xFFFF0000u);
   }
+  // block maximum of magnitudes (four independent chains) -> E8M0 scale (the 0.75 round-up rule)
+  auto scale_of = [&]() __attribute__((always_inline)) {
+    float m4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 16; j++) m4[j & 3] = fmaxf(fmaxf(m4[j & 3], fabsf(ev[j])), fabsf(od[j]));
+    return e8m0_from_amax_bits(__float_as_uint(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))));
+  };
+  uint32_t scales = 0;
+#pragma unroll
+  for (int term = 0; term < 2; term++) {
+    const uint32_t e = scale_of();
+    scales |= e << (8 * term);
+    const float sv = e8m0_as_scale_operand(e);
+    // code 2j <- ev[j], code 2j + 1 <- od[j].  The conversion reads its sources over several passes
+    // while it writes its six result registers, so the result must not share a register with a
+    // source: the instruction is issued with an early-clobber output.
+    fp6x32_t codes;
+    asm("v_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, %3" : "=&v"(codes) : "v"(ev), "v"(od), "v"(sv));
+#pragma unroll
+    for (int d = 0; d < 6; d++) slot[6 * term + d] = codes[d];
+    // the dequantized term in bf16 (exact), pairs (2j, 2j + 1) per word: half the registers of binary32
+    const auto deq = __builtin_bit_cast(u32x16_t, __builtin_amdgcn_cvt_scalef32_pk32_bf16_fp6(codes, sv));
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+      ev[j] = ev[j] - __uint_as_float(deq[j] << 16);
+      od[j] = od[j] - __uint_as_float(deq[j] & 0xFFFF0000u);
+    }
+  }
+  const uint32_t e2 = scale_of();
+  const float sv = e8m0_as_scale_operand(e2);
+#pragma unroll
+  for (int d = 0; d < 4; d++) {
+    uint32_t p = 0;
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, ev[4 * d], od[4 * d], sv, 0);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, ev[4 * d + 1], od[4 * d + 1], sv, 1);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, ev[4 * d + 2], od[4 * d + 2], sv, 2);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, ev[4 * d + 3], od[4 * d + 3], sv, 3);
+    slot[12 + d] = p;
+  }
+  return scales | (e2 << 16);
 }
 
 // 32 bf16 (w[j]: elements 2j, 2j + 1) -> E2M1 codes, element i in nibble i of the 16 bytes

@@ -50,24 +50,12 @@ __global__ __launch_bounds__(256) void linear_prep_kernel(const uint16_t* __rest
     uint32_t w[16];
 #pragma unroll
     for (int j = 0; j < 16; j++) w[j] = src[w2_perm(2 * j) / 2];
-    const uint32_t e0 = e8m0_from_amax_bits(amax_bits32(w) << 16);
-    const fp6x32_t t0 = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(as_bf16x32(w), e8m0_as_scale_operand(e0));
-    sub_fp6(w, t0, e8m0_as_scale_operand(e0));
-    const uint32_t e1 = e8m0_from_amax_bits(amax_bits32(w) << 16);
-    const fp6x32_t t1 = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(as_bf16x32(w), e8m0_as_scale_operand(e1));
-    sub_fp6(w, t1, e8m0_as_scale_operand(e1));
-    const uint32_t e2 = e8m0_from_amax_bits(amax_bits32(w) << 16);
     uint32_t slot[SLOT / 4];
-#pragma unroll
-    for (int d = 0; d < 6; d++) {
-      slot[d] = t0[d];
-      slot[6 + d] = t1[d];
-    }
-    fp4_from_bf16(w, e8m0_as_scale_operand(e2), slot + 12);
+    const uint32_t scales = split3_bf16(w, slot);
     const int64_t blk = rg * nkt + b / 2;
     const int L = (int)((b & 1) * 32 + rlo);
     store_slot<kActBf16>(actq + blk * 64 * SLOT, L, slot);
-    acts[blk * 64 + L] = e0 | (e1 << 8) | (e2 << 16);
+    acts[blk * 64 + L] = scales;
   }
 }
 

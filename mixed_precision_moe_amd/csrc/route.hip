@@ -85,20 +85,7 @@ MX_DEV void xprep_waves(const uint16_t* __restrict__ x, int64_t ldx, int64_t H, 
     uint32_t slot[SLOT / 4];
     uint32_t scales;
     if constexpr (AF == kActBf16) {
-      const uint32_t e0 = e8m0_from_amax_bits(amax_bits32(w) << 16);
-      const fp6x32_t t0 = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(as_bf16x32(w), e8m0_as_scale_operand(e0));
-      sub_fp6(w, t0, e8m0_as_scale_operand(e0));
-      const uint32_t e1 = e8m0_from_amax_bits(amax_bits32(w) << 16);
-      const fp6x32_t t1 = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(as_bf16x32(w), e8m0_as_scale_operand(e1));
-      sub_fp6(w, t1, e8m0_as_scale_operand(e1));
-      const uint32_t e2 = e8m0_from_amax_bits(amax_bits32(w) << 16);
-#pragma unroll
-      for (int d = 0; d < 6; d++) {
-        slot[d] = t0[d];
-        slot[6 + d] = t1[d];
-      }
-      fp4_from_bf16(w, e8m0_as_scale_operand(e2), slot + 12);
-      scales = e0 | (e1 << 8) | (e2 << 16);
+      scales = split3_bf16(w, slot);
     } else if constexpr (AF == kActMxfp8) {
       const uint32_t e = e8m0_e4m3_from_amax_bits(amax_bits32(w) << 16);
       fp8_from_bf16(w, e8m0_as_scale_operand(e), slot);
