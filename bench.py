@@ -26,6 +26,7 @@ import argparse
 import ctypes
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -194,12 +195,33 @@ class HipEvents:
             self.hip.hipEventDestroy(h)
 
 
+# After the warm-up steps, each timed workload first runs about this much more of the same work: the
+# GPU's clock takes a few milliseconds of load to settle (from idle the prefill step runs 0.65-0.82 ms
+# for its first ~15 steps, then 0.61-0.62 ms), and the timed steps measure the sustained rate.
+SETTLE_MS = 50.0
+
+
+def settle(run_one):
+    """Runs `run_one()` for about SETTLE_MS of GPU time; returns how many times it ran."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run_one()
+    torch.cuda.synchronize()
+    one_ms = max((time.perf_counter() - t0) * 1e3, 1e-3)
+    n = int(math.ceil(SETTLE_MS / one_ms))
+    for _ in range(n):
+        run_one()
+    return n + 1
+
+
 def time_moe(b, steps, warmup):
     """Wall-clock ms per step over `steps` back-to-back steps (synchronized on both sides), the mean
     device time of each stage, and the median device time of a whole step (from the events the
-    library records on its stream at the stage boundaries)."""
+    library records on its stream at the stage boundaries).  The warm-up steps and the settling steps
+    (b.settle_steps) run before, untimed."""
     for _ in range(warmup):
         b.step()
+    b.settle_steps = settle(b.step)
     ns = len(STAGES) + 1
     evs = HipEvents(steps * ns)
     torch.cuda.synchronize()
@@ -226,7 +248,13 @@ def time_launches(one, n, warmup):
         one(i)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    one(0)
+    torch.cuda.synchronize()
+    nsettle = int(math.ceil(SETTLE_MS / max((time.perf_counter() - t0) * 1e3, 1e-3)))
     torch.cuda._sleep(20_000_000)
+    for i in range(nsettle):  # queued behind the sleep, run just before the timed launches
+        one(i)
     ev[0].record()
     for i in range(n):
         one(i)
@@ -315,7 +343,7 @@ def bench_linear(steps, warmup, M=8192, N=7168, K=7168):
 def moe_result(b, name, ms, stages, median_ms, iters):
     cfg = b.cfg
     return {"workload": name, "T": cfg.T, "E": cfg.E, "top_k": cfg.k, "H": cfg.H, "I": cfg.I, "bias": cfg.bias,
-            "iterations": iters, "ms": ms, "device_ms_median": median_ms,
+            "iterations": iters, "settle_steps": getattr(b, "settle_steps", 0), "ms": ms, "device_ms_median": median_ms,
             "stages_ms": {n: float(v) for n, v in zip(STAGES, stages)},
             "TFLOP_s": moe_flops(cfg) / (ms * 1e-3) / 1e12}
 
@@ -380,6 +408,7 @@ def run_prefill(args):
     b = MoeBench(cfg, rotations=2)
     log("[bench] timing prefill MoE")
     ms, stages, med = time_moe(b, args.steps, args.warmup)
+    b.prefill_settle_steps = b.settle_steps
     o = b.outputs()
     load = b.expert_load()
     variants = {}
@@ -552,6 +581,9 @@ def main():
         "config": {"workload": "prefill-shaped MXFP4 MoE layer, bf16 tokens", "T": cfg.T, "E": cfg.E, "top_k": cfg.k,
                    "H": cfg.H, "I": cfg.I, "bias": cfg.bias, "parallelism": "single GPU"},
         "roofline": roofline,
+        "settle_steps": b.prefill_settle_steps,
+        "timing": f"{args.steps} steps timed after {args.warmup} warm-up steps and {b.prefill_settle_steps} settling steps "
+                  f"(about {SETTLE_MS:g} ms of the same work, while the GPU clock settles under load)",
         "device_ms_median": med,
         "stages_ms": {n: float(v) for n, v in zip(STAGES, stages)},
         "layer_frac_of_fp4_peak": value / PEAK_FP4_TFLOPS,
